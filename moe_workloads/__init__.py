@@ -1,0 +1,267 @@
+"""Seeded synthetic workloads for the routed MoE feed-forward layer.
+
+This module only *makes inputs*: it draws seeded random tensors with the
+shapes and value distributions of the five layer configurations and encodes
+them in their storage format (bf16 bit patterns or fp32).  It holds none of
+the layer's arithmetic (no router, no top-k, no sort, no projection), so both
+the CPU oracle and the GPU path can take their inputs from here without
+sharing any part of the method.
+
+Workloads (shapes follow the article "Mixture of Experts (MoEs) in
+Transformers", sections "From Dense to Sparse" and "Weight Loading Refactor":
+gpt-oss-20b uses 4 of 32 experts, DeepSeek-V3 stores 256 experts per layer):
+
+  c1      tiny fp32       T=64     d=128  f=256   E=8   k=2  softmax
+  c2      Mixtral-shaped  T=4096   d=4096 f=14336 E=8   k=2  softmax
+  c3_tN   gpt-oss-shaped  T=N      d=2880 f=2880  E=32  k=4  softmax  (decode)
+  c4      fine-grained    T=8192   d=2048 f=768   E=128 k=8  softmax  Zipf(1.1)
+  c5      DeepSeek-shaped T=16384  d=7168 f=2048  E=256 k=8  sigmoid  Zipf(1.0)
+                                                        + shared expert f_s=2048
+
+Storage layout (the packed per-layer expert tensors the article's weight
+loading produces, see its "Dynamic Weight Loading with WeightConverter"
+subsection):
+
+  x          [T, d]          hidden states, ~N(0, 1)
+  w_router   [E, d]          router projection, ~N(0, 0.02); the scaled-down shapes
+                             use 0.02*sqrt(d_full/d) so their logits keep the
+                             full-size spread against the Zipf bias
+  bias       [E] fp32/None   router logit bias (Zipf popularity prior)
+  w_gate_up  [E, 2f, d]      rows [0, f) = gate, rows [f, 2f) = up, ~N(0, 0.02)
+  w_down     [E, d, f]       ~N(0, 0.02)
+  shared     ([1, 2f_s, d], [1, d, f_s]) or None
+
+Seeds: every tensor (and every expert of a packed tensor) has its own PCG64
+stream keyed by (workload seed, tensor id, expert id), so any one expert can
+be regenerated alone and experts can be generated in parallel threads.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+# tensor ids for the seed key
+_X, _WR, _BIASPERM, _WGU, _WD, _SGU, _SD, _LOGITS = 0, 1, 2, 3, 4, 5, 6, 7
+
+WEIGHT_STD = 0.02
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    d: int
+    f: int
+    E: int
+    k: int
+    score: str            # "softmax" | "sigmoid"
+    dtype: str            # "f32" | "bf16"
+    zipf_s: Optional[float] = None
+    f_shared: int = 0
+    seed: int = 0
+    router_std: float = 0.02   # scaled-down shapes raise it to keep the full-size logit spread
+
+    @property
+    def P(self) -> int:
+        """Routed (token, slot) pairs."""
+        return self.T * self.k
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    "c1": Workload("c1", 64, 128, 256, 8, 2, "softmax", "f32", seed=1),
+    "c2": Workload("c2", 4096, 4096, 14336, 8, 2, "softmax", "bf16", seed=2),
+    "c3_t1": Workload("c3_t1", 1, 2880, 2880, 32, 4, "softmax", "bf16", seed=31),
+    "c3_t8": Workload("c3_t8", 8, 2880, 2880, 32, 4, "softmax", "bf16", seed=38),
+    "c3_t32": Workload("c3_t32", 32, 2880, 2880, 32, 4, "softmax", "bf16", seed=332),
+    "c3_t64": Workload("c3_t64", 64, 2880, 2880, 32, 4, "softmax", "bf16", seed=364),
+    "c4": Workload("c4", 8192, 2048, 768, 128, 8, "softmax", "bf16", zipf_s=1.1, seed=4),
+    "c5": Workload("c5", 16384, 7168, 2048, 256, 8, "sigmoid", "bf16", zipf_s=1.0,
+                   f_shared=2048, seed=5),
+}
+
+# Scaled-down shapes of the same families: small enough for the oracle to
+# finish in seconds, large enough to span several GEMM tiles and leave a
+# ragged tail in every tiled dimension that the layer allows to be ragged
+# (T and the per-expert row counts).
+SMALL_WORKLOADS = {
+    "c1": WORKLOADS["c1"],
+    "c2s": Workload("c2s", 333, 512, 768, 8, 2, "softmax", "bf16", seed=102,
+                    router_std=0.02 * (4096 / 512) ** 0.5),
+    "c3s_t1": Workload("c3s_t1", 1, 576, 640, 32, 4, "softmax", "bf16", seed=131,
+                       router_std=0.02 * (2880 / 576) ** 0.5),
+    "c3s_t37": Workload("c3s_t37", 37, 576, 640, 32, 4, "softmax", "bf16", seed=137,
+                        router_std=0.02 * (2880 / 576) ** 0.5),
+    "c4s": Workload("c4s", 517, 256, 192, 128, 8, "softmax", "bf16", zipf_s=1.1, seed=104,
+                    router_std=0.02 * (2048 / 256) ** 0.5),
+    "c5s": Workload("c5s", 301, 448, 128, 256, 8, "sigmoid", "bf16", zipf_s=1.0,
+                    f_shared=192, seed=105, router_std=0.02 * (7168 / 448) ** 0.5),
+}
+
+
+def get(name: str) -> Workload:
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    return SMALL_WORKLOADS[name]
+
+
+# ---------------------------------------------------------------- encodings
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even.
+
+    Inputs are finite normal random draws, so NaN/Inf handling is not needed.
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    tmp = np.right_shift(u, 16)
+    np.bitwise_and(tmp, 1, out=tmp)
+    tmp += np.uint32(0x7FFF)
+    tmp += u
+    tmp >>= 16
+    return tmp.astype(np.uint16)
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> the exact fp32 values they encode."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def values(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage array -> the exact values it encodes, as float64."""
+    if dtype == "bf16":
+        return bf16_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def _encode(a32: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits(a32) if dtype == "bf16" else np.ascontiguousarray(a32, np.float32)
+
+
+def _rng(wl: Workload, tensor: int, idx: int = 0) -> np.random.Generator:
+    return np.random.default_rng([wl.seed, tensor, idx])
+
+
+def _normal(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    a = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return a
+
+
+# ---------------------------------------------------------------- tensors
+
+def gen_x(wl: Workload, T: Optional[int] = None) -> np.ndarray:
+    """Hidden states [T, d] ~ N(0, 1) in storage format."""
+    T = wl.T if T is None else T
+    return _encode(_normal(_rng(wl, _X), (T, wl.d), 1.0), wl.dtype)
+
+
+def gen_router(wl: Workload):
+    """(w_router [E, d] in storage format, bias [E] fp32 or None).
+
+    With a Zipf exponent s, expert e gets the log-prior bias ln p_r with
+    p_r = r^-s / sum_{r'=1..E} r'^-s, where r = rank(e) is a seeded
+    permutation of 1..E.  This skews expert popularity toward a Zipf law
+    (the realised load is reported, not tuned).
+    """
+    w = _encode(_normal(_rng(wl, _WR), (wl.E, wl.d), wl.router_std), wl.dtype)
+    if wl.zipf_s is None:
+        return w, None
+    ranks = _rng(wl, _BIASPERM).permutation(wl.E) + 1
+    r = np.arange(1, wl.E + 1, dtype=np.float64)
+    p = r ** (-wl.zipf_s)
+    p /= p.sum()
+    bias = np.log(p[ranks - 1]).astype(np.float32)
+    return w, bias
+
+
+def gen_expert(wl: Workload, e: int):
+    """(w_gate_up[e] [2f, d], w_down[e] [d, f]) in storage format."""
+    gu = _encode(_normal(_rng(wl, _WGU, e), (2 * wl.f, wl.d), WEIGHT_STD), wl.dtype)
+    dn = _encode(_normal(_rng(wl, _WD, e), (wl.d, wl.f), WEIGHT_STD), wl.dtype)
+    return gu, dn
+
+
+def gen_shared(wl: Workload):
+    """Shared expert ([1, 2f_s, d], [1, d, f_s]) in storage format, or None."""
+    if not wl.f_shared:
+        return None
+    fs = wl.f_shared
+    gu = _encode(_normal(_rng(wl, _SGU), (1, 2 * fs, wl.d), WEIGHT_STD), wl.dtype)
+    dn = _encode(_normal(_rng(wl, _SD), (1, wl.d, fs), WEIGHT_STD), wl.dtype)
+    return gu, dn
+
+
+def default_threads() -> int:
+    n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def iter_experts(wl: Workload, experts=None, threads: Optional[int] = None):
+    """Yield (e, w_gate_up[e], w_down[e]) in expert order, generated in a
+    thread pool (numpy's generators release the GIL while filling)."""
+    experts = list(range(wl.E)) if experts is None else list(experts)
+    threads = threads or default_threads()
+    with ThreadPoolExecutor(threads) as ex:
+        window = 2 * threads
+        futs = {}
+        for i, e in enumerate(experts):
+            futs[i] = ex.submit(gen_expert, wl, e)
+            if i >= window:
+                j = i - window
+                yield (experts[j],) + futs.pop(j).result()
+        for j in sorted(futs):
+            yield (experts[j],) + futs[j].result()
+
+
+def gen_all_experts(wl: Workload, threads: Optional[int] = None):
+    """Packed (w_gate_up [E, 2f, d], w_down [E, d, f]) in storage format."""
+    sdt = np.uint16 if wl.dtype == "bf16" else np.float32
+    gu = np.empty((wl.E, 2 * wl.f, wl.d), sdt)
+    dn = np.empty((wl.E, wl.d, wl.f), sdt)
+    for e, g, w in iter_experts(wl, threads=threads):
+        gu[e] = g
+        dn[e] = w
+    return gu, dn
+
+
+# ---------------------------------------------------------------- test data
+
+def gen_tied_logits(T: int, E: int, seed: int, levels: int = 6) -> np.ndarray:
+    """fp32 logits [T, E] drawn from a few discrete levels, so that most rows
+    hold exact ties (for checking the lowest-index tie rule bit-exactly)."""
+    rng = np.random.default_rng([seed, _LOGITS])
+    lv = rng.integers(0, levels, size=(T, E)).astype(np.float32)
+    return (lv * np.float32(0.5) - np.float32(1.0)).astype(np.float32)
+
+
+def gen_logits(T: int, E: int, seed: int, std: float = 1.5) -> np.ndarray:
+    """Continuous fp32 logits [T, E] ~ N(0, std)."""
+    rng = np.random.default_rng([seed, _LOGITS, 1])
+    return _normal(rng, (T, E), std)
+
+
+def gen_ids(T: int, E: int, k: int, seed: int, zipf_s: Optional[float] = None) -> np.ndarray:
+    """A valid routing table [T, k] int32: k distinct experts per token,
+    drawn uniformly or with Zipf popularity (for permutation tests that do
+    not go through the router)."""
+    rng = np.random.default_rng([seed, _LOGITS, 2])
+    if zipf_s is None:
+        p = np.full(E, 1.0 / E)
+    else:
+        p = np.arange(1, E + 1, dtype=np.float64) ** (-zipf_s)
+        p /= p.sum()
+    out = np.empty((T, k), np.int32)
+    for t in range(T):
+        out[t] = rng.choice(E, size=k, replace=False, p=p)
+    return out
