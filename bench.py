@@ -1,0 +1,290 @@
+"""Benchmark of the routed MoE FFN layer (libmoe) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+A step is one pass of the whole layer -- router logits + top-k, sort by
+expert, grouped gate/up + SwiGLU, grouped down projection, (shared expert),
+weighted combine -- over one resident batch of synthetic inputs.  Prints
+one JSON line: layer tokens/s for the workload, the roofline position of
+its dominant kernel (timed with HIP events on the launch stream), and the
+CPU oracle timed on a bounded sample of the same workload.
+
+The default workload is the Mixtral-shaped prefill layer (T=4096, d=4096,
+f=14336, E=8, top-2, bf16).  The other workloads (c3_t1 ... c3_t64 decode,
+c4, c5) can be selected with --workload; decode workloads evict the caches
+between steps and are timed per step with events.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import moe_workloads as W  # noqa: E402
+
+METRIC = "MoE layer tokens/s + % peak bf16 MFMA (prefill) / % peak HBM GB/s (decode)"
+
+# MI355X published peaks (dense, no sparsity)
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+
+KERNEL_SOURCES = {
+    "gateup": ["gemm_bf16.hip", "grouped_gemm.h", "common.h"],
+    "decode_gateup": ["decode.hip", "common.h"],
+}
+
+
+# ------------------------------------------------------------ accounting
+
+def decode_tokens_per_s(bandwidth_bytes_per_s: float, active_params: float, bytes_per_param: float) -> float:
+    """Bandwidth model of decode speed: every generated token reads every
+    active parameter once, so tokens/s ~ bandwidth / (active params x bytes
+    per param)."""
+    return bandwidth_bytes_per_s / (active_params * bytes_per_param)
+
+
+def layer_flops(wl) -> float:
+    """Algorithmic FLOPs of one layer call: router + 3 expert GEMMs per
+    routed pair (+ the shared expert on every token)."""
+    return (2.0 * wl.T * wl.d * wl.E + 6.0 * wl.T * wl.k * wl.d * wl.f
+            + 6.0 * wl.T * wl.d * wl.f_shared)
+
+
+def layer_bytes(wl, active: int) -> float:
+    """Algorithmic HBM bytes of one layer call: each active expert's weights
+    once, the router weights, x read and y written once (+ shared expert)."""
+    b = wl.elem_bytes
+    return b * (3.0 * wl.d * wl.f * active + wl.d * wl.E + 2.0 * wl.T * wl.d + 3.0 * wl.d * wl.f_shared)
+
+
+def gateup_flops(wl) -> float:
+    """Grouped gate/up projection: 2 x (2f) x d FLOPs per routed row."""
+    return 4.0 * wl.P * wl.d * wl.f
+
+
+def gateup_bytes(wl, active: int) -> float:
+    """Gate/up kernel: active experts' [2f, d] weights + routed rows in + H out."""
+    b = wl.elem_bytes
+    return b * (2.0 * wl.f * wl.d * active + wl.P * wl.d + wl.P * wl.f)
+
+
+# ------------------------------------------------------------ setup
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "mixture_experts_ffn_04_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM traffic per launch from the rocprofv3 counter summary under
+    profiles/, or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}:{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def setup(wl, device):
+    import torch
+    from mixture_experts_ffn_04_amd import MoeLayer, MoeWeights
+
+    def dev(a, shape=None):
+        if wl.dtype == "bf16":
+            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+        return t if shape is None else t.view(shape)
+
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    x = W.gen_x(wl)
+    wr, bias = W.gen_router(wl)
+    gu = torch.empty(wl.E, 2 * wl.f, wl.d, dtype=tdt, device=device)
+    dn = torch.empty(wl.E, wl.d, wl.f, dtype=tdt, device=device)
+    host_experts = {}
+    keep = wl.E * 3 * wl.d * wl.f * wl.elem_bytes <= (4 << 30)
+    for e, g, w in W.iter_experts(wl):
+        gu[e].copy_(dev(g))
+        dn[e].copy_(dev(w))
+        if keep:
+            host_experts[e] = (g, w)
+    sh = W.gen_shared(wl)
+    weights = MoeWeights(dev(wr), None if bias is None else torch.from_numpy(bias).to(device), gu, dn,
+                         None if sh is None else dev(sh[0]), None if sh is None else dev(sh[1]))
+    layer = MoeLayer(weights, wl.k, wl.score)
+    host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=sh)
+    return layer, dev(x), host
+
+
+# ------------------------------------------------------------ CPU oracle
+
+def cpu_baseline(wl, host, sample_tokens: int):
+    """Time the CPU oracle (router + eager expert loop, float64) on the first
+    `sample_tokens` tokens of the workload.  Input generation is excluded;
+    decoding the stored bf16 values for the oracle is included."""
+    from oracle import moe_oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    S = min(sample_tokens, wl.T)
+    experts = host["experts"]
+
+    def fetch(e):
+        if e in experts:
+            g, w = experts[e]
+        else:
+            g, w = W.gen_expert(wl, e)
+        return W.values(g, wl.dtype), W.values(w, wl.dtype)
+
+    t0 = time.perf_counter()
+    x = W.values(host["x"][:S], wl.dtype)
+    L = O.router_logits(x, W.values(host["wr"], wl.dtype), host["bias"])
+    ids, w = O.route(L, wl.k, wl.score)
+    sh = host["shared"]
+    shared = None if sh is None else (W.values(sh[0], wl.dtype), W.values(sh[1], wl.dtype))
+    O.moe_layer_eager(x, ids, w, fetch, wl.E, shared)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {S} of {wl.T} tokens of workload {wl.name}: float64 router + eager "
+                      f"per-expert loop over the {len(np.unique(ids))} experts they select; "
+                      f"{dt:.1f} s wall"}
+
+
+# ------------------------------------------------------------ main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--cpu-sample", type=int, default=48, help="tokens for the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--kernels", action="store_true", help="also print per-stage times to stderr")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the layer runs on a single MI355X and this build has no "
+              "multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    device = torch.device("cuda:0")
+    wl = W.get(args.workload)
+    decode = args.workload.startswith("c3")
+
+    layer, x, host = setup(wl, device)
+    st = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        layer.forward(x)
+    torch.cuda.synchronize()
+    counts = layer.counts.cpu().numpy()
+    active = int((counts > 0).sum())
+
+    marks = {}
+    if decode:
+        # each step reads a cold cache: a 1 GiB write evicts L2 and the 256 MB
+        # Infinity Cache between steps (outside the per-step events)
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=device)
+        step_ev = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            flush.fill_(float(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            layer.forward(x, marks=marks)
+            e1.record(st)
+            step_ev.append((e0, e1))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = float(np.mean([a.elapsed_time(b) for a, b in step_ev]))
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            layer.forward(x, marks=marks)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = wall * 1e3 / args.steps
+
+    stage_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in marks.items()}
+    tokens_per_s = wl.T / (ms * 1e-3)
+
+    if decode:
+        kname = "decode_gateup"
+        alg = gateup_bytes(wl, active)
+        achieved = alg / (stage_ms["gateup"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBPS}
+    else:
+        kname = "gateup"
+        alg = gateup_flops(wl)
+        peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+        achieved = alg / (stage_ms["gateup"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    roof["kernel"] = kname
+    roof["kernel_ms"] = stage_ms["gateup"]
+    roof["traffic"] = load_traffic(kname, wl.name)
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.f, "experts": wl.E,
+                   "top_k": wl.k, "score": wl.score, "zipf_s": wl.zipf_s, "shared_d_ff": wl.f_shared,
+                   "active_experts": active, "parallelism": "single GPU",
+                   "timing": "per-step events, caches flushed between steps" if decode
+                   else "wall clock over the timed steps"},
+        "roofline": roof,
+        "layer": {"tflops": layer_flops(wl) / (ms * 1e-3) / 1e12,
+                  "mfma_frac": layer_flops(wl) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "gbps": layer_bytes(wl, active) / (ms * 1e-3) / 1e9,
+                  "hbm_frac": layer_bytes(wl, active) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                  "stage_ms": stage_ms, "wall_s": wall},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_sample)
+    if args.kernels:
+        print(json.dumps(stage_ms), file=sys.stderr)
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,212 @@
+/*
+ * libmoe -- the routed mixture-of-experts feed-forward layer on one AMD
+ * Instinct MI355X (CDNA4, gfx950), as a C ABI.
+ *
+ * The layer is the one described in "Mixture of Experts (MoEs) in
+ * Transformers" (Hugging Face blog).  Section "From Dense to Sparse": a dense
+ * feed-forward layer is replaced by a set of experts (learnable
+ * sub-networks) and, per token, a router selects a few of them from the
+ * token's hidden representation.  Section "Expert Backend": an execution
+ * strategy must send tokens to their selected experts' weights, run the
+ * projections, apply the routing weights and collect / reorder the results;
+ * its "grouped_mm" strategy sorts tokens by expert ID, groups them and runs
+ * one grouped GEMM.  The calls below are those steps, in order:
+ *
+ *   moe_route                        router logits, top-k, routing weights
+ *   moe_topk                         top-k + weights from given logits
+ *   moe_permute                      sort by expert ID (histogram, scan,
+ *                                    stable scatter) + gather of the rows
+ *   moe_grouped_gemm_gateup_swiglu   per-expert gate/up projection + SwiGLU
+ *   moe_grouped_gemm_down            per-expert down projection
+ *   moe_unpermute_combine            weighted combine back to token order
+ *   moe_decode_gateup_swiglu         small-batch variants that stream only
+ *   moe_decode_down                  the active experts' weights
+ *
+ * Expert weights are packed per layer in one contiguous tensor, the layout
+ * the article's "Dynamic Weight Loading with WeightConverter" subsection
+ * produces: per-expert gate (w1) and up (w3) matrices of shape [f, d] are
+ * stacked over experts and concatenated along dim 1, giving
+ * w_gate_up[E][2f][d] (rows [0, f) gate, rows [f, 2f) up); the down
+ * projection is w_down[E][d][f].  All matrices are row-major.
+ *
+ * Conventions shared by every call
+ *   - Every data pointer is DEVICE memory owned by the caller.  The library
+ *     never allocates, frees, retains pointers past the return, or
+ *     synchronises; work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream) and the call returns after validation and launch.
+ *   - Host-side validation runs before any launch; on any error nothing is
+ *     launched and outputs are untouched.  Calls never abort and no C++
+ *     exception crosses the ABI.  Faults inside kernels are asynchronous and
+ *     surface at the caller's next synchronisation.
+ *   - T == 0 (or rows == 0) is valid and launches nothing (moe_permute still
+ *     zero-fills counts / offsets).
+ *   - d and f must be multiples of 64; 1 <= k <= min(E, 16); 1 <= E <= 256;
+ *     T * k < 2^31.  Data pointers must be 16-byte aligned.
+ *   - Outputs must not alias inputs.
+ *   - Index tensors are int32; routing weights and logits are fp32; the
+ *     activation / weight element type is given by `dtype` (bf16 or fp32).
+ *     bf16 paths accumulate in fp32 and round results to bf16 (RNE).
+ *   - The library keeps no state: concurrent calls on different streams with
+ *     disjoint buffers are allowed.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, negative size, k/E out of range   */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels handle       */
+  MOE_ERR_ALIGNMENT = 3,    /* pointer not 16-byte aligned, d or f not % 64    */
+  MOE_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required      */
+  MOE_ERR_HIP = 5           /* a HIP launch reported an error                  */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+/* ABI version (MOE_ABI_VERSION of the built library). */
+MOE_API int moe_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+MOE_API const char* moe_status_string(moe_status s);
+
+/*
+ * Router (article, "From Dense to Sparse": the router selects a small subset
+ * of experts per token from its hidden representation).
+ *
+ *   logits[t][e]  = sum_i x[t][i] * w_router[e][i] + bias[e]      (fp32)
+ *   topk_ids[t][j] = expert with the j-th largest logit of token t; equal
+ *                    logits go to the lower expert index
+ *   topk_w[t][j]   = softmax over the k selected logits, or for
+ *                    MOE_SCORE_SIGMOID sigmoid(logit) / sum of the k selected
+ *                    sigmoids (both sum to 1 over j)
+ *
+ *   x        [T][d]  dtype          w_router [E][d] dtype
+ *   bias     [E] fp32, may be NULL  logits   [T][E] fp32 (output)
+ *   topk_ids [T][k] int32 (output)  topk_w   [T][k] fp32 (output)
+ */
+MOE_API moe_status moe_route(const void* x, const void* w_router, const float* bias,
+                     int64_t T, int64_t d, int32_t E, int32_t k, moe_dtype dtype,
+                     moe_score score, float* logits, int32_t* topk_ids,
+                     float* topk_w, void* stream);
+
+/*
+ * The selection half of moe_route on caller-supplied fp32 logits [T][E]
+ * (same outputs and tie rule).  No alignment requirement on `logits`.
+ */
+MOE_API moe_status moe_topk(const float* logits, int64_t T, int32_t E, int32_t k,
+                    moe_score score, int32_t* topk_ids, float* topk_w,
+                    void* stream);
+
+/* Bytes of device workspace moe_permute needs for these sizes. */
+MOE_API size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t E);
+
+/*
+ * Sort the routed (token, slot) pairs by expert ID ("grouped_mm" strategy,
+ * article section "Expert Backend").  With p = t*k + j:
+ *
+ *   counts[e]    = #{p : topk_ids[p] == e}
+ *   offsets[0]   = 0, offsets[e+1] = offsets[e] + counts[e]  (offsets[E] = T*k)
+ *   perm[r]      = the p placed at row r; rows of expert e are
+ *                  [offsets[e], offsets[e+1]) in ascending p (stable)
+ *   inv_perm[p]  = row of p
+ *   x_perm[r][:] = x[perm[r] / k][:]     (skipped when x_perm is NULL)
+ *
+ *   topk_ids [T*k] int32 in [0, E)      x [T][d] dtype (may be NULL iff x_perm is)
+ *   counts [E], offsets [E+1], perm [T*k], inv_perm [T*k]  int32 outputs
+ *   x_perm [T*k][d] dtype output
+ *   ws / ws_bytes: device scratch of at least moe_permute_workspace_size()
+ * Ids outside [0, E) are counted nowhere and make the outputs undefined
+ * (no out-of-bounds access happens).
+ */
+MOE_API moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_t T, int64_t d,
+                       int32_t E, int32_t k, moe_dtype dtype, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                       void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped gate/up projection with SwiGLU, one group per expert:
+ *
+ *   for e, for r in [offsets[e], offsets[e+1]):
+ *     g = x_perm[r] . w_gate_up[e][n]      (n < f, gate)
+ *     u = x_perm[r] . w_gate_up[e][f + n]  (up)
+ *     h[r][n] = silu(g) * u,  silu(g) = g / (1 + exp(-g))
+ *
+ *   x_perm [rows][d], w_gate_up [E][2f][d], h [rows][f]  (dtype)
+ *   offsets [E+1] int32 (device), non-decreasing, offsets[0] = 0,
+ *   offsets[E] <= rows.  Rows past offsets[E] are not written.  Offsets are
+ *   clamped to [0, rows] on the device, so malformed offsets give wrong
+ *   results but no out-of-bounds access.
+ */
+MOE_API moe_status moe_grouped_gemm_gateup_swiglu(const void* x_perm, const void* w_gate_up,
+                                          const int32_t* offsets, int64_t rows,
+                                          int64_t d, int64_t f, int32_t E,
+                                          moe_dtype dtype, void* h, void* stream);
+
+/*
+ * Grouped down projection, one group per expert:
+ *   y_perm[r][c] = h[r] . w_down[e][c]   for r in expert e's rows, c < d
+ *
+ *   h [rows][f], w_down [E][d][f], y_perm [rows][d]  (dtype); offsets as above.
+ */
+MOE_API moe_status moe_grouped_gemm_down(const void* h, const void* w_down,
+                                 const int32_t* offsets, int64_t rows, int64_t d,
+                                 int64_t f, int32_t E, moe_dtype dtype,
+                                 void* y_perm, void* stream);
+
+/*
+ * Apply the routing weights and collect the rows back in token order
+ * (article section "Expert Backend"):
+ *   y[t][c] = sum_{j<k} topk_w[t][j] * y_perm[inv_perm[t*k + j]][c]
+ *             (+ y_shared[t][c] when y_shared is not NULL)
+ * summed in fp32 in increasing j, then the shared row, then rounded once.
+ * Deterministic: no atomics.
+ *
+ *   y_perm [T*k][d], y_shared [T][d] or NULL, y [T][d]  (dtype)
+ *   inv_perm [T*k] int32, topk_w [T][k] fp32
+ * inv_perm entries are clamped to [0, T*k).
+ */
+MOE_API moe_status moe_unpermute_combine(const void* y_perm, const int32_t* inv_perm,
+                                 const float* topk_w, const void* y_shared,
+                                 int64_t T, int64_t d, int32_t k, moe_dtype dtype,
+                                 void* y, void* stream);
+
+/*
+ * Small-batch (decode) variants of the two grouped projections, for rows
+ * <= 1024: same arguments and results as the grouped calls, but the work is
+ * split along the weight rows of the experts that have rows, so each active
+ * expert's weights are streamed from HBM once and experts with no rows are
+ * never read (article, "From Dense to Sparse": decode speed follows the
+ * active parameters; section "Expert Backend": the small-batch strategy).
+ * rows > 1024 returns MOE_ERR_UNSUPPORTED.
+ */
+MOE_API moe_status moe_decode_gateup_swiglu(const void* x_perm, const void* w_gate_up,
+                                    const int32_t* offsets, int64_t rows, int64_t d,
+                                    int64_t f, int32_t E, moe_dtype dtype, void* h,
+                                    void* stream);
+
+MOE_API moe_status moe_decode_down(const void* h, const void* w_down, const int32_t* offsets,
+                           int64_t rows, int64_t d, int64_t f, int32_t E,
+                           moe_dtype dtype, void* y_perm, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_H */

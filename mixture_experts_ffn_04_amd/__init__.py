@@ -1,0 +1,7 @@
+"""libmoe: the routed mixture-of-experts FFN layer on AMD MI355X (gfx950).
+
+The compute runs in hand-written HIP kernels behind the C ABI declared in
+include/libmoe.h (built into libmoe.so); `binding` is the Python binding.
+"""
+from . import binding  # noqa: F401
+from .binding import MoeLayer, MoeWeights  # noqa: F401

@@ -1,0 +1,278 @@
+"""Thin Python binding over the libmoe C ABI (include/libmoe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+of libmoe.so.  PyTorch supplies device memory and the current HIP stream.
+There is no fallback: if libmoe.so is missing or no GPU is present the calls
+raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGNMENT, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+
+EXPORTS = (
+    "moe_abi_version", "moe_status_string", "moe_route", "moe_topk",
+    "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_gateup_swiglu",
+    "moe_grouped_gemm_down", "moe_unpermute_combine", "moe_decode_gateup_swiglu",
+    "moe_decode_down",
+)
+
+_lib: Optional[ctypes.CDLL] = None
+
+P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+
+_SIGS = {
+    "moe_abi_version": ([], ctypes.c_int),
+    "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "moe_route": ([P, P, P, I64, I64, I32, I32, ctypes.c_int, ctypes.c_int, P, P, P, P], ctypes.c_int),
+    "moe_topk": ([P, I64, I32, I32, ctypes.c_int, P, P, P], ctypes.c_int),
+    "moe_permute_workspace_size": ([I64, I32, I32], SZ),
+    "moe_permute": ([P, P, I64, I64, I32, I32, ctypes.c_int, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+    "moe_grouped_gemm_gateup_swiglu": ([P, P, P, I64, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
+    "moe_grouped_gemm_down": ([P, P, P, I64, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
+    "moe_unpermute_combine": ([P, P, P, P, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
+    "moe_decode_gateup_swiglu": ([P, P, P, I64, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
+    "moe_decode_down": ([P, P, P, I64, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = load().moe_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe.so (after torch, so the HIP runtime torch loaded is the
+    one the library binds to).  Raises if the library is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libmoe.so not built ({path}); run __graft_entry__.build() "
+                           "or python -m mixture_experts_ffn_04_amd.build")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+SCORES = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
+
+
+# ------------------------------------------------------------- single calls
+
+def route(x, w_router, bias, k: int, score: str, logits, topk_ids, topk_w, stream=None):
+    T, d = x.shape
+    E = w_router.shape[0]
+    _check("moe_route", load().moe_route(_ptr(x), _ptr(w_router), _ptr(bias), T, d, E, k, _dt(x),
+                                         SCORES[score], _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                         _stream(stream)))
+
+
+def topk(logits, k: int, score: str, topk_ids, topk_w, stream=None):
+    T, E = logits.shape
+    _check("moe_topk", load().moe_topk(_ptr(logits), T, E, k, SCORES[score], _ptr(topk_ids),
+                                       _ptr(topk_w), _stream(stream)))
+
+
+def permute_workspace_size(T: int, k: int, E: int) -> int:
+    return int(load().moe_permute_workspace_size(T, k, E))
+
+
+def permute(topk_ids, x, E: int, counts, offsets, perm, inv_perm, x_perm, ws, stream=None):
+    T, k = topk_ids.shape
+    d = x.shape[1] if x is not None else 0
+    dt = _dt(x) if x is not None else MOE_BF16
+    _check("moe_permute", load().moe_permute(_ptr(topk_ids), _ptr(x), T, d, E, k, dt, _ptr(counts),
+                                             _ptr(offsets), _ptr(perm), _ptr(inv_perm), _ptr(x_perm),
+                                             _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
+                                             _stream(stream)))
+
+
+def gateup_swiglu(x_perm, w_gate_up, offsets, h, decode: bool = False, stream=None):
+    rows, d = x_perm.shape
+    E, f2, _ = w_gate_up.shape
+    fn = "moe_decode_gateup_swiglu" if decode else "moe_grouped_gemm_gateup_swiglu"
+    _check(fn, getattr(load(), fn)(_ptr(x_perm), _ptr(w_gate_up), _ptr(offsets), rows, d, f2 // 2, E,
+                                   _dt(x_perm), _ptr(h), _stream(stream)))
+
+
+def down(h, w_down, offsets, y_perm, decode: bool = False, stream=None):
+    rows, f = h.shape
+    E, d, _ = w_down.shape
+    fn = "moe_decode_down" if decode else "moe_grouped_gemm_down"
+    _check(fn, getattr(load(), fn)(_ptr(h), _ptr(w_down), _ptr(offsets), rows, d, f, E, _dt(h),
+                                   _ptr(y_perm), _stream(stream)))
+
+
+def unpermute_combine(y_perm, inv_perm, topk_w, y_shared, y, stream=None):
+    T, k = topk_w.shape
+    d = y.shape[1]
+    _check("moe_unpermute_combine", load().moe_unpermute_combine(
+        _ptr(y_perm), _ptr(inv_perm), _ptr(topk_w), _ptr(y_shared), T, d, k, _dt(y), _ptr(y),
+        _stream(stream)))
+
+
+# ------------------------------------------------------------- whole layer
+
+@dataclass
+class MoeWeights:
+    w_router: torch.Tensor           # [E, d]
+    bias: Optional[torch.Tensor]     # [E] fp32 or None
+    w_gate_up: torch.Tensor          # [E, 2f, d]
+    w_down: torch.Tensor             # [E, d, f]
+    shared_gate_up: Optional[torch.Tensor] = None   # [1, 2f_s, d]
+    shared_down: Optional[torch.Tensor] = None      # [1, d, f_s]
+
+
+class MoeLayer:
+    """The routed MoE FFN layer over preallocated device buffers.
+
+    forward(x) enqueues, on the current stream: moe_route, moe_permute,
+    gate/up + SwiGLU and down projections (grouped, or decode variants for
+    small batches), the shared expert when present, and the weighted
+    combine.  Buffers are allocated once per token count and reused.
+    """
+
+    DECODE_MAX_ROWS = 256
+
+    def __init__(self, weights: MoeWeights, k: int, score: str, mode: str = "auto"):
+        load()
+        self.w = weights
+        self.k = k
+        self.score = score
+        self.mode = mode
+        self.E, self.d = weights.w_router.shape
+        self.f = weights.w_down.shape[2]
+        self.dev = weights.w_router.device
+        self.dtype = weights.w_gate_up.dtype
+        self._T = None
+
+    def _alloc(self, T: int):
+        if self._T == T:
+            return
+        dev, dt, k, E, d, f = self.dev, self.dtype, self.k, self.E, self.d, self.f
+        P = T * k
+        i32 = torch.int32
+        self.logits = torch.empty(T, E, device=dev, dtype=torch.float32)
+        self.ids = torch.empty(T, k, device=dev, dtype=i32)
+        self.wts = torch.empty(T, k, device=dev, dtype=torch.float32)
+        self.counts = torch.empty(E, device=dev, dtype=i32)
+        self.offsets = torch.empty(E + 1, device=dev, dtype=i32)
+        self.perm = torch.empty(P, device=dev, dtype=i32)
+        self.inv_perm = torch.empty(P, device=dev, dtype=i32)
+        self.x_perm = torch.empty(P, d, device=dev, dtype=dt)
+        self.h = torch.empty(P, f, device=dev, dtype=dt)
+        self.y_perm = torch.empty(P, d, device=dev, dtype=dt)
+        self.ws = torch.empty(max(1, permute_workspace_size(T, k, E)), device=dev, dtype=torch.uint8)
+        self.y = torch.empty(T, d, device=dev, dtype=dt)
+        if self.w.shared_gate_up is not None:
+            fs = self.w.shared_down.shape[2]
+            self.s_off = torch.tensor([0, T], device=dev, dtype=i32)
+            self.s_h = torch.empty(T, fs, device=dev, dtype=dt)
+            self.s_y = torch.empty(T, d, device=dev, dtype=dt)
+        self._T = T
+
+    def use_decode(self, T: int) -> bool:
+        if self.mode == "decode":
+            return True
+        if self.mode == "grouped":
+            return False
+        return T * self.k <= self.DECODE_MAX_ROWS
+
+    def forward(self, x: torch.Tensor, stream=None, marks: Optional[dict] = None) -> torch.Tensor:
+        """Run the layer on x [T, d].  With `marks` (a dict), a pair of timing
+        events recorded on the launch stream brackets every stage and is
+        appended to marks[stage]."""
+        T = x.shape[0]
+        self._alloc(T)
+        w = self.w
+        dec = self.use_decode(T)
+        st = torch.cuda.current_stream() if stream is None else stream
+
+        def mark(name, fn, *a):
+            if marks is None:
+                fn(*a)
+                return
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            fn(*a)
+            e1.record(st)
+            marks.setdefault(name, []).append((e0, e1))
+
+        mark("route", route, x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st)
+        mark("permute", permute, self.ids, x, self.E, self.counts, self.offsets, self.perm, self.inv_perm,
+             self.x_perm, self.ws, st)
+        mark("gateup", gateup_swiglu, self.x_perm, w.w_gate_up, self.offsets, self.h, dec, st)
+        mark("down", down, self.h, w.w_down, self.offsets, self.y_perm, dec, st)
+        ys = None
+        if w.shared_gate_up is not None:
+            sdec = dec and T <= self.DECODE_MAX_ROWS
+            mark("shared_gateup", gateup_swiglu, x, w.shared_gate_up, self.s_off, self.s_h, sdec, st)
+            mark("shared_down", down, self.s_h, w.shared_down, self.s_off, self.s_y, sdec, st)
+            ys = self.s_y
+        mark("combine", unpermute_combine, self.y_perm, self.inv_perm, self.wts, ys, self.y, st)
+        return self.y
+
+
+# The C ABI's own names, for callers that mirror include/libmoe.h.
+moe_route = route
+moe_topk = topk
+moe_permute_workspace_size = permute_workspace_size
+moe_permute = permute
+moe_grouped_gemm_gateup_swiglu = gateup_swiglu
+moe_grouped_gemm_down = down
+moe_unpermute_combine = unpermute_combine
+
+
+def moe_decode_gateup_swiglu(x_perm, w_gate_up, offsets, h, stream=None):
+    gateup_swiglu(x_perm, w_gate_up, offsets, h, True, stream)
+
+
+def moe_decode_down(h, w_down, offsets, y_perm, stream=None):
+    down(h, w_down, offsets, y_perm, True, stream)

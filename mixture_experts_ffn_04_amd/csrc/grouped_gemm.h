@@ -1,0 +1,134 @@
+// Grouped GEMM machinery for the MoE layer on gfx950.
+//
+// One launch computes, for every group g (an expert) owning the rows
+// [off[g], off[g+1]) of A:
+//
+//     C[r][n] = sum_k A[r][k] * B[g][n][k]          (B row-major [N][K])
+//
+// A and B are both K-contiguous, so every MFMA operand is a 16-byte run of
+// one row.  The epilogue is fused:
+//   EPI_STORE   C in the element type                 (down projection)
+//   EPI_SWIGLU  B's rows [0, N) are gate and [N, 2N) are up; output column n
+//               is silu(C_gate[n]) * C_up[n]          (gate/up projection)
+//   EPI_F32B    C + bias[n] as fp32                   (router logits)
+//
+// This is the "grouped_mm" expert execution of the article "Mixture of
+// Experts (MoEs) in Transformers" (section "Expert Backend"): the token rows
+// are already sorted by expert and one grouped GEMM covers all experts.
+//
+// Tile schedule.  Each workgroup reads offsets[] (G <= 256 entries) and scans
+// the per-group tile counts itself, so there is no host round trip, no
+// workspace, and empty experts cost nothing.  Tiles are numbered group-major,
+// then in blocks of SN column tiles, then by row tile, then by the column
+// tile inside the block, so the workgroups that run together share their
+// weight tiles (same column block) and their token tiles (same row tile).
+// Workgroup ids are remapped so that each XCD (ids are dealt to the 8 XCDs
+// round-robin) walks one contiguous 1/8 of that order.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32B = 2 };
+
+struct GemmArgs {
+  const void* A;          // [rows][K]
+  const void* B;          // [G][b_rows][K], b_rows = N (2N for SWIGLU)
+  const int32_t* off;     // [G+1] group row offsets (device); NULL -> one group [0, rows)
+  const float* bias;      // [N] for EPI_F32B (may be NULL)
+  void* C;                // [rows][N] (SWIGLU: [rows][N] too, N = f)
+  int64_t rows;           // rows of A and C
+  int64_t K;
+  int64_t N;              // output columns
+  int G;                  // groups
+};
+
+struct TileLoc {
+  int g;         // group
+  int row0;      // first A/C row of the tile
+  int row_end;   // end of the group's rows
+  int n0;        // first output column
+};
+
+// Locate this workgroup's tile.  Must be called by all NT threads; returns
+// false (for the whole workgroup) when the block id is past the last tile.
+//   BM     rows per tile, BNO output columns per tile, SN column-block width
+template <int NT, int BM, int BNO, int SN>
+__device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl) {
+  static_assert(NT >= kMaxE, "one group per thread");
+  __shared__ int s_pref[kMaxE];
+  __shared__ int s_wsum[NT / 64];
+  __shared__ int s_hit[4];
+  const int t = threadIdx.x;
+  const int rows = static_cast<int>(a.rows);
+  const int ntiles = static_cast<int>((a.N + BNO - 1) / BNO);
+  int lo = 0, hi = 0, cnt = 0;
+  if (t < a.G) {
+    lo = a.off ? clamp_off(a.off[t], rows) : 0;
+    hi = a.off ? clamp_off(a.off[t + 1], rows) : rows;
+    if (hi < lo) hi = lo;
+    cnt = ((hi - lo + BM - 1) / BM) * ntiles;
+  }
+  // block exclusive scan of cnt
+  const int lane = t & 63, w = t >> 6;
+  int v = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) s_wsum[w] = v;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    int s = s_wsum[i];
+    base += (i < w) ? s : 0;
+    total += s;
+  }
+  const int excl = base + v - cnt;
+  if (t < a.G) s_pref[t] = excl;
+
+  const int bid = static_cast<int>(blockIdx.x);
+  if (bid >= total) return false;     // uniform: total is the same in every thread
+  // XCD-aware remap of the block id to the logical tile index
+  const int q = total >> 3;
+  const int L = (bid < (q << 3)) ? ((bid & 7) * q + (bid >> 3)) : bid;
+  if (t < a.G && cnt > 0 && L >= excl && L < excl + cnt) {
+    s_hit[0] = t;
+    s_hit[1] = lo;
+    s_hit[2] = hi;
+  }
+  __syncthreads();
+  const int g = s_hit[0];
+  const int glo = s_hit[1], ghi = s_hit[2];
+  const int local = L - s_pref[g];
+  const int mt_g = (ghi - glo + BM - 1) / BM;
+  const int nbf = ntiles / SN;
+  int mt, nt;
+  if (local < nbf * mt_g * SN) {
+    const int nb = local / (mt_g * SN);
+    const int r = local - nb * (mt_g * SN);
+    mt = r / SN;
+    nt = nb * SN + (r - mt * SN);
+  } else {
+    const int snr = ntiles - nbf * SN;
+    const int r = local - nbf * mt_g * SN;
+    mt = r / snr;
+    nt = nbf * SN + (r - mt * snr);
+  }
+  tl.g = g;
+  tl.row0 = glo + mt * BM;
+  tl.row_end = ghi;
+  tl.n0 = nt * BNO;
+  return true;
+}
+
+// Upper bound on the tiles of a grouped launch (used as the grid size):
+// every group adds at most one partial row tile.
+inline int64_t grouped_tile_bound(int64_t rows, int G, int BM, int64_t N, int BNO) {
+  return (ceil_div(rows, BM) + G) * ceil_div(N, BNO);
+}
+
+}  // namespace moe

@@ -1,0 +1,190 @@
+// Sort the routed (token, slot) pairs by expert ID and group them -- the
+// first step of the "grouped_mm" strategy (article "Mixture of Experts (MoEs)
+// in Transformers", section "Expert Backend") -- and gather the token rows
+// into that order.
+//
+// Four launches, no host synchronisation:
+//   1. histogram  chunks of kChunk pairs; per-chunk expert counts with LDS
+//                 atomics (order-free, so deterministic) -> ws counts[chunk][E]
+//   2. scan       one workgroup: per expert, running sum over chunks (the
+//                 chunk's base inside the expert's group), then an exclusive
+//                 scan over experts -> counts, offsets, per-chunk bases
+//   3. scatter    one wave per chunk walks its pairs 64 at a time in order;
+//                 the rank of a pair among equal experts in the wave comes
+//                 from ballots on the bits of the expert id (a match-any), so
+//                 positions are stable without atomics on the ranks
+//   4. gather     x_perm[r] = x[perm[r] / k], 16-byte loads and stores, one
+//                 wave per row
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = 1024;   // pairs per chunk
+
+size_t ws_bytes_for(int64_t P, int E) {
+  const int64_t chunks = ceil_div(P, kChunk);
+  return static_cast<size_t>(chunks) * static_cast<size_t>(E) * sizeof(int32_t);
+}
+
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                   int32_t* __restrict__ cc) {
+  __shared__ int h[kMaxE];
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * kChunk;
+  const int p1 = min(P, p0 + kChunk);
+  for (int p = p0 + threadIdx.x; p < p1; p += 256) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) cc[static_cast<int64_t>(blockIdx.x) * E + e] = h[e];
+}
+
+// One workgroup of 256 threads (E <= 256): thread e owns expert e.
+__global__ __launch_bounds__(256) void scan_kernel(int32_t* __restrict__ cc, int chunks, int E,
+                                                   int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ offsets) {
+  __shared__ int wsum[4];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E) {
+    for (int c = 0; c < chunks; ++c) {
+      const int64_t i = static_cast<int64_t>(c) * E + e;
+      const int v = cc[i];
+      cc[i] = tot;          // base of chunk c inside expert e's group
+      tot += v;
+    }
+  }
+  const int lane = e & 63, w = e >> 6;
+  int v = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += wsum[i];
+  const int excl = base + v - tot;
+  if (e < E) {
+    counts[e] = tot;
+    offsets[e] = excl;
+    for (int c = 0; c < chunks; ++c) cc[static_cast<int64_t>(c) * E + e] += excl;
+  }
+  if (e == E - 1) offsets[E] = excl + tot;
+}
+
+// One wave per chunk.
+__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                     int nbits, const int32_t* __restrict__ cc,
+                                                     int32_t* __restrict__ perm,
+                                                     int32_t* __restrict__ inv_perm) {
+  __shared__ int base[kMaxE];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) base[e] = cc[static_cast<int64_t>(blockIdx.x) * E + e];
+  __syncthreads();
+  const int p0 = blockIdx.x * kChunk;
+  const int p1 = min(P, p0 + kChunk);
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  for (int s = p0; s < p1; s += 64) {
+    const int p = s + lane;
+    int e = -1;
+    if (p < p1) e = ids[p];
+    const bool ok = e >= 0 && e < E;
+    uint64_t m = __ballot(ok);
+#pragma unroll 1
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = ok && ((e >> b) & 1);
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    // m: lanes holding the same expert (valid lanes only)
+    int pos = 0;
+    if (ok) {
+      const int rank = __popcll(m & below);
+      pos = base[e] + rank;
+    }
+    __syncthreads();   // every lane has read base[] for this step
+    if (ok) {
+      const int cnt = __popcll(m);
+      const int leader = 63 - __clzll(m);          // highest lane of the group
+      if (lane == leader) base[e] += cnt;
+      perm[pos] = p;
+      inv_perm[p] = pos;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ perm,
+                                                     int P, int T, int k, int64_t row_chunks,
+                                                     uint4* __restrict__ xp) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= P) return;
+  const int lane = threadIdx.x & 63;
+  int64_t t = perm[r] / k;
+  t = t < 0 ? 0 : (t >= T ? T - 1 : t);   // rows left unwritten by invalid ids stay in bounds
+  const uint4* src = x + t * row_chunks;
+  uint4* dst = xp + static_cast<int64_t>(r) * row_chunks;
+  for (int64_t c = lane; c < row_chunks; c += 64) dst[c] = src[c];
+}
+
+__global__ void zero_kernel(int32_t* __restrict__ a, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) a[i] = 0;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1 || E > kMaxE) return 0;
+  return ws_bytes_for(T * k, E);
+}
+
+extern "C" moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_t T, int64_t d,
+                                  int32_t E, int32_t k, moe_dtype dtype, int32_t* counts,
+                                  int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_perm,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || d < 0 || E < 1 || k < 1 || k > E || k > kMaxK) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (!valid_dtype(dtype)) return MOE_ERR_INVALID_ARG;
+  const int64_t P = T * k;
+  if (P >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (x_perm && (d % 64 != 0)) return MOE_ERR_ALIGNMENT;
+  if (x_perm && !x) return MOE_ERR_INVALID_ARG;
+  if (x_perm && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_ALIGNMENT;
+  hipStream_t st = as_stream(stream);
+  if (P == 0) {
+    // a fill kernel rather than hipMemsetAsync, so the call can be captured in a graph
+    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(kMaxE), 0, st, counts, E);
+    hipLaunchKernelGGL(zero_kernel, dim3(2), dim3(kMaxE), 0, st, offsets, E + 1);
+    return launch_status();
+  }
+  if (!topk_ids || !perm || !inv_perm) return MOE_ERR_INVALID_ARG;
+  const size_t need = ws_bytes_for(P, E);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  int32_t* cc = static_cast<int32_t*>(ws);
+  const int chunks = static_cast<int>(ceil_div(P, kChunk));
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+
+  hipLaunchKernelGGL(hist_kernel, dim3(chunks), dim3(256), 0, st, topk_ids, static_cast<int>(P), E, cc);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, st, cc, chunks, E, counts, offsets);
+  hipLaunchKernelGGL(scatter_kernel, dim3(chunks), dim3(64), 0, st, topk_ids, static_cast<int>(P), E, nbits,
+                     cc, perm, inv_perm);
+  if (x_perm) {
+    const int64_t row_chunks = d * elem_bytes(dtype) / 16;
+    hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(ceil_div(P, 4))), dim3(256), 0, st,
+                       static_cast<const uint4*>(x), perm, static_cast<int>(P), static_cast<int>(T), k,
+                       row_chunks,
+                       static_cast<uint4*>(x_perm));
+  }
+  return launch_status();
+}

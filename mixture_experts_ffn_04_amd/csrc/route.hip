@@ -1,0 +1,156 @@
+// Router: logits, top-k selection and routing weights.
+//
+// Article "Mixture of Experts (MoEs) in Transformers", section "From Dense
+// to Sparse": for each token a router picks a small subset of the experts
+// from the token's hidden representation.
+//
+// Logits are a dense contraction x[T][d] . w_router[E][d]^T, computed by the
+// grouped GEMM kernels as a single group with a "+ bias, fp32" epilogue.
+//
+// Selection: one wave per token.  Lane l holds logits l, l+64, l+128, l+192
+// (E <= 256).  k rounds of a wave-wide arg-max on the key (logit, -index)
+// -- larger logit first, equal logits to the lower index -- each round
+// removing the winner from its lane.  The k winners, in selection order,
+// give the weights: a softmax over the selected logits, or sigmoid scores
+// divided by their sum.
+#include "grouped_gemm.h"
+
+namespace moe {
+
+moe_status gemm_bf16_logits(const GemmArgs& a, hipStream_t st);
+moe_status gemm_f32_logits(const GemmArgs& a, hipStream_t st);
+
+namespace {
+
+constexpr int kTokPerBlock = 4;   // one wave each
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                   int score, int32_t* __restrict__ ids,
+                                                   float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (tok >= T) return;
+  const float* row = logits + static_cast<int64_t>(tok) * E;
+  float v[4];
+  bool live[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    live[i] = e < E;
+    v[i] = live[i] ? row[e] : 0.0f;
+  }
+  float sel_v[kMaxK];
+  int sel_i[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j >= k) break;
+    // lane-local best
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (live[i] && (bi == 0x7fffffff || better(v[i], e, bv, bi))) { bv = v[i]; bi = e; }
+    }
+    // wave arg-max on (value, -index); lanes with nothing left carry index INT_MAX
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      const bool take = (oi != 0x7fffffff) && (bi == 0x7fffffff || better(ov, oi, bv, bi));
+      if (take) { bv = ov; bi = oi; }
+    }
+    sel_v[j] = bv;
+    sel_i[j] = bi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i == bi) live[i] = false;
+  }
+  if (lane == 0) {
+    float w[kMaxK];
+    float s = 0.0f;
+    if (score == MOE_SCORE_SOFTMAX) {
+      const float m = sel_v[0];
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j >= k) break;
+        w[j] = expf(sel_v[j] - m);
+        s += w[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) {
+        if (j >= k) break;
+        w[j] = 1.0f / (1.0f + expf(-sel_v[j]));
+        s += w[j];
+      }
+    }
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) break;
+      ids[static_cast<int64_t>(tok) * k + j] = sel_i[j];
+      wts[static_cast<int64_t>(tok) * k + j] = w[j] * inv;
+    }
+  }
+}
+
+moe_status check_topk_args(int64_t T, int32_t E, int32_t k, moe_score score) {
+  if (T < 0 || E < 1 || k < 1 || k > E || k > kMaxK) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (T * static_cast<int64_t>(k) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, moe_score score,
+                       int32_t* ids, float* w, hipStream_t st) {
+  const int64_t blocks = ceil_div(T, kTokPerBlock);
+  hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, logits,
+                     static_cast<int>(T), E, k, static_cast<int>(score), ids, w);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_topk(const float* logits, int64_t T, int32_t E, int32_t k, moe_score score,
+                               int32_t* topk_ids, float* topk_w, void* stream) {
+  moe_status s = check_topk_args(T, E, k, score);
+  if (s != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  return launch_topk(logits, T, E, k, score, topk_ids, topk_w, as_stream(stream));
+}
+
+extern "C" moe_status moe_route(const void* x, const void* w_router, const float* bias, int64_t T,
+                                int64_t d, int32_t E, int32_t k, moe_dtype dtype, moe_score score,
+                                float* logits, int32_t* topk_ids, float* topk_w, void* stream) {
+  moe_status s = check_topk_args(T, E, k, score);
+  if (s != MOE_OK) return s;
+  if (!valid_dtype(dtype) || d <= 0) return MOE_ERR_INVALID_ARG;
+  if (d % 64 != 0) return MOE_ERR_ALIGNMENT;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits)) return MOE_ERR_ALIGNMENT;
+  GemmArgs a{};
+  a.A = x;
+  a.B = w_router;
+  a.off = nullptr;
+  a.bias = bias;
+  a.C = logits;
+  a.rows = T;
+  a.K = d;
+  a.N = E;
+  a.G = 1;
+  hipStream_t st = as_stream(stream);
+  s = (dtype == MOE_BF16) ? gemm_bf16_logits(a, st) : gemm_f32_logits(a, st);
+  if (s != MOE_OK) return s;
+  return launch_topk(logits, T, E, k, score, topk_ids, topk_w, st);
+}

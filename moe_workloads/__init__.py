@@ -265,3 +265,11 @@ def gen_ids(T: int, E: int, k: int, seed: int, zipf_s: Optional[float] = None) -
     for t in range(T):
         out[t] = rng.choice(E, size=k, replace=False, p=p)
     return out
+
+
+def gen_matrix(shape, seed: int, std: float = 1.0, dtype: str = "bf16") -> np.ndarray:
+    """A seeded ~N(0, std) array in storage format (stand-alone inputs for
+    testing one stage of the layer, e.g. activations fed to the down
+    projection or expert outputs fed to the combine)."""
+    rng = np.random.default_rng([seed, _LOGITS, 3])
+    return _encode(_normal(rng, tuple(shape), std), dtype)

@@ -18,6 +18,6 @@ def gpu():
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    from mixture_experts_ffn_04_amd import libmoe
+    from mixture_experts_ffn_04_amd import binding as libmoe
     libmoe.load()       # raises if the HIP library is missing
     return torch.device("cuda:0")

@@ -1,0 +1,376 @@
+"""GPU parity: every libmoe call against the CPU oracle on the scaled-down
+workloads (several tiles, ragged tails, empty experts), plus edge cases.
+All calls go through the C ABI (ctypes binding)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as W
+from oracle import moe_oracle as O
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["c1", "c2s", "c3s_t1", "c3s_t37", "c4s", "c5s"]
+
+
+def B():
+    from mixture_experts_ffn_04_amd import binding
+    return binding
+
+
+def _i32(a, dev="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+def _f32(a, dev="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def _oracle_routing(wl, inp):
+    x = W.values(inp["x"], wl.dtype)
+    wr = W.values(inp["wr"], wl.dtype)
+    L = O.router_logits(x, wr, inp["bias"])
+    ids, w = O.route(L, wl.k, wl.score)
+    return x, wr, L, ids, w
+
+
+def test_native_library_is_the_one_loaded(gpu):
+    lib = B().load()
+    assert lib.moe_abi_version() == 1
+    maps = open("/proc/self/maps").read()
+    assert B().LIB_PATH in maps
+    hip = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(hip) == 1, f"more than one HIP runtime mapped: {hip}"
+
+
+# ------------------------------------------------------------------ top-k
+
+TOPK_CASES = [(64, 8, 2, "softmax"), (333, 32, 4, "softmax"), (517, 128, 8, "softmax"),
+              (301, 256, 8, "sigmoid"), (40, 256, 16, "softmax"), (17, 5, 5, "sigmoid"),
+              (9, 1, 1, "softmax"), (70, 200, 3, "sigmoid")]
+
+
+@pytest.mark.parametrize("tied", [False, True])
+@pytest.mark.parametrize("T,E,k,score", TOPK_CASES)
+def test_topk_given_logits(gpu, T, E, k, score, tied):
+    """Same fp32 logits in -> bit-identical ids (ties to the lower index)."""
+    seed = T * 1000 + E + k
+    L = W.gen_tied_logits(T, E, seed, levels=4) if tied else W.gen_logits(T, E, seed)
+    ids = torch.empty(T, k, dtype=torch.int32, device=gpu)
+    w = torch.empty(T, k, dtype=torch.float32, device=gpu)
+    B().topk(_f32(L), k, score, ids, w)
+    torch.cuda.synchronize()
+    ref_ids = O.select_topk(L, k)
+    ref_w = O.routing_weights(L.astype(np.float64), ref_ids, score)
+    assert (ids.cpu().numpy() == ref_ids).all()
+    assert np.abs(w.cpu().numpy() - ref_w).max() <= 1e-6
+
+
+# ------------------------------------------------------------------ route
+
+@pytest.mark.parametrize("name", SMALL)
+def test_route(gpu, name):
+    wl, inp = U.small_inputs(name)
+    x, wr, L, ref_ids, ref_w = _oracle_routing(wl, inp)
+    T, E, k = wl.T, wl.E, wl.k
+    logits = torch.empty(T, E, dtype=torch.float32, device=gpu)
+    ids = torch.empty(T, k, dtype=torch.int32, device=gpu)
+    w = torch.empty(T, k, dtype=torch.float32, device=gpu)
+    bias = None if inp["bias"] is None else _f32(inp["bias"])
+    B().route(U.dev_tensor(inp["x"], wl.dtype), U.dev_tensor(inp["wr"], wl.dtype), bias, k, wl.score,
+              logits, ids, w)
+    torch.cuda.synchronize()
+    gl = logits.cpu().numpy().astype(np.float64)
+    assert (np.abs(gl - L) <= O.logit_error_bound(x, wr, inp["bias"])).all()
+    same = U.routing_agreement(ids.cpu().numpy(), L, x, wr, inp["bias"], k)
+    assert np.abs(w.cpu().numpy()[same] - ref_w[same]).max() <= U.WEIGHT_ABS
+
+
+# ---------------------------------------------------------------- permute
+
+PERMUTE_IDS = [(3000, 256, 8, 1.0), (2049, 8, 2, None), (1024, 128, 8, 1.1), (5, 4, 4, None),
+               (700, 1, 1, None), (4000, 32, 4, None)]
+
+
+def _run_permute(ids, x_dev, E, dtype):
+    T, k = ids.shape
+    P = T * k
+    b = B()
+    dev = "cuda"
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(P, dtype=torch.int32, device=dev)
+    inv = torch.empty(P, dtype=torch.int32, device=dev)
+    xp = None if x_dev is None else torch.empty(P, x_dev.shape[1], dtype=x_dev.dtype, device=dev)
+    ws = torch.empty(max(1, b.permute_workspace_size(T, k, E)), dtype=torch.uint8, device=dev)
+    b.permute(_i32(ids), x_dev, E, counts, offsets, perm, inv, xp, ws)
+    torch.cuda.synchronize()
+    return counts, offsets, perm, inv, xp
+
+
+@pytest.mark.parametrize("T,E,k,s", PERMUTE_IDS)
+def test_permute_bit_exact(gpu, T, E, k, s):
+    ids = W.gen_ids(T, E, k, seed=T + E, zipf_s=s)
+    x = W.gen_matrix((T, 64), seed=T, dtype="bf16")
+    counts, offsets, perm, inv, xp = _run_permute(ids, U.dev_tensor(x, "bf16"), E, "bf16")
+    rc, ro, rp, ri = O.permute(ids, E)
+    assert (counts.cpu().numpy() == rc).all()
+    assert (offsets.cpu().numpy() == ro).all()
+    assert (perm.cpu().numpy() == rp).all()
+    assert (inv.cpu().numpy() == ri).all()
+    assert (U.host_bits(xp) == x[rp // k]).all()
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_permute_workload(gpu, name):
+    wl, inp = U.small_inputs(name)
+    _, _, _, ids, _ = _oracle_routing(wl, inp)
+    counts, offsets, perm, inv, xp = _run_permute(ids, U.dev_tensor(inp["x"], wl.dtype), wl.E, wl.dtype)
+    rc, ro, rp, ri = O.permute(ids, wl.E)
+    assert (counts.cpu().numpy() == rc).all() and (offsets.cpu().numpy() == ro).all()
+    assert (perm.cpu().numpy() == rp).all() and (inv.cpu().numpy() == ri).all()
+    assert (U.host_bits(xp) == np.asarray(inp["x"])[rp // wl.k]).all()
+
+
+def test_permute_empty(gpu):
+    b = B()
+    counts = torch.full((8,), 7, dtype=torch.int32, device=gpu)
+    offsets = torch.full((9,), 7, dtype=torch.int32, device=gpu)
+    ids = torch.empty(0, 2, dtype=torch.int32, device=gpu)
+    ws = torch.empty(16, dtype=torch.uint8, device=gpu)
+    b.permute(ids, None, 8, counts, offsets, torch.empty(0, dtype=torch.int32, device=gpu),
+              torch.empty(0, dtype=torch.int32, device=gpu), None, ws)
+    torch.cuda.synchronize()
+    assert (counts.cpu() == 0).all() and (offsets.cpu() == 0).all()
+
+
+# ------------------------------------------------------- expert projections
+
+def _grouped_inputs(name):
+    wl, inp = U.small_inputs(name)
+    _, _, _, ids, w = _oracle_routing(wl, inp)
+    counts, offsets, perm, inv = O.permute(ids, wl.E)
+    x_perm = np.asarray(inp["x"])[perm // wl.k]          # storage-format rows in grouped order
+    return wl, inp, ids, w, offsets, perm, inv, x_perm
+
+
+@pytest.mark.parametrize("decode", [False, True], ids=["grouped", "decode"])
+@pytest.mark.parametrize("name", SMALL)
+def test_gateup_swiglu(gpu, name, decode):
+    wl, inp, ids, w, offsets, perm, inv, x_perm = _grouped_inputs(name)
+    if decode and wl.P > 1024:
+        pytest.skip("decode calls take at most 1024 rows")
+    h = torch.empty(wl.P, wl.f, dtype=U.torch_dtype(wl.dtype), device=gpu)
+    B().gateup_swiglu(U.dev_tensor(x_perm, wl.dtype), U.dev_tensor(inp["gu"], wl.dtype), _i32(offsets), h,
+                      decode=decode)
+    torch.cuda.synchronize()
+    ref = O.grouped_gate_up_swiglu(W.values(x_perm, wl.dtype), W.values(inp["gu"], wl.dtype), offsets)
+    U.assert_close(U.host_values(h), ref, wl.dtype, f"{name} H")
+
+
+@pytest.mark.parametrize("decode", [False, True], ids=["grouped", "decode"])
+@pytest.mark.parametrize("name", SMALL)
+def test_down(gpu, name, decode):
+    wl, inp, ids, w, offsets, perm, inv, x_perm = _grouped_inputs(name)
+    if decode and wl.P > 1024:
+        pytest.skip("decode calls take at most 1024 rows")
+    h = W.gen_matrix((wl.P, wl.f), seed=wl.seed + 7, std=0.5, dtype=wl.dtype)
+    y = torch.empty(wl.P, wl.d, dtype=U.torch_dtype(wl.dtype), device=gpu)
+    B().down(U.dev_tensor(h, wl.dtype), U.dev_tensor(inp["dn"], wl.dtype), _i32(offsets), y, decode=decode)
+    torch.cuda.synchronize()
+    ref = O.grouped_down(W.values(h, wl.dtype), W.values(inp["dn"], wl.dtype), offsets)
+    U.assert_close(U.host_values(y), ref, wl.dtype, f"{name} Y_perm")
+
+
+@pytest.mark.parametrize("shared", [False, True])
+@pytest.mark.parametrize("name", SMALL)
+def test_combine(gpu, name, shared):
+    wl, inp, ids, w, offsets, perm, inv, x_perm = _grouped_inputs(name)
+    yp = W.gen_matrix((wl.P, wl.d), seed=wl.seed + 8, dtype=wl.dtype)
+    ys = W.gen_matrix((wl.T, wl.d), seed=wl.seed + 9, dtype=wl.dtype) if shared else None
+    wf32 = w.astype(np.float32)
+    y = torch.empty(wl.T, wl.d, dtype=U.torch_dtype(wl.dtype), device=gpu)
+    B().unpermute_combine(U.dev_tensor(yp, wl.dtype), _i32(inv), _f32(wf32),
+                          None if ys is None else U.dev_tensor(ys, wl.dtype), y)
+    torch.cuda.synchronize()
+    ref = O.unpermute_combine(W.values(yp, wl.dtype), inv, wf32,
+                              None if ys is None else W.values(ys, wl.dtype))
+    U.assert_close(U.host_values(y), ref, wl.dtype, f"{name} y")
+
+
+# ------------------------------------------------------------ whole layer
+
+def _layer_ref(wl, inp, x=None):
+    x64 = W.values(inp["x"] if x is None else x, wl.dtype)
+    wr = W.values(inp["wr"], wl.dtype)
+    gu = W.values(inp["gu"], wl.dtype)
+    dn = W.values(inp["dn"], wl.dtype)
+    sh = None if inp["shared"] is None else tuple(W.values(a, wl.dtype) for a in inp["shared"])
+    out = O.moe_layer(x64, wr, inp["bias"], gu, dn, wl.k, wl.score, sh)
+    return x64, wr, out
+
+
+@pytest.mark.parametrize("mode", ["grouped", "decode"])
+@pytest.mark.parametrize("name", SMALL)
+def test_layer(gpu, name, mode):
+    wl, inp = U.small_inputs(name)
+    if mode == "decode" and wl.P > 1024:
+        pytest.skip("decode calls take at most 1024 rows")
+    layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score, mode=mode)
+    y = layer.forward(U.dev_tensor(inp["x"], wl.dtype))
+    torch.cuda.synchronize()
+    x64, wr, out = _layer_ref(wl, inp)
+    same = U.routing_agreement(layer.ids.cpu().numpy(), out["logits"], x64, wr, inp["bias"], wl.k)
+    U.assert_close(U.host_values(y)[same], out["y"][same], wl.dtype, f"{name} layer")
+
+
+def test_layer_deterministic_and_token_equivariant(gpu):
+    wl, inp = U.small_inputs("c4s")
+    layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score)
+    x = U.dev_tensor(inp["x"], wl.dtype)
+    y1 = U.host_bits(layer.forward(x).clone())
+    y2 = U.host_bits(layer.forward(x).clone())
+    assert (y1 == y2).all(), "two runs differ"
+    pi = np.random.default_rng(3).permutation(wl.T)
+    yp = U.host_bits(layer.forward(x[torch.from_numpy(pi).to(gpu)].contiguous()).clone())
+    assert (yp == y1[pi]).all(), "not equivariant under a token permutation"
+
+
+def test_layer_zero_tokens(gpu):
+    wl, inp = U.small_inputs("c2s")
+    layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score)
+    y = layer.forward(torch.empty(0, wl.d, dtype=torch.bfloat16, device=gpu))
+    torch.cuda.synchronize()
+    assert y.shape == (0, wl.d)
+
+
+@pytest.mark.parametrize("mode", ["grouped", "decode"])
+def test_layer_one_token(gpu, mode):
+    wl, inp = U.small_inputs("c5s")
+    x1 = np.asarray(inp["x"])[5:6]
+    layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score, mode=mode)
+    y = layer.forward(U.dev_tensor(x1, wl.dtype))
+    torch.cuda.synchronize()
+    x64, wr, out = _layer_ref(wl, inp, x1)
+    U.routing_agreement(layer.ids.cpu().numpy(), out["logits"], x64, wr, inp["bias"], wl.k, max_frac=0)
+    U.assert_close(U.host_values(y), out["y"], wl.dtype, "T=1")
+
+
+def _custom_layer(T, d, f, E, k, seed, score="softmax", dtype="bf16"):
+    wl = W.Workload(f"custom{seed}", T, d, f, E, k, score, dtype, seed=seed, router_std=0.1)
+    x = W.gen_x(wl)
+    wr, bias = W.gen_router(wl)
+    gu, dn = W.gen_all_experts(wl)
+    return wl, dict(x=x, wr=wr, bias=bias, gu=gu, dn=dn, shared=None)
+
+
+@pytest.mark.parametrize("mode", ["grouped", "decode"])
+def test_layer_k_equals_E(gpu, mode):
+    wl, inp = _custom_layer(77, 128, 192, 6, 6, 901)
+    layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score, mode=mode)
+    y = layer.forward(U.dev_tensor(inp["x"], wl.dtype))
+    torch.cuda.synchronize()
+    x64, wr, out = _layer_ref(wl, inp)
+    U.routing_agreement(layer.ids.cpu().numpy(), out["logits"], x64, wr, None, wl.k)
+    assert (np.sort(layer.ids.cpu().numpy(), 1) == np.arange(6)).all()
+    U.assert_close(U.host_values(y), out["y"], wl.dtype, "k=E")
+
+
+@pytest.mark.parametrize("mode", ["grouped", "decode"])
+def test_layer_single_expert_is_dense(gpu, mode):
+    """E = 1, k = 1: the layer is the dense SwiGLU FFN of that expert."""
+    wl, inp = _custom_layer(150, 256, 320, 1, 1, 902)
+    layer = B().MoeLayer(U.device_weights(wl, inp), 1, "softmax", mode=mode)
+    y = layer.forward(U.dev_tensor(inp["x"], wl.dtype))
+    torch.cuda.synchronize()
+    ref = O.expert_ffn(W.values(inp["x"], "bf16"), W.values(inp["gu"][0], "bf16"), W.values(inp["dn"][0], "bf16"))
+    U.assert_close(U.host_values(y), ref, "bf16", "E=1")
+    assert (layer.wts.cpu() == 1.0).all()
+
+
+@pytest.mark.parametrize("mode", ["grouped", "decode"])
+def test_layer_all_tokens_one_expert(gpu, mode):
+    """A router bias that sends every token to expert 5 first: one full
+    group, every other group of the first slot empty; with k = 1 the output
+    is expert 5's dense FFN."""
+    wl, inp = _custom_layer(260, 128, 128, 16, 1, 903)
+    inp = dict(inp, bias=np.where(np.arange(16) == 5, 100.0, 0.0).astype(np.float32))
+    layer = B().MoeLayer(U.device_weights(wl, inp), 1, "softmax", mode=mode)
+    y = layer.forward(U.dev_tensor(inp["x"], wl.dtype))
+    torch.cuda.synchronize()
+    assert (layer.ids.cpu() == 5).all()
+    cnt = layer.counts.cpu().numpy()
+    assert cnt[5] == 260 and cnt.sum() == 260
+    ref = O.expert_ffn(W.values(inp["x"], "bf16"), W.values(inp["gu"][5], "bf16"), W.values(inp["dn"][5], "bf16"))
+    U.assert_close(U.host_values(y), ref, "bf16", "one expert")
+
+
+def test_layer_identical_experts_is_dense(gpu):
+    wl, inp = _custom_layer(199, 192, 256, 12, 3, 904, score="sigmoid")
+    inp = dict(inp, gu=np.repeat(inp["gu"][:1], 12, 0), dn=np.repeat(inp["dn"][:1], 12, 0))
+    layer = B().MoeLayer(U.device_weights(wl, inp), 3, "sigmoid")
+    y = layer.forward(U.dev_tensor(inp["x"], wl.dtype))
+    torch.cuda.synchronize()
+    ref = O.expert_ffn(W.values(inp["x"], "bf16"), W.values(inp["gu"][0], "bf16"), W.values(inp["dn"][0], "bf16"))
+    U.assert_close(U.host_values(y), ref, "bf16", "identical experts")
+
+
+@pytest.mark.parametrize("name", ["c4s", "c3s_t37"])
+def test_outputs_stay_in_bounds(gpu, name):
+    """Canary guard regions around every output buffer stay untouched."""
+    wl, inp = U.small_inputs(name)
+    b = B()
+    T, d, f, E, k, P = wl.T, wl.d, wl.f, wl.E, wl.k, wl.P
+    G = 4096
+    canary = 0x5A5A
+
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * G,), canary, dtype=torch.int16, device=gpu)
+        if dtype == torch.int32:
+            buf = torch.full((n + 2 * G,), 0x5A5A5A5A, dtype=torch.int32, device=gpu)
+            return buf, buf[G:G + n]
+        if dtype == torch.float32:
+            buf = torch.full((n + 2 * G,), 0x5A5A5A5A, dtype=torch.int32, device=gpu)
+            return buf, buf[G:G + n].view(torch.float32)
+        return buf, buf[G:G + n].view(torch.bfloat16)
+
+    bufs = {}
+    bufs["logits"] = guarded(T * E, torch.float32)
+    bufs["ids"] = guarded(T * k, torch.int32)
+    bufs["w"] = guarded(T * k, torch.float32)
+    bufs["counts"] = guarded(E, torch.int32)
+    bufs["offsets"] = guarded(E + 1, torch.int32)
+    bufs["perm"] = guarded(P, torch.int32)
+    bufs["inv"] = guarded(P, torch.int32)
+    bufs["xp"] = guarded(P * d, torch.bfloat16)
+    bufs["h"] = guarded(P * f, torch.bfloat16)
+    bufs["yp"] = guarded(P * d, torch.bfloat16)
+    bufs["y"] = guarded(T * d, torch.bfloat16)
+    v = {n: t[1] for n, t in bufs.items()}
+    wts = U.device_weights(wl, inp)
+    x = U.dev_tensor(inp["x"], wl.dtype)
+    ws = torch.empty(b.permute_workspace_size(T, k, E), dtype=torch.uint8, device=gpu)
+    b.route(x, wts.w_router, wts.bias, k, wl.score, v["logits"].view(T, E), v["ids"].view(T, k), v["w"].view(T, k))
+    b.permute(v["ids"].view(T, k), x, E, v["counts"], v["offsets"], v["perm"], v["inv"], v["xp"].view(P, d), ws)
+    for dec in ((False, True) if P <= 1024 else (False,)):
+        b.gateup_swiglu(v["xp"].view(P, d), wts.w_gate_up, v["offsets"], v["h"].view(P, f), decode=dec)
+        b.down(v["h"].view(P, f), wts.w_down, v["offsets"], v["yp"].view(P, d), decode=dec)
+    b.unpermute_combine(v["yp"].view(P, d), v["inv"], v["w"].view(T, k), None, v["y"].view(T, d))
+    torch.cuda.synchronize()
+    for name, (buf, _) in bufs.items():
+        head, tail = buf[:G].cpu(), buf[-G:].cpu()
+        fill = 0x5A5A5A5A if buf.dtype == torch.int32 else canary
+        assert (head == fill).all() and (tail == fill).all(), f"{name}: guard region overwritten"
+
+
+def test_invalid_arguments_rejected(gpu):
+    lib = B().load()
+    x = torch.zeros(16, 100, dtype=torch.bfloat16, device=gpu)
+    assert lib.moe_route(x.data_ptr(), x.data_ptr(), None, 16, 100, 8, 2, 1, 0, x.data_ptr(),
+                         x.data_ptr(), x.data_ptr(), None) == B().MOE_ERR_ALIGNMENT
+    assert lib.moe_topk(x.data_ptr(), 16, 8, 9, 0, x.data_ptr(), x.data_ptr(), None) == B().MOE_ERR_INVALID_ARG
+    assert lib.moe_decode_down(x.data_ptr(), x.data_ptr(), x.data_ptr(), 5000, 64, 64, 4, 1, x.data_ptr(),
+                               None) == B().MOE_ERR_UNSUPPORTED
