@@ -179,7 +179,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--cpu-sample", type=int, default=48, help="tokens for the CPU oracle baseline")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernels", action="store_true", help="also print per-stage times to stderr")
     args = ap.parse_args(argv)
