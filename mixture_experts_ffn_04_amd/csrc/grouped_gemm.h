@@ -118,10 +118,11 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl) {
     mt = r / snr;
     nt = nbf * SN + (r - mt * snr);
   }
-  tl.g = g;
-  tl.row0 = glo + mt * BM;
-  tl.row_end = ghi;
-  tl.n0 = nt * BNO;
+  // workgroup-uniform: keep them in scalar registers
+  tl.g = __builtin_amdgcn_readfirstlane(g);
+  tl.row0 = __builtin_amdgcn_readfirstlane(glo + mt * BM);
+  tl.row_end = __builtin_amdgcn_readfirstlane(ghi);
+  tl.n0 = __builtin_amdgcn_readfirstlane(nt * BNO);
   return true;
 }
 
