@@ -171,6 +171,101 @@ def cpu_baseline(wl, host, sample_tokens: int):
                       f"{dt:.1f} s wall"}
 
 
+# ------------------------------------------------------------ profiles
+
+def copy_probe(nbytes: int, reps: int = 3):
+    """A plain device-to-device copy of known size (torch's copy kernel), to
+    calibrate what the HBM byte counters read for a known amount of data."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def summarize_trace(d: str, title: str, command: str, out: str):
+    """rocprofv3 --kernel-trace --stats CSV -> a short markdown table."""
+    rows = _read_csv(_find(d, "kernel_stats.csv"))
+    lines = [f"# {title}", "", "Command:", "", "```", command, "```", "",
+             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                     f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.1f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out)
+
+
+def _pmc_by_kernel(d: str):
+    import collections
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _read_csv(_find(d, "counter_collection.csv")):
+        acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return acc
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                      kernel_match: str, kernel: str, workload: str, copy_bytes: int, command: str,
+                      out_md: str, out_json: str):
+    """Two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    over the benchmark -> HBM bytes per launch of the matched kernel, each
+    counter scaled by what it reads, in its own passes, for a plain copy of
+    copy_bytes (bench.py --copy-probe)."""
+    f = _pmc_by_kernel(fetch_dir)
+    w = _pmc_by_kernel(write_dir)
+    cf = _pmc_by_kernel(copy_fetch_dir)
+    cw = _pmc_by_kernel(copy_write_dir)
+
+    def per_dispatch(tab, match, counter):
+        vals = [v for k, c in tab.items() if match in k for v in c.get(counter, [])]
+        if not vals:
+            raise ValueError(f"no {counter} for {match}")
+        return float(np.median(vals)) * 1024.0
+
+    copy_fetch = per_dispatch(cf, "copy", "FETCH_SIZE")
+    copy_write = per_dispatch(cw, "copy", "WRITE_SIZE")
+    sf, sw = copy_bytes / copy_fetch, copy_bytes / copy_write
+    kf = per_dispatch(f, kernel_match, "FETCH_SIZE") * sf
+    kw = per_dispatch(w, kernel_match, "WRITE_SIZE") * sw
+    rec = {"source_hash": kernel_source_hash(kernel), "bytes_per_launch": kf + kw,
+           "fetch_bytes": kf, "write_bytes": kw, "copy_scale_fetch": sf, "copy_scale_write": sw,
+           "kernel_match": kernel_match}
+    table = {}
+    if os.path.exists(out_json):
+        table = json.load(open(out_json))
+    table[f"{kernel}:{workload}"] = rec
+    with open(out_json, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+    lines = [f"# HBM traffic: {kernel} on workload {workload}", "", "Commands:", "", "```", command, "```", "",
+             f"- copy calibration: {copy_bytes} bytes copied; FETCH_SIZE read {copy_fetch:.4g} B "
+             f"(scale {sf:.4f}), WRITE_SIZE read {copy_write:.4g} B (scale {sw:.4f})",
+             f"- kernel `{kernel_match}`: fetch {kf/1e6:.2f} MB, write {kw/1e6:.2f} MB per launch "
+             f"(scaled, median over dispatches)",
+             f"- source hash of the kernel files when measured: {rec['source_hash']}"]
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out_md)
+
+
 # ------------------------------------------------------------ main
 
 def main(argv=None):
@@ -182,7 +277,24 @@ def main(argv=None):
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernels", action="store_true", help="also print per-stage times to stderr")
+    ap.add_argument("--copy-probe", type=int, default=0, help="run a plain copy of this many bytes and exit")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("DIR", "TITLE", "COMMAND", "OUT"))
+    ap.add_argument("--summarize-traffic", nargs=11,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "MATCH", "KERNEL",
+                             "WORKLOAD", "COPY_BYTES", "COMMAND", "OUT_MD", "OUT_JSON"))
     args = ap.parse_args(argv)
+
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return 0
+    if args.summarize_traffic:
+        a = list(args.summarize_traffic)
+        a[7] = int(a[7])
+        summarize_traffic(*a)
+        return 0
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the layer runs on a single MI355X and this build has no "

@@ -3,14 +3,15 @@
  * Instinct MI355X (CDNA4, gfx950), as a C ABI.
  *
  * The layer is the one described in "Mixture of Experts (MoEs) in
- * Transformers" (Hugging Face blog).  Section "From Dense to Sparse": a dense
- * feed-forward layer is replaced by a set of experts (learnable
- * sub-networks) and, per token, a router selects a few of them from the
- * token's hidden representation.  Section "Expert Backend": an execution
- * strategy must send tokens to their selected experts' weights, run the
- * projections, apply the routing weights and collect / reorder the results;
- * its "grouped_mm" strategy sorts tokens by expert ID, groups them and runs
- * one grouped GEMM.  The calls below are those steps, in order:
+ * Transformers" (Hugging Face blog).  Section "From Dense to Sparse": a
+ * bank of small trainable feed-forward networks (experts) stands in for a
+ * dense feed-forward block, and for each token a router picks a few of them
+ * from that token's activations.  Section "Expert Backend": an execution
+ * strategy has to route tokens to their chosen experts' weights, run the
+ * projections, scale by the routing weights and return the results in
+ * token order; its "grouped_mm" strategy orders tokens by expert, makes
+ * each expert's tokens contiguous and runs one grouped matrix product.
+ * The calls below are those steps, in order:
  *
  *   moe_route                        router logits, top-k, routing weights
  *   moe_topk                         top-k + weights from given logits
@@ -22,7 +23,7 @@
  *   moe_decode_gateup_swiglu         small-batch variants that stream only
  *   moe_decode_down                  the active experts' weights
  *
- * Expert weights are packed per layer in one contiguous tensor, the layout
+ * All experts of a layer share one packed buffer per projection, the layout
  * the article's "Dynamic Weight Loading with WeightConverter" subsection
  * produces: per-expert gate (w1) and up (w3) matrices of shape [f, d] are
  * stacked over experts and concatenated along dim 1, giving
@@ -87,8 +88,8 @@ MOE_API int moe_abi_version(void);
 MOE_API const char* moe_status_string(moe_status s);
 
 /*
- * Router (article, "From Dense to Sparse": the router selects a small subset
- * of experts per token from its hidden representation).
+ * Router (article, "From Dense to Sparse": per token, a few experts are
+ * chosen from scores computed on the token's activations).
  *
  *   logits[t][e]  = sum_i x[t][i] * w_router[e][i] + bias[e]      (fp32)
  *   topk_ids[t][j] = expert with the j-th largest logit of token t; equal
@@ -118,8 +119,9 @@ MOE_API moe_status moe_topk(const float* logits, int64_t T, int32_t E, int32_t k
 MOE_API size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t E);
 
 /*
- * Sort the routed (token, slot) pairs by expert ID ("grouped_mm" strategy,
- * article section "Expert Backend").  With p = t*k + j:
+ * Order the routed (token, slot) pairs by expert ID, each expert's pairs
+ * contiguous ("grouped_mm" strategy, article section "Expert Backend").
+ * With p = t*k + j:
  *
  *   counts[e]    = #{p : topk_ids[p] == e}
  *   offsets[0]   = 0, offsets[e+1] = offsets[e] + counts[e]  (offsets[E] = T*k)

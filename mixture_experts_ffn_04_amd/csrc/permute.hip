@@ -1,7 +1,7 @@
-// Sort the routed (token, slot) pairs by expert ID and group them -- the
-// first step of the "grouped_mm" strategy (article "Mixture of Experts (MoEs)
-// in Transformers", section "Expert Backend") -- and gather the token rows
-// into that order.
+// Order the routed (token, slot) pairs by expert ID so each expert's pairs
+// are contiguous -- the first step of the "grouped_mm" strategy (article
+// "Mixture of Experts (MoEs) in Transformers", section "Expert Backend") --
+// and gather the token rows into that order.
 //
 // Four launches, no host synchronisation:
 //   1. histogram  chunks of kChunk pairs; per-chunk expert counts with LDS

@@ -1,8 +1,8 @@
 // Router: logits, top-k selection and routing weights.
 //
 // Article "Mixture of Experts (MoEs) in Transformers", section "From Dense
-// to Sparse": for each token a router picks a small subset of the experts
-// from the token's hidden representation.
+// to Sparse": per token, a few experts are chosen from scores computed on
+// the token's activations.
 //
 // Logits are a dense contraction x[T][d] . w_router[E][d]^T, computed by the
 // grouped GEMM kernels as a single group with a "+ bias, fp32" epilogue.

@@ -5,17 +5,19 @@ import this module.  The product path (the HIP library and its binding)
 never calls it, and it shares no code with that path.
 
 What it computes.  The article "Mixture of Experts (MoEs) in Transformers"
-(Hugging Face blog) describes the layer in its section "From Dense to
-Sparse": dense feed-forward layers are replaced by a set of experts, each a
-learnable sub-network, and for every token a router picks a small subset of
-them from the token's hidden representation.  Its section "Expert Backend"
-states what any execution strategy must do -- send each token to its selected
-experts' weights, run the projections, apply the routing weights, then
-collect and reorder the results -- and names three strategies: "eager"
-(loop over the selected experts, projections per expert; the correctness
-reference), "batched_mm" (per-token copies of the selected weights, one
-batched GEMM) and "grouped_mm" (sort tokens by expert ID, group, one grouped
-GEMM).  All three compute the same sum
+(Hugging Face blog), section "From Dense to Sparse": some dense
+feed-forward blocks of a Transformer become a bank of experts -- each one a
+small trainable network -- and a router chooses, per token and from that
+token's activations, the few experts that will process it.  Section
+"Expert Backend" lists the duties of any execution strategy (route each
+token to the weights of its chosen experts, run their projections, scale by
+the routing weights, and put the results back in token order) and three
+interchangeable strategies: "eager" (iterate over the experts that received
+tokens, running each expert's projections in turn; meant for checking and
+debugging), "batched_mm" (copy the chosen weights per token and run one
+batched matrix product) and "grouped_mm" (order the tokens by the expert
+they were routed to, make each expert's tokens contiguous, run one grouped
+matrix product).  All three evaluate the same sum
 
     y_t = sum_j  w_tj * FFN_{e_tj}(x_t)      (+ S(x_t) with a shared expert)
 
@@ -69,7 +71,7 @@ def _f64(a) -> np.ndarray:
 def router_logits(x, w_router, bias=None) -> np.ndarray:
     """logits[t, e] = sum_i x[t, i] * w_router[e, i] + bias[e]   (float64).
 
-    The router scores every expert from the token's hidden representation
+    Every expert gets a score computed from the token's activations
     (article, section "From Dense to Sparse").
     """
     L = _f64(x) @ _f64(w_router).T
@@ -123,8 +125,8 @@ def route(logits, k: int, score: str, decide_dtype=np.float32):
 # ----------------------------------------------------------- sort by expert
 
 def permute(ids, E: int):
-    """Sort the routed pairs by expert ID ("grouped_mm": sort tokens by expert
-    ID and group them; article section "Expert Backend").
+    """Order the routed pairs by expert ID and make each expert's pairs
+    contiguous (the "grouped_mm" strategy, article section "Expert Backend").
 
     Returns
       counts[e]    number of pairs routed to expert e

@@ -1,0 +1,82 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports exactly
+what include/libmoe.h declares, and its host-side validation returns the
+documented status codes before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmoe.h")
+
+
+def declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mixture_experts_ffn_04_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    return binding.load()
+
+
+def test_header_declares_the_path():
+    names = declared()
+    for n in ["moe_route", "moe_topk", "moe_permute", "moe_permute_workspace_size",
+              "moe_grouped_gemm_gateup_swiglu", "moe_grouped_gemm_down", "moe_unpermute_combine",
+              "moe_decode_gateup_swiglu", "moe_decode_down", "moe_abi_version", "moe_status_string"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from mixture_experts_ffn_04_amd import binding
+    for n in declared():
+        assert hasattr(lib, n), n
+    assert set(binding.EXPORTS) == set(declared())
+
+
+def test_version_and_strings(lib):
+    assert lib.moe_abi_version() == 1
+    for s in range(6):
+        assert lib.moe_status_string(s)
+    assert b"unknown" in lib.moe_status_string(99)
+
+
+def test_validation_without_gpu(lib):
+    from mixture_experts_ffn_04_amd import binding as B
+    P = 4096   # a fake, 16-byte aligned "device" address: validation fails before any use
+    # k out of range, E too large, unknown score
+    assert lib.moe_topk(P, 10, 8, 0, 0, P, P, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_topk(P, 10, 8, 9, 0, P, P, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_topk(P, 10, 300, 2, 0, P, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_topk(P, 10, 8, 17, 0, P, P, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_topk(P, 10, 8, 2, 7, P, P, None) == B.MOE_ERR_INVALID_ARG
+    # d not a multiple of 64, misaligned pointer, null
+    assert lib.moe_route(P, P, None, 10, 100, 8, 2, 1, 0, P, P, P, None) == B.MOE_ERR_ALIGNMENT
+    assert lib.moe_route(P + 2, P, None, 10, 128, 8, 2, 1, 0, P, P, P, None) == B.MOE_ERR_ALIGNMENT
+    assert lib.moe_route(None, P, None, 10, 128, 8, 2, 1, 0, P, P, P, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(P, P, None, 10, 128, 8, 2, 5, 0, P, P, P, None) == B.MOE_ERR_INVALID_ARG
+    # T = 0 is a valid no-op
+    assert lib.moe_route(None, None, None, 0, 128, 8, 2, 1, 0, None, None, None, None) == B.MOE_OK
+    assert lib.moe_topk(None, 0, 8, 2, 0, None, None, None) == B.MOE_OK
+    # permute workspace
+    need = lib.moe_permute_workspace_size(1000, 4, 32)
+    assert need >= 4 * 32
+    assert lib.moe_permute(P, P, 1000, 128, 32, 4, 1, P, P, P, P, P, P, need - 1, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_permute(P, P, 1000, 128, 32, 4, 1, P, P, P, P, P, None, need, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_permute(P, P, 1000, 100, 32, 4, 1, P, P, P, P, P, P, need, None) == B.MOE_ERR_ALIGNMENT
+    # projections
+    for fn in (lib.moe_grouped_gemm_gateup_swiglu, lib.moe_grouped_gemm_down,
+               lib.moe_decode_gateup_swiglu, lib.moe_decode_down):
+        assert fn(P, P, P, 100, 128, 96, 8, 1, P, None) == B.MOE_ERR_ALIGNMENT
+        assert fn(P, P, P, 100, 128, 128, 0, 1, P, None) == B.MOE_ERR_INVALID_ARG
+        assert fn(P, P, P, 100, 128, 128, 257, 1, P, None) == B.MOE_ERR_UNSUPPORTED
+        assert fn(P, P, None, 100, 128, 128, 8, 1, P, None) == B.MOE_ERR_INVALID_ARG
+        assert fn(None, None, None, 0, 128, 128, 8, 1, None, None) == B.MOE_OK
+    assert lib.moe_decode_down(P, P, P, 1025, 128, 128, 8, 1, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_unpermute_combine(P, P, P, None, 10, 100, 2, 1, P, None) == B.MOE_ERR_ALIGNMENT
+    assert lib.moe_unpermute_combine(P, P, P, None, 10, 128, 0, 1, P, None) == B.MOE_ERR_INVALID_ARG

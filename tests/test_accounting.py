@@ -1,0 +1,40 @@
+"""Host-side accounting of bench.py against the article's own worked example
+(tests/golden/decode_bandwidth_model.json) and the closed-form work counts."""
+import json
+import os
+
+import pytest
+
+import bench
+import moe_workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "decode_bandwidth_model.json")
+
+
+def test_decode_bandwidth_model_matches_article():
+    g = json.load(open(GOLDEN))
+    est = bench.decode_tokens_per_s(g["memory_bandwidth_GB_per_s"] * 1e9, g["active_params_billion"] * 1e9,
+                                    g["bytes_per_param_bf16"])
+    assert round(est) == g["estimate_tokens_per_s"]                      # 800 / (3.6 * 2) = 111.1
+    assert abs(est - g["measured_tokens_per_s"]) / g["measured_tokens_per_s"] < 0.05
+
+
+@pytest.mark.parametrize("name,flops", [("c2", 2.886e12), ("c4", 6.228e11), ("c5", 1.305e13)])
+def test_layer_flops(name, flops):
+    assert abs(bench.layer_flops(W.get(name)) - flops) / flops < 2e-3
+
+
+def test_layer_bytes_c5():
+    wl = W.get("c5")
+    assert abs(bench.layer_bytes(wl, 256) - 23.11e9) / 23.11e9 < 2e-3
+
+
+def test_gateup_counts():
+    wl = W.get("c2")
+    assert bench.gateup_flops(wl) == 4.0 * 8192 * 4096 * 14336
+    assert bench.gateup_bytes(wl, 8) == 2 * (2 * 14336 * 4096 * 8 + 8192 * 4096 + 8192 * 14336)
+
+
+def test_multi_gpu_request_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
