@@ -10,13 +10,14 @@
 // of the experts that have tokens, and experts with no tokens are never
 // read.
 //
-// Workgroup = (expert g, 16 output columns), 4 waves.  The K dimension is
-// dealt to the waves in 32-element steps (wave w takes steps w, w+4, ...),
-// so the workgroup streams each 16-row weight slab in 256-byte runs per row
-// with many loads in flight; the four partial sums meet in LDS.  The tokens
-// of the expert (up to 64 per pass) are the 16-wide operand of
-// v_mfma_f32_16x16x32_bf16, the weight rows the 16-tall one, so each lane
-// ends with 4 consecutive output columns of one token row.
+// Workgroup = (expert g, 16 output columns), 4 waves.  Each wave takes a
+// contiguous quarter of K and streams it in unrolled batches (all loads of
+// a batch issued before its MFMAs); the four partial sums meet in LDS.  The
+// number of 16-token chunks (1, 2 or 4) is chosen per workgroup up front so
+// the streaming loop itself has no branches.  The tokens of the expert (up
+// to 64 per pass) are the 16-wide operand of v_mfma_f32_16x16x32_bf16, the
+// weight rows the 16-tall one, so each lane ends with 4 consecutive output
+// columns of one token row.
 #include "common.h"
 
 namespace moe {
@@ -24,60 +25,105 @@ namespace {
 
 constexpr int kMC = 4;        // 16-row token chunks per pass (64 tokens)
 
+typedef __attribute__((address_space(1))) const u32x4 gu4;
+
+// token rows: reused by every weight tile of the expert, so cached loads
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+  return __builtin_bit_cast(bf16x8, *(const gu4*)p);
 }
 
-template <bool SWIGLU>
+// weight rows: cached loads.  Each load instruction covers 64 of the 128
+// bytes of a line per row; the neighbouring step reads the other half from
+// L2 (non-temporal loads measured slower for this pattern).
+__device__ __forceinline__ bf16x8 ld8_stream(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *(const gu4*)p);
+}
+
+// Partial sums of one wave over K steps [s0, s1) (32 elements each) for MC
+// token chunks, in batches of U steps with every load of a batch issued
+// before its MFMAs, so each wave keeps U x (NH + MC) 1 KB loads in flight.
+// The last batch is padded: its steps past s1 load the last valid step and
+// use a zero token fragment, so they add nothing and cost no extra round
+// trip.
+template <bool SWIGLU, int MC, int U>
+__device__ __forceinline__ void decode_partial(const uint16_t* wg, const uint16_t* wu, const uint16_t* const* xr,
+                                               int s0, int s1, f32x4* ag, f32x4* au) {
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) {
+    ag[mc] = f32x4{};
+    au[mc] = f32x4{};
+  }
+  const bf16x8 zero8 = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  for (int s = s0; s < s1; s += U) {
+    bf16x8 wgf[U], wuf[U], tf[U][MC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int su = s + u < s1 ? s + u : s1 - 1;
+      const int64_t k0 = static_cast<int64_t>(su) * 32;
+      wgf[u] = ld8_stream(wg + k0);
+      if (SWIGLU) wuf[u] = ld8_stream(wu + k0);
+#pragma unroll
+      for (int mc = 0; mc < MC; ++mc) tf[u][mc] = ld8(xr[mc] + k0);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // the whole batch of loads is issued before any MFMA waits
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = s + u < s1;
+#pragma unroll
+      for (int mc = 0; mc < MC; ++mc) {
+        const bf16x8 t = live ? tf[u][mc] : zero8;
+        ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wgf[u], t, ag[mc], 0, 0, 0);
+        if (SWIGLU) au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wuf[u], t, au[mc], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// EPI: 0 = bf16 store, 1 = SwiGLU pairs (bf16), 2 = fp32 + bias (router
+// logits for small batches; N need not be a multiple of 16 there).
+template <int EPI>
 __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                                                     const int32_t* __restrict__ off, int rows, int K, int N, int G,
-                                                     uint16_t* __restrict__ C) {
+                                                     const int32_t* __restrict__ off, const float* __restrict__ bias,
+                                                     int rows, int K, int N, int G, void* __restrict__ Cv) {
+  constexpr bool SWIGLU = EPI == 1;
   constexpr int NH = SWIGLU ? 2 : 1;
   __shared__ float red[4][kMC][NH][4][64];
-  const int ntiles = N / 16;
+  const int ntiles = (N + 15) / 16;
   const int g = blockIdx.x / ntiles;
   if (g >= G) return;
   const int n0 = (blockIdx.x - g * ntiles) * 16;
-  const int lo = clamp_off(off[g], rows);
-  const int hi = clamp_off(off[g + 1], rows);
+  const int lo = off ? clamp_off(off[g], rows) : 0;
+  const int hi = off ? clamp_off(off[g + 1], rows) : rows;
   if (hi <= lo) return;                      // expert without tokens: its weights are never read
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, kq = lane >> 4;
   const int64_t brows = SWIGLU ? 2 * static_cast<int64_t>(N) : N;
   const uint16_t* Bg = B + static_cast<int64_t>(g) * brows * K;
-  const uint16_t* wg = Bg + static_cast<int64_t>(n0 + i16) * K + kq * 8;
-  const uint16_t* wu = Bg + static_cast<int64_t>(SWIGLU ? N + n0 + i16 : n0 + i16) * K + kq * 8;
+  const int wrow = n0 + i16 < N ? n0 + i16 : N - 1;     // past-N rows read a valid row; never stored
+  const uint16_t* wg = Bg + static_cast<int64_t>(wrow) * K + kq * 8;
+  const uint16_t* wu = Bg + static_cast<int64_t>(SWIGLU ? N + wrow : wrow) * K + kq * 8;
+  // contiguous K range per wave
   const int steps = K / 32;
-  const bf16x8 zero8 = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  const int per = (steps + 3) / 4;
+  const int s0 = min(steps, wave * per);
+  const int s1 = min(steps, s0 + per);
 
   for (int m0 = lo; m0 < hi; m0 += 16 * kMC) {
     const int mcn = min(kMC, (hi - m0 + 15) / 16);
-    f32x4 ag[kMC], au[kMC];
     const uint16_t* xr[kMC];
-    bool xv[kMC];
 #pragma unroll
     for (int mc = 0; mc < kMC; ++mc) {
-      ag[mc] = f32x4{};
-      au[mc] = f32x4{};
-      const int row = m0 + mc * 16 + i16;
-      xv[mc] = (mc < mcn) && (row < hi);
-      xr[mc] = A + static_cast<int64_t>(xv[mc] ? row : lo) * K + kq * 8;
+      const int row = m0 + mc * 16 + i16;        // rows past the group read a valid row; never stored
+      xr[mc] = A + static_cast<int64_t>(row < hi ? row : lo) * K + kq * 8;
     }
-#pragma unroll 4
-    for (int s = wave; s < steps; s += 4) {
-      const int64_t k0 = static_cast<int64_t>(s) * 32;
-      const bf16x8 wgf = ld8(wg + k0);
-      bf16x8 wuf = zero8;
-      if (SWIGLU) wuf = ld8(wu + k0);
-#pragma unroll
-      for (int mc = 0; mc < kMC; ++mc) {
-        if (mc < mcn) {
-          const bf16x8 tf = xv[mc] ? ld8(xr[mc] + k0) : zero8;
-          ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wgf, tf, ag[mc], 0, 0, 0);
-          if (SWIGLU) au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wuf, tf, au[mc], 0, 0, 0);
-        }
-      }
+    f32x4 ag[kMC], au[kMC];
+    if (mcn == 1) {
+      decode_partial<SWIGLU, 1, 8>(wg, wu, xr, s0, s1, ag, au);
+    } else if (mcn == 2) {
+      decode_partial<SWIGLU, 2, 4>(wg, wu, xr, s0, s1, ag, au);
+    } else {
+      decode_partial<SWIGLU, 4, 4>(wg, wu, xr, s0, s1, ag, au);
     }
 #pragma unroll
     for (int mc = 0; mc < kMC; ++mc) {
@@ -106,33 +152,48 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
           }
           o[r] = gs;
         }
-        uint2 v;
-        v.x = pack_bf16x2(o[0], o[1]);
-        v.y = pack_bf16x2(o[2], o[3]);
-        *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * N + n0 + 4 * kq) = v;
+        if (EPI == 2) {
+          float* C = static_cast<float*>(Cv) + static_cast<int64_t>(row) * N;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int n = n0 + 4 * kq + r;
+            if (n < N) C[n] = o[r] + (bias ? bias[n] : 0.0f);
+          }
+        } else {
+          uint2 v;
+          v.x = pack_bf16x2(o[0], o[1]);
+          v.y = pack_bf16x2(o[2], o[3]);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Cv) + static_cast<int64_t>(row) * N + n0 + 4 * kq) = v;
+        }
       }
     }
     __syncthreads();
   }
 }
 
+template <int EPI>
+moe_status launch_decode(const void* A, const void* B, const int32_t* off, const float* bias, int64_t rows,
+                         int64_t K, int64_t N, int G, void* C, hipStream_t st) {
+  const int64_t grid = static_cast<int64_t>(G) * ceil_div(N, 16);
+  if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(decode_kernel<EPI>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), off, bias,
+                     static_cast<int>(rows), static_cast<int>(K), static_cast<int>(N), G, C);
+  return launch_status();
+}
+
 }  // namespace
 
 moe_status decode_bf16(bool swiglu, const void* A, const void* B, const int32_t* off, int64_t rows, int64_t K,
                        int64_t N, int G, void* C, hipStream_t st) {
-  const int64_t grid = static_cast<int64_t>(G) * (N / 16);
-  if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  if (swiglu)
-    hipLaunchKernelGGL(decode_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), off,
-                       static_cast<int>(rows), static_cast<int>(K), static_cast<int>(N), G,
-                       static_cast<uint16_t*>(C));
-  else
-    hipLaunchKernelGGL(decode_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), off,
-                       static_cast<int>(rows), static_cast<int>(K), static_cast<int>(N), G,
-                       static_cast<uint16_t*>(C));
-  return launch_status();
+  return swiglu ? launch_decode<1>(A, B, off, nullptr, rows, K, N, G, C, st)
+                : launch_decode<0>(A, B, off, nullptr, rows, K, N, G, C, st);
+}
+
+// Router logits for small batches: one group of T rows, N = E experts.
+moe_status decode_bf16_logits(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d,
+                              int32_t E, float* logits, hipStream_t st) {
+  return launch_decode<2>(x, w_router, nullptr, bias, T, d, E, 1, logits, st);
 }
 
 }  // namespace moe

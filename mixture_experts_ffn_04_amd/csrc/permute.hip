@@ -3,7 +3,8 @@
 // "Mixture of Experts (MoEs) in Transformers", section "Expert Backend") --
 // and gather the token rows into that order.
 //
-// Four launches, no host synchronisation:
+// Four launches (two when all pairs fit one chunk: histogram, scan and
+// scatter then share one workgroup), no host synchronisation:
 //   1. histogram  chunks of kChunk pairs; per-chunk expert counts with LDS
 //                 atomics (order-free, so deterministic) -> ws counts[chunk][E]
 //   2. scan       one workgroup: per expert, running sum over chunks (the
@@ -132,6 +133,72 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
   for (int64_t c = lane; c < row_chunks; c += 64) dst[c] = src[c];
 }
 
+// All of histogram, scan and stable scatter in one workgroup, for at most
+// kChunk pairs (small batches): one launch instead of three.
+__global__ __launch_bounds__(256) void permute_small_kernel(const int32_t* __restrict__ ids, int P, int E, int nbits,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ perm,
+                                                            int32_t* __restrict__ inv_perm) {
+  __shared__ int h[kMaxE];
+  __shared__ int base[kMaxE];
+  __shared__ int wsum[4];
+  const int t = threadIdx.x;
+  for (int e = t; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  for (int p = t; p < P; p += 256) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  // exclusive scan over experts, thread e owns expert e
+  const int lane = t & 63, w = t >> 6;
+  const int c = t < E ? h[t] : 0;
+  int v = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  int pre = 0;
+  for (int i = 0; i < w; ++i) pre += wsum[i];
+  const int excl = pre + v - c;
+  if (t < E) {
+    counts[t] = c;
+    offsets[t] = excl;
+    base[t] = excl;
+  }
+  if (t == E - 1) offsets[E] = excl + c;
+  __syncthreads();
+  if (w != 0) return;
+  // stable scatter by the first wave, 64 pairs at a time in order
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  for (int s0 = 0; s0 < P; s0 += 64) {
+    const int p = s0 + lane;
+    int e = -1;
+    if (p < P) e = ids[p];
+    const bool ok = e >= 0 && e < E;
+    uint64_t m = __ballot(ok);
+#pragma unroll 1
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = ok && ((e >> b) & 1);
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    int pos = 0;
+    if (ok) pos = base[e] + __popcll(m & below);
+    __builtin_amdgcn_wave_barrier();
+    if (ok) {
+      if (lane == 63 - __clzll(m)) base[e] += __popcll(m);
+      perm[pos] = p;
+      inv_perm[p] = pos;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 __global__ void zero_kernel(int32_t* __restrict__ a, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) a[i] = 0;
@@ -175,10 +242,15 @@ extern "C" moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
 
-  hipLaunchKernelGGL(hist_kernel, dim3(chunks), dim3(256), 0, st, topk_ids, static_cast<int>(P), E, cc);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, st, cc, chunks, E, counts, offsets);
-  hipLaunchKernelGGL(scatter_kernel, dim3(chunks), dim3(64), 0, st, topk_ids, static_cast<int>(P), E, nbits,
-                     cc, perm, inv_perm);
+  if (chunks == 1) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(256), 0, st, topk_ids, static_cast<int>(P), E, nbits,
+                       counts, offsets, perm, inv_perm);
+  } else {
+    hipLaunchKernelGGL(hist_kernel, dim3(chunks), dim3(256), 0, st, topk_ids, static_cast<int>(P), E, cc);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, st, cc, chunks, E, counts, offsets);
+    hipLaunchKernelGGL(scatter_kernel, dim3(chunks), dim3(64), 0, st, topk_ids, static_cast<int>(P), E, nbits,
+                       cc, perm, inv_perm);
+  }
   if (x_perm) {
     const int64_t row_chunks = d * elem_bytes(dtype) / 16;
     hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(ceil_div(P, 4))), dim3(256), 0, st,

@@ -5,7 +5,8 @@
 // the token's activations.
 //
 // Logits are a dense contraction x[T][d] . w_router[E][d]^T, computed by the
-// grouped GEMM kernels as a single group with a "+ bias, fp32" epilogue.
+// grouped GEMM kernels as a single group with a "+ bias, fp32" epilogue, or
+// for small batches by the split-K streaming kernel of the decode path.
 //
 // Selection: one wave per token.  Lane l holds logits l, l+64, l+128, l+192
 // (E <= 256).  k rounds of a wave-wide arg-max on the key (logit, -index)
@@ -19,6 +20,12 @@ namespace moe {
 
 moe_status gemm_bf16_logits(const GemmArgs& a, hipStream_t st);
 moe_status gemm_f32_logits(const GemmArgs& a, hipStream_t st);
+moe_status decode_bf16_logits(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d,
+                              int32_t E, float* logits, hipStream_t st);
+
+// Up to this many tokens the bf16 logits run on the split-K streaming kernel
+// (many workgroups even for one token); above it, on the tiled MFMA GEMM.
+constexpr int64_t kSmallRouteTokens = 256;
 
 namespace {
 
@@ -150,7 +157,10 @@ extern "C" moe_status moe_route(const void* x, const void* w_router, const float
   a.N = E;
   a.G = 1;
   hipStream_t st = as_stream(stream);
-  s = (dtype == MOE_BF16) ? gemm_bf16_logits(a, st) : gemm_f32_logits(a, st);
+  if (dtype == MOE_BF16 && T <= kSmallRouteTokens)
+    s = decode_bf16_logits(x, w_router, bias, T, d, E, logits, st);
+  else
+    s = (dtype == MOE_BF16) ? gemm_bf16_logits(a, st) : gemm_f32_logits(a, st);
   if (s != MOE_OK) return s;
   return launch_topk(logits, T, E, k, score, topk_ids, topk_w, st);
 }
