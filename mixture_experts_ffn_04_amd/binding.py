@@ -224,10 +224,11 @@ class MoeLayer:
             return False
         return T * self.k <= self.DECODE_MAX_ROWS
 
-    def forward(self, x: torch.Tensor, stream=None, marks: Optional[dict] = None) -> torch.Tensor:
+    def forward(self, x: torch.Tensor, stream=None, marks: Optional[dict] = None,
+                stages: Optional[tuple] = None) -> torch.Tensor:
         """Run the layer on x [T, d].  With `marks` (a dict), a pair of timing
-        events recorded on the launch stream brackets every stage and is
-        appended to marks[stage]."""
+        events recorded on the launch stream brackets every stage (or only the
+        stages named in `stages`) and is appended to marks[stage]."""
         T = x.shape[0]
         self._alloc(T)
         w = self.w
@@ -235,7 +236,7 @@ class MoeLayer:
         st = torch.cuda.current_stream() if stream is None else stream
 
         def mark(name, fn, *a):
-            if marks is None:
+            if marks is None or (stages is not None and name not in stages):
                 fn(*a)
                 return
             e0 = torch.cuda.Event(enable_timing=True)

@@ -1,23 +1,23 @@
-// bf16 grouped GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
+// bf16 grouped GEMMs on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// Workgroup: WM x WN waves.  Tile: BM token rows x BN weight rows x 64 K.
-// The MFMA runs the transposed product -- weight rows are its 32-row
-// operand, token rows its 32-column operand -- so each lane ends up with 4
-// consecutive output columns of one token row and writes them as one 8-byte
-// (bf16) or 16-byte (fp32) store.
+// Both kernels run the transposed product -- weight rows are the MFMA's
+// 32-row operand, token rows its 32-column operand -- so each lane ends up
+// with 4 consecutive output columns of one token row and writes them as one
+// 8-byte (bf16) or 16-byte (fp32) store.  Both operands are K-contiguous
+// rows, so a fragment (32 rows x 16 K) is one ds_read_b128 per lane.
 //
-// Data movement per K stage (64 elements = 128 bytes per row):
-//   global -> registers: 16-byte loads, 8 threads per row, so each load
-//   instruction moves whole 128-byte row segments;
-//   registers -> LDS: chunk c of row r lands at chunk position c ^ (r & 7),
-//   an XOR swizzle that keeps both the row-wise stores and the MFMA
-//   fragment reads (one 16-byte chunk from each of 32 consecutive rows)
-//   free of bank conflicts;
-//   LDS -> registers: one ds_read_b128 per 32x16 fragment, the fragments of
-//   the next 16-wide K slice read while the MFMAs of the current one run.
-// Two LDS buffers, one barrier per stage.  This register-staged kernel
-// serves the router logits; the expert projections use the direct-to-LDS
-// kernel further down.
+//  * gemm_bf16_dtl_kernel (expert projections): buffer loads straight into
+//    LDS (no register staging) with NS LDS stages of BK K-elements, so loads
+//    run NS-1 stages ahead of the MFMAs.
+//  * gemm_bf16_kernel (router logits): loads staged through registers into
+//    two LDS buffers.
+//
+// LDS layout: tile row r holds the BK elements of one weight or token row
+// as 16-byte chunks; chunk c is stored at position c ^ swz(r).  gfx950
+// serves a ds_read_b128 16 lanes (256 bytes, all 64 banks) per cycle; a
+// fragment read takes one chunk from each of 32 consecutive rows, and swz
+// spreads every group of 16 such rows over all 64 banks (and keeps the
+// row-wise writes conflict free).
 #include "grouped_gemm.h"
 
 namespace moe {
@@ -25,38 +25,41 @@ namespace moe {
 namespace {
 
 typedef __attribute__((address_space(1))) const u32x4 gu4;   // 16 bytes in global memory
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBK = 64;          // K per LDS stage
-constexpr int kChunks = kBK / 8; // 16-byte chunks per row per stage
+// raw buffer descriptor word 3 for gfx9-family untyped 32-bit accesses
+constexpr int kBufFlags = 0x00020000;
 
-// LDS swizzle: chunk c of tile row r is stored at chunk position
-// c ^ swz(r).  gfx950 serves a ds_read_b128 16 lanes (256 bytes, all 64
-// banks) per cycle; a row is 128 bytes, so even and odd rows fall in
-// different bank halves and the 8 same-parity rows among 16 consecutive
-// ones need 8 distinct positions, which swz gives.  It is also a
-// permutation within every aligned group of 8 rows (the 8-lane / 32-bank
-// case) and keeps the row-wise stores conflict free.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// CH = 16-byte chunks per tile row (8 for 128-byte rows, 4 for 64-byte rows).
+// 128-byte rows: rows r and r+1 sit in different 128-byte bank halves, and
+// the 8 same-parity rows among 16 need 8 distinct positions.  64-byte rows:
+// r % 4 picks the 64-byte quarter, so the 4 rows sharing it need 4 distinct
+// positions.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if (CH == 8) return (r & 7) ^ ((r >> 3) & 1);
+  return (r >> 2) & 3;
+}
 
-// Scheduling groups (sched_group_barrier masks): keep each K slice's MFMAs
-// interleaved with the LDS reads of the next slice, so LDS latency hides
-// under MFMA execution even with one wave per SIMD.
+// Scheduling groups (sched_group_barrier masks): each K slice's MFMAs are
+// interleaved one-to-one with the LDS reads of the next slice, so LDS
+// latency hides under MFMA execution.
 #define MOE_SG(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
 #define MOE_SG_MFMA 0x008
 #define MOE_SG_VMEM 0x020
 #define MOE_SG_DSR 0x100
 #define MOE_SG_DSW 0x200
 
-// One LDS stage: NV global loads, then the NR fragment reads of the first
-// K slice, then for each of the 4 slices its NM MFMAs paired one-to-one
-// with the reads of the next slice, then NW LDS writes of the next stage.
-template <int NR, int NM, int NV, int NW>
+// One LDS stage of KS 16-wide K slices: NV global loads, the NR fragment
+// reads of the first slice, then per slice its NM MFMAs paired with the
+// reads of the next slice, then NW LDS writes of the next stage.
+template <int NR, int NM, int NV, int NW, int KS>
 __device__ __forceinline__ void sched_stage() {
   constexpr int P = NR < NM ? NR : NM;
   if (NV) MOE_SG(MOE_SG_VMEM, NV);
   MOE_SG(MOE_SG_DSR, NR);
 #pragma unroll
-  for (int ks = 0; ks < 3; ++ks) {
+  for (int ks = 0; ks + 1 < KS; ++ks) {
 #pragma unroll
     for (int i = 0; i < P; ++i) {
       MOE_SG(MOE_SG_MFMA, 1);
@@ -69,89 +72,41 @@ __device__ __forceinline__ void sched_stage() {
   if (NW) MOE_SG(MOE_SG_DSW, NW);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int SN>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int NT = 64 * WM * WN;
-  constexpr int TM = BM / WM;             // token rows per wave
-  constexpr int TN = BN / WN;             // weight rows per wave
-  constexpr int FM = TM / 32;             // 32-row fragments per wave (tokens)
-  constexpr int FN = TN / 32;             // 32-row fragments per wave (weights)
-  static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "fragment shape");
-  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
-  constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;   // output columns per tile
-  constexpr int ROWS_PER_LD = NT / kChunks;                // rows per load instruction
-  static_assert(BN % ROWS_PER_LD == 0 && BM % ROWS_PER_LD == 0, "load shape");
-  constexpr int LD_B = BN / ROWS_PER_LD;                   // weight-tile loads per thread
-  constexpr int LD_A = BM / ROWS_PER_LD;                   // token-tile loads per thread
-  constexpr int STAGE = (BN + BM) * kChunks;               // 16-byte units per LDS stage
-
-  __shared__ u32x4 lds[2 * STAGE];
-
-  TileLoc tl;
-  if (!locate_tile<NT, BM, BNO, SN>(a, tl)) return;
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave % WM;
-  const int wn = wave / WM;
-  const int64_t K = a.K;
-  const int64_t N = a.N;
-
-  // ---- global load descriptors.  Rows past the group end (tokens) or past
-  // N (weights) read a valid row instead: they only feed output rows /
-  // columns that the epilogue masks, so no zero-fill select is needed.
-  const int ck = t & (kChunks - 1);     // chunk within the row
-  const int rr = t / kChunks;           // row within a slab of ROWS_PER_LD rows
-  const uint16_t* Ab = static_cast<const uint16_t*>(a.A);
-  const uint16_t* Bb = static_cast<const uint16_t*>(a.B) +
-      static_cast<int64_t>(tl.g) * ((EPI == EPI_SWIGLU) ? 2 * N : N) * K;
-
-  const gu4* bsrc[LD_B];
-#pragma unroll
-  for (int i = 0; i < LD_B; ++i) {
-    const int r = i * ROWS_PER_LD + rr;          // weight-tile row
-    int64_t src;
-    if (EPI == EPI_SWIGLU) {
-      const int half = r / (BN / 2);
-      const int64_t n = tl.n0 + (r - half * (BN / 2));
-      src = half * N + (n < N ? n : 0);
-    } else {
-      const int64_t n = tl.n0 + r;
-      src = n < N ? n : 0;
-    }
-    bsrc[i] = (const gu4*)(Bb + src * K + ck * 8);
-  }
-  const gu4* asrc[LD_A];
-#pragma unroll
-  for (int i = 0; i < LD_A; ++i) {
-    const int64_t row = static_cast<int64_t>(tl.row0) + i * ROWS_PER_LD + rr;
-    asrc[i] = (const gu4*)(Ab + (row < tl.row_end ? row : tl.row0) * K + ck * 8);
-  }
-
-  // stage kt_ -> register set (rb_, ra_)
-#define MOE_GLOAD(rb_, ra_, kt_)                                                        \
+// Fragment reads of K slice ks (16 wide) from LDS stage s_ with CH chunks
+// per row, and the FM x FN MFMAs on them.
+#define MOE_FRAGS(wf_, tf_, s_, ks_)                                                    \
   do {                                                                                  \
-    const int64_t o_ = static_cast<int64_t>(kt_) * (kBK / 8);                           \
-    _Pragma("unroll") for (int i = 0; i < LD_B; ++i) rb_[i] = bsrc[i][o_];              \
-    _Pragma("unroll") for (int i = 0; i < LD_A; ++i) ra_[i] = asrc[i][o_];              \
+    const int c_ = ((ks_) * 2 + khalf) ^ sw;                                            \
+    _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                   \
+      wf_[fn] = __builtin_bit_cast(bf16x8, (s_)[(wrow[fn] + l32) * CH + c_]);           \
+    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm)                                   \
+      tf_[fm] = __builtin_bit_cast(bf16x8, (s_)[(BN + wm * TM + fm * 32 + l32) * CH + c_]); \
   } while (0)
-  // register set -> LDS buffer buf_
-#define MOE_LSTORE(rb_, ra_, buf_)                                                      \
+#define MOE_MFMAS(wf_, tf_)                                                             \
   do {                                                                                  \
-    u32x4* s_ = lds + (buf_) * STAGE;                                                   \
-    _Pragma("unroll") for (int i = 0; i < LD_B; ++i) {                                  \
-      const int r_ = i * ROWS_PER_LD + rr;                                              \
-      s_[r_ * kChunks + (ck ^ swz(r_))] = rb_[i];                                      \
-    }                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < LD_A; ++i) {                                  \
-      const int r_ = BN + i * ROWS_PER_LD + rr;                                         \
-      s_[r_ * kChunks + (ck ^ swz(r_))] = ra_[i];                                      \
+    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm)                                   \
+      _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                 \
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf_[fn], tf_[fm], acc[fm][fn], 0, 0, 0); \
+  } while (0)
+// all KS slices of one stage, the reads of slice ks+1 in flight during the
+// MFMAs of slice ks
+#define MOE_COMPUTE(s_)                                                                 \
+  do {                                                                                  \
+    bf16x8 wf0[FN], tf0[FM], wf1[FN], tf1[FM];                                          \
+    MOE_FRAGS(wf0, tf0, s_, 0);                                                         \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ks += 2) {                              \
+      MOE_FRAGS(wf1, tf1, s_, ks + 1);                                                  \
+      MOE_MFMAS(wf0, tf0);                                                              \
+      if (ks + 2 < KS) MOE_FRAGS(wf0, tf0, s_, ks + 2);                                 \
+      MOE_MFMAS(wf1, tf1);                                                              \
     }                                                                                   \
   } while (0)
 
-  // ---- fragment rows in the LDS tile
-  int wrow[FN];
+// Fragment row of each of the FN weight fragments of wave column wn.  With
+// SwiGLU the tile holds BN/2 gate rows then the matching BN/2 up rows, and a
+// wave takes the same columns from both halves.
+template <int EPI, int BN, int TN, int FN>
+__device__ __forceinline__ void weight_frag_rows(int wn, int* wrow) {
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
     if (EPI == EPI_SWIGLU) {
@@ -161,66 +116,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
       wrow[fn] = wn * TN + fn * 32;
     }
   }
-  const int l32 = lane & 31;
-  const int khalf = lane >> 5;
-  const int sw = swz(l32);                 // every fragment starts on a multiple of 16 rows
+}
 
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-
-  // fragments of K slice ks_ (16 wide) from LDS buffer buf_
-#define MOE_FRAGS(wf_, tf_, buf_, ks_)                                                  \
-  do {                                                                                  \
-    const u32x4* s_ = lds + (buf_) * STAGE;                                             \
-    const int c_ = ((ks_) * 2 + khalf) ^ sw;                                            \
-    _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                   \
-      wf_[fn] = __builtin_bit_cast(bf16x8, s_[(wrow[fn] + l32) * kChunks + c_]);        \
-    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm)                                   \
-      tf_[fm] = __builtin_bit_cast(bf16x8, s_[(BN + wm * TM + fm * 32 + l32) * kChunks + c_]); \
-  } while (0)
-#define MOE_MFMAS(wf_, tf_)                                                             \
-  do {                                                                                  \
-    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm)                                   \
-      _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                 \
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf_[fn], tf_[fm], acc[fm][fn], 0, 0, 0); \
-  } while (0)
-#define MOE_COMPUTE(buf_)                                                               \
-  do {                                                                                  \
-    bf16x8 wf0[FN], tf0[FM], wf1[FN], tf1[FM];                                          \
-    MOE_FRAGS(wf0, tf0, buf_, 0);                                                       \
-    MOE_FRAGS(wf1, tf1, buf_, 1);                                                       \
-    MOE_MFMAS(wf0, tf0);                                                                \
-    MOE_FRAGS(wf0, tf0, buf_, 2);                                                       \
-    MOE_MFMAS(wf1, tf1);                                                                \
-    MOE_FRAGS(wf1, tf1, buf_, 3);                                                       \
-    MOE_MFMAS(wf0, tf0);                                                                \
-    MOE_MFMAS(wf1, tf1);                                                                \
-  } while (0)
-
-  const int nk = static_cast<int>(K / kBK);
-  u32x4 rb[LD_B], ra[LD_A];
-  MOE_GLOAD(rb, ra, 0);
-  MOE_LSTORE(rb, ra, 0);
-  __syncthreads();
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    MOE_GLOAD(rb, ra, kt + 1);          // in flight during the MFMAs below
-    MOE_COMPUTE(kt & 1);
-    MOE_LSTORE(rb, ra, (kt + 1) & 1);
-    sched_stage<FN + FM, FN * FM, LD_B + LD_A, LD_B + LD_A>();
-    __syncthreads();
-  }
-  MOE_COMPUTE((nk - 1) & 1);
-
-#undef MOE_COMPUTE
-#undef MOE_MFMAS
-#undef MOE_FRAGS
-#undef MOE_GLOAD
-#undef MOE_LSTORE
-
-  // ---- epilogue: lane holds output columns 8q + 4*khalf + {0..3} of token row l32
+// Epilogue: lane holds output columns 8q + 4*khalf + {0..3} of token row l32
+// in each 32x32 accumulator block.
+template <int EPI, int FM, int FN, int TM, int TN>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const TileLoc& tl, const f32x16 (&acc)[FM][FN],
+                                           int wm, int wn, int l32, int khalf) {
+  const int64_t N = a.N;
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     const int64_t row = static_cast<int64_t>(tl.row0) + wm * TM + fm * 32 + l32;
@@ -274,24 +177,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant: global_load_lds_dwordx4 writes each 16-byte chunk
-// straight into LDS (no register staging), which leaves room for three LDS
-// stages, so the loads of stage k+2 are in flight while stage k is consumed.
-// Each wave load instruction fills 8 rows x 128 bytes; lane t writes LDS
-// slot t of that 1 KB block, so it fetches the global chunk that the XOR
-// swizzle maps onto that slot.
+// Direct-to-LDS kernel (expert projections).
 //
-// Synchronisation per stage: s_waitcnt vmcnt(LPS) (this wave's loads of the
-// stage to consume have landed; the next stage's LPS loads may still be in
-// flight) and lgkmcnt(0) (this wave's LDS reads of the buffer about to be
-// refilled are complete), then s_barrier.  The barrier is not the
-// __syncthreads() fence: that fence would wait for every outstanding LDS DMA.
-// After the loop all DMA is drained before the epilogue.
+// Synchronisation per stage: s_waitcnt vmcnt((NS-2)*LPS) (this wave's loads
+// of the stage about to be consumed have landed; the NS-2 younger stages may
+// still be in flight) and lgkmcnt(0) (this wave's LDS reads of the buffer
+// about to be refilled are complete), then s_barrier.  This is not the
+// __syncthreads() fence, which would wait for every outstanding LDS DMA.
+// After the loop all DMA is drained before the epilogue, so nothing lands
+// in LDS after the workgroup ends.
 
-template <int LPS>
+template <int VM>
 __device__ __forceinline__ void wait_stage_barrier() {
-  static_assert(LPS < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((LPS & 15) | (7 << 4) | (0 << 8) | ((LPS >> 4) << 14));
+  static_assert(VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -301,12 +200,10 @@ __device__ __forceinline__ void drain_vm() {
   asm volatile("" ::: "memory");
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // One LDS DMA: 64 lanes x 16 bytes from buffer rs at per-lane byte offset
 // voff (+ soff) into LDS [lds_addr, lds_addr + 1024).  Written as asm so the
 // compiler does not add its own conservative "all LDS DMA done" wait before
-// later LDS reads of the other buffer; the kernel waits explicitly (vmcnt)
+// later LDS reads of another stage; the kernel waits explicitly (vmcnt)
 // before the barrier that publishes a stage.  The instruction has no
 // register outputs.  Nothing else in these kernels uses m0.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, int voff, int soff, unsigned lds_addr) {
@@ -318,10 +215,7 @@ __device__ __forceinline__ unsigned lds_addr_of(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void*)p));
 }
 
-// raw buffer descriptor word 3 for gfx9-family untyped 32-bit accesses
-constexpr int kBufFlags = 0x00020000;
-
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int NS>
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the body uses device-only types; the host pass needs only the stub
   constexpr int NW = WM * WN;
@@ -330,13 +224,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   constexpr int FM = TM / 32, FN = TN / 32;
   static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "fragment shape");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
+  static_assert(BK == 64 || BK == 32, "stage width");
+  static_assert(NS >= 2 && NS <= 4, "LDS stages");
+  constexpr int CH = BK / 8;                          // 16-byte chunks per tile row
+  constexpr int KS = BK / 16;                         // 16-wide K slices per stage
+  constexpr int RPI = 64 / CH;                        // tile rows per 1 KB load instruction
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   constexpr int ROWS = BN + BM;                       // tile rows per stage
-  static_assert(ROWS % (8 * NW) == 0, "8 rows per wave load");
-  constexpr int LPS = ROWS / (8 * NW);                // load instructions per wave per stage
-  constexpr int STAGE = ROWS * kChunks;               // 16-byte units per stage
+  static_assert(BN % (RPI * NW) == 0 && BM % (RPI * NW) == 0, "rows per wave");
+  constexpr int LPS = ROWS / (RPI * NW);              // load instructions per wave per stage
+  constexpr int LB = BN / (RPI * NW);                 // ... of which weight rows
+  constexpr int STAGE = ROWS * CH;                    // 16-byte units per stage
 
-  static_assert(NS == 2 || NS == 3, "LDS stages");
   __shared__ u32x4 lds[NS * STAGE];
 
   TileLoc tl;
@@ -369,18 +268,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, wrecords, kBufFlags);
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase), 0, arecords, kBufFlags);
 
-  // Load instruction i of this wave fills 8 tile rows: the first LB
-  // instructions cover weight rows 8*(wave + NW*i), the rest token rows.
-  // Lane t -> row +t/8, LDS slot t%8, global chunk (t%8) ^ (row & 7).
-  constexpr int LB = BN / (8 * NW);
-  static_assert(BN % (8 * NW) == 0 && BM % (8 * NW) == 0, "rows per wave");
+  // Load instruction i of this wave fills RPI tile rows: the first LB
+  // instructions cover weight rows, the rest token rows.  Lane t -> row
+  // +t/CH, LDS slot t%CH, global chunk (t%CH) ^ swz(row).
   int voff[LPS];
-  int dst_unit[LPS];
+  int dst[LPS];
 #pragma unroll
   for (int i = 0; i < LPS; ++i) {
-    const int row0 = (i < LB) ? 8 * (wave + NW * i) : BN + 8 * (wave + NW * (i - LB));
-    const int r = row0 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
+    const int row0 = (i < LB) ? RPI * (wave + NW * i) : BN + RPI * (wave + NW * (i - LB));
+    const int r = row0 + lane / CH;
+    const int c = (lane % CH) ^ swz<CH>(r);
     int64_t off;
     if (i < LB) {
       if (EPI == EPI_SWIGLU) {
@@ -393,32 +290,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
       off = static_cast<int64_t>(r - BN) * rowb;
     }
     voff[i] = static_cast<int>(off) + c * 16;
-    dst_unit[i] = row0 * kChunks;
+    dst[i] = row0 * CH * 16;                           // byte offset inside a stage
   }
-
   const unsigned lds0 = lds_addr_of(lds);
+
 #define MOE_DMA(buf_, kt_)                                                              \
   do {                                                                                  \
-    const int so_ = (kt_) * (kBK * 2);                                                  \
+    const int so_ = (kt_) * (BK * 2);                                                   \
     const unsigned b_ = lds0 + static_cast<unsigned>(buf_) * (STAGE * 16);              \
     _Pragma("unroll") for (int i = 0; i < LPS; ++i)                                     \
-      lds_dma16(i < LB ? wrs : ars, voff[i], so_,                                       \
-                __builtin_amdgcn_readfirstlane(b_ + dst_unit[i] * 16));                  \
+      lds_dma16(i < LB ? wrs : ars, voff[i], so_, __builtin_amdgcn_readfirstlane(b_ + dst[i])); \
   } while (0)
 
   int wrow[FN];
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-    if (EPI == EPI_SWIGLU) {
-      const int hf = fn / (FN / 2);
-      wrow[fn] = hf * (BN / 2) + wn * (TN / 2) + (fn - hf * (FN / 2)) * 32;
-    } else {
-      wrow[fn] = wn * TN + fn * 32;
-    }
-  }
+  weight_frag_rows<EPI, BN, TN, FN>(wn, wrow);
   const int l32 = lane & 31;
   const int khalf = lane >> 5;
-  const int sw = swz(l32);
+  const int sw = swz<CH>(l32);                  // every fragment starts on a multiple of 16 rows
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -426,136 +314,159 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-#define MOE_FRAGS(wf_, tf_, s_, ks_)                                                    \
-  do {                                                                                  \
-    const int c_ = ((ks_) * 2 + khalf) ^ sw;                                            \
-    _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                   \
-      wf_[fn] = __builtin_bit_cast(bf16x8, s_[(wrow[fn] + l32) * kChunks + c_]);        \
-    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm)                                   \
-      tf_[fm] = __builtin_bit_cast(bf16x8, s_[(BN + wm * TM + fm * 32 + l32) * kChunks + c_]); \
-  } while (0)
-#define MOE_MFMAS(wf_, tf_)                                                             \
-  do {                                                                                  \
-    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm)                                   \
-      _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                 \
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf_[fn], tf_[fm], acc[fm][fn], 0, 0, 0); \
-  } while (0)
-#define MOE_COMPUTE(s_)                                                                 \
-  do {                                                                                  \
-    bf16x8 wf0[FN], tf0[FM], wf1[FN], tf1[FM];                                          \
-    MOE_FRAGS(wf0, tf0, s_, 0);                                                         \
-    MOE_FRAGS(wf1, tf1, s_, 1);                                                         \
-    MOE_MFMAS(wf0, tf0);                                                                \
-    MOE_FRAGS(wf0, tf0, s_, 2);                                                         \
-    MOE_MFMAS(wf1, tf1);                                                                \
-    MOE_FRAGS(wf1, tf1, s_, 3);                                                         \
-    MOE_MFMAS(wf0, tf0);                                                                \
-    MOE_MFMAS(wf1, tf1);                                                                \
-  } while (0)
-
-  const int nk = static_cast<int>(K / kBK);
+  const int nk = static_cast<int>(K / BK);
   const int last = nk - 1;
-  if (NS == 3) {
-    const u32x4* const l0 = lds;
-    const u32x4* const l1 = lds + STAGE;
-    const u32x4* const l2 = lds + 2 * STAGE;
-    MOE_DMA(0, 0);
-    MOE_DMA(1, 1 < last ? 1 : last);
-    for (int kt = 0; kt < nk; kt += 3) {
-      wait_stage_barrier<LPS>();
-      MOE_DMA(2, kt + 2 < last ? kt + 2 : last);
-      MOE_COMPUTE(l0);
-      sched_stage<FN + FM, FN * FM, LPS, 0>();
-      if (kt + 1 >= nk) break;
-      wait_stage_barrier<LPS>();
-      MOE_DMA(0, kt + 3 < last ? kt + 3 : last);
-      MOE_COMPUTE(l1);
-      sched_stage<FN + FM, FN * FM, LPS, 0>();
-      if (kt + 2 >= nk) break;
-      wait_stage_barrier<LPS>();
-      MOE_DMA(1, kt + 4 < last ? kt + 4 : last);
-      MOE_COMPUTE(l2);
-      sched_stage<FN + FM, FN * FM, LPS, 0>();
-    }
-  } else {
-    // two stages: the loads of stage k+1 are issued right after the barrier
-    // that opens stage k and have its whole MFMA time to land
-    MOE_DMA(0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_stage_barrier<0>();
-      const int cur = kt & 1;
-      MOE_DMA(cur ^ 1, kt + 1 < last ? kt + 1 : last);
-      MOE_COMPUTE((lds + cur * STAGE));
-      sched_stage<FN + FM, FN * FM, LPS, 0>();
-    }
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) MOE_DMA(p, p < last ? p : last);
+  int cur = 0;                                    // buffer of stage kt
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_stage_barrier<(NS - 2) * LPS>();
+    // refill the buffer consumed in the previous iteration with stage kt+NS-1
+    // (clamped past the end: extra loads of valid memory, never consumed)
+    const int nb = cur == 0 ? NS - 1 : cur - 1;
+    MOE_DMA(nb, kt + NS - 1 < last ? kt + NS - 1 : last);
+    const u32x4* s = lds + cur * STAGE;
+    MOE_COMPUTE(s);
+    sched_stage<FN + FM, FN * FM, LPS, 0, KS>();
+    cur = cur + 1 == NS ? 0 : cur + 1;
   }
   drain_vm();
+#undef MOE_DMA
+
+  store_tile<EPI, FM, FN, TM, TN>(a, tl, acc, wm, wn, l32, khalf);
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged kernel (router logits): 128-byte LDS rows, two buffers,
+// one barrier per stage; the global loads of stage k+1 are issued before
+// the MFMAs of stage k.
+
+template <int BM, int BN, int WM, int WN, int EPI, int SN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "fragment shape");
+  static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
+  constexpr int BK = 64;
+  constexpr int CH = BK / 8;
+  constexpr int KS = BK / 16;
+  constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  constexpr int ROWS_PER_LD = NT / CH;                     // rows per load instruction
+  static_assert(BN % ROWS_PER_LD == 0 && BM % ROWS_PER_LD == 0, "load shape");
+  constexpr int LD_B = BN / ROWS_PER_LD;                   // weight-tile loads per thread
+  constexpr int LD_A = BM / ROWS_PER_LD;                   // token-tile loads per thread
+  constexpr int STAGE = (BN + BM) * CH;                    // 16-byte units per LDS stage
+
+  __shared__ u32x4 lds[2 * STAGE];
+
+  TileLoc tl;
+  if (!locate_tile<NT, BM, BNO, SN>(a, tl)) return;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+  const int64_t K = a.K;
+  const int64_t N = a.N;
+
+  // Rows past the group end (tokens) or past N (weights) read a valid row
+  // instead: they only feed output rows / columns that the epilogue masks.
+  const int ck = t & (CH - 1);          // chunk within the row
+  const int rr = t / CH;                // row within a slab of ROWS_PER_LD rows
+  const uint16_t* Ab = static_cast<const uint16_t*>(a.A);
+  const uint16_t* Bb = static_cast<const uint16_t*>(a.B) +
+      static_cast<int64_t>(tl.g) * ((EPI == EPI_SWIGLU) ? 2 * N : N) * K;
+
+  const gu4* bsrc[LD_B];
+#pragma unroll
+  for (int i = 0; i < LD_B; ++i) {
+    const int r = i * ROWS_PER_LD + rr;          // weight-tile row
+    int64_t src;
+    if (EPI == EPI_SWIGLU) {
+      const int half = r / (BN / 2);
+      const int64_t n = tl.n0 + (r - half * (BN / 2));
+      src = half * N + (n < N ? n : 0);
+    } else {
+      const int64_t n = tl.n0 + r;
+      src = n < N ? n : 0;
+    }
+    bsrc[i] = (const gu4*)(Bb + src * K + ck * 8);
+  }
+  const gu4* asrc[LD_A];
+#pragma unroll
+  for (int i = 0; i < LD_A; ++i) {
+    const int64_t row = static_cast<int64_t>(tl.row0) + i * ROWS_PER_LD + rr;
+    asrc[i] = (const gu4*)(Ab + (row < tl.row_end ? row : tl.row0) * K + ck * 8);
+  }
+
+#define MOE_GLOAD(rb_, ra_, kt_)                                                        \
+  do {                                                                                  \
+    const int64_t o_ = static_cast<int64_t>(kt_) * (BK / 8);                            \
+    _Pragma("unroll") for (int i = 0; i < LD_B; ++i) rb_[i] = bsrc[i][o_];              \
+    _Pragma("unroll") for (int i = 0; i < LD_A; ++i) ra_[i] = asrc[i][o_];              \
+  } while (0)
+#define MOE_LSTORE(rb_, ra_, buf_)                                                      \
+  do {                                                                                  \
+    u32x4* s_ = lds + (buf_) * STAGE;                                                   \
+    _Pragma("unroll") for (int i = 0; i < LD_B; ++i) {                                  \
+      const int r_ = i * ROWS_PER_LD + rr;                                              \
+      s_[r_ * CH + (ck ^ swz<CH>(r_))] = rb_[i];                                        \
+    }                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < LD_A; ++i) {                                  \
+      const int r_ = BN + i * ROWS_PER_LD + rr;                                         \
+      s_[r_ * CH + (ck ^ swz<CH>(r_))] = ra_[i];                                        \
+    }                                                                                   \
+  } while (0)
+
+  int wrow[FN];
+  weight_frag_rows<EPI, BN, TN, FN>(wn, wrow);
+  const int l32 = lane & 31;
+  const int khalf = lane >> 5;
+  const int sw = swz<CH>(l32);
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+  const int nk = static_cast<int>(K / BK);
+  u32x4 rb[LD_B], ra[LD_A];
+  MOE_GLOAD(rb, ra, 0);
+  MOE_LSTORE(rb, ra, 0);
+  __syncthreads();
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    MOE_GLOAD(rb, ra, kt + 1);          // in flight during the MFMAs below
+    MOE_COMPUTE(lds + (kt & 1) * STAGE);
+    MOE_LSTORE(rb, ra, (kt + 1) & 1);
+    sched_stage<FN + FM, FN * FM, LD_B + LD_A, LD_B + LD_A, KS>();
+    __syncthreads();
+  }
+  MOE_COMPUTE(lds + ((nk - 1) & 1) * STAGE);
+#undef MOE_GLOAD
+#undef MOE_LSTORE
+
+  store_tile<EPI, FM, FN, TM, TN>(a, tl, acc, wm, wn, l32, khalf);
+}
 
 #undef MOE_COMPUTE
 #undef MOE_MFMAS
 #undef MOE_FRAGS
-#undef MOE_DMA
 
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int64_t row = static_cast<int64_t>(tl.row0) + wm * TM + fm * 32 + l32;
-    if (row >= tl.row_end) continue;
-    if (EPI == EPI_SWIGLU) {
-      uint16_t* C = static_cast<uint16_t*>(a.C) + row * N;
-#pragma unroll
-      for (int fg = 0; fg < FN / 2; ++fg) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = tl.n0 + wn * (TN / 2) + fg * 32 + q * 8 + khalf * 4;
-          if (n >= N) continue;
-          const f32x16& g = acc[fm][fg];
-          const f32x16& u = acc[fm][fg + FN / 2];
-          uint2 o;
-          o.x = pack_bf16x2(silu(g[4 * q + 0]) * u[4 * q + 0], silu(g[4 * q + 1]) * u[4 * q + 1]);
-          o.y = pack_bf16x2(silu(g[4 * q + 2]) * u[4 * q + 2], silu(g[4 * q + 3]) * u[4 * q + 3]);
-          *reinterpret_cast<uint2*>(C + n) = o;
-        }
-      }
-    } else if (EPI == EPI_STORE) {
-      uint16_t* C = static_cast<uint16_t*>(a.C) + row * N;
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = tl.n0 + wn * TN + fn * 32 + q * 8 + khalf * 4;
-          if (n >= N) continue;
-          const f32x16& c = acc[fm][fn];
-          uint2 o;
-          o.x = pack_bf16x2(c[4 * q + 0], c[4 * q + 1]);
-          o.y = pack_bf16x2(c[4 * q + 2], c[4 * q + 3]);
-          *reinterpret_cast<uint2*>(C + n) = o;
-        }
-      }
-    } else {  // EPI_F32B
-      float* C = static_cast<float*>(a.C) + row * N;
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t n = tl.n0 + wn * TN + fn * 32 + q * 8 + khalf * 4 + e;
-            if (n < N) C[n] = acc[fm][fn][4 * q + e] + (a.bias ? a.bias[n] : 0.0f);
-          }
-        }
-      }
-    }
-  }
-#endif
-}
-
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int NS>
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS>
 moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int64_t grid = grouped_tile_bound(a.rows, a.G, BM, a.N, BNO);
   if (grid <= 0) return MOE_OK;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, NS>), dim3(static_cast<unsigned>(grid)),
+  // byte offsets inside one expert's weights must fit the 32-bit descriptor range
+  const int64_t wbytes = ((EPI == EPI_SWIGLU) ? 2 : 1) * a.N * a.K * 2;
+  if (wbytes >= (int64_t(1) << 31) || static_cast<int64_t>(BM) * a.K * 2 >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, NS>), dim3(static_cast<unsigned>(grid)),
                      dim3(64 * WM * WN), 0, st, a);
   return launch_status();
 }
@@ -573,15 +484,15 @@ moe_status launch(const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// Entry points used by the C ABI (argument checks are done by the caller).
 // Expert projections: 256 token rows x 256 weight rows per tile, 8 waves
-// (2 along tokens x 4 along weights, 128 x 64 each), two direct-to-LDS stages.
+// (2 along tokens x 4 along weights, 128 x 64 each), two 64-wide
+// direct-to-LDS stages.
 moe_status gemm_bf16_gateup_swiglu(const GemmArgs& a, hipStream_t st) {
-  return launch_dtl<256, 256, 2, 4, EPI_SWIGLU, 8, 2>(a, st);
+  return launch_dtl<256, 256, 2, 4, EPI_SWIGLU, 8, 64, 2>(a, st);
 }
 
 moe_status gemm_bf16_down(const GemmArgs& a, hipStream_t st) {
-  return launch_dtl<256, 256, 2, 4, EPI_STORE, 8, 2>(a, st);
+  return launch_dtl<256, 256, 2, 4, EPI_STORE, 8, 64, 2>(a, st);
 }
 
 moe_status gemm_bf16_logits(const GemmArgs& a, hipStream_t st) {
