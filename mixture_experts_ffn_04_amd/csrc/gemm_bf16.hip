@@ -73,32 +73,33 @@ __device__ __forceinline__ void sched_stage() {
 }
 
 // Fragment reads of K slice ks (16 wide) from LDS stage s_ with CH chunks
-// per row, and the FM x FN MFMAs on them.
-#define MOE_FRAGS(wf_, tf_, s_, ks_)                                                    \
+// per row -- the FN weight fragments and the first NF_ token fragments --
+// and the NF_ x FN MFMAs on them.
+#define MOE_FRAGS(wf_, tf_, s_, ks_, NF_)                                               \
   do {                                                                                  \
     const int c_ = ((ks_) * 2 + khalf) ^ sw;                                            \
     _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                   \
       wf_[fn] = __builtin_bit_cast(bf16x8, (s_)[(wrow[fn] + l32) * CH + c_]);           \
-    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm)                                   \
+    _Pragma("unroll") for (int fm = 0; fm < (NF_); ++fm)                                \
       tf_[fm] = __builtin_bit_cast(bf16x8, (s_)[(BN + wm * TM + fm * 32 + l32) * CH + c_]); \
   } while (0)
-#define MOE_MFMAS(wf_, tf_)                                                             \
+#define MOE_MFMAS(wf_, tf_, NF_)                                                        \
   do {                                                                                  \
-    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm)                                   \
+    _Pragma("unroll") for (int fm = 0; fm < (NF_); ++fm)                                \
       _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                 \
         acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf_[fn], tf_[fm], acc[fm][fn], 0, 0, 0); \
   } while (0)
 // all KS slices of one stage, the reads of slice ks+1 in flight during the
 // MFMAs of slice ks
-#define MOE_COMPUTE(s_)                                                                 \
+#define MOE_COMPUTE(s_, NF_)                                                            \
   do {                                                                                  \
     bf16x8 wf0[FN], tf0[FM], wf1[FN], tf1[FM];                                          \
-    MOE_FRAGS(wf0, tf0, s_, 0);                                                         \
+    MOE_FRAGS(wf0, tf0, s_, 0, NF_);                                                    \
     _Pragma("unroll") for (int ks = 0; ks < KS; ks += 2) {                              \
-      MOE_FRAGS(wf1, tf1, s_, ks + 1);                                                  \
-      MOE_MFMAS(wf0, tf0);                                                              \
-      if (ks + 2 < KS) MOE_FRAGS(wf0, tf0, s_, ks + 2);                                 \
-      MOE_MFMAS(wf1, tf1);                                                              \
+      MOE_FRAGS(wf1, tf1, s_, ks + 1, NF_);                                             \
+      MOE_MFMAS(wf0, tf0, NF_);                                                         \
+      if (ks + 2 < KS) MOE_FRAGS(wf0, tf0, s_, ks + 2, NF_);                            \
+      MOE_MFMAS(wf1, tf1, NF_);                                                         \
     }                                                                                   \
   } while (0)
 
@@ -215,7 +216,9 @@ __device__ __forceinline__ unsigned lds_addr_of(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void*)p));
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS>
+// SP: the DMA instructions of a stage are spread over the fragment reads of
+// its first SP K slices rather than issued in one burst.
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the body uses device-only types; the host pass needs only the stub
   constexpr int NW = WM * WN;
@@ -226,6 +229,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
   static_assert(BK == 64 || BK == 32, "stage width");
   static_assert(NS >= 2 && NS <= 4, "LDS stages");
+  static_assert(FM <= 4, "active-fragment specialisations cover up to 4 token fragments");
   constexpr int CH = BK / 8;                          // 16-byte chunks per tile row
   constexpr int KS = BK / 16;                         // 16-wide K slices per stage
   constexpr int RPI = 64 / CH;                        // tile rows per 1 KB load instruction
@@ -235,6 +239,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   constexpr int LPS = ROWS / (RPI * NW);              // load instructions per wave per stage
   constexpr int LB = BN / (RPI * NW);                 // ... of which weight rows
   constexpr int STAGE = ROWS * CH;                    // 16-byte units per stage
+  static_assert(SP >= 1 && SP <= KS && LPS % SP == 0, "DMA spread");
 
   __shared__ u32x4 lds[NS * STAGE];
 
@@ -243,11 +248,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave % WM;
-  const int wn = wave / WM;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  // Waves w and w+4 share a SIMD.  Row block wm = wave / WN puts waves of
+  // different row blocks on each SIMD, so when the tile's last token rows
+  // are missing (the ragged end of an expert's group) the MFMAs a wave skips
+  // shorten its SIMD's work instead of idling it.
+  const int wm = wave / WN;
+  const int wn = wave % WN;
   const int64_t K = a.K;
   const int64_t N = a.N;
+  // token fragments of this wave holding at least one row of the group
+  const int trows = min(tl.row_end - tl.row0, BM) - wm * TM;
+  const int nfm = trows <= 0 ? 0 : min(FM, (trows + 31) / 32);
 
   // Buffer descriptors based at the tile's first weight row and first token
   // row; num_records is the valid extent, so rows past N or past the
@@ -319,18 +331,65 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p) MOE_DMA(p, p < last ? p : last);
   int cur = 0;                                    // buffer of stage kt
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_stage_barrier<(NS - 2) * LPS>();
-    // refill the buffer consumed in the previous iteration with stage kt+NS-1
-    // (clamped past the end: extra loads of valid memory, never consumed)
-    const int nb = cur == 0 ? NS - 1 : cur - 1;
-    MOE_DMA(nb, kt + NS - 1 < last ? kt + NS - 1 : last);
-    const u32x4* s = lds + cur * STAGE;
-    MOE_COMPUTE(s);
-    sched_stage<FN + FM, FN * FM, LPS, 0, KS>();
-    cur = cur + 1 == NS ? 0 : cur + 1;
+  // Part p < SP of the DMA of one stage (stage offset so_, LDS buffer b_).
+#define MOE_DMA_PART(p_)                                                                \
+  if ((p_) < SP) {                                                                      \
+    _Pragma("unroll") for (int i = (p_) * (LPS / SP); i < ((p_) + 1) * (LPS / SP); ++i) \
+      lds_dma16(i < LB ? wrs : ars, voff[i], so_, __builtin_amdgcn_readfirstlane(b_ + dst[i])); \
+  }
+  // MOE_COMPUTE with the stage's DMA parts issued after the reads of slices 0..SP-1
+#define MOE_COMPUTE_DMA(s_, NF_)                                                        \
+  do {                                                                                  \
+    bf16x8 wf0[FN], tf0[FM], wf1[FN], tf1[FM];                                          \
+    MOE_FRAGS(wf0, tf0, s_, 0, NF_);                                                    \
+    MOE_DMA_PART(0);                                                                    \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ks += 2) {                              \
+      MOE_FRAGS(wf1, tf1, s_, ks + 1, NF_);                                             \
+      MOE_DMA_PART(ks + 1);                                                             \
+      MOE_MFMAS(wf0, tf0, NF_);                                                         \
+      if (ks + 2 < KS) {                                                                \
+        MOE_FRAGS(wf0, tf0, s_, ks + 2, NF_);                                           \
+        MOE_DMA_PART(ks + 2);                                                           \
+      }                                                                                 \
+      MOE_MFMAS(wf1, tf1, NF_);                                                         \
+    }                                                                                   \
+  } while (0)
+  // The K loop, specialised on the number of active token fragments (every
+  // wave takes part in the loads and barriers, whatever its share).  Each
+  // iteration refills the buffer consumed in the previous one with stage
+  // kt+NS-1 (clamped past the end: extra loads of valid memory, never
+  // consumed).
+#define MOE_DTL_LOOP(NF_)                                                               \
+  for (int kt = 0; kt < nk; ++kt) {                                                     \
+    wait_stage_barrier<(NS - 2) * LPS>();                                               \
+    const int nb = cur == 0 ? NS - 1 : cur - 1;                                         \
+    const int kd = kt + NS - 1 < last ? kt + NS - 1 : last;                             \
+    if ((NF_) > 0) {                                                                    \
+      const int so_ = kd * (BK * 2);                                                    \
+      const unsigned b_ = lds0 + static_cast<unsigned>(nb) * (STAGE * 16);              \
+      const u32x4* s = lds + cur * STAGE;                                               \
+      MOE_COMPUTE_DMA(s, (NF_));                                                        \
+      sched_stage<FN + (NF_), FN * ((NF_) > 0 ? (NF_) : 1), 0, 0, KS>();                \
+    } else {                                                                            \
+      MOE_DMA(nb, kd);                                                                  \
+    }                                                                                   \
+    cur = cur + 1 == NS ? 0 : cur + 1;                                                  \
+  }
+  if (nfm == FM) {
+    MOE_DTL_LOOP(FM)
+  } else if (nfm == 0) {
+    MOE_DTL_LOOP(0)
+  } else if (nfm == 1) {
+    MOE_DTL_LOOP(1)
+  } else if (nfm == 2) {
+    MOE_DTL_LOOP(FM > 2 ? 2 : FM)
+  } else {
+    MOE_DTL_LOOP(FM > 3 ? 3 : FM)
   }
   drain_vm();
+#undef MOE_DTL_LOOP
+#undef MOE_COMPUTE_DMA
+#undef MOE_DMA_PART
 #undef MOE_DMA
 
   store_tile<EPI, FM, FN, TM, TN>(a, tl, acc, wm, wn, l32, khalf);
@@ -440,12 +499,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
   __syncthreads();
   for (int kt = 0; kt + 1 < nk; ++kt) {
     MOE_GLOAD(rb, ra, kt + 1);          // in flight during the MFMAs below
-    MOE_COMPUTE(lds + (kt & 1) * STAGE);
+    MOE_COMPUTE(lds + (kt & 1) * STAGE, FM);
     MOE_LSTORE(rb, ra, (kt + 1) & 1);
     sched_stage<FN + FM, FN * FM, LD_B + LD_A, LD_B + LD_A, KS>();
     __syncthreads();
   }
-  MOE_COMPUTE(lds + ((nk - 1) & 1) * STAGE);
+  MOE_COMPUTE(lds + ((nk - 1) & 1) * STAGE, FM);
 #undef MOE_GLOAD
 #undef MOE_LSTORE
 
@@ -456,7 +515,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 #undef MOE_MFMAS
 #undef MOE_FRAGS
 
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS>
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP = 1>
 moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int64_t grid = grouped_tile_bound(a.rows, a.G, BM, a.N, BNO);
@@ -466,7 +525,7 @@ moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   const int64_t wbytes = ((EPI == EPI_SWIGLU) ? 2 : 1) * a.N * a.K * 2;
   if (wbytes >= (int64_t(1) << 31) || static_cast<int64_t>(BM) * a.K * 2 >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, NS>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, NS, SP>), dim3(static_cast<unsigned>(grid)),
                      dim3(64 * WM * WN), 0, st, a);
   return launch_status();
 }
@@ -488,11 +547,11 @@ moe_status launch(const GemmArgs& a, hipStream_t st) {
 // (2 along tokens x 4 along weights, 128 x 64 each), two 64-wide
 // direct-to-LDS stages.
 moe_status gemm_bf16_gateup_swiglu(const GemmArgs& a, hipStream_t st) {
-  return launch_dtl<256, 256, 2, 4, EPI_SWIGLU, 8, 64, 2>(a, st);
+  return launch_dtl<256, 256, 2, 4, EPI_SWIGLU, 8, 64, 2, 2>(a, st);
 }
 
 moe_status gemm_bf16_down(const GemmArgs& a, hipStream_t st) {
-  return launch_dtl<256, 256, 2, 4, EPI_STORE, 8, 64, 2>(a, st);
+  return launch_dtl<256, 256, 2, 4, EPI_STORE, 8, 64, 2, 2>(a, st);
 }
 
 moe_status gemm_bf16_logits(const GemmArgs& a, hipStream_t st) {
