@@ -21,7 +21,9 @@
  *   moe_grouped_gemm_down            per-expert down projection
  *   moe_unpermute_combine            weighted combine back to token order
  *   moe_decode_gateup_swiglu         small-batch variants that stream only
- *   moe_decode_down                  the active experts' weights
+ *   moe_decode_gateup_swiglu_gather  the active experts' weights (the
+ *   moe_decode_down                  _gather form reads the rows through
+ *                                    the sort instead of x_perm)
  *
  * All experts of a layer share one packed buffer per projection, the layout
  * the article's "Dynamic Weight Loading with WeightConverter" subsection
@@ -206,6 +208,19 @@ MOE_API moe_status moe_decode_gateup_swiglu(const void* x_perm, const void* w_ga
 MOE_API moe_status moe_decode_down(const void* h, const void* w_down, const int32_t* offsets,
                            int64_t rows, int64_t d, int64_t f, int32_t E,
                            moe_dtype dtype, void* y_perm, void* stream);
+
+/*
+ * moe_decode_gateup_swiglu with the row gather of moe_permute folded into
+ * its loads: input row r is x[perm[r] / k] for the token activations
+ * x [rows/k][d] and perm as written by moe_permute, so moe_permute can be
+ * called with x_perm = NULL.  rows = T*k must be a multiple of k (1 <= k <=
+ * 16, else MOE_ERR_INVALID_ARG); perm entries are clamped to [0, rows).
+ * bf16 only (MOE_ERR_UNSUPPORTED for fp32); rows <= 1024.
+ */
+MOE_API moe_status moe_decode_gateup_swiglu_gather(const void* x, const int32_t* perm, int32_t k,
+                                           const void* w_gate_up, const int32_t* offsets,
+                                           int64_t rows, int64_t d, int64_t f, int32_t E,
+                                           moe_dtype dtype, void* h, void* stream);
 
 #ifdef __cplusplus
 }

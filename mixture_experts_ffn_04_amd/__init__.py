@@ -4,4 +4,4 @@ The compute runs in hand-written HIP kernels behind the C ABI declared in
 include/libmoe.h (built into libmoe.so); `binding` is the Python binding.
 """
 from . import binding  # noqa: F401
-from .binding import MoeLayer, MoeWeights  # noqa: F401
+from .binding import MoeLayer, MoeLayerGraph, MoeWeights  # noqa: F401

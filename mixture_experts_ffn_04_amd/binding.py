@@ -25,7 +25,7 @@ EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_route", "moe_topk",
     "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_gateup_swiglu",
     "moe_grouped_gemm_down", "moe_unpermute_combine", "moe_decode_gateup_swiglu",
-    "moe_decode_down",
+    "moe_decode_down", "moe_decode_gateup_swiglu_gather",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -44,6 +44,7 @@ _SIGS = {
     "moe_unpermute_combine": ([P, P, P, P, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
     "moe_decode_gateup_swiglu": ([P, P, P, I64, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
     "moe_decode_down": ([P, P, P, I64, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
+    "moe_decode_gateup_swiglu_gather": ([P, P, I32, P, P, I64, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
 }
 
 
@@ -141,6 +142,16 @@ def gateup_swiglu(x_perm, w_gate_up, offsets, h, decode: bool = False, stream=No
                                    _dt(x_perm), _ptr(h), _stream(stream)))
 
 
+def gateup_swiglu_gather(x, perm, k: int, w_gate_up, offsets, h, stream=None):
+    """Decode gate/up + SwiGLU reading row r as x[perm[r] // k] (no x_perm)."""
+    rows = perm.shape[0]
+    d = x.shape[1]
+    E, f2, _ = w_gate_up.shape
+    _check("moe_decode_gateup_swiglu_gather", load().moe_decode_gateup_swiglu_gather(
+        _ptr(x), _ptr(perm), k, _ptr(w_gate_up), _ptr(offsets), rows, d, f2 // 2, E, _dt(x), _ptr(h),
+        _stream(stream)))
+
+
 def down(h, w_down, offsets, y_perm, decode: bool = False, stream=None):
     rows, f = h.shape
     E, d, _ = w_down.shape
@@ -224,41 +235,118 @@ class MoeLayer:
             return False
         return T * self.k <= self.DECODE_MAX_ROWS
 
-    def forward(self, x: torch.Tensor, stream=None, marks: Optional[dict] = None,
-                stages: Optional[tuple] = None) -> torch.Tensor:
-        """Run the layer on x [T, d].  With `marks` (a dict), a pair of timing
-        events recorded on the launch stream brackets every stage (or only the
-        stages named in `stages`) and is appended to marks[stage]."""
+    STAGES = ("route", "permute", "gateup", "down", "shared_gateup", "shared_down", "combine")
+
+    def stages(self, x: torch.Tensor, st) -> list:
+        """The layer on x [T, d] as (stage name, call, args) in launch order."""
         T = x.shape[0]
         self._alloc(T)
         w = self.w
         dec = self.use_decode(T)
-        st = torch.cuda.current_stream() if stream is None else stream
+        # bf16 decode reads the token rows through the sort (no x_perm copy)
+        gather = dec and self.dtype == torch.bfloat16
+        out = [
+            ("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st)),
+            ("permute", permute, (self.ids, x, self.E, self.counts, self.offsets, self.perm, self.inv_perm,
+                                  None if gather else self.x_perm, self.ws, st)),
+            ("gateup", gateup_swiglu_gather, (x, self.perm, self.k, w.w_gate_up, self.offsets, self.h, st))
+            if gather else
+            ("gateup", gateup_swiglu, (self.x_perm, w.w_gate_up, self.offsets, self.h, dec, st)),
+            ("down", down, (self.h, w.w_down, self.offsets, self.y_perm, dec, st)),
+        ]
+        ys = None
+        if w.shared_gate_up is not None:
+            sdec = dec and T <= self.DECODE_MAX_ROWS
+            out.append(("shared_gateup", gateup_swiglu, (x, w.shared_gate_up, self.s_off, self.s_h, sdec, st)))
+            out.append(("shared_down", down, (self.s_h, w.shared_down, self.s_off, self.s_y, sdec, st)))
+            ys = self.s_y
+        out.append(("combine", unpermute_combine, (self.y_perm, self.inv_perm, self.wts, ys, self.y, st)))
+        return out
 
-        def mark(name, fn, *a):
+    def forward(self, x: torch.Tensor, stream=None, marks: Optional[dict] = None,
+                stages: Optional[tuple] = None, run: Optional[tuple] = None) -> torch.Tensor:
+        """Run the layer on x [T, d].  With `marks` (a dict), a pair of timing
+        events recorded on the launch stream brackets every stage (or only the
+        stages named in `stages`) and is appended to marks[stage].  With
+        `run`, only the stages named there are enqueued."""
+        st = torch.cuda.current_stream() if stream is None else stream
+        for name, fn, a in self.stages(x, st):
+            if run is not None and name not in run:
+                continue
             if marks is None or (stages is not None and name not in stages):
                 fn(*a)
-                return
+                continue
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(st)
             fn(*a)
             e1.record(st)
             marks.setdefault(name, []).append((e0, e1))
-
-        mark("route", route, x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st)
-        mark("permute", permute, self.ids, x, self.E, self.counts, self.offsets, self.perm, self.inv_perm,
-             self.x_perm, self.ws, st)
-        mark("gateup", gateup_swiglu, self.x_perm, w.w_gate_up, self.offsets, self.h, dec, st)
-        mark("down", down, self.h, w.w_down, self.offsets, self.y_perm, dec, st)
-        ys = None
-        if w.shared_gate_up is not None:
-            sdec = dec and T <= self.DECODE_MAX_ROWS
-            mark("shared_gateup", gateup_swiglu, x, w.shared_gate_up, self.s_off, self.s_h, sdec, st)
-            mark("shared_down", down, self.s_h, w.shared_down, self.s_off, self.s_y, sdec, st)
-            ys = self.s_y
-        mark("combine", unpermute_combine, self.y_perm, self.inv_perm, self.wts, ys, self.y, st)
         return self.y
+
+
+class MoeLayerGraph:
+    """One forward of the layer at a fixed token count T, captured in HIP
+    graphs: a replay costs one graph launch per segment instead of one host
+    call per stage, which is what bounds a decode step.
+
+    The graphs own their buffers (a private MoeLayer over the same weights)
+    and a static input `x` [T, d]: write the tokens into `x`, then call
+    replay(), which enqueues the layer on the current stream and returns the
+    static output [T, d].  Each stage named in `timed` is captured as a
+    segment of its own and bracketed by timing events on the stream between
+    segment replays; stage_ms() reads them for the last replay once it has
+    completed.  Replays of one MoeLayerGraph must not overlap.
+    """
+
+    def __init__(self, weights: MoeWeights, k: int, score: str, T: int, mode: str = "auto",
+                 timed: tuple = ()):
+        self.layer = L = MoeLayer(weights, k, score, mode)
+        self.T = T
+        self.x = torch.zeros(T, L.d, dtype=L.dtype, device=L.dev)
+        side = torch.cuda.Stream(device=L.dev)
+        side.wait_stream(torch.cuda.current_stream(L.dev))
+        with torch.cuda.stream(side):
+            L.forward(self.x)                    # allocates the buffers outside the capture
+        torch.cuda.current_stream(L.dev).wait_stream(side)
+        torch.cuda.synchronize(L.dev)
+        names = [n for n, _, _ in L.stages(self.x, side)]
+        segs, cur = [], []
+        for n in names:
+            if n in timed:
+                if cur:
+                    segs.append((tuple(cur), False))
+                segs.append(((n,), True))
+                cur = []
+            else:
+                cur.append(n)
+        if cur:
+            segs.append((tuple(cur), False))
+        self.segments = []
+        for run, is_timed in segs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                L.forward(self.x, run=run)
+            self.segments.append((run, is_timed, g))
+        self.y = L.y
+        self._ev = {}
+
+    def replay(self) -> torch.Tensor:
+        st = torch.cuda.current_stream(self.layer.dev)
+        for run, is_timed, g in self.segments:
+            if is_timed:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                g.replay()
+                e1.record(st)
+                self._ev[run[0]] = (e0, e1)
+            else:
+                g.replay()
+        return self.y
+
+    def stage_ms(self) -> dict:
+        return {name: e0.elapsed_time(e1) for name, (e0, e1) in self._ev.items()}
 
 
 # The C ABI's own names, for callers that mirror include/libmoe.h.
@@ -277,3 +365,6 @@ def moe_decode_gateup_swiglu(x_perm, w_gate_up, offsets, h, stream=None):
 
 def moe_decode_down(h, w_down, offsets, y_perm, stream=None):
     down(h, w_down, offsets, y_perm, True, stream)
+
+
+moe_decode_gateup_swiglu_gather = gateup_swiglu_gather

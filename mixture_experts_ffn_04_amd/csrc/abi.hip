@@ -8,7 +8,7 @@ moe_status gemm_bf16_down(const GemmArgs& a, hipStream_t st);
 moe_status gemm_f32_gateup_swiglu(const GemmArgs& a, hipStream_t st);
 moe_status gemm_f32_down(const GemmArgs& a, hipStream_t st);
 moe_status decode_bf16(bool swiglu, const void* A, const void* B, const int32_t* off, int64_t rows, int64_t K,
-                       int64_t N, int G, void* C, hipStream_t st);
+                       int64_t N, int G, void* C, hipStream_t st, const int32_t* rowmap = nullptr, int kdiv = 1);
 
 namespace {
 
@@ -87,6 +87,19 @@ extern "C" moe_status moe_decode_gateup_swiglu(const void* x_perm, const void* w
   if (dtype == MOE_F32)
     return gemm_f32_gateup_swiglu(proj_args(x_perm, w_gate_up, offsets, rows, d, f, E, h), as_stream(stream));
   return decode_bf16(true, x_perm, w_gate_up, offsets, rows, d, f, E, h, as_stream(stream));
+}
+
+extern "C" moe_status moe_decode_gateup_swiglu_gather(const void* x, const int32_t* perm, int32_t k,
+                                                      const void* w_gate_up, const int32_t* offsets, int64_t rows,
+                                                      int64_t d, int64_t f, int32_t E, moe_dtype dtype, void* h,
+                                                      void* stream) {
+  moe_status s = check_proj(x, w_gate_up, offsets, rows, d, f, E, dtype, h);
+  if (s != MOE_OK) return s;
+  if (k < 1 || k > kMaxK || rows % k != 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!perm) return MOE_ERR_INVALID_ARG;
+  if (rows > kDecodeMaxRows || dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  return decode_bf16(true, x, w_gate_up, offsets, rows, d, f, E, h, as_stream(stream), perm, k);
 }
 
 extern "C" moe_status moe_decode_down(const void* h, const void* w_down, const int32_t* offsets, int64_t rows,

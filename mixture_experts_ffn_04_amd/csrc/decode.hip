@@ -81,9 +81,12 @@ __device__ __forceinline__ void decode_partial(const uint16_t* wg, const uint16_
 
 // EPI: 0 = bf16 store, 1 = SwiGLU pairs (bf16), 2 = fp32 + bias (router
 // logits for small batches; N need not be a multiple of 16 there).
+// rowmap (may be NULL): input row r is A[rowmap[r] / kdiv] (rowmap entries
+// clamped to [0, rows)), the row gather of the sort folded into the loads.
 template <int EPI>
 __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                      const int32_t* __restrict__ off, const float* __restrict__ bias,
+                                                     const int32_t* __restrict__ rowmap, int kdiv,
                                                      int rows, int K, int N, int G, void* __restrict__ Cv) {
   constexpr bool SWIGLU = EPI == 1;
   constexpr int NH = SWIGLU ? 2 : 1;
@@ -115,7 +118,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int mc = 0; mc < kMC; ++mc) {
       const int row = m0 + mc * 16 + i16;        // rows past the group read a valid row; never stored
-      xr[mc] = A + static_cast<int64_t>(row < hi ? row : lo) * K + kq * 8;
+      int src = row < hi ? row : lo;
+      if (rowmap) src = clamp_off(rowmap[src], rows - 1) / kdiv;
+      xr[mc] = A + static_cast<int64_t>(src) * K + kq * 8;
     }
     f32x4 ag[kMC], au[kMC];
     if (mcn == 1) {
@@ -172,12 +177,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
 }
 
 template <int EPI>
-moe_status launch_decode(const void* A, const void* B, const int32_t* off, const float* bias, int64_t rows,
-                         int64_t K, int64_t N, int G, void* C, hipStream_t st) {
+moe_status launch_decode(const void* A, const void* B, const int32_t* off, const float* bias, const int32_t* rowmap,
+                         int kdiv, int64_t rows, int64_t K, int64_t N, int G, void* C, hipStream_t st) {
   const int64_t grid = static_cast<int64_t>(G) * ceil_div(N, 16);
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(decode_kernel<EPI>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), off, bias,
+                     static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), off, bias, rowmap, kdiv,
                      static_cast<int>(rows), static_cast<int>(K), static_cast<int>(N), G, C);
   return launch_status();
 }
@@ -185,15 +190,15 @@ moe_status launch_decode(const void* A, const void* B, const int32_t* off, const
 }  // namespace
 
 moe_status decode_bf16(bool swiglu, const void* A, const void* B, const int32_t* off, int64_t rows, int64_t K,
-                       int64_t N, int G, void* C, hipStream_t st) {
-  return swiglu ? launch_decode<1>(A, B, off, nullptr, rows, K, N, G, C, st)
-                : launch_decode<0>(A, B, off, nullptr, rows, K, N, G, C, st);
+                       int64_t N, int G, void* C, hipStream_t st, const int32_t* rowmap, int kdiv) {
+  return swiglu ? launch_decode<1>(A, B, off, nullptr, rowmap, kdiv, rows, K, N, G, C, st)
+                : launch_decode<0>(A, B, off, nullptr, rowmap, kdiv, rows, K, N, G, C, st);
 }
 
 // Router logits for small batches: one group of T rows, N = E experts.
 moe_status decode_bf16_logits(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d,
                               int32_t E, float* logits, hipStream_t st) {
-  return launch_decode<2>(x, w_router, nullptr, bias, T, d, E, 1, logits, st);
+  return launch_decode<2>(x, w_router, nullptr, bias, nullptr, 1, T, d, E, 1, logits, st);
 }
 
 }  // namespace moe

@@ -23,8 +23,10 @@ moe_status gemm_f32_logits(const GemmArgs& a, hipStream_t st);
 moe_status decode_bf16_logits(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d,
                               int32_t E, float* logits, hipStream_t st);
 
-// Up to this many tokens the bf16 logits run on the split-K streaming kernel
-// (many workgroups even for one token); above it, on the tiled MFMA GEMM.
+// bf16 router logits by batch size: up to kTinyRouteTokens tokens (and
+// d <= 8192), one wave per (expert row, few tokens); up to kSmallRouteTokens, the split-K
+// streaming kernel; above, the tiled MFMA GEMM.
+constexpr int64_t kTinyRouteTokens = 64;
 constexpr int64_t kSmallRouteTokens = 256;
 
 namespace {
@@ -35,13 +37,11 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                   int score, int32_t* __restrict__ ids,
-                                                   float* __restrict__ wts) {
+// Selection and weights for one token, by one whole wave: row = the
+// token's E logits (global memory or LDS).
+__device__ __forceinline__ void topk_token(const float* row, int E, int k, int score, int32_t* __restrict__ ids,
+                                           float* __restrict__ wts) {
   const int lane = threadIdx.x & 63;
-  const int tok = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
-  if (tok >= T) return;
-  const float* row = logits + static_cast<int64_t>(tok) * E;
   float v[4];
   bool live[4];
 #pragma unroll
@@ -100,10 +100,89 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
       if (j >= k) break;
-      ids[static_cast<int64_t>(tok) * k + j] = sel_i[j];
-      wts[static_cast<int64_t>(tok) * k + j] = w[j] * inv;
+      ids[j] = sel_i[j];
+      wts[j] = w[j] * inv;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                   int score, int32_t* __restrict__ ids,
+                                                   float* __restrict__ wts) {
+  const int tok = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+  if (tok >= T) return;
+  topk_token(logits + static_cast<int64_t>(tok) * E, E, k, score, ids + static_cast<int64_t>(tok) * k,
+             wts + static_cast<int64_t>(tok) * k);
+}
+
+// Small batches (bf16): router logits with one wave per (expert, block of
+// TOK tokens).  Every load of the wave -- its NCH 16-byte chunks of the
+// expert's row and of each token's row -- is issued before any arithmetic,
+// so the whole router matrix and the tokens are requested in one round
+// trip.  Each logit is an fp32 dot product of 8-element chunks summed
+// across the wave, plus the bias.  d <= 64 * 8 * NCH.
+template <int NCH, int TOK>
+__global__ __launch_bounds__(256) void logits_small_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wr,
+                                                           const float* __restrict__ bias, int T, int d, int E,
+                                                           float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);       // (token block, expert), expert fastest
+  const int e = item % E;
+  const int t0 = (item / E) * TOK;
+  if (t0 >= T) return;
+  const int nt = min(TOK, T - t0);
+  const int nc = d / 8;
+  const uint16_t* w = wr + static_cast<int64_t>(e) * d;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 wv[NCH];
+  u32x4 xv[TOK][NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = lane + 64 * j;
+    wv[j] = c < nc ? *reinterpret_cast<const u32x4*>(w + c * 8) : zero;
+  }
+#pragma unroll
+  for (int i = 0; i < TOK; ++i) {
+    const uint16_t* xt = x + static_cast<int64_t>(t0 + (i < nt ? i : 0)) * d;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + 64 * j;
+      xv[i][j] = c < nc ? *reinterpret_cast<const u32x4*>(xt + c * 8) : zero;
+    }
+  }
+  float acc[TOK];
+#pragma unroll
+  for (int i = 0; i < TOK; ++i) {
+    acc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[i] += bf16_to_f32(static_cast<uint16_t>(wv[j][q] & 0xffffu)) *
+                  bf16_to_f32(static_cast<uint16_t>(xv[i][j][q] & 0xffffu));
+        acc[i] += bf16_to_f32(static_cast<uint16_t>(wv[j][q] >> 16)) * bf16_to_f32(static_cast<uint16_t>(xv[i][j][q] >> 16));
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc[i] += __shfl_xor(acc[i], o, 64);
+  }
+  if (lane == 0) {
+    const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < TOK; ++i)
+      if (i < nt) logits[static_cast<int64_t>(t0 + i) * E + e] = acc[i] + b;
+  }
+}
+
+template <int NCH, int TOK>
+moe_status launch_logits_small(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d,
+                               int32_t E, float* logits, hipStream_t st) {
+  const int64_t items = ceil_div(T, TOK) * E;
+  hipLaunchKernelGGL((logits_small_kernel<NCH, TOK>), dim3(static_cast<unsigned>(ceil_div(items, 4))), dim3(256), 0,
+                     st, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router), bias,
+                     static_cast<int>(T), static_cast<int>(d), E, logits);
+  return launch_status();
 }
 
 moe_status check_topk_args(int64_t T, int32_t E, int32_t k, moe_score score) {
@@ -157,7 +236,11 @@ extern "C" moe_status moe_route(const void* x, const void* w_router, const float
   a.N = E;
   a.G = 1;
   hipStream_t st = as_stream(stream);
-  if (dtype == MOE_BF16 && T <= kSmallRouteTokens)
+  if (dtype == MOE_BF16 && T <= kTinyRouteTokens && d <= 4096)
+    s = launch_logits_small<8, 4>(x, w_router, bias, T, d, E, logits, st);
+  else if (dtype == MOE_BF16 && T <= kTinyRouteTokens && d <= 8192)
+    s = launch_logits_small<16, 2>(x, w_router, bias, T, d, E, logits, st);
+  else if (dtype == MOE_BF16 && T <= kSmallRouteTokens)
     s = decode_bf16_logits(x, w_router, bias, T, d, E, logits, st);
   else
     s = (dtype == MOE_BF16) ? gemm_bf16_logits(a, st) : gemm_f32_logits(a, st);

@@ -28,7 +28,8 @@ def test_header_declares_the_path():
     names = declared()
     for n in ["moe_route", "moe_topk", "moe_permute", "moe_permute_workspace_size",
               "moe_grouped_gemm_gateup_swiglu", "moe_grouped_gemm_down", "moe_unpermute_combine",
-              "moe_decode_gateup_swiglu", "moe_decode_down", "moe_abi_version", "moe_status_string"]:
+              "moe_decode_gateup_swiglu", "moe_decode_down", "moe_decode_gateup_swiglu_gather",
+              "moe_abi_version", "moe_status_string"]:
         assert n in names
 
 
@@ -78,5 +79,13 @@ def test_validation_without_gpu(lib):
         assert fn(P, P, None, 100, 128, 128, 8, 1, P, None) == B.MOE_ERR_INVALID_ARG
         assert fn(None, None, None, 0, 128, 128, 8, 1, None, None) == B.MOE_OK
     assert lib.moe_decode_down(P, P, P, 1025, 128, 128, 8, 1, P, None) == B.MOE_ERR_UNSUPPORTED
+    g = lib.moe_decode_gateup_swiglu_gather
+    assert g(P, P, 3, P, P, 100, 128, 128, 8, 1, P, None) == B.MOE_ERR_INVALID_ARG     # rows % k != 0
+    assert g(P, P, 0, P, P, 100, 128, 128, 8, 1, P, None) == B.MOE_ERR_INVALID_ARG     # k < 1
+    assert g(P, None, 2, P, P, 100, 128, 128, 8, 1, P, None) == B.MOE_ERR_INVALID_ARG  # no perm
+    assert g(P, P, 2, P, P, 100, 128, 128, 8, 0, P, None) == B.MOE_ERR_UNSUPPORTED     # fp32
+    assert g(P, P, 2, P, P, 1026, 128, 128, 8, 1, P, None) == B.MOE_ERR_UNSUPPORTED    # rows > 1024
+    assert g(P, P, 2, P, P, 100, 128, 96, 8, 1, P, None) == B.MOE_ERR_ALIGNMENT
+    assert g(None, None, 2, None, None, 0, 128, 128, 8, 1, None, None) == B.MOE_OK
     assert lib.moe_unpermute_combine(P, P, P, None, 10, 100, 2, 1, P, None) == B.MOE_ERR_ALIGNMENT
     assert lib.moe_unpermute_combine(P, P, P, None, 10, 128, 0, 1, P, None) == B.MOE_ERR_INVALID_ARG

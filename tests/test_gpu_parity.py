@@ -171,6 +171,24 @@ def test_gateup_swiglu(gpu, name, decode):
     U.assert_close(U.host_values(h), ref, wl.dtype, f"{name} H")
 
 
+@pytest.mark.parametrize("name", [n for n in SMALL if n != "c1"])
+def test_decode_gateup_swiglu_gather(gpu, name):
+    """The decode gate/up reading rows through the sort equals the oracle on
+    the gathered rows (and is bit-identical to the call on x_perm)."""
+    wl, inp, ids, w, offsets, perm, inv, x_perm = _grouped_inputs(name)
+    if wl.P > 1024:
+        pytest.skip("decode calls take at most 1024 rows")
+    gu = U.dev_tensor(inp["gu"], wl.dtype)
+    h = torch.empty(wl.P, wl.f, dtype=U.torch_dtype(wl.dtype), device=gpu)
+    B().gateup_swiglu_gather(U.dev_tensor(inp["x"], wl.dtype), _i32(perm), wl.k, gu, _i32(offsets), h)
+    hp = torch.empty_like(h)
+    B().gateup_swiglu(U.dev_tensor(x_perm, wl.dtype), gu, _i32(offsets), hp, decode=True)
+    torch.cuda.synchronize()
+    ref = O.grouped_gate_up_swiglu(W.values(x_perm, wl.dtype), W.values(inp["gu"], wl.dtype), offsets)
+    U.assert_close(U.host_values(h), ref, wl.dtype, f"{name} H (gather)")
+    assert (U.host_bits(h) == U.host_bits(hp)).all()
+
+
 @pytest.mark.parametrize("decode", [False, True], ids=["grouped", "decode"])
 @pytest.mark.parametrize("name", SMALL)
 def test_down(gpu, name, decode):
@@ -237,6 +255,31 @@ def test_layer_deterministic_and_token_equivariant(gpu):
     pi = np.random.default_rng(3).permutation(wl.T)
     yp = U.host_bits(layer.forward(x[torch.from_numpy(pi).to(gpu)].contiguous()).clone())
     assert (yp == y1[pi]).all(), "not equivariant under a token permutation"
+
+
+@pytest.mark.parametrize("name", ["c1", "c3s_t1", "c3s_t37", "c5s"])
+def test_graph_replay_matches_eager(gpu, name):
+    """The layer captured in a HIP graph replays bit-identically to the eager
+    calls, replay after replay, with new tokens written into the graph's
+    input and other eager work on the stream between replays."""
+    wl, inp = U.small_inputs(name)
+    weights = U.device_weights(wl, inp)
+    eager = B().MoeLayer(weights, wl.k, wl.score)
+    x1 = U.dev_tensor(inp["x"], wl.dtype)
+    pi = torch.from_numpy(np.random.default_rng(5).permutation(wl.T)).to(gpu)
+    x2 = (x1[pi] * 0.5).contiguous()
+    y1 = U.host_bits(eager.forward(x1).clone())
+    y2 = U.host_bits(eager.forward(x2).clone())
+    g = B().MoeLayerGraph(weights, wl.k, wl.score, wl.T, timed=("gateup",))
+    for rep in range(4):
+        src, ref = (x1, y1) if rep % 2 == 0 else (x2, y2)
+        g.x.copy_(src)
+        y = g.replay()
+        torch.cuda.synchronize()
+        assert (U.host_bits(y) == ref).all(), f"replay {rep} differs from the eager layer"
+        assert 0.0 < g.stage_ms()["gateup"] < 1e3
+        eager.forward(x2 if rep % 2 == 0 else x1)
+        torch.cuda.synchronize()
 
 
 def test_layer_zero_tokens(gpu):
