@@ -136,10 +136,12 @@ def setup(wl, device):
 
 # ------------------------------------------------------------ CPU oracle
 
-def cpu_baseline(wl, host, sample_tokens: int):
+def cpu_baseline(wl, host, sample_tokens: int, target_s: float = 15.0):
     """Time the CPU oracle (router + eager expert loop, float64) on the first
-    `sample_tokens` tokens of the workload.  Input generation is excluded;
-    decoding the stored bf16 values for the oracle is included."""
+    `sample_tokens` tokens of the workload; when that takes well under
+    target_s seconds, time it again on enough tokens (at most T) to take
+    about target_s.  Input generation is excluded; decoding the stored bf16
+    values for the oracle is included."""
     from oracle import moe_oracle as O
     try:
         import threadpoolctl
@@ -157,14 +159,21 @@ def cpu_baseline(wl, host, sample_tokens: int):
             g, w = W.gen_expert(wl, e)
         return W.values(g, wl.dtype), W.values(w, wl.dtype)
 
-    t0 = time.perf_counter()
-    x = W.values(host["x"][:S], wl.dtype)
-    L = O.router_logits(x, W.values(host["wr"], wl.dtype), host["bias"])
-    ids, w = O.route(L, wl.k, wl.score)
-    sh = host["shared"]
-    shared = None if sh is None else (W.values(sh[0], wl.dtype), W.values(sh[1], wl.dtype))
-    O.moe_layer_eager(x, ids, w, fetch, wl.E, shared)
-    dt = time.perf_counter() - t0
+    def run(S):
+        t0 = time.perf_counter()
+        x = W.values(host["x"][:S], wl.dtype)
+        L = O.router_logits(x, W.values(host["wr"], wl.dtype), host["bias"])
+        ids, w = O.route(L, wl.k, wl.score)
+        sh = host["shared"]
+        shared = None if sh is None else (W.values(sh[0], wl.dtype), W.values(sh[1], wl.dtype))
+        O.moe_layer_eager(x, ids, w, fetch, wl.E, shared)
+        return time.perf_counter() - t0, ids
+
+    dt, ids = run(S)
+    if target_s and dt < 0.5 * target_s and S < wl.T:
+        # a bounded sample of about target_s seconds of CPU work
+        S = min(wl.T, max(S + 1, int(S * target_s / dt)))
+        dt, ids = run(S)
     return {"value": S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {S} of {wl.T} tokens of workload {wl.name}: float64 router + eager "
                       f"per-expert loop over the {len(np.unique(ids))} experts they select; "
@@ -183,6 +192,97 @@ def copy_probe(nbytes: int, reps: int = 3):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": nbytes, "reps": reps}))
+
+
+def _smi_sample():
+    """One amd-smi reading: socket power (W) and the gfx clocks (MHz) of the
+    XCDs, or None where amd-smi is missing."""
+    import csv
+    import io
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--csv"], capture_output=True, text=True,
+                             timeout=20).stdout
+        row = list(csv.DictReader(io.StringIO(out.strip())))[0]
+    except (OSError, subprocess.SubprocessError, IndexError, ValueError):
+        return None
+    clk = [float(row[k]) for k in row if k.startswith("gfx_") and k.endswith("_clk") and k[4:-4].isdigit()
+           and row[k] not in ("N/A", "")]
+    try:
+        power = float(row.get("socket_power", "nan"))
+    except ValueError:
+        power = float("nan")
+    return {"power_w": power, "gfx_clk_mhz": clk}
+
+
+def clock_probe(workload: str, seconds: float, command: str, out: str):
+    """Run the dominant kernel (gate/up) back to back for `seconds` while
+    sampling the reported gfx clocks and socket power, then the same for a
+    plain torch.matmul of the workload's gate/up shape (hipBLASLt), and write
+    a markdown summary: the achieved TFLOP/s next to the clock it ran at."""
+    import threading
+    import torch
+    from mixture_experts_ffn_04_amd import binding as Bnd
+    wl = W.get(workload)
+    layer, x, _ = setup(wl, torch.device("cuda:0"))
+    layer.forward(x)
+    torch.cuda.synchronize()
+    L = layer
+    flops = gateup_flops(wl)
+
+    def gate():
+        Bnd.gateup_swiglu(L.x_perm, L.w.w_gate_up, L.offsets, L.h, L.use_decode(wl.T))
+
+    P = wl.T * wl.k
+    a = torch.randn(P, wl.d, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(wl.d, 2 * wl.f, dtype=torch.bfloat16, device="cuda")
+
+    def dense():
+        torch.matmul(a, b)
+
+    rows = []
+    for name, fn in (("libmoe gate/up (grouped, fused SwiGLU)", gate), ("torch.matmul (hipBLASLt), same P x d x 2f", dense)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        samples, stop = [], []
+
+        def sampler():
+            while not stop:
+                r = _smi_sample()
+                if r is not None:
+                    samples.append(r)
+                time.sleep(0.25)
+
+        th = threading.Thread(target=sampler)
+        th.start()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n, t0 = 0, time.time()
+        e0.record()
+        while time.time() - t0 < seconds:
+            for _ in range(10):
+                fn()
+            n += 10
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        stop.append(1)
+        th.join()
+        ms = e0.elapsed_time(e1) / n
+        clk = [float(np.mean(s["gfx_clk_mhz"])) for s in samples[1:] if s["gfx_clk_mhz"]]
+        pw = [s["power_w"] for s in samples[1:]]
+        rows.append((name, ms, flops / (ms * 1e-3) / 1e12, float(np.median(clk)) if clk else float("nan"),
+                     float(np.median(pw)) if pw else float("nan"), len(samples)))
+    lines = [f"# Clock and power under load: gate/up on workload {workload}", "", "Command:", "", "```", command,
+             "```", "",
+             "| kernel | ms per launch | TFLOP/s | median gfx clock (MHz, mean over XCDs) | median socket power (W) | samples |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r[0]} | {r[1]:.3f} | {r[2]:.0f} | {r[3]:.0f} | {r[4]:.0f} | {r[5]} |")
+    lines += ["", f"Dense bf16 peak at the measured clock = 2.5 PFLOP/s x clock / 2400 MHz."]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def _read_csv(path):
@@ -278,6 +378,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernels", action="store_true", help="also print per-stage times to stderr")
     ap.add_argument("--copy-probe", type=int, default=0, help="run a plain copy of this many bytes and exit")
+    ap.add_argument("--clock-probe", nargs=4, metavar=("WORKLOAD", "SECONDS", "COMMAND", "OUT"),
+                    help="gate/up and hipBLASLt back to back while sampling clocks and power; write OUT")
     ap.add_argument("--summarize-trace", nargs=4, metavar=("DIR", "TITLE", "COMMAND", "OUT"))
     ap.add_argument("--summarize-traffic", nargs=11,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "MATCH", "KERNEL",
@@ -294,6 +396,10 @@ def main(argv=None):
         return 0
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return 0
+    if args.clock_probe:
+        w, sec, cmd, out = args.clock_probe
+        clock_probe(w, float(sec), cmd, out)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
