@@ -222,7 +222,6 @@ def clock_probe(workload: str, seconds: float, command: str, out: str):
     a markdown summary: the achieved TFLOP/s next to the clock it ran at."""
     import threading
     import torch
-    from mixture_experts_ffn_04_amd import binding as Bnd
     wl = W.get(workload)
     layer, x, _ = setup(wl, torch.device("cuda:0"))
     layer.forward(x)
@@ -230,8 +229,12 @@ def clock_probe(workload: str, seconds: float, command: str, out: str):
     L = layer
     flops = gateup_flops(wl)
 
+    st = torch.cuda.current_stream()
+    gate_stage = [a for n, fn, a in L.stages(x, st) if n == "gateup"][0]
+    gate_fn = [fn for n, fn, a in L.stages(x, st) if n == "gateup"][0]
+
     def gate():
-        Bnd.gateup_swiglu(L.x_perm, L.w.w_gate_up, L.offsets, L.h, L.use_decode(wl.T))
+        gate_fn(*gate_stage)
 
     P = wl.T * wl.k
     a = torch.randn(P, wl.d, dtype=torch.bfloat16, device="cuda")

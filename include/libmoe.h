@@ -18,6 +18,8 @@
  *   moe_permute                      sort by expert ID (histogram, scan,
  *                                    stable scatter) + gather of the rows
  *   moe_grouped_gemm_gateup_swiglu   per-expert gate/up projection + SwiGLU
+ *   moe_grouped_gemm_gateup_swiglu_gather  the same, reading the rows
+ *                                    through the sort instead of x_perm
  *   moe_grouped_gemm_down            per-expert down projection
  *   moe_unpermute_combine            weighted combine back to token order
  *   moe_decode_gateup_swiglu         small-batch variants that stream only
@@ -190,6 +192,21 @@ MOE_API moe_status moe_unpermute_combine(const void* y_perm, const int32_t* inv_
                                  const float* topk_w, const void* y_shared,
                                  int64_t T, int64_t d, int32_t k, moe_dtype dtype,
                                  void* y, void* stream);
+
+/*
+ * moe_grouped_gemm_gateup_swiglu with the row gather of moe_permute folded
+ * into the tile loads: input row r is x[perm[r] / k] for the token
+ * activations x [rows/k][d] and perm as written by moe_permute (same sort),
+ * so moe_permute can be called with x_perm = NULL and the x_perm copy is
+ * neither written nor read.  rows = T*k must be a multiple of k (1 <= k <=
+ * 16, else MOE_ERR_INVALID_ARG); perm entries are clamped to [0, rows).
+ * bf16 only (MOE_ERR_UNSUPPORTED for fp32, and when x exceeds 2 GiB).
+ */
+MOE_API moe_status moe_grouped_gemm_gateup_swiglu_gather(const void* x, const int32_t* perm,
+                                                 int32_t k, const void* w_gate_up,
+                                                 const int32_t* offsets, int64_t rows,
+                                                 int64_t d, int64_t f, int32_t E,
+                                                 moe_dtype dtype, void* h, void* stream);
 
 /*
  * Small-batch (decode) variants of the two grouped projections, for rows

@@ -25,7 +25,7 @@ EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_route", "moe_topk",
     "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_gateup_swiglu",
     "moe_grouped_gemm_down", "moe_unpermute_combine", "moe_decode_gateup_swiglu",
-    "moe_decode_down", "moe_decode_gateup_swiglu_gather",
+    "moe_decode_down", "moe_decode_gateup_swiglu_gather", "moe_grouped_gemm_gateup_swiglu_gather",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -45,6 +45,8 @@ _SIGS = {
     "moe_decode_gateup_swiglu": ([P, P, P, I64, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
     "moe_decode_down": ([P, P, P, I64, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
     "moe_decode_gateup_swiglu_gather": ([P, P, I32, P, P, I64, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
+    "moe_grouped_gemm_gateup_swiglu_gather": ([P, P, I32, P, P, I64, I64, I64, I32, ctypes.c_int, P, P],
+                                              ctypes.c_int),
 }
 
 
@@ -142,14 +144,15 @@ def gateup_swiglu(x_perm, w_gate_up, offsets, h, decode: bool = False, stream=No
                                    _dt(x_perm), _ptr(h), _stream(stream)))
 
 
-def gateup_swiglu_gather(x, perm, k: int, w_gate_up, offsets, h, stream=None):
-    """Decode gate/up + SwiGLU reading row r as x[perm[r] // k] (no x_perm)."""
+def gateup_swiglu_gather(x, perm, k: int, w_gate_up, offsets, h, decode: bool = False, stream=None):
+    """Gate/up + SwiGLU reading row r as x[perm[r] // k] (no x_perm), grouped
+    or decode form."""
     rows = perm.shape[0]
     d = x.shape[1]
     E, f2, _ = w_gate_up.shape
-    _check("moe_decode_gateup_swiglu_gather", load().moe_decode_gateup_swiglu_gather(
-        _ptr(x), _ptr(perm), k, _ptr(w_gate_up), _ptr(offsets), rows, d, f2 // 2, E, _dt(x), _ptr(h),
-        _stream(stream)))
+    fn = "moe_decode_gateup_swiglu_gather" if decode else "moe_grouped_gemm_gateup_swiglu_gather"
+    _check(fn, getattr(load(), fn)(_ptr(x), _ptr(perm), k, _ptr(w_gate_up), _ptr(offsets), rows, d, f2 // 2, E,
+                                   _dt(x), _ptr(h), _stream(stream)))
 
 
 def down(h, w_down, offsets, y_perm, decode: bool = False, stream=None):
@@ -243,13 +246,13 @@ class MoeLayer:
         self._alloc(T)
         w = self.w
         dec = self.use_decode(T)
-        # bf16 decode reads the token rows through the sort (no x_perm copy)
-        gather = dec and self.dtype == torch.bfloat16
+        # bf16 gate/up reads the token rows through the sort (no x_perm copy)
+        gather = self.dtype == torch.bfloat16
         out = [
             ("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st)),
             ("permute", permute, (self.ids, x, self.E, self.counts, self.offsets, self.perm, self.inv_perm,
                                   None if gather else self.x_perm, self.ws, st)),
-            ("gateup", gateup_swiglu_gather, (x, self.perm, self.k, w.w_gate_up, self.offsets, self.h, st))
+            ("gateup", gateup_swiglu_gather, (x, self.perm, self.k, w.w_gate_up, self.offsets, self.h, dec, st))
             if gather else
             ("gateup", gateup_swiglu, (self.x_perm, w.w_gate_up, self.offsets, self.h, dec, st)),
             ("down", down, (self.h, w.w_down, self.offsets, self.y_perm, dec, st)),
@@ -367,4 +370,9 @@ def moe_decode_down(h, w_down, offsets, y_perm, stream=None):
     down(h, w_down, offsets, y_perm, True, stream)
 
 
-moe_decode_gateup_swiglu_gather = gateup_swiglu_gather
+def moe_decode_gateup_swiglu_gather(x, perm, k, w_gate_up, offsets, h, stream=None):
+    gateup_swiglu_gather(x, perm, k, w_gate_up, offsets, h, True, stream)
+
+
+def moe_grouped_gemm_gateup_swiglu_gather(x, perm, k, w_gate_up, offsets, h, stream=None):
+    gateup_swiglu_gather(x, perm, k, w_gate_up, offsets, h, False, stream)

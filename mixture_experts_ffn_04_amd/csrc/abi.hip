@@ -69,6 +69,23 @@ extern "C" moe_status moe_grouped_gemm_gateup_swiglu(const void* x_perm, const v
   return dtype == MOE_BF16 ? gemm_bf16_gateup_swiglu(a, as_stream(stream)) : gemm_f32_gateup_swiglu(a, as_stream(stream));
 }
 
+extern "C" moe_status moe_grouped_gemm_gateup_swiglu_gather(const void* x, const int32_t* perm, int32_t k,
+                                                            const void* w_gate_up, const int32_t* offsets,
+                                                            int64_t rows, int64_t d, int64_t f, int32_t E,
+                                                            moe_dtype dtype, void* h, void* stream) {
+  moe_status s = check_proj(x, w_gate_up, offsets, rows, d, f, E, dtype, h);
+  if (s != MOE_OK) return s;
+  if (k < 1 || k > kMaxK || rows % k != 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!perm) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  GemmArgs a = proj_args(x, w_gate_up, offsets, rows, d, f, E, h);
+  a.rowmap = perm;
+  a.kdiv = k;
+  a.a_rows = rows / k;
+  return gemm_bf16_gateup_swiglu(a, as_stream(stream));
+}
+
 extern "C" moe_status moe_grouped_gemm_down(const void* h, const void* w_down, const int32_t* offsets, int64_t rows,
                                             int64_t d, int64_t f, int32_t E, moe_dtype dtype, void* y_perm,
                                             void* stream) {

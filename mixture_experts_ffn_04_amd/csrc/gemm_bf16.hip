@@ -275,8 +275,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
     wbase += tl.n0 * rowb;
     wrecords = static_cast<int>((N - tl.n0) * rowb);
   }
-  const char* abase = static_cast<const char*>(a.A) + static_cast<int64_t>(tl.row0) * rowb;
-  const int arecords = static_cast<int>(min(tl.row_end - tl.row0, BM) * rowb);
+  // Token rows: the tile's own rows of A, or (row gather) rows of A picked
+  // through rowmap, the descriptor then spanning all of A.
+  const bool gather = a.rowmap != nullptr;
+  const char* abase = static_cast<const char*>(a.A) + (gather ? 0 : static_cast<int64_t>(tl.row0) * rowb);
+  const int arecords = gather ? static_cast<int>(a.a_rows * rowb)
+                              : static_cast<int>(min(tl.row_end - tl.row0, BM) * rowb);
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, wrecords, kBufFlags);
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase), 0, arecords, kBufFlags);
 
@@ -298,6 +302,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
       } else {
         off = static_cast<int64_t>(r) * rowb;
       }
+    } else if (gather) {
+      // rows past the group's end read row 0 (their results are never stored)
+      const int grow = tl.row0 + (r - BN);
+      const int src = grow < tl.row_end ? clamp_off(a.rowmap[grow], static_cast<int>(a.rows) - 1) / a.kdiv : 0;
+      off = static_cast<int64_t>(src) * rowb;
     } else {
       off = static_cast<int64_t>(r - BN) * rowb;
     }
@@ -525,6 +534,7 @@ moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   const int64_t wbytes = ((EPI == EPI_SWIGLU) ? 2 : 1) * a.N * a.K * 2;
   if (wbytes >= (int64_t(1) << 31) || static_cast<int64_t>(BM) * a.K * 2 >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
+  if (a.rowmap && (a.kdiv < 1 || a.a_rows * a.K * 2 >= (int64_t(1) << 31))) return MOE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, NS, SP>), dim3(static_cast<unsigned>(grid)),
                      dim3(64 * WM * WN), 0, st, a);
   return launch_status();

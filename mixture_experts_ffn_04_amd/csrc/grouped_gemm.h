@@ -42,6 +42,11 @@ struct GemmArgs {
   int64_t K;
   int64_t N;              // output columns
   int G;                  // groups
+  // Optional row gather (bf16 tile kernel): A row r is A[rowmap[r] / kdiv]
+  // (rowmap entries clamped to [0, rows)); A then has a_rows rows.
+  const int32_t* rowmap;
+  int kdiv;
+  int64_t a_rows;
 };
 
 struct TileLoc {

@@ -171,18 +171,20 @@ def test_gateup_swiglu(gpu, name, decode):
     U.assert_close(U.host_values(h), ref, wl.dtype, f"{name} H")
 
 
+@pytest.mark.parametrize("decode", [False, True], ids=["grouped", "decode"])
 @pytest.mark.parametrize("name", [n for n in SMALL if n != "c1"])
-def test_decode_gateup_swiglu_gather(gpu, name):
-    """The decode gate/up reading rows through the sort equals the oracle on
-    the gathered rows (and is bit-identical to the call on x_perm)."""
+def test_gateup_swiglu_gather(gpu, name, decode):
+    """Gate/up reading rows through the sort equals the oracle on the
+    gathered rows and is bit-identical to the same call on x_perm."""
     wl, inp, ids, w, offsets, perm, inv, x_perm = _grouped_inputs(name)
-    if wl.P > 1024:
+    if decode and wl.P > 1024:
         pytest.skip("decode calls take at most 1024 rows")
     gu = U.dev_tensor(inp["gu"], wl.dtype)
     h = torch.empty(wl.P, wl.f, dtype=U.torch_dtype(wl.dtype), device=gpu)
-    B().gateup_swiglu_gather(U.dev_tensor(inp["x"], wl.dtype), _i32(perm), wl.k, gu, _i32(offsets), h)
+    B().gateup_swiglu_gather(U.dev_tensor(inp["x"], wl.dtype), _i32(perm), wl.k, gu, _i32(offsets), h,
+                             decode=decode)
     hp = torch.empty_like(h)
-    B().gateup_swiglu(U.dev_tensor(x_perm, wl.dtype), gu, _i32(offsets), hp, decode=True)
+    B().gateup_swiglu(U.dev_tensor(x_perm, wl.dtype), gu, _i32(offsets), hp, decode=decode)
     torch.cuda.synchronize()
     ref = O.grouped_gate_up_swiglu(W.values(x_perm, wl.dtype), W.values(inp["gu"], wl.dtype), offsets)
     U.assert_close(U.host_values(h), ref, wl.dtype, f"{name} H (gather)")
