@@ -557,11 +557,11 @@ moe_status launch(const GemmArgs& a, hipStream_t st) {
 // (2 along tokens x 4 along weights, 128 x 64 each), two 64-wide
 // direct-to-LDS stages.
 moe_status gemm_bf16_gateup_swiglu(const GemmArgs& a, hipStream_t st) {
-  return launch_dtl<256, 256, 2, 4, EPI_SWIGLU, 8, 64, 2, 2>(a, st);
+  return launch_dtl<256, 256, 2, 4, EPI_SWIGLU, 16, 64, 2, 2>(a, st);
 }
 
 moe_status gemm_bf16_down(const GemmArgs& a, hipStream_t st) {
-  return launch_dtl<256, 256, 2, 4, EPI_STORE, 8, 64, 2, 2>(a, st);
+  return launch_dtl<256, 256, 2, 4, EPI_STORE, 16, 64, 2, 2>(a, st);
 }
 
 moe_status gemm_bf16_logits(const GemmArgs& a, hipStream_t st) {
