@@ -564,9 +564,12 @@ moe_status gemm_bf16_down(const GemmArgs& a, hipStream_t st) {
   return launch_dtl<256, 256, 2, 4, EPI_STORE, 16, 64, 2, 2>(a, st);
 }
 
+// Router logits: few output columns, so small token tiles keep every CU
+// busy (measured best per expert count on the MoE shapes).
 moe_status gemm_bf16_logits(const GemmArgs& a, hipStream_t st) {
-  if (a.N <= 64) return launch<128, 64, 4, 1, EPI_F32B, 1>(a, st);
-  return launch<128, 256, 2, 2, EPI_F32B, 1>(a, st);
+  if (a.N <= 64) return launch<64, 64, 2, 2, EPI_F32B, 1>(a, st);
+  if (a.N <= 128) return launch<32, 128, 1, 4, EPI_F32B, 1>(a, st);
+  return launch<64, 128, 2, 2, EPI_F32B, 1>(a, st);
 }
 
 }  // namespace moe

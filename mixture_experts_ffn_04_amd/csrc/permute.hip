@@ -22,6 +22,7 @@ namespace moe {
 namespace {
 
 constexpr int kChunk = 1024;   // pairs per chunk
+constexpr int kScanBatch = 16; // chunks loaded together by the scan
 
 size_t ws_bytes_for(int64_t P, int E) {
   const int64_t chunks = ceil_div(P, kChunk);
@@ -50,12 +51,20 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t* __restrict__ cc, int
   __shared__ int wsum[4];
   const int e = threadIdx.x;
   int tot = 0;
+  // Batches of kScanBatch chunks: the loads of a batch are independent, so
+  // they are all issued before the running sum (one memory round trip per
+  // batch instead of per chunk).
   if (e < E) {
-    for (int c = 0; c < chunks; ++c) {
-      const int64_t i = static_cast<int64_t>(c) * E + e;
-      const int v = cc[i];
-      cc[i] = tot;          // base of chunk c inside expert e's group
-      tot += v;
+    for (int c0 = 0; c0 < chunks; c0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j)
+        v[j] = c0 + j < chunks ? cc[static_cast<int64_t>(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (c0 + j < chunks) cc[static_cast<int64_t>(c0 + j) * E + e] = tot;   // base of the chunk in e's group
+        tot += v[j];
+      }
     }
   }
   const int lane = e & 63, w = e >> 6;
@@ -73,7 +82,15 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t* __restrict__ cc, int
   if (e < E) {
     counts[e] = tot;
     offsets[e] = excl;
-    for (int c = 0; c < chunks; ++c) cc[static_cast<int64_t>(c) * E + e] += excl;
+    for (int c0 = 0; c0 < chunks; c0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j)
+        v[j] = c0 + j < chunks ? cc[static_cast<int64_t>(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j)
+        if (c0 + j < chunks) cc[static_cast<int64_t>(c0 + j) * E + e] = v[j] + excl;
+    }
   }
   if (e == E - 1) offsets[E] = excl + tot;
 }

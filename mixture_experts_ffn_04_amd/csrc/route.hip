@@ -23,10 +23,12 @@ moe_status gemm_f32_logits(const GemmArgs& a, hipStream_t st);
 moe_status decode_bf16_logits(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d,
                               int32_t E, float* logits, hipStream_t st);
 
-// bf16 router logits by batch size: up to kTinyRouteTokens tokens (and
-// d <= 8192), one wave per (expert row, few tokens); up to kSmallRouteTokens, the split-K
-// streaming kernel; above, the tiled MFMA GEMM.
+// bf16 router logits: one wave per (expert row, few tokens) up to
+// kTinyRouteTokens tokens or kTinyRouteExperts experts (d <= 8192); else up
+// to kSmallRouteTokens tokens the split-K streaming kernel; above, the tiled
+// MFMA GEMM.
 constexpr int64_t kTinyRouteTokens = 64;
+constexpr int kTinyRouteExperts = 16;
 constexpr int64_t kSmallRouteTokens = 256;
 
 namespace {
@@ -236,9 +238,11 @@ extern "C" moe_status moe_route(const void* x, const void* w_router, const float
   a.N = E;
   a.G = 1;
   hipStream_t st = as_stream(stream);
-  if (dtype == MOE_BF16 && T <= kTinyRouteTokens && d <= 4096)
+  const bool tiny = (T <= kTinyRouteTokens || E <= kTinyRouteExperts) &&
+                    ceil_div(T, 2) * E < (int64_t(1) << 31);          // (token block, expert) items fit an int
+  if (dtype == MOE_BF16 && tiny && d <= 4096)
     s = launch_logits_small<8, 4>(x, w_router, bias, T, d, E, logits, st);
-  else if (dtype == MOE_BF16 && T <= kTinyRouteTokens && d <= 8192)
+  else if (dtype == MOE_BF16 && tiny && d <= 8192)
     s = launch_logits_small<16, 2>(x, w_router, bias, T, d, E, logits, st);
   else if (dtype == MOE_BF16 && T <= kSmallRouteTokens)
     s = decode_bf16_logits(x, w_router, bias, T, d, E, logits, st);
