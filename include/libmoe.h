@@ -22,6 +22,8 @@
  *                                    through the sort instead of x_perm
  *   moe_grouped_gemm_down            per-expert down projection
  *   moe_unpermute_combine            weighted combine back to token order
+ *   moe_localize_ids                 expert-parallel share: global ids to
+ *                                    local ones, other experts masked
  *   moe_decode_gateup_swiglu         small-batch variants that stream only
  *   moe_decode_gateup_swiglu_gather  the active experts' weights (the
  *   moe_decode_down                  _gather form reads the rows through
@@ -134,12 +136,15 @@ MOE_API size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t E);
  *   inv_perm[p]  = row of p
  *   x_perm[r][:] = x[perm[r] / k][:]     (skipped when x_perm is NULL)
  *
- *   topk_ids [T*k] int32 in [0, E)      x [T][d] dtype (may be NULL iff x_perm is)
+ *   topk_ids [T*k] int32             x [T][d] dtype (may be NULL iff x_perm is)
  *   counts [E], offsets [E+1], perm [T*k], inv_perm [T*k]  int32 outputs
  *   x_perm [T*k][d] dtype output
  *   ws / ws_bytes: device scratch of at least moe_permute_workspace_size()
- * Ids outside [0, E) are counted nowhere and make the outputs undefined
- * (no out-of-bounds access happens).
+ * Ids outside [0, E) mark pairs routed to experts this call does not hold
+ * (an expert-parallel share, see moe_localize_ids): they get no row, are
+ * counted nowhere and get inv_perm[p] = -1, so offsets[E] is the number of
+ * pairs held here; perm and x_perm rows past offsets[E] are not written.
+ * 1 <= k <= 16 (k may exceed E for such a share).
  */
 MOE_API moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_t T, int64_t d,
                        int32_t E, int32_t k, moe_dtype dtype, int32_t* counts,
@@ -186,12 +191,29 @@ MOE_API moe_status moe_grouped_gemm_down(const void* h, const void* w_down,
  *
  *   y_perm [T*k][d], y_shared [T][d] or NULL, y [T][d]  (dtype)
  *   inv_perm [T*k] int32, topk_w [T][k] fp32
- * inv_perm entries are clamped to [0, T*k).
+ * A negative inv_perm entry (a pair handled by another expert-parallel
+ * share) adds nothing; the others are clamped to [0, T*k).
  */
 MOE_API moe_status moe_unpermute_combine(const void* y_perm, const int32_t* inv_perm,
                                  const float* topk_w, const void* y_shared,
                                  int64_t T, int64_t d, int32_t k, moe_dtype dtype,
                                  void* y, void* stream);
+
+/*
+ * Expert-parallel share (article, section "Expert Parallelism"): a device
+ * that holds the experts [e_begin, e_begin + e_count) maps the router's
+ * global ids to its local ones and masks the pairs of experts held
+ * elsewhere:
+ *   local_ids[i] = topk_ids[i] - e_begin   if e_begin <= topk_ids[i] < e_begin + e_count
+ *                = -1                      otherwise
+ * local_ids then feeds moe_permute with E = e_count and the share's slice
+ * of the packed expert weights; moe_unpermute_combine gives the share's
+ * partial output, and the partial outputs of all shares sum to the layer's
+ * output (the exchange between devices is not part of this library).
+ *   topk_ids, local_ids [n] int32 (device); 0 <= e_begin, 1 <= e_count <= 256.
+ */
+MOE_API moe_status moe_localize_ids(const int32_t* topk_ids, int64_t n, int32_t e_begin,
+                                    int32_t e_count, int32_t* local_ids, void* stream);
 
 /*
  * moe_grouped_gemm_gateup_swiglu with the row gather of moe_permute folded

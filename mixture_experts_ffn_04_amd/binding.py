@@ -26,6 +26,7 @@ EXPORTS = (
     "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_gateup_swiglu",
     "moe_grouped_gemm_down", "moe_unpermute_combine", "moe_decode_gateup_swiglu",
     "moe_decode_down", "moe_decode_gateup_swiglu_gather", "moe_grouped_gemm_gateup_swiglu_gather",
+    "moe_localize_ids",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -47,6 +48,7 @@ _SIGS = {
     "moe_decode_gateup_swiglu_gather": ([P, P, I32, P, P, I64, I64, I64, I32, ctypes.c_int, P, P], ctypes.c_int),
     "moe_grouped_gemm_gateup_swiglu_gather": ([P, P, I32, P, P, I64, I64, I64, I32, ctypes.c_int, P, P],
                                               ctypes.c_int),
+    "moe_localize_ids": ([P, I64, I32, I32, P, P], ctypes.c_int),
 }
 
 
@@ -122,6 +124,12 @@ def topk(logits, k: int, score: str, topk_ids, topk_w, stream=None):
                                        _ptr(topk_w), _stream(stream)))
 
 
+def localize_ids(topk_ids, e_begin: int, e_count: int, local_ids, stream=None):
+    """Expert-parallel share: global ids -> ids local to [e_begin, e_begin+e_count), -1 elsewhere."""
+    _check("moe_localize_ids", load().moe_localize_ids(_ptr(topk_ids), topk_ids.numel(), e_begin, e_count,
+                                                       _ptr(local_ids), _stream(stream)))
+
+
 def permute_workspace_size(T: int, k: int, E: int) -> int:
     return int(load().moe_permute_workspace_size(T, k, E))
 
@@ -190,17 +198,35 @@ class MoeLayer:
     gate/up + SwiGLU and down projections (grouped, or decode variants for
     small batches), the shared expert when present, and the weighted
     combine.  Buffers are allocated once per token count and reused.
+
+    experts=(e_begin, e_count) makes it one expert-parallel share: the
+    router (weights.w_router) covers all experts, weights.w_gate_up and
+    weights.w_down hold only experts [e_begin, e_begin + e_count), and
+    forward returns the share's partial output (the pairs of other experts
+    masked by moe_localize_ids); the partial outputs of all shares sum to
+    the layer's output.
     """
 
     DECODE_MAX_ROWS = 256
 
-    def __init__(self, weights: MoeWeights, k: int, score: str, mode: str = "auto"):
+    def __init__(self, weights: MoeWeights, k: int, score: str, mode: str = "auto",
+                 experts: Optional[tuple] = None):
         load()
         self.w = weights
         self.k = k
         self.score = score
         self.mode = mode
-        self.E, self.d = weights.w_router.shape
+        self.E, self.d = weights.w_router.shape          # experts seen by the router
+        self.E_loc = weights.w_gate_up.shape[0]          # experts held here
+        if experts is None:
+            if self.E_loc != self.E:
+                raise ValueError("expert weights cover a share of the experts: pass experts=(e_begin, e_count)")
+            self.e_begin = None
+        else:
+            e_begin, e_count = experts
+            if e_count != self.E_loc or e_begin < 0 or e_begin + e_count > self.E:
+                raise ValueError("experts=(e_begin, e_count) does not match the expert weights")
+            self.e_begin = int(e_begin)
         self.f = weights.w_down.shape[2]
         self.dev = weights.w_router.device
         self.dtype = weights.w_gate_up.dtype
@@ -215,14 +241,16 @@ class MoeLayer:
         self.logits = torch.empty(T, E, device=dev, dtype=torch.float32)
         self.ids = torch.empty(T, k, device=dev, dtype=i32)
         self.wts = torch.empty(T, k, device=dev, dtype=torch.float32)
-        self.counts = torch.empty(E, device=dev, dtype=i32)
-        self.offsets = torch.empty(E + 1, device=dev, dtype=i32)
+        El = self.E_loc
+        self.counts = torch.empty(El, device=dev, dtype=i32)
+        self.offsets = torch.empty(El + 1, device=dev, dtype=i32)
+        self.lids = torch.empty(T, k, device=dev, dtype=i32) if self.e_begin is not None else None
         self.perm = torch.empty(P, device=dev, dtype=i32)
         self.inv_perm = torch.empty(P, device=dev, dtype=i32)
         self.x_perm = torch.empty(P, d, device=dev, dtype=dt)
         self.h = torch.empty(P, f, device=dev, dtype=dt)
         self.y_perm = torch.empty(P, d, device=dev, dtype=dt)
-        self.ws = torch.empty(max(1, permute_workspace_size(T, k, E)), device=dev, dtype=torch.uint8)
+        self.ws = torch.empty(max(1, permute_workspace_size(T, k, El)), device=dev, dtype=torch.uint8)
         self.y = torch.empty(T, d, device=dev, dtype=dt)
         if self.w.shared_gate_up is not None:
             fs = self.w.shared_down.shape[2]
@@ -238,7 +266,7 @@ class MoeLayer:
             return False
         return T * self.k <= self.DECODE_MAX_ROWS
 
-    STAGES = ("route", "permute", "gateup", "down", "shared_gateup", "shared_down", "combine")
+    STAGES = ("route", "localize", "permute", "gateup", "down", "shared_gateup", "shared_down", "combine")
 
     def stages(self, x: torch.Tensor, st) -> list:
         """The layer on x [T, d] as (stage name, call, args) in launch order."""
@@ -248,9 +276,13 @@ class MoeLayer:
         dec = self.use_decode(T)
         # bf16 gate/up reads the token rows through the sort (no x_perm copy)
         gather = self.dtype == torch.bfloat16
-        out = [
-            ("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st)),
-            ("permute", permute, (self.ids, x, self.E, self.counts, self.offsets, self.perm, self.inv_perm,
+        out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st))]
+        ids = self.ids
+        if self.e_begin is not None:
+            out.append(("localize", localize_ids, (self.ids, self.e_begin, self.E_loc, self.lids, st)))
+            ids = self.lids
+        out += [
+            ("permute", permute, (ids, x, self.E_loc, self.counts, self.offsets, self.perm, self.inv_perm,
                                   None if gather else self.x_perm, self.ws, st)),
             ("gateup", gateup_swiglu_gather, (x, self.perm, self.k, w.w_gate_up, self.offsets, self.h, dec, st))
             if gather else
@@ -360,6 +392,7 @@ moe_permute = permute
 moe_grouped_gemm_gateup_swiglu = gateup_swiglu
 moe_grouped_gemm_down = down
 moe_unpermute_combine = unpermute_combine
+moe_localize_ids = localize_ids
 
 
 def moe_decode_gateup_swiglu(x_perm, w_gate_up, offsets, h, stream=None):

@@ -30,8 +30,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   for (int j = 0; j < kMaxK; ++j) {
     if (j >= k) break;
     int r = inv[static_cast<int64_t>(t) * k + j];
+    // a negative entry marks a pair handled elsewhere: it adds nothing
+    wt[j] = r < 0 ? 0.0f : w[static_cast<int64_t>(t) * k + j];
     rows[j] = r < 0 ? 0 : (r >= P ? P - 1 : r);
-    wt[j] = w[static_cast<int64_t>(t) * k + j];
   }
   for (int64_t c = lane; c < row_chunks; c += 64) {
     constexpr int NE = BF16 ? 8 : 4;

@@ -132,16 +132,18 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
       if (lane == leader) base[e] += cnt;
       perm[pos] = p;
       inv_perm[p] = pos;
+    } else if (p < p1) {
+      inv_perm[p] = -1;                            // routed to an expert not in this call
     }
     __syncthreads();
   }
 }
 
 __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ perm,
-                                                     int P, int T, int k, int64_t row_chunks,
-                                                     uint4* __restrict__ xp) {
+                                                     const int32_t* __restrict__ rows_used, int P, int T, int k,
+                                                     int64_t row_chunks, uint4* __restrict__ xp) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= P) return;
+  if (r >= P || r >= *rows_used) return;           // rows past offsets[E] do not exist
   const int lane = threadIdx.x & 63;
   int64_t t = perm[r] / k;
   t = t < 0 ? 0 : (t >= T ? T - 1 : t);   // rows left unwritten by invalid ids stay in bounds
@@ -211,6 +213,8 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t* __res
       if (lane == 63 - __clzll(m)) base[e] += __popcll(m);
       perm[pos] = p;
       inv_perm[p] = pos;
+    } else if (p < P) {
+      inv_perm[p] = -1;                            // routed to an expert not in this call
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -235,7 +239,9 @@ extern "C" moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_
                                   int32_t E, int32_t k, moe_dtype dtype, int32_t* counts,
                                   int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_perm,
                                   void* ws, size_t ws_bytes, void* stream) {
-  if (T < 0 || d < 0 || E < 1 || k < 1 || k > E || k > kMaxK) return MOE_ERR_INVALID_ARG;
+  // k may exceed E: with an expert-parallel share, the pairs of experts held
+  // elsewhere carry ids outside [0, E)
+  if (T < 0 || d < 0 || E < 1 || k < 1 || k > kMaxK) return MOE_ERR_INVALID_ARG;
   if (E > kMaxE) return MOE_ERR_UNSUPPORTED;
   if (!valid_dtype(dtype)) return MOE_ERR_INVALID_ARG;
   const int64_t P = T * k;
@@ -271,9 +277,38 @@ extern "C" moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_
   if (x_perm) {
     const int64_t row_chunks = d * elem_bytes(dtype) / 16;
     hipLaunchKernelGGL(gather_kernel, dim3(static_cast<unsigned>(ceil_div(P, 4))), dim3(256), 0, st,
-                       static_cast<const uint4*>(x), perm, static_cast<int>(P), static_cast<int>(T), k,
-                       row_chunks,
-                       static_cast<uint4*>(x_perm));
+                       static_cast<const uint4*>(x), perm, offsets + E, static_cast<int>(P), static_cast<int>(T),
+                       k, row_chunks, static_cast<uint4*>(x_perm));
   }
   return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Expert-parallel share (article "Mixture of Experts (MoEs) in Transformers",
+// section "Expert Parallelism"): a device holds the experts
+// [e_begin, e_begin + e_count); the router's global ids become local ids,
+// and pairs whose expert lives elsewhere are masked (-1), so moe_permute
+// gives them no row and moe_unpermute_combine adds nothing for them.
+namespace moe {
+namespace {
+__global__ __launch_bounds__(256) void localize_kernel(const int32_t* __restrict__ ids, int64_t n, int e_begin,
+                                                       int e_count, int32_t* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int e = ids[i] - e_begin;
+  out[i] = (e >= 0 && e < e_count) ? e : -1;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_localize_ids(const int32_t* topk_ids, int64_t n, int32_t e_begin, int32_t e_count,
+                                       int32_t* local_ids, void* stream) {
+  if (n < 0 || e_begin < 0 || e_count < 1) return MOE_ERR_INVALID_ARG;
+  if (e_count > moe::kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (n >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (n == 0) return MOE_OK;
+  if (!topk_ids || !local_ids) return MOE_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(moe::localize_kernel, dim3(static_cast<unsigned>(moe::ceil_div(n, 256))), dim3(256), 0,
+                     moe::as_stream(stream), topk_ids, n, e_begin, e_count, local_ids);
+  return moe::launch_status();
 }

@@ -29,7 +29,7 @@ def test_header_declares_the_path():
     for n in ["moe_route", "moe_topk", "moe_permute", "moe_permute_workspace_size",
               "moe_grouped_gemm_gateup_swiglu", "moe_grouped_gemm_down", "moe_unpermute_combine",
               "moe_decode_gateup_swiglu", "moe_decode_down", "moe_decode_gateup_swiglu_gather",
-              "moe_grouped_gemm_gateup_swiglu_gather",
+              "moe_grouped_gemm_gateup_swiglu_gather", "moe_localize_ids",
               "moe_abi_version", "moe_status_string"]:
         assert n in names
 
@@ -85,6 +85,11 @@ def test_validation_without_gpu(lib):
         assert g(P, None, 2, P, P, 100, 128, 128, 8, 1, P, None) == B.MOE_ERR_INVALID_ARG  # no perm
         assert g(P, P, 2, P, P, 100, 128, 128, 8, 0, P, None) == B.MOE_ERR_UNSUPPORTED     # fp32
         assert g(None, None, 2, None, None, 0, 128, 128, 8, 1, None, None) == B.MOE_OK
+    assert lib.moe_localize_ids(P, 10, 0, 0, P, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_localize_ids(P, 10, -1, 4, P, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_localize_ids(P, 10, 0, 257, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_localize_ids(None, 0, 0, 4, None, None) == B.MOE_OK
+    assert lib.moe_localize_ids(None, 10, 0, 4, P, None) == B.MOE_ERR_INVALID_ARG
     g = lib.moe_decode_gateup_swiglu_gather
     assert g(P, P, 3, P, P, 100, 128, 128, 8, 1, P, None) == B.MOE_ERR_INVALID_ARG     # rows % k != 0
     assert g(P, P, 0, P, P, 100, 128, 128, 8, 1, P, None) == B.MOE_ERR_INVALID_ARG     # k < 1

@@ -247,6 +247,74 @@ def test_layer(gpu, name, mode):
     U.assert_close(U.host_values(y)[same], out["y"][same], wl.dtype, f"{name} layer")
 
 
+# ------------------------------------------------------- expert-parallel share
+
+def test_localize_ids(gpu):
+    rng = np.random.default_rng(11)
+    ids = rng.integers(0, 64, size=(257, 8)).astype(np.int32)
+    out = torch.empty(ids.shape, dtype=torch.int32, device=gpu)
+    B().localize_ids(_i32(ids), 16, 24, out)
+    torch.cuda.synchronize()
+    ref = np.where((ids >= 16) & (ids < 40), ids - 16, -1)
+    assert (out.cpu().numpy() == ref).all()
+
+
+@pytest.mark.parametrize("T,E,k,s", [(300, 8, 4, 1), (2000, 16, 8, 2), (5, 4, 6, 3)])
+def test_permute_masked_pairs(gpu, T, E, k, s):
+    """Pairs with ids outside [0, E) get no row and inv_perm -1; the held
+    pairs are sorted exactly as numpy's stable argsort orders them."""
+    rng = np.random.default_rng(s)
+    ids = rng.integers(-3, E + 3, size=(T, k)).astype(np.int32)
+    b = B()
+    counts = torch.empty(E, dtype=torch.int32, device=gpu)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=gpu)
+    perm = torch.full((T * k,), -7, dtype=torch.int32, device=gpu)
+    inv = torch.empty(T * k, dtype=torch.int32, device=gpu)
+    ws = torch.empty(max(1, b.permute_workspace_size(T, k, E)), dtype=torch.uint8, device=gpu)
+    b.permute(_i32(ids), None, E, counts, offsets, perm, inv, None, ws)
+    torch.cuda.synchronize()
+    flat = ids.reshape(-1)
+    held = (flat >= 0) & (flat < E)
+    order = np.nonzero(held)[0][np.argsort(flat[held], kind="stable")]
+    n = int(held.sum())
+    assert (counts.cpu().numpy() == np.bincount(flat[held], minlength=E)).all()
+    assert offsets.cpu().numpy()[E] == n
+    assert (perm.cpu().numpy()[:n] == order).all()
+    ref_inv = np.full(T * k, -1)
+    ref_inv[order] = np.arange(n)
+    assert (inv.cpu().numpy() == ref_inv).all()
+
+
+@pytest.mark.parametrize("mode", ["grouped", "decode"])
+@pytest.mark.parametrize("name", ["c2s", "c3s_t37", "c4s", "c5s"])
+def test_expert_parallel_partition_sum(gpu, name, mode):
+    """Four expert-parallel shares (router over all experts, each share
+    holding a quarter of the expert weights, the shared expert on share 0):
+    their partial outputs sum to the oracle's layer output."""
+    wl, inp = U.small_inputs(name)
+    if mode == "decode" and wl.P > 1024:
+        pytest.skip("decode calls take at most 1024 rows")
+    full = U.device_weights(wl, inp)
+    x = U.dev_tensor(inp["x"], wl.dtype)
+    n = 4
+    ec = wl.E // n
+    total = np.zeros((wl.T, wl.d))
+    ids = None
+    for g in range(n):
+        w = B().MoeWeights(full.w_router, full.bias, full.w_gate_up[g * ec:(g + 1) * ec],
+                           full.w_down[g * ec:(g + 1) * ec],
+                           full.shared_gate_up if g == 0 else None, full.shared_down if g == 0 else None)
+        layer = B().MoeLayer(w, wl.k, wl.score, mode=mode, experts=(g * ec, ec))
+        y = layer.forward(x)
+        torch.cuda.synchronize()
+        total += U.host_values(y)
+        if ids is None:
+            ids = layer.ids.cpu().numpy()
+    x64, wr, out = _layer_ref(wl, inp)
+    same = U.routing_agreement(ids, out["logits"], x64, wr, inp["bias"], wl.k)
+    U.assert_close(total[same], out["y"][same], wl.dtype, f"{name} sum of {n} expert-parallel shares")
+
+
 def test_layer_deterministic_and_token_equivariant(gpu):
     wl, inp = U.small_inputs("c4s")
     layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score)
