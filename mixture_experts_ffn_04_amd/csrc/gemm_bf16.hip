@@ -18,6 +18,8 @@
 // fragment read takes one chunk from each of 32 consecutive rows, and swz
 // spreads every group of 16 such rows over all 64 banks (and keeps the
 // row-wise writes conflict free).
+#include <atomic>
+
 #include "grouped_gemm.h"
 
 namespace moe {
@@ -196,6 +198,14 @@ __device__ __forceinline__ void wait_stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier after this wave's LDS accesses (lgkmcnt(0)); global
+// stores still in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void drain_vm() {
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14));   // vmcnt(0)
   asm volatile("" ::: "memory");
@@ -218,9 +228,72 @@ __device__ __forceinline__ unsigned lds_addr_of(const void* p) {
 
 // SP: the DMA instructions of a stage are spread over the fragment reads of
 // its first SP K slices rather than issued in one burst.
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)   // the body uses device-only types; the host pass needs only the stub
+// Epilogue through LDS (bf16 outputs): every lane writes its 4-column
+// pieces into a row-major copy of the output tile in LDS (chunk c of row r
+// at c ^ (r % NCH), which spreads a fragment's 32 rows over the banks),
+// then every thread stores whole 16-byte chunks of whole rows, so each
+// store instruction covers full rows of C instead of 16-byte pieces of 32
+// rows.  smem holds BM * BNO * 2 bytes; the caller has made sure no wave
+// still reads or loads into it.
+template <int EPI, int FM, int FN, int TM, int TN, int BM, int BNO, int NT>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const TileLoc& tl, const f32x16 (&acc)[FM][FN],
+                                               int wm, int wn, int l32, int khalf, char* smem) {
+  constexpr int RB = BNO * 2;          // bytes per tile row
+  constexpr int NCH = RB / 16;         // 16-byte chunks per tile row
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int r = wm * TM + fm * 32 + l32;
+    char* row = smem + r * RB;
+    const int sz = r % NCH;
+    if (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int fg = 0; fg < FN / 2; ++fg) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = (wn * (TN / 2) + fg * 32 + q * 8) / 8;
+          const f32x16& g = acc[fm][fg];
+          const f32x16& u = acc[fm][fg + FN / 2];
+          uint2 o;
+          o.x = pack_bf16x2(silu(g[4 * q + 0]) * u[4 * q + 0], silu(g[4 * q + 1]) * u[4 * q + 1]);
+          o.y = pack_bf16x2(silu(g[4 * q + 2]) * u[4 * q + 2], silu(g[4 * q + 3]) * u[4 * q + 3]);
+          *reinterpret_cast<uint2*>(row + ((ch ^ sz) * 16) + khalf * 8) = o;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = (wn * TN + fn * 32 + q * 8) / 8;
+          const f32x16& c = acc[fm][fn];
+          uint2 o;
+          o.x = pack_bf16x2(c[4 * q + 0], c[4 * q + 1]);
+          o.y = pack_bf16x2(c[4 * q + 2], c[4 * q + 3]);
+          *reinterpret_cast<uint2*>(row + ((ch ^ sz) * 16) + khalf * 8) = o;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int nrows = min(tl.row_end - tl.row0, BM);
+  const int64_t N = a.N;
+  uint16_t* C = static_cast<uint16_t*>(a.C) + static_cast<int64_t>(tl.row0) * N + tl.n0;
+#pragma unroll 4
+  for (int c = threadIdx.x; c < BM * NCH; c += NT) {
+    const int r = c / NCH;
+    const int ch = c - r * NCH;
+    if (r >= nrows) break;                     // rows past the group: never stored (c only grows)
+    if (tl.n0 + ch * 8 >= N) continue;          // columns past N (N is a multiple of 64)
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * RB + ((ch ^ (r % NCH)) * 16));
+    *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(r) * N + ch * 8) = v;
+  }
+}
+
+// One tile, all threads of the workgroup.  Returns with every LDS load of
+// the tile complete; a following tile may reuse LDS after a workgroup
+// barrier.
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int NS, int SP, int LDS_EPI>
+__device__ __forceinline__ void dtl_tile(const GemmArgs& a, const TileLoc& tl) {
   constexpr int NW = WM * WN;
   constexpr int NT = 64 * NW;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -242,9 +315,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   static_assert(SP >= 1 && SP <= KS && LPS % SP == 0, "DMA spread");
 
   __shared__ u32x4 lds[NS * STAGE];
-
-  TileLoc tl;
-  if (!locate_tile<NT, BM, BNO, SN>(a, tl)) return;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -401,7 +471,39 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
 #undef MOE_DMA_PART
 #undef MOE_DMA
 
-  store_tile<EPI, FM, FN, TM, TN>(a, tl, acc, wm, wn, l32, khalf);
+  if (LDS_EPI && NS * STAGE * 16 >= BM * BNO * 2) {
+    __syncthreads();                             // every wave is past its last LDS read and DMA
+    store_tile_lds<EPI, FM, FN, TM, TN, BM, BNO, NT>(a, tl, acc, wm, wn, l32, khalf, reinterpret_cast<char*>(lds));
+  } else {
+    store_tile<EPI, FM, FN, TM, TN>(a, tl, acc, wm, wn, l32, khalf);
+  }
+}
+
+// One tile per workgroup, in the order of locate_tile.
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP, int LDS_EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the body uses device-only types; the host pass needs only the stub
+  constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  TileLoc tl;
+  if (!locate_tile<64 * WM * WN, BM, BNO, SN>(a, tl)) return;
+  dtl_tile<BM, BN, WM, WN, EPI, BK, NS, SP, LDS_EPI>(a, tl);
+#endif
+}
+
+// Persistent form: one workgroup per CU walks tiles bid, bid + grid, ... of
+// the same order, so a tile's last stores drain while the next tile is
+// located and its first stage loads.
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP, int LDS_EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_pers_kernel(GemmArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NT = 64 * WM * WN;
+  constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  __shared__ TilePlanLds plan;
+  const int total = tile_plan<NT, BM, BNO>(a, plan);
+  for (int j = static_cast<int>(blockIdx.x); j < total; j += static_cast<int>(gridDim.x)) {
+    if (j != static_cast<int>(blockIdx.x)) lds_barrier();   // every wave is done with the last tile's LDS
+    dtl_tile<BM, BN, WM, WN, EPI, BK, NS, SP, LDS_EPI>(a, tile_at<BM, BNO, SN>(a, plan, total, j));
+  }
 #endif
 }
 
@@ -524,7 +626,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 #undef MOE_MFMAS
 #undef MOE_FRAGS
 
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP = 1>
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP = 1, int LDS_EPI = 0>
 moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int64_t grid = grouped_tile_bound(a.rows, a.G, BM, a.N, BNO);
@@ -535,7 +637,38 @@ moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   if (wbytes >= (int64_t(1) << 31) || static_cast<int64_t>(BM) * a.K * 2 >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
   if (a.rowmap && (a.kdiv < 1 || a.a_rows * a.K * 2 >= (int64_t(1) << 31))) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, NS, SP>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, NS, SP, LDS_EPI>), dim3(static_cast<unsigned>(grid)),
+                     dim3(64 * WM * WN), 0, st, a);
+  return launch_status();
+}
+
+// Compute units of the current device (the persistent grid), cached per device.
+int persistent_grid() {
+  static std::atomic<int> cache[64];                  // per device; 0 = not yet queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP = 1, int LDS_EPI = 0>
+moe_status launch_pers(const GemmArgs& a, hipStream_t st) {
+  constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  const int64_t bound = grouped_tile_bound(a.rows, a.G, BM, a.N, BNO);
+  if (bound <= 0) return MOE_OK;
+  if (bound > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  const int64_t wbytes = ((EPI == EPI_SWIGLU) ? 2 : 1) * a.N * a.K * 2;
+  if (wbytes >= (int64_t(1) << 31) || static_cast<int64_t>(BM) * a.K * 2 >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  if (a.rowmap && (a.kdiv < 1 || a.a_rows * a.K * 2 >= (int64_t(1) << 31))) return MOE_ERR_UNSUPPORTED;
+  const int cus = persistent_grid();
+  if (cus <= 0) return MOE_ERR_HIP;
+  const int grid = static_cast<int>(bound < cus ? bound : cus);
+  hipLaunchKernelGGL((gemm_bf16_pers_kernel<BM, BN, WM, WN, EPI, SN, BK, NS, SP, LDS_EPI>), dim3(grid),
                      dim3(64 * WM * WN), 0, st, a);
   return launch_status();
 }
@@ -553,6 +686,7 @@ moe_status launch(const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
+
 // Expert projections: 256 token rows x 256 weight rows per tile, 8 waves
 // (2 along tokens x 4 along weights, 128 x 64 each), two 64-wide
 // direct-to-LDS stages.
@@ -560,8 +694,14 @@ moe_status gemm_bf16_gateup_swiglu(const GemmArgs& a, hipStream_t st) {
   return launch_dtl<256, 256, 2, 4, EPI_SWIGLU, 16, 64, 2, 2>(a, st);
 }
 
+// The down projection's output tile is 256 columns wide, so its epilogue
+// goes through LDS (whole-row stores; measured faster on every MoE shape,
+// while the 128-column SwiGLU tile of gate/up measured slower that way).
+// With a short K loop (K <= 1024: a tile's prologue and epilogue weigh more
+// than the dispatcher's dynamic balance) the persistent launch is faster.
 moe_status gemm_bf16_down(const GemmArgs& a, hipStream_t st) {
-  return launch_dtl<256, 256, 2, 4, EPI_STORE, 16, 64, 2, 2>(a, st);
+  if (a.K <= 1024) return launch_pers<256, 256, 2, 4, EPI_STORE, 16, 64, 2, 2, 1>(a, st);
+  return launch_dtl<256, 256, 2, 4, EPI_STORE, 16, 64, 2, 2, 1>(a, st);
 }
 
 // Router logits: few output columns, so small token tiles keep every CU

@@ -60,26 +60,26 @@ struct TileLoc {
   int n0;        // first output column
 };
 
-// Locate this workgroup's tile.  Must be called by all NT threads; returns
-// false (for the whole workgroup) when the block id is past the last tile.
-//   BM     rows per tile, BNO output columns per tile, SN column-block width
-template <int NT, int BM, int BNO, int SN>
-__device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl) {
+// Tile counts of the groups and their exclusive scan, for all NT threads:
+// thread t < G gets its group's row range [lo, hi), tile count cnt and the
+// index excl of its first tile; every thread gets the total.  Contains one
+// workgroup barrier.
+template <int NT, int BM, int BNO>
+__device__ __forceinline__ int scan_tiles(const GemmArgs& a, int& lo, int& hi, int& cnt, int& excl) {
   static_assert(NT >= kMaxE, "one group per thread");
-  __shared__ int s_pref[kMaxE];
   __shared__ int s_wsum[NT / 64];
-  __shared__ int s_hit[4];
   const int t = threadIdx.x;
   const int rows = static_cast<int>(a.rows);
   const int ntiles = static_cast<int>((a.N + BNO - 1) / BNO);
-  int lo = 0, hi = 0, cnt = 0;
+  lo = 0;
+  hi = 0;
+  cnt = 0;
   if (t < a.G) {
     lo = a.off ? clamp_off(a.off[t], rows) : 0;
     hi = a.off ? clamp_off(a.off[t + 1], rows) : rows;
     if (hi < lo) hi = lo;
     cnt = ((hi - lo + BM - 1) / BM) * ntiles;
   }
-  // block exclusive scan of cnt
   const int lane = t & 63, w = t >> 6;
   int v = cnt;
 #pragma unroll
@@ -96,26 +96,26 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl) {
     base += (i < w) ? s : 0;
     total += s;
   }
-  const int excl = base + v - cnt;
-  if (t < a.G) s_pref[t] = excl;
+  excl = base + v - cnt;
+  return total;
+}
 
-  const int bid = static_cast<int>(blockIdx.x);
-  if (bid >= total) return false;     // uniform: total is the same in every thread
-  // Remap of the block id to the logical tile index: even ids walk the
-  // first half of the order, odd ids the second, so the tiles running
-  // together on one XCD (ids are dealt to the 8 XCDs round-robin) come from
-  // a stretch of the order shared with three other XCDs
+// Logical tile index of launch slot bid.  Even slots walk the first half of
+// the order, odd slots the second, so the tiles running together on one XCD
+// (slots are dealt to the 8 XCDs round-robin) come from a stretch of the
+// order shared with three other XCDs: fewer experts' weights are in flight
+// at once than with one contiguous stretch per XCD.
+__device__ __forceinline__ int tile_order(int bid, int total) {
   const int q = total >> 1;
-  const int L = (bid < (q << 1)) ? ((bid & 1) * q + (bid >> 1)) : bid;
-  if (t < a.G && cnt > 0 && L >= excl && L < excl + cnt) {
-    s_hit[0] = t;
-    s_hit[1] = lo;
-    s_hit[2] = hi;
-  }
-  __syncthreads();
-  const int g = s_hit[0];
-  const int glo = s_hit[1], ghi = s_hit[2];
-  const int local = L - s_pref[g];
+  return (bid < (q << 1)) ? ((bid & 1) * q + (bid >> 1)) : bid;
+}
+
+// Tile coordinates of logical tile `local` of group g (rows [glo, ghi)):
+// column blocks of SN tiles, row tiles within a block, a narrower last block
+// when SN does not divide the column tiles.
+template <int BM, int BNO, int SN>
+__device__ __forceinline__ TileLoc tile_coords(const GemmArgs& a, int g, int glo, int ghi, int local) {
+  const int ntiles = static_cast<int>((a.N + BNO - 1) / BNO);
   const int mt_g = (ghi - glo + BM - 1) / BM;
   const int nbf = ntiles / SN;
   int mt, nt;
@@ -131,11 +131,67 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl) {
     nt = nbf * SN + (r - mt * snr);
   }
   // workgroup-uniform: keep them in scalar registers
+  TileLoc tl;
   tl.g = __builtin_amdgcn_readfirstlane(g);
   tl.row0 = __builtin_amdgcn_readfirstlane(glo + mt * BM);
   tl.row_end = __builtin_amdgcn_readfirstlane(ghi);
   tl.n0 = __builtin_amdgcn_readfirstlane(nt * BNO);
+  return tl;
+}
+
+// Locate this workgroup's tile.  Must be called by all NT threads; returns
+// false (for the whole workgroup) when the block id is past the last tile.
+//   BM     rows per tile, BNO output columns per tile, SN column-block width
+template <int NT, int BM, int BNO, int SN>
+__device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl) {
+  __shared__ int s_hit[4];
+  int lo, hi, cnt, excl;
+  const int total = scan_tiles<NT, BM, BNO>(a, lo, hi, cnt, excl);
+  const int bid = static_cast<int>(blockIdx.x);
+  if (bid >= total) return false;     // uniform: total is the same in every thread
+  const int L = tile_order(bid, total);
+  if (static_cast<int>(threadIdx.x) < a.G && cnt > 0 && L >= excl && L < excl + cnt) {
+    s_hit[0] = threadIdx.x;
+    s_hit[1] = lo;
+    s_hit[2] = hi;
+    s_hit[3] = excl;
+  }
+  __syncthreads();
+  tl = tile_coords<BM, BNO, SN>(a, s_hit[0], s_hit[1], s_hit[2], L - s_hit[3]);
   return true;
+}
+
+// Persistent form of the same order: the group table is built once per
+// workgroup (tile_plan), then tile_at maps any logical slot to its tile by
+// a binary search over the group prefixes.
+struct TilePlanLds {
+  int pref[kMaxE];   // first tile of each group
+  int lo[kMaxE];
+  int hi[kMaxE];
+};
+
+template <int NT, int BM, int BNO>
+__device__ __forceinline__ int tile_plan(const GemmArgs& a, TilePlanLds& p) {
+  int lo, hi, cnt, excl;
+  const int total = scan_tiles<NT, BM, BNO>(a, lo, hi, cnt, excl);
+  if (static_cast<int>(threadIdx.x) < a.G) {
+    p.pref[threadIdx.x] = excl;
+    p.lo[threadIdx.x] = lo;
+    p.hi[threadIdx.x] = hi;
+  }
+  __syncthreads();
+  return total;
+}
+
+template <int BM, int BNO, int SN>
+__device__ __forceinline__ TileLoc tile_at(const GemmArgs& a, const TilePlanLds& p, int total, int bid) {
+  const int L = tile_order(bid, total);
+  // last group whose first tile is <= L: it has tiles (a later group with
+  // the same prefix would be the one found), and L is below its end
+  int g = 0;
+  for (int step = kMaxE / 2; step > 0; step >>= 1)
+    if (g + step < a.G && p.pref[g + step] <= L) g += step;
+  return tile_coords<BM, BNO, SN>(a, g, p.lo[g], p.hi[g], L - p.pref[g]);
 }
 
 // Upper bound on the tiles of a grouped launch (used as the grid size):

@@ -205,6 +205,25 @@ def test_down(gpu, name, decode):
     U.assert_close(U.host_values(y), ref, wl.dtype, f"{name} Y_perm")
 
 
+@pytest.mark.parametrize("T,E,k,K,N", [(20000, 160, 4, 256, 512), (8000, 48, 4, 1024, 768), (3000, 24, 2, 1088, 512)])
+def test_down_many_tiles(gpu, T, E, k, K, N):
+    """Down projection with more output tiles than compute units, skewed
+    expert sizes, experts 1, 3, ..., 15 empty, short (K <= 1024: one
+    workgroup per compute unit walks several tiles) and longer K loops."""
+    ids = W.gen_ids(T, E - 8, k, seed=T + K, zipf_s=1.6)
+    ids = np.where(ids < 8, ids * 2, ids + 8).astype(np.int32)
+    counts, offsets, _, _ = O.permute(ids, E)
+    assert (counts[1:16:2] == 0).all()
+    P = T * k
+    h = W.gen_matrix((P, K), seed=K + 1, std=0.5)
+    dn = W.gen_matrix((E, N, K), seed=K + 2, std=0.05)
+    y = torch.empty(P, N, dtype=torch.bfloat16, device=gpu)
+    B().down(U.dev_tensor(h, "bf16"), U.dev_tensor(dn, "bf16"), _i32(offsets), y)
+    torch.cuda.synchronize()
+    ref = O.grouped_down(W.values(h, "bf16"), W.values(dn, "bf16"), offsets)
+    U.assert_close(U.host_values(y), ref, "bf16", f"T={T} E={E} K={K} N={N} Y_perm")
+
+
 @pytest.mark.parametrize("shared", [False, True])
 @pytest.mark.parametrize("name", SMALL)
 def test_combine(gpu, name, shared):
