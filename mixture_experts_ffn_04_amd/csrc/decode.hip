@@ -87,7 +87,7 @@ template <int EPI>
 __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                      const int32_t* __restrict__ off, const float* __restrict__ bias,
                                                      const int32_t* __restrict__ rowmap, int kdiv,
-                                                     int rows, int K, int N, int G, void* __restrict__ Cv) {
+                                                     int rows, int K, int N, int G, int rb, void* __restrict__ Cv) {
   constexpr bool SWIGLU = EPI == 1;
   constexpr int NH = SWIGLU ? 2 : 1;
   __shared__ float red[4][kMC][NH][4][64];
@@ -95,8 +95,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
   const int g = blockIdx.x / ntiles;
   if (g >= G) return;
   const int n0 = (blockIdx.x - g * ntiles) * 16;
-  const int lo = off ? clamp_off(off[g], rows) : 0;
-  const int hi = off ? clamp_off(off[g + 1], rows) : rows;
+  int lo = off ? clamp_off(off[g], rows) : 0;
+  int hi = off ? clamp_off(off[g + 1], rows) : rows;
+  if (rb > 0) {                              // row split: this workgroup takes rows [lo + y*rb, +rb) of the group
+    lo += static_cast<int>(blockIdx.y) * rb;
+    hi = min(hi, lo + rb);
+  }
   if (hi <= lo) return;                      // expert without tokens: its weights are never read
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -176,14 +180,18 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
   }
 }
 
+// rb > 0: the rows of each group are split into blocks of rb rows, one
+// workgroup per (column tile, row block); gridDim.y covers the largest group.
 template <int EPI>
 moe_status launch_decode(const void* A, const void* B, const int32_t* off, const float* bias, const int32_t* rowmap,
-                         int kdiv, int64_t rows, int64_t K, int64_t N, int G, void* C, hipStream_t st) {
+                         int kdiv, int64_t rows, int64_t K, int64_t N, int G, void* C, hipStream_t st, int rb = 0) {
   const int64_t grid = static_cast<int64_t>(G) * ceil_div(N, 16);
-  if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(decode_kernel<EPI>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+  const int64_t gy = rb > 0 ? ceil_div(rows, rb) : 1;
+  if (grid > 0x7fffffff || gy > 65535) return MOE_ERR_UNSUPPORTED;
+  if (gy == 0) return MOE_OK;
+  hipLaunchKernelGGL(decode_kernel<EPI>, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(gy)), dim3(256), 0, st,
                      static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), off, bias, rowmap, kdiv,
-                     static_cast<int>(rows), static_cast<int>(K), static_cast<int>(N), G, C);
+                     static_cast<int>(rows), static_cast<int>(K), static_cast<int>(N), G, rb, C);
   return launch_status();
 }
 
@@ -196,9 +204,10 @@ moe_status decode_bf16(bool swiglu, const void* A, const void* B, const int32_t*
 }
 
 // Router logits for small batches: one group of T rows, N = E experts.
+// rb > 0 splits the T rows over workgroups in blocks of rb.
 moe_status decode_bf16_logits(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d,
-                              int32_t E, float* logits, hipStream_t st) {
-  return launch_decode<2>(x, w_router, nullptr, bias, nullptr, 1, T, d, E, 1, logits, st);
+                              int32_t E, float* logits, hipStream_t st, int rb) {
+  return launch_decode<2>(x, w_router, nullptr, bias, nullptr, 1, T, d, E, 1, logits, st, rb);
 }
 
 }  // namespace moe

@@ -21,15 +21,20 @@ namespace moe {
 moe_status gemm_bf16_logits(const GemmArgs& a, hipStream_t st);
 moe_status gemm_f32_logits(const GemmArgs& a, hipStream_t st);
 moe_status decode_bf16_logits(const void* x, const void* w_router, const float* bias, int64_t T, int64_t d,
-                              int32_t E, float* logits, hipStream_t st);
+                              int32_t E, float* logits, hipStream_t st, int rb);
 
-// bf16 router logits: one wave per (expert row, few tokens) up to
-// kTinyRouteTokens tokens or kTinyRouteExperts experts (d <= 8192); else up
-// to kSmallRouteTokens tokens the split-K streaming kernel; above, the tiled
-// MFMA GEMM.
-constexpr int64_t kTinyRouteTokens = 64;
-constexpr int kTinyRouteExperts = 16;
-constexpr int64_t kSmallRouteTokens = 256;
+// bf16 router logits, by size (measured on MI355X):
+//  - T*E <= kTinyRouteItems (d <= 8192): one wave per (expert row, few
+//    tokens), every load issued up front;
+//  - E <= kStreamRouteExperts or T <= kStreamRouteTokens: the streaming
+//    split-K kernel with the tokens split into blocks of 16 (32 once that
+//    makes at least kStreamRouteBlocks workgroups), one workgroup per
+//    (16 experts, token block);
+//  - above: the tiled MFMA GEMM, which reuses tokens across 128 experts.
+constexpr int64_t kTinyRouteItems = 8192;
+constexpr int kStreamRouteExperts = 64;
+constexpr int64_t kStreamRouteTokens = 1024;
+constexpr int64_t kStreamRouteBlocks = 1024;
 
 namespace {
 
@@ -238,16 +243,18 @@ extern "C" moe_status moe_route(const void* x, const void* w_router, const float
   a.N = E;
   a.G = 1;
   hipStream_t st = as_stream(stream);
-  const bool tiny = (T <= kTinyRouteTokens || E <= kTinyRouteExperts) &&
-                    ceil_div(T, 2) * E < (int64_t(1) << 31);          // (token block, expert) items fit an int
-  if (dtype == MOE_BF16 && tiny && d <= 4096)
+  const bool tiny = T * E <= kTinyRouteItems;
+  const bool stream_ok = (E <= kStreamRouteExperts || T <= kStreamRouteTokens) && ceil_div(T, 16) <= 65535;
+  if (dtype == MOE_BF16 && tiny && d <= 4096) {
     s = launch_logits_small<8, 4>(x, w_router, bias, T, d, E, logits, st);
-  else if (dtype == MOE_BF16 && tiny && d <= 8192)
+  } else if (dtype == MOE_BF16 && tiny && d <= 8192) {
     s = launch_logits_small<16, 2>(x, w_router, bias, T, d, E, logits, st);
-  else if (dtype == MOE_BF16 && T <= kSmallRouteTokens)
-    s = decode_bf16_logits(x, w_router, bias, T, d, E, logits, st);
-  else
+  } else if (dtype == MOE_BF16 && stream_ok) {
+    const int rb = ceil_div(T, 16) * ceil_div(E, 16) < kStreamRouteBlocks ? 16 : 32;
+    s = decode_bf16_logits(x, w_router, bias, T, d, E, logits, st, rb);
+  } else {
     s = (dtype == MOE_BF16) ? gemm_bf16_logits(a, st) : gemm_f32_logits(a, st);
+  }
   if (s != MOE_OK) return s;
   return launch_topk(logits, T, E, k, score, topk_ids, topk_w, st);
 }

@@ -89,6 +89,32 @@ def test_route(gpu, name):
     assert np.abs(w.cpu().numpy()[same] - ref_w[same]).max() <= U.WEIGHT_ABS
 
 
+# router logits through each of its kernels, chosen by size: one wave per
+# (expert, few tokens) at d <= 4096 and d <= 8192, the streaming kernel with
+# 16- and 32-token blocks, the tiled GEMM
+ROUTER_PATHS = [(40, 8, 4096, 2), (50, 16, 6144, 4), (300, 40, 1024, 4), (8192, 64, 256, 8), (1100, 96, 512, 6),
+                (1030, 8, 320, 2)]
+
+
+@pytest.mark.parametrize("T,E,d,k", ROUTER_PATHS)
+def test_router_logit_paths(gpu, T, E, d, k):
+    xs = W.gen_matrix((T, d), seed=T + d, std=1.0)
+    ws = W.gen_matrix((E, d), seed=E + d, std=0.05)
+    bias = np.asarray(W.gen_matrix((E,), seed=E, std=0.1, dtype="f32"), np.float32)
+    x, wr = W.values(xs, "bf16"), W.values(ws, "bf16")
+    L = O.router_logits(x, wr, bias)
+    _, ref_w = O.route(L, k, "softmax")
+    logits = torch.empty(T, E, dtype=torch.float32, device=gpu)
+    ids = torch.empty(T, k, dtype=torch.int32, device=gpu)
+    w = torch.empty(T, k, dtype=torch.float32, device=gpu)
+    B().route(U.dev_tensor(xs, "bf16"), U.dev_tensor(ws, "bf16"), _f32(bias), k, "softmax", logits, ids, w)
+    torch.cuda.synchronize()
+    gl = logits.cpu().numpy().astype(np.float64)
+    assert (np.abs(gl - L) <= O.logit_error_bound(x, wr, bias)).all()
+    same = U.routing_agreement(ids.cpu().numpy(), L, x, wr, bias, k)
+    assert np.abs(w.cpu().numpy()[same] - ref_w[same]).max() <= U.WEIGHT_ABS
+
+
 # ---------------------------------------------------------------- permute
 
 PERMUTE_IDS = [(3000, 256, 8, 1.0), (2049, 8, 2, None), (1024, 128, 8, 1.1), (5, 4, 4, None),
