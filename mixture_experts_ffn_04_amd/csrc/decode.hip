@@ -79,6 +79,29 @@ __device__ __forceinline__ void decode_partial(const uint16_t* wg, const uint16_
   }
 }
 
+// Index of the j-th group with rows (in group order), or -1; all 256
+// threads of the workgroup call it (G <= 256).  A decode batch of P < G
+// rows touches at most P groups, so the grid then covers only P groups and
+// no workgroup is spent on an expert without tokens (with P >= G the grid
+// covers every group and empty ones exit at once, which measured faster
+// than the search).
+__device__ __forceinline__ int nth_active_group(const int32_t* __restrict__ off, int G, int rows, int j) {
+  __shared__ int s_cnt[4];
+  __shared__ int s_g;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  bool act = false;
+  if (t < G) act = clamp_off(off[t + 1], rows) > clamp_off(off[t], rows);
+  const uint64_t m = __ballot(act);
+  if (lane == 0) s_cnt[w] = __popcll(m);
+  if (t == 0) s_g = -1;
+  __syncthreads();
+  int rank = __popcll(m & ((uint64_t(1) << lane) - 1));
+  for (int i = 0; i < w; ++i) rank += s_cnt[i];
+  if (act && rank == j) s_g = t;
+  __syncthreads();
+  return s_g;
+}
+
 // EPI: 0 = bf16 store, 1 = SwiGLU pairs (bf16), 2 = fp32 + bias (router
 // logits for small batches; N need not be a multiple of 16 there).
 // rowmap (may be NULL): input row r is A[rowmap[r] / kdiv] (rowmap entries
@@ -92,9 +115,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
   constexpr int NH = SWIGLU ? 2 : 1;
   __shared__ float red[4][kMC][NH][4][64];
   const int ntiles = (N + 15) / 16;
-  const int g = blockIdx.x / ntiles;
-  if (g >= G) return;
-  const int n0 = (blockIdx.x - g * ntiles) * 16;
+  const int j = blockIdx.x / ntiles;
+  const int n0 = (blockIdx.x - j * ntiles) * 16;
+  // compact grid: block row j is the j-th group that has rows
+  const int g = (off && rows < G) ? nth_active_group(off, G, rows, j) : j;
+  if (g < 0 || g >= G) return;
   int lo = off ? clamp_off(off[g], rows) : 0;
   int hi = off ? clamp_off(off[g + 1], rows) : rows;
   if (rb > 0) {                              // row split: this workgroup takes rows [lo + y*rb, +rb) of the group
@@ -185,10 +210,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
 template <int EPI>
 moe_status launch_decode(const void* A, const void* B, const int32_t* off, const float* bias, const int32_t* rowmap,
                          int kdiv, int64_t rows, int64_t K, int64_t N, int G, void* C, hipStream_t st, int rb = 0) {
-  const int64_t grid = static_cast<int64_t>(G) * ceil_div(N, 16);
+  if (off && G > 256) return MOE_ERR_UNSUPPORTED;                      // one group per thread
+  const int64_t groups = off ? (G < rows ? G : rows) : G;             // at most `rows` groups have rows
+  const int64_t grid = groups * ceil_div(N, 16);
   const int64_t gy = rb > 0 ? ceil_div(rows, rb) : 1;
   if (grid > 0x7fffffff || gy > 65535) return MOE_ERR_UNSUPPORTED;
-  if (gy == 0) return MOE_OK;
+  if (grid == 0 || gy == 0) return MOE_OK;
   hipLaunchKernelGGL(decode_kernel<EPI>, dim3(static_cast<unsigned>(grid), static_cast<unsigned>(gy)), dim3(256), 0, st,
                      static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), off, bias, rowmap, kdiv,
                      static_cast<int>(rows), static_cast<int>(K), static_cast<int>(N), G, rb, C);
