@@ -44,6 +44,26 @@ __device__ __forceinline__ void add_plain(float (&acc)[8], const uint4& v) {
   }
 }
 
+// Streaming forms: the rows are read and the output written exactly once,
+// so when they are far larger than the caches the non-temporal hint keeps
+// them from evicting what is reused.
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+  if (!NT) return *p;
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(uint4* p, const uint4& v) {
+  if (!NT) {
+    *p = v;
+    return;
+  }
+  const u32x4 u = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
+}
+
 template <bool BF16>
 __device__ __forceinline__ uint4 pack_out(const float (&acc)[8]) {
   uint4 o;
@@ -66,7 +86,8 @@ __device__ __forceinline__ uint4 pack_out(const float (&acc)[8]) {
 // arithmetic, so 2k + 2 independent 16-byte loads per lane are in flight.
 // KT == 0: any k, one chunk and one row at a time.  Both sum in the same
 // order (increasing j, then the shared row), so they give identical bits.
-template <bool BF16, int KT>
+// NT: non-temporal loads of the expert rows and stores of the output.
+template <bool BF16, int KT, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ yp, const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, const uint4* __restrict__ ys,
                                                       int T, int k, int64_t row_chunks,
@@ -96,8 +117,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
       uint4 v0[KR], v1[KR], s0{}, s1{};
 #pragma unroll
       for (int j = 0; j < KR; ++j) {
-        v0[j] = yp[static_cast<int64_t>(rows[j]) * row_chunks + c0];
-        v1[j] = yp[static_cast<int64_t>(rows[j]) * row_chunks + c1];
+        v0[j] = load16<NT>(yp + static_cast<int64_t>(rows[j]) * row_chunks + c0);
+        v1[j] = load16<NT>(yp + static_cast<int64_t>(rows[j]) * row_chunks + c1);
       }
       if (ysr) {
         s0 = ysr[c0];
@@ -113,8 +134,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
         add_plain<BF16>(a0, s0);
         add_plain<BF16>(a1, s1);
       }
-      yr[c0] = pack_out<BF16>(a0);
-      if (two) yr[c1] = pack_out<BF16>(a1);
+      store16<NT>(yr + c0, pack_out<BF16>(a0));
+      if (two) store16<NT>(yr + c1, pack_out<BF16>(a1));
     }
   } else {
     for (int64_t c = lane; c < row_chunks; c += 64) {
@@ -122,23 +143,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int j = 0; j < KR; ++j) {
         if (j >= kk) break;
-        add_scaled<BF16>(acc, yp[static_cast<int64_t>(rows[j]) * row_chunks + c], wt[j]);
+        add_scaled<BF16>(acc, load16<NT>(yp + static_cast<int64_t>(rows[j]) * row_chunks + c), wt[j]);
       }
       if (ysr) add_plain<BF16>(acc, ysr[c]);
-      yr[c] = pack_out<BF16>(acc);
+      store16<NT>(yr + c, pack_out<BF16>(acc));
     }
   }
 }
 
-template <bool BF16>
-void launch_combine(const void* y_perm, const int32_t* inv_perm, const float* topk_w, const void* y_shared,
-                    int T, int k, int64_t row_chunks, void* y, hipStream_t st) {
+// Expert rows beyond this many bytes are streamed with the non-temporal
+// hint (measured: 1.9 GB of rows 475 -> 401 us; at 268 MB and below, where
+// the rows the down projection just wrote are still partly in the 256 MB
+// Infinity Cache, the hint measured slower).
+constexpr int64_t kStreamCombineBytes = int64_t(512) << 20;
+
+template <bool BF16, bool NT>
+void launch_combine_nt(const void* y_perm, const int32_t* inv_perm, const float* topk_w, const void* y_shared,
+                       int T, int k, int64_t row_chunks, void* y, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(ceil_div(T, kRowsPerBlock)));
   const uint4* yp = static_cast<const uint4*>(y_perm);
   const uint4* ys = static_cast<const uint4*>(y_shared);
   uint4* yo = static_cast<uint4*>(y);
 #define MOE_COMBINE_K(KT_) \
-  hipLaunchKernelGGL((combine_kernel<BF16, KT_>), grid, dim3(256), 0, st, yp, inv_perm, topk_w, ys, T, k, row_chunks, yo)
+  hipLaunchKernelGGL((combine_kernel<BF16, KT_, NT>), grid, dim3(256), 0, st, yp, inv_perm, topk_w, ys, T, k, row_chunks, yo)
   switch (k) {
     case 1: MOE_COMBINE_K(1); break;
     case 2: MOE_COMBINE_K(2); break;
@@ -148,6 +175,15 @@ void launch_combine(const void* y_perm, const int32_t* inv_perm, const float* to
     default: MOE_COMBINE_K(0); break;
   }
 #undef MOE_COMBINE_K
+}
+
+template <bool BF16>
+void launch_combine(const void* y_perm, const int32_t* inv_perm, const float* topk_w, const void* y_shared,
+                    int T, int k, int64_t row_chunks, void* y, hipStream_t st) {
+  if (static_cast<int64_t>(T) * k * row_chunks * 16 > kStreamCombineBytes)
+    launch_combine_nt<BF16, true>(y_perm, inv_perm, topk_w, y_shared, T, k, row_chunks, y, st);
+  else
+    launch_combine_nt<BF16, false>(y_perm, inv_perm, topk_w, y_shared, T, k, row_chunks, y, st);
 }
 
 }  // namespace

@@ -266,6 +266,23 @@ def test_combine(gpu, name, shared):
     U.assert_close(U.host_values(y), ref, wl.dtype, f"{name} y")
 
 
+@pytest.mark.parametrize("T,d,k,shared", [(11000, 4096, 8, False), (22000, 4096, 3, True)])
+def test_combine_streaming(gpu, T, d, k, shared):
+    """Expert rows larger than 512 MB take the non-temporal streaming form
+    (compile-time k = 8, and the any-k loop with k = 3)."""
+    ids = W.gen_ids(T, 16, k, seed=T + k)
+    _, _, _, inv = O.permute(ids, 16)
+    P = T * k
+    yp = W.gen_matrix((P, d), seed=T + 1)
+    ys = W.gen_matrix((T, d), seed=T + 2) if shared else None
+    w = np.asarray(W.gen_matrix((T, k), seed=T + 3, dtype="f32"), np.float32)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device=gpu)
+    B().unpermute_combine(U.dev_tensor(yp, "bf16"), _i32(inv), _f32(w), None if ys is None else U.dev_tensor(ys, "bf16"), y)
+    torch.cuda.synchronize()
+    ref = O.unpermute_combine(W.values(yp, "bf16"), inv, w, None if ys is None else W.values(ys, "bf16"))
+    U.assert_close(U.host_values(y), ref, "bf16", f"T={T} k={k} y")
+
+
 # ------------------------------------------------------------ whole layer
 
 def _layer_ref(wl, inp, x=None):
