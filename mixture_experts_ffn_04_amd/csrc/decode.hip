@@ -32,11 +32,21 @@ __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *(const gu4*)p);
 }
 
-// weight rows: cached loads.  Each load instruction covers 64 of the 128
-// bytes of a line per row; the neighbouring step reads the other half from
-// L2 (non-temporal loads measured slower for this pattern).
+// weight rows: cached loads.  Each load instruction touches whole 128-byte
+// lines of its 16 rows (every other 16 bytes); the other step of the pair
+// reads the rest from L2.  Non-temporal loads measured about 10% slower.
 __device__ __forceinline__ bf16x8 ld8_stream(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *(const gu4*)p);
+}
+
+// K layout of a step: steps 2j and 2j+1 together cover elements
+// [64j, 64j + 64) of every row; lane (row i, quarter q) holds elements
+// 64j + 16q + [0, 8) in step 2j and 64j + 16q + [8, 16) in step 2j+1, so the
+// two load instructions of a step pair each span whole 128-byte lines of the
+// 16 rows (the row base pointers already include 16q).  Weights and tokens
+// use the same layout, which only permutes the reduction over K.
+__device__ __forceinline__ int64_t step_offset(int s) {
+  return static_cast<int64_t>(s >> 1) * 64 + (s & 1) * 8;
 }
 
 // Partial sums of one wave over K steps [s0, s1) (32 elements each) for MC
@@ -59,7 +69,7 @@ __device__ __forceinline__ void decode_partial(const uint16_t* wg, const uint16_
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int su = s + u < s1 ? s + u : s1 - 1;
-      const int64_t k0 = static_cast<int64_t>(su) * 32;
+      const int64_t k0 = step_offset(su);
       wgf[u] = ld8_stream(wg + k0);
       if (SWIGLU) wuf[u] = ld8_stream(wu + k0);
 #pragma unroll
@@ -133,11 +143,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
   const int64_t brows = SWIGLU ? 2 * static_cast<int64_t>(N) : N;
   const uint16_t* Bg = B + static_cast<int64_t>(g) * brows * K;
   const int wrow = n0 + i16 < N ? n0 + i16 : N - 1;     // past-N rows read a valid row; never stored
-  const uint16_t* wg = Bg + static_cast<int64_t>(wrow) * K + kq * 8;
-  const uint16_t* wu = Bg + static_cast<int64_t>(SWIGLU ? N + wrow : wrow) * K + kq * 8;
-  // contiguous K range per wave
+  const uint16_t* wg = Bg + static_cast<int64_t>(wrow) * K + kq * 16;
+  const uint16_t* wu = Bg + static_cast<int64_t>(SWIGLU ? N + wrow : wrow) * K + kq * 16;
+  // contiguous K range per wave, in whole step pairs (K % 64 == 0)
   const int steps = K / 32;
-  const int per = (steps + 3) / 4;
+  const int per = ((steps + 7) / 8) * 2;
   const int s0 = min(steps, wave * per);
   const int s1 = min(steps, s0 + per);
 
@@ -149,7 +159,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
       const int row = m0 + mc * 16 + i16;        // rows past the group read a valid row; never stored
       int src = row < hi ? row : lo;
       if (rowmap) src = clamp_off(rowmap[src], rows - 1) / kdiv;
-      xr[mc] = A + static_cast<int64_t>(src) * K + kq * 8;
+      xr[mc] = A + static_cast<int64_t>(src) * K + kq * 16;
     }
     f32x4 ag[kMC], au[kMC];
     if (mcn == 1) {
