@@ -7,8 +7,9 @@
 // rows, so a fragment (32 rows x 16 K) is one ds_read_b128 per lane.
 //
 //  * gemm_bf16_dtl_kernel (expert projections): buffer loads straight into
-//    LDS (no register staging) with NS LDS stages of BK K-elements, so loads
-//    run NS-1 stages ahead of the MFMAs.
+//    LDS (no register staging); three weight stages and two token stages of
+//    64 K-elements, so weight loads run two stages and token loads one stage
+//    ahead of the MFMAs.
 //  * gemm_bf16_kernel (router logits): loads staged through registers into
 //    two LDS buffers.
 //
@@ -18,8 +19,6 @@
 // fragment read takes one chunk from each of 32 consecutive rows, and swz
 // spreads every group of 16 such rows over all 64 banks (and keeps the
 // row-wise writes conflict free).
-#include <atomic>
-
 #include "grouped_gemm.h"
 
 namespace moe {
@@ -182,9 +181,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, const TileLoc& tl,
 // ---------------------------------------------------------------------------
 // Direct-to-LDS kernel (expert projections).
 //
-// Synchronisation per stage: s_waitcnt vmcnt((NS-2)*LPS) (this wave's loads
-// of the stage about to be consumed have landed; the NS-2 younger stages may
-// still be in flight) and lgkmcnt(0) (this wave's LDS reads of the buffer
+// Synchronisation per stage: s_waitcnt vmcnt(n) (this wave's loads of the
+// stage about to be consumed have landed; only the n youngest loads may
+// still be in flight) and lgkmcnt(0) (this wave's LDS reads of the buffers
 // about to be refilled are complete), then s_barrier.  This is not the
 // __syncthreads() fence, which would wait for every outstanding LDS DMA.
 // After the loop all DMA is drained before the epilogue, so nothing lands
@@ -194,14 +193,6 @@ template <int VM>
 __device__ __forceinline__ void wait_stage_barrier() {
   static_assert(VM < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Workgroup barrier after this wave's LDS accesses (lgkmcnt(0)); global
-// stores still in flight are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -289,32 +280,65 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const TileLoc&
   }
 }
 
-// One tile, all threads of the workgroup.  Returns with every LDS load of
-// the tile complete; a following tile may reuse LDS after a workgroup
-// barrier.
-template <int BM, int BN, int WM, int WN, int EPI, int BK, int NS, int SP, int LDS_EPI>
-__device__ __forceinline__ void dtl_tile(const GemmArgs& a, const TileLoc& tl) {
+// Fragment reads of K slice ks (16 wide) -- the FN weight fragments from
+// weight stage sw_ and the first NF_ token fragments from token stage sx_ --
+// and the NF_ x FN MFMAs on them.
+#define MOE_DTL_FRAGS(wf_, tf_, sw_, sx_, ks_, NF_)                                     \
+  do {                                                                                  \
+    const int c_ = ((ks_) * 2 + khalf) ^ sw;                                            \
+    _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                   \
+      wf_[fn] = __builtin_bit_cast(bf16x8, (sw_)[(wrow[fn] + l32) * CH + c_]);          \
+    _Pragma("unroll") for (int fm = 0; fm < (NF_); ++fm)                                \
+      tf_[fm] = __builtin_bit_cast(bf16x8, (sx_)[(wm * TM + fm * 32 + l32) * CH + c_]); \
+  } while (0)
+#define MOE_DTL_MFMAS(wf_, tf_, NF_)                                                    \
+  do {                                                                                  \
+    _Pragma("unroll") for (int fm = 0; fm < (NF_); ++fm)                                \
+      _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                 \
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf_[fn], tf_[fm], acc[fm][fn], 0, 0, 0); \
+  } while (0)
+
+// One tile per workgroup, in the order of locate_tile.
+//
+// Stages: weight rows come from the Infinity Cache or HBM (each weight tile
+// is shared by only the few row tiles of its expert), token rows mostly
+// from L2 (shared by every column tile of the expert).  So the 160 KB of
+// LDS hold three weight stages and two token stages of BK = 64: the loads
+// of stage k+2's weights and stage k+1's tokens are issued during stage k.
+// Per stage each wave issues its token loads before its weight loads, so
+// s_waitcnt vmcnt(LB) at the top of stage k (only stage k+1's weights may
+// still be in flight) means stage k's tokens and weights have landed; the
+// s_barrier after it publishes them and also tells every wave that the
+// buffers of stage k-1, refilled during stage k, are no longer read.
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int SP, int LDS_EPI>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the body uses device-only types; the host pass needs only the stub
   constexpr int NW = WM * WN;
   constexpr int NT = 64 * NW;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "fragment shape");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
-  static_assert(BK == 64 || BK == 32, "stage width");
-  static_assert(NS >= 2 && NS <= 4, "LDS stages");
+  static_assert(BK == 64, "stage width");
   static_assert(FM <= 4, "active-fragment specialisations cover up to 4 token fragments");
   constexpr int CH = BK / 8;                          // 16-byte chunks per tile row
   constexpr int KS = BK / 16;                         // 16-wide K slices per stage
   constexpr int RPI = 64 / CH;                        // tile rows per 1 KB load instruction
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  constexpr int ROWS = BN + BM;                       // tile rows per stage
   static_assert(BN % (RPI * NW) == 0 && BM % (RPI * NW) == 0, "rows per wave");
-  constexpr int LPS = ROWS / (RPI * NW);              // load instructions per wave per stage
-  constexpr int LB = BN / (RPI * NW);                 // ... of which weight rows
-  constexpr int STAGE = ROWS * CH;                    // 16-byte units per stage
+  constexpr int LB = BN / (RPI * NW);                 // weight load instructions per wave per stage
+  constexpr int LX = BM / (RPI * NW);                 // token load instructions
+  constexpr int LPS = LB + LX;
+  constexpr int WSTG = BN * CH, XSTG = BM * CH;       // 16-byte units per weight / token stage
+  constexpr int LDS_UNITS = 3 * WSTG + 2 * XSTG;
+  static_assert(LDS_UNITS * 16 <= 160 * 1024, "LDS");
   static_assert(SP >= 1 && SP <= KS && LPS % SP == 0, "DMA spread");
 
-  __shared__ u32x4 lds[NS * STAGE];
+  __shared__ u32x4 lds[LDS_UNITS];
+
+  TileLoc tl;
+  if (!locate_tile<NT, BM, BNO, SN>(a, tl, reinterpret_cast<int*>(lds))) return;
+  __syncthreads();                                    // the scratch is read by all before the loads overwrite it
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -354,18 +378,19 @@ __device__ __forceinline__ void dtl_tile(const GemmArgs& a, const TileLoc& tl) {
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, wrecords, kBufFlags);
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase), 0, arecords, kBufFlags);
 
-  // Load instruction i of this wave fills RPI tile rows: the first LB
-  // instructions cover weight rows, the rest token rows.  Lane t -> row
-  // +t/CH, LDS slot t%CH, global chunk (t%CH) ^ swz(row).
+  // Load instruction i of this wave fills RPI rows of a stage: the first LX
+  // instructions token rows, the rest weight rows.  Lane t -> row +t/CH,
+  // LDS slot t%CH, global chunk (t%CH) ^ swz(row).
   int voff[LPS];
   int dst[LPS];
 #pragma unroll
   for (int i = 0; i < LPS; ++i) {
-    const int row0 = (i < LB) ? RPI * (wave + NW * i) : BN + RPI * (wave + NW * (i - LB));
+    const bool tok = i < LX;
+    const int row0 = RPI * (wave + NW * (tok ? i : i - LX));
     const int r = row0 + lane / CH;
     const int c = (lane % CH) ^ swz<CH>(r);
     int64_t off;
-    if (i < LB) {
+    if (!tok) {
       if (EPI == EPI_SWIGLU) {
         const int half = r / (BN / 2);
         off = (half * N + tl.n0 + (r - half * (BN / 2))) * rowb;
@@ -374,23 +399,28 @@ __device__ __forceinline__ void dtl_tile(const GemmArgs& a, const TileLoc& tl) {
       }
     } else if (gather) {
       // rows past the group's end read row 0 (their results are never stored)
-      const int grow = tl.row0 + (r - BN);
+      const int grow = tl.row0 + r;
       const int src = grow < tl.row_end ? clamp_off(a.rowmap[grow], static_cast<int>(a.rows) - 1) / a.kdiv : 0;
       off = static_cast<int64_t>(src) * rowb;
     } else {
-      off = static_cast<int64_t>(r - BN) * rowb;
+      off = static_cast<int64_t>(r) * rowb;
     }
     voff[i] = static_cast<int>(off) + c * 16;
     dst[i] = row0 * CH * 16;                           // byte offset inside a stage
   }
-  const unsigned lds0 = lds_addr_of(lds);
+  const unsigned ldsw = lds_addr_of(lds);                          // weight stages 0..2
+  const unsigned ldsx = ldsw + 3u * WSTG * 16u;                    // token stages 0..1
 
-#define MOE_DMA(buf_, kt_)                                                              \
-  do {                                                                                  \
-    const int so_ = (kt_) * (BK * 2);                                                   \
-    const unsigned b_ = lds0 + static_cast<unsigned>(buf_) * (STAGE * 16);              \
-    _Pragma("unroll") for (int i = 0; i < LPS; ++i)                                     \
-      lds_dma16(i < LB ? wrs : ars, voff[i], so_, __builtin_amdgcn_readfirstlane(b_ + dst[i])); \
+  // Load instruction i for weight stage kw_ into weight buffer wb_, or token
+  // stage kx_ into token buffer xb_.
+#define MOE_DTL_DMA(i_, wb_, kw_, xb_, kx_)                                                          \
+  do {                                                                                              \
+    if ((i_) < LX)                                                                                  \
+      lds_dma16(ars, voff[i_], (kx_) * (BK * 2),                                                    \
+                __builtin_amdgcn_readfirstlane(ldsx + static_cast<unsigned>(xb_) * (XSTG * 16) + dst[i_])); \
+    else                                                                                            \
+      lds_dma16(wrs, voff[i_], (kw_) * (BK * 2),                                                    \
+                __builtin_amdgcn_readfirstlane(ldsw + static_cast<unsigned>(wb_) * (WSTG * 16) + dst[i_])); \
   } while (0)
 
   int wrow[FN];
@@ -407,52 +437,60 @@ __device__ __forceinline__ void dtl_tile(const GemmArgs& a, const TileLoc& tl) {
 
   const int nk = static_cast<int>(K / BK);
   const int last = nk - 1;
+  // Prologue: tokens and weights of stage 0, then the weights of stage 1
+  // (stages past the end are clamped: extra loads of valid memory, never
+  // consumed).
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p) MOE_DMA(p, p < last ? p : last);
-  int cur = 0;                                    // buffer of stage kt
-  // Part p < SP of the DMA of one stage (stage offset so_, LDS buffer b_).
-#define MOE_DMA_PART(p_)                                                                \
+  for (int i = 0; i < LPS; ++i) MOE_DTL_DMA(i, 0, 0, 0, 0);
+#pragma unroll
+  for (int i = LX; i < LPS; ++i) MOE_DTL_DMA(i, 1, (1 < last ? 1 : last), 0, 0);
+  int cw = 0, cx = 0;                           // weight and token buffers of stage kt
+  // Part p < SP of the loads of one stage (tokens first), issued after the
+  // fragment reads of K slice p.
+#define MOE_DTL_PART(p_)                                                                \
   if ((p_) < SP) {                                                                      \
     _Pragma("unroll") for (int i = (p_) * (LPS / SP); i < ((p_) + 1) * (LPS / SP); ++i) \
-      lds_dma16(i < LB ? wrs : ars, voff[i], so_, __builtin_amdgcn_readfirstlane(b_ + dst[i])); \
+      MOE_DTL_DMA(i, nbw, kw, nbx, kx);                                                 \
   }
-  // MOE_COMPUTE with the stage's DMA parts issued after the reads of slices 0..SP-1
-#define MOE_COMPUTE_DMA(s_, NF_)                                                        \
+  // All KS slices of one stage, the reads of slice ks+1 in flight during the
+  // MFMAs of slice ks, the stage's loads spread over its first SP slices.
+#define MOE_DTL_COMPUTE(NF_)                                                            \
   do {                                                                                  \
+    const u32x4* sw_ = lds + cw * WSTG;                                                 \
+    const u32x4* sx_ = lds + 3 * WSTG + cx * XSTG;                                      \
     bf16x8 wf0[FN], tf0[FM], wf1[FN], tf1[FM];                                          \
-    MOE_FRAGS(wf0, tf0, s_, 0, NF_);                                                    \
-    MOE_DMA_PART(0);                                                                    \
+    MOE_DTL_FRAGS(wf0, tf0, sw_, sx_, 0, NF_);                                          \
+    MOE_DTL_PART(0);                                                                    \
     _Pragma("unroll") for (int ks = 0; ks < KS; ks += 2) {                              \
-      MOE_FRAGS(wf1, tf1, s_, ks + 1, NF_);                                             \
-      MOE_DMA_PART(ks + 1);                                                             \
-      MOE_MFMAS(wf0, tf0, NF_);                                                         \
+      MOE_DTL_FRAGS(wf1, tf1, sw_, sx_, ks + 1, NF_);                                   \
+      MOE_DTL_PART(ks + 1);                                                             \
+      MOE_DTL_MFMAS(wf0, tf0, NF_);                                                     \
       if (ks + 2 < KS) {                                                                \
-        MOE_FRAGS(wf0, tf0, s_, ks + 2, NF_);                                           \
-        MOE_DMA_PART(ks + 2);                                                           \
+        MOE_DTL_FRAGS(wf0, tf0, sw_, sx_, ks + 2, NF_);                                 \
+        MOE_DTL_PART(ks + 2);                                                           \
       }                                                                                 \
-      MOE_MFMAS(wf1, tf1, NF_);                                                         \
+      MOE_DTL_MFMAS(wf1, tf1, NF_);                                                     \
     }                                                                                   \
   } while (0)
   // The K loop, specialised on the number of active token fragments (every
-  // wave takes part in the loads and barriers, whatever its share).  Each
-  // iteration refills the buffer consumed in the previous one with stage
-  // kt+NS-1 (clamped past the end: extra loads of valid memory, never
-  // consumed).
+  // wave takes part in the loads and barriers, whatever its share).  Stage
+  // kt refills the buffers of stage kt-1: tokens of stage kt+1 and weights
+  // of stage kt+2.
 #define MOE_DTL_LOOP(NF_)                                                               \
   for (int kt = 0; kt < nk; ++kt) {                                                     \
-    wait_stage_barrier<(NS - 2) * LPS>();                                               \
-    const int nb = cur == 0 ? NS - 1 : cur - 1;                                         \
-    const int kd = kt + NS - 1 < last ? kt + NS - 1 : last;                             \
+    wait_stage_barrier<LB>();                                                           \
+    const int kx = kt + 1 < last ? kt + 1 : last;                                       \
+    const int kw = kt + 2 < last ? kt + 2 : last;                                       \
+    const int nbx = cx ^ 1;                                                             \
+    const int nbw = cw == 0 ? 2 : cw - 1;                                               \
     if ((NF_) > 0) {                                                                    \
-      const int so_ = kd * (BK * 2);                                                    \
-      const unsigned b_ = lds0 + static_cast<unsigned>(nb) * (STAGE * 16);              \
-      const u32x4* s = lds + cur * STAGE;                                               \
-      MOE_COMPUTE_DMA(s, (NF_));                                                        \
+      MOE_DTL_COMPUTE((NF_));                                                           \
       sched_stage<FN + (NF_), FN * ((NF_) > 0 ? (NF_) : 1), 0, 0, KS>();                \
     } else {                                                                            \
-      MOE_DMA(nb, kd);                                                                  \
+      _Pragma("unroll") for (int i = 0; i < LPS; ++i) MOE_DTL_DMA(i, nbw, kw, nbx, kx); \
     }                                                                                   \
-    cur = cur + 1 == NS ? 0 : cur + 1;                                                  \
+    cw = cw == 2 ? 0 : cw + 1;                                                          \
+    cx ^= 1;                                                                            \
   }
   if (nfm == FM) {
     MOE_DTL_LOOP(FM)
@@ -467,45 +505,21 @@ __device__ __forceinline__ void dtl_tile(const GemmArgs& a, const TileLoc& tl) {
   }
   drain_vm();
 #undef MOE_DTL_LOOP
-#undef MOE_COMPUTE_DMA
-#undef MOE_DMA_PART
-#undef MOE_DMA
+#undef MOE_DTL_COMPUTE
+#undef MOE_DTL_PART
+#undef MOE_DTL_DMA
 
-  if (LDS_EPI && NS * STAGE * 16 >= BM * BNO * 2) {
+  if (LDS_EPI) {
+    static_assert(!LDS_EPI || LDS_UNITS * 16 >= BM * BNO * 2, "output tile fits the stages");
     __syncthreads();                             // every wave is past its last LDS read and DMA
     store_tile_lds<EPI, FM, FN, TM, TN, BM, BNO, NT>(a, tl, acc, wm, wn, l32, khalf, reinterpret_cast<char*>(lds));
   } else {
     store_tile<EPI, FM, FN, TM, TN>(a, tl, acc, wm, wn, l32, khalf);
   }
-}
-
-// One tile per workgroup, in the order of locate_tile.
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP, int LDS_EPI>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)   // the body uses device-only types; the host pass needs only the stub
-  constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  TileLoc tl;
-  if (!locate_tile<64 * WM * WN, BM, BNO, SN>(a, tl)) return;
-  dtl_tile<BM, BN, WM, WN, EPI, BK, NS, SP, LDS_EPI>(a, tl);
 #endif
 }
-
-// Persistent form: one workgroup per CU walks tiles bid, bid + grid, ... of
-// the same order, so a tile's last stores drain while the next tile is
-// located and its first stage loads.
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP, int LDS_EPI>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_pers_kernel(GemmArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NT = 64 * WM * WN;
-  constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  __shared__ TilePlanLds plan;
-  const int total = tile_plan<NT, BM, BNO>(a, plan);
-  for (int j = static_cast<int>(blockIdx.x); j < total; j += static_cast<int>(gridDim.x)) {
-    if (j != static_cast<int>(blockIdx.x)) lds_barrier();   // every wave is done with the last tile's LDS
-    dtl_tile<BM, BN, WM, WN, EPI, BK, NS, SP, LDS_EPI>(a, tile_at<BM, BNO, SN>(a, plan, total, j));
-  }
-#endif
-}
+#undef MOE_DTL_FRAGS
+#undef MOE_DTL_MFMAS
 
 // ---------------------------------------------------------------------------
 // Register-staged kernel (router logits): 128-byte LDS rows, two buffers,
@@ -626,7 +640,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs a) {
 #undef MOE_MFMAS
 #undef MOE_FRAGS
 
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP = 1, int LDS_EPI = 0>
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int SP = 1, int LDS_EPI = 0>
 moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   const int64_t grid = grouped_tile_bound(a.rows, a.G, BM, a.N, BNO);
@@ -637,38 +651,7 @@ moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   if (wbytes >= (int64_t(1) << 31) || static_cast<int64_t>(BM) * a.K * 2 >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
   if (a.rowmap && (a.kdiv < 1 || a.a_rows * a.K * 2 >= (int64_t(1) << 31))) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, NS, SP, LDS_EPI>), dim3(static_cast<unsigned>(grid)),
-                     dim3(64 * WM * WN), 0, st, a);
-  return launch_status();
-}
-
-// Compute units of the current device (the persistent grid), cached per device.
-int persistent_grid() {
-  static std::atomic<int> cache[64];                  // per device; 0 = not yet queried
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int NS, int SP = 1, int LDS_EPI = 0>
-moe_status launch_pers(const GemmArgs& a, hipStream_t st) {
-  constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  const int64_t bound = grouped_tile_bound(a.rows, a.G, BM, a.N, BNO);
-  if (bound <= 0) return MOE_OK;
-  if (bound > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  const int64_t wbytes = ((EPI == EPI_SWIGLU) ? 2 : 1) * a.N * a.K * 2;
-  if (wbytes >= (int64_t(1) << 31) || static_cast<int64_t>(BM) * a.K * 2 >= (int64_t(1) << 31))
-    return MOE_ERR_UNSUPPORTED;
-  if (a.rowmap && (a.kdiv < 1 || a.a_rows * a.K * 2 >= (int64_t(1) << 31))) return MOE_ERR_UNSUPPORTED;
-  const int cus = persistent_grid();
-  if (cus <= 0) return MOE_ERR_HIP;
-  const int grid = static_cast<int>(bound < cus ? bound : cus);
-  hipLaunchKernelGGL((gemm_bf16_pers_kernel<BM, BN, WM, WN, EPI, SN, BK, NS, SP, LDS_EPI>), dim3(grid),
+  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, SP, LDS_EPI>), dim3(static_cast<unsigned>(grid)),
                      dim3(64 * WM * WN), 0, st, a);
   return launch_status();
 }
@@ -688,20 +671,17 @@ moe_status launch(const GemmArgs& a, hipStream_t st) {
 
 
 // Expert projections: 256 token rows x 256 weight rows per tile, 8 waves
-// (2 along tokens x 4 along weights, 128 x 64 each), two 64-wide
-// direct-to-LDS stages.
+// (2 along tokens x 4 along weights, 128 x 64 each), 64-wide K stages
+// loaded straight into LDS, each stage's loads spread over its 4 K slices.
 moe_status gemm_bf16_gateup_swiglu(const GemmArgs& a, hipStream_t st) {
-  return launch_dtl<256, 256, 2, 4, EPI_SWIGLU, 16, 64, 2, 2>(a, st);
+  return launch_dtl<256, 256, 2, 4, EPI_SWIGLU, 16, 64, 4, 0>(a, st);
 }
 
 // The down projection's output tile is 256 columns wide, so its epilogue
 // goes through LDS (whole-row stores; measured faster on every MoE shape,
 // while the 128-column SwiGLU tile of gate/up measured slower that way).
-// With a short K loop (K <= 1024: a tile's prologue and epilogue weigh more
-// than the dispatcher's dynamic balance) the persistent launch is faster.
 moe_status gemm_bf16_down(const GemmArgs& a, hipStream_t st) {
-  if (a.K <= 1024) return launch_pers<256, 256, 2, 4, EPI_STORE, 16, 64, 2, 2, 1>(a, st);
-  return launch_dtl<256, 256, 2, 4, EPI_STORE, 16, 64, 2, 2, 1>(a, st);
+  return launch_dtl<256, 256, 2, 4, EPI_STORE, 16, 64, 4, 1>(a, st);
 }
 
 // Router logits: few output columns, so small token tiles keep every CU

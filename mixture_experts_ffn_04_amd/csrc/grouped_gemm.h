@@ -64,10 +64,10 @@ struct TileLoc {
 // thread t < G gets its group's row range [lo, hi), tile count cnt and the
 // index excl of its first tile; every thread gets the total.  Contains one
 // workgroup barrier.
+// s_wsum: NT/64 ints of LDS.
 template <int NT, int BM, int BNO>
-__device__ __forceinline__ int scan_tiles(const GemmArgs& a, int& lo, int& hi, int& cnt, int& excl) {
+__device__ __forceinline__ int scan_tiles(const GemmArgs& a, int& lo, int& hi, int& cnt, int& excl, int* s_wsum) {
   static_assert(NT >= kMaxE, "one group per thread");
-  __shared__ int s_wsum[NT / 64];
   const int t = threadIdx.x;
   const int rows = static_cast<int>(a.rows);
   const int ntiles = static_cast<int>((a.N + BNO - 1) / BNO);
@@ -142,11 +142,13 @@ __device__ __forceinline__ TileLoc tile_coords(const GemmArgs& a, int g, int glo
 // Locate this workgroup's tile.  Must be called by all NT threads; returns
 // false (for the whole workgroup) when the block id is past the last tile.
 //   BM     rows per tile, BNO output columns per tile, SN column-block width
+//   scratch  NT/64 + 4 ints of LDS, free again once this returns and every
+//            thread has passed one more workgroup barrier
 template <int NT, int BM, int BNO, int SN>
-__device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl) {
-  __shared__ int s_hit[4];
+__device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl, int* scratch) {
+  int* s_hit = scratch + NT / 64;
   int lo, hi, cnt, excl;
-  const int total = scan_tiles<NT, BM, BNO>(a, lo, hi, cnt, excl);
+  const int total = scan_tiles<NT, BM, BNO>(a, lo, hi, cnt, excl, scratch);
   const int bid = static_cast<int>(blockIdx.x);
   if (bid >= total) return false;     // uniform: total is the same in every thread
   const int L = tile_order(bid, total);
@@ -161,37 +163,11 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl) {
   return true;
 }
 
-// Persistent form of the same order: the group table is built once per
-// workgroup (tile_plan), then tile_at maps any logical slot to its tile by
-// a binary search over the group prefixes.
-struct TilePlanLds {
-  int pref[kMaxE];   // first tile of each group
-  int lo[kMaxE];
-  int hi[kMaxE];
-};
-
-template <int NT, int BM, int BNO>
-__device__ __forceinline__ int tile_plan(const GemmArgs& a, TilePlanLds& p) {
-  int lo, hi, cnt, excl;
-  const int total = scan_tiles<NT, BM, BNO>(a, lo, hi, cnt, excl);
-  if (static_cast<int>(threadIdx.x) < a.G) {
-    p.pref[threadIdx.x] = excl;
-    p.lo[threadIdx.x] = lo;
-    p.hi[threadIdx.x] = hi;
-  }
-  __syncthreads();
-  return total;
-}
-
-template <int BM, int BNO, int SN>
-__device__ __forceinline__ TileLoc tile_at(const GemmArgs& a, const TilePlanLds& p, int total, int bid) {
-  const int L = tile_order(bid, total);
-  // last group whose first tile is <= L: it has tiles (a later group with
-  // the same prefix would be the one found), and L is below its end
-  int g = 0;
-  for (int step = kMaxE / 2; step > 0; step >>= 1)
-    if (g + step < a.G && p.pref[g + step] <= L) g += step;
-  return tile_coords<BM, BNO, SN>(a, g, p.lo[g], p.hi[g], L - p.pref[g]);
+// The same with scratch of its own.
+template <int NT, int BM, int BNO, int SN>
+__device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl) {
+  __shared__ int scratch[NT / 64 + 4];
+  return locate_tile<NT, BM, BNO, SN>(a, tl, scratch);
 }
 
 // Upper bound on the tiles of a grouped launch (used as the grid size):
