@@ -250,6 +250,53 @@ def test_down_many_tiles(gpu, T, E, k, K, N):
     U.assert_close(U.host_values(y), ref, "bf16", f"T={T} E={E} K={K} N={N} Y_perm")
 
 
+# decode calls with at most two rows per expert on average run the
+# vector-ALU form: K up to 2048, 3072 and 4096 (its three register
+# layouts), one expert holding many of the rows, empty experts
+DECODE_ROWS = [(16, 20, 1024, 192), (32, 60, 2880, 256), (64, 100, 3968, 320)]
+
+
+def _skewed_offsets(E, rows, seed):
+    rng = np.random.default_rng(seed)
+    counts = np.zeros(E, np.int64)
+    counts[E // 3] = rows // 2                      # one expert takes half the rows
+    rest = rng.choice(np.arange(E)[np.arange(E) != E // 3], size=rows - rows // 2)
+    np.add.at(counts, rest, 1)
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("E,rows,K,N", DECODE_ROWS)
+def test_decode_few_rows_per_expert(gpu, E, rows, K, N):
+    offsets = _skewed_offsets(E, rows, seed=K)
+    assert rows <= 2 * E and (np.diff(offsets) == 0).any()
+    xs = W.gen_matrix((rows, K), seed=K + 11)
+    gu = W.gen_matrix((E, 2 * N, K), seed=K + 12, std=0.05)
+    dn = W.gen_matrix((E, N, K), seed=K + 13, std=0.05)
+    h = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    y = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    B().gateup_swiglu(U.dev_tensor(xs, "bf16"), U.dev_tensor(gu, "bf16"), _i32(offsets), h, decode=True)
+    B().down(U.dev_tensor(xs, "bf16"), U.dev_tensor(dn, "bf16"), _i32(offsets), y, decode=True)
+    torch.cuda.synchronize()
+    x64 = W.values(xs, "bf16")
+    U.assert_close(U.host_values(h), O.grouped_gate_up_swiglu(x64, W.values(gu, "bf16"), offsets), "bf16", "H")
+    U.assert_close(U.host_values(y), O.grouped_down(x64, W.values(dn, "bf16"), offsets), "bf16", "Y_perm")
+
+
+def test_decode_few_rows_gather(gpu):
+    """The vector-ALU form reading token rows through the sort."""
+    T, E, k, K, N = 6, 32, 4, 2880, 256
+    ids = W.gen_ids(T, E, k, seed=5)
+    _, offsets, perm, _ = O.permute(ids, E)
+    xs = W.gen_matrix((T, K), seed=21)
+    gu = W.gen_matrix((E, 2 * N, K), seed=22, std=0.05)
+    h = torch.empty(T * k, N, dtype=torch.bfloat16, device=gpu)
+    B().gateup_swiglu_gather(U.dev_tensor(xs, "bf16"), _i32(perm), k, U.dev_tensor(gu, "bf16"), _i32(offsets), h,
+                             decode=True)
+    torch.cuda.synchronize()
+    ref = O.grouped_gate_up_swiglu(W.values(xs, "bf16")[perm // k], W.values(gu, "bf16"), offsets)
+    U.assert_close(U.host_values(h), ref, "bf16", "H (gather)")
+
+
 @pytest.mark.parametrize("shared", [False, True])
 @pytest.mark.parametrize("name", SMALL)
 def test_combine(gpu, name, shared):
