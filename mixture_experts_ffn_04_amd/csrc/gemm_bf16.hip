@@ -281,8 +281,8 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const TileLoc&
 }
 
 // Fragment reads of K slice ks (16 wide) -- the FN weight fragments from
-// weight stage sw_ and the first NF_ token fragments from token stage sx_ --
-// and the NF_ x FN MFMAs on them.
+// weight stage sw_ and the first NF_ token fragments from token stage sx_
+// (their MFMAs are MOE_MFMAS).
 #define MOE_DTL_FRAGS(wf_, tf_, sw_, sx_, ks_, NF_)                                     \
   do {                                                                                  \
     const int c_ = ((ks_) * 2 + khalf) ^ sw;                                            \
@@ -290,12 +290,6 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const TileLoc&
       wf_[fn] = __builtin_bit_cast(bf16x8, (sw_)[(wrow[fn] + l32) * CH + c_]);          \
     _Pragma("unroll") for (int fm = 0; fm < (NF_); ++fm)                                \
       tf_[fm] = __builtin_bit_cast(bf16x8, (sx_)[(wm * TM + fm * 32 + l32) * CH + c_]); \
-  } while (0)
-#define MOE_DTL_MFMAS(wf_, tf_, NF_)                                                    \
-  do {                                                                                  \
-    _Pragma("unroll") for (int fm = 0; fm < (NF_); ++fm)                                \
-      _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                 \
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf_[fn], tf_[fm], acc[fm][fn], 0, 0, 0); \
   } while (0)
 
 // One tile per workgroup, in the order of locate_tile.
@@ -464,12 +458,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
     _Pragma("unroll") for (int ks = 0; ks < KS; ks += 2) {                              \
       MOE_DTL_FRAGS(wf1, tf1, sw_, sx_, ks + 1, NF_);                                   \
       MOE_DTL_PART(ks + 1);                                                             \
-      MOE_DTL_MFMAS(wf0, tf0, NF_);                                                     \
+      MOE_MFMAS(wf0, tf0, NF_);                                                     \
       if (ks + 2 < KS) {                                                                \
         MOE_DTL_FRAGS(wf0, tf0, sw_, sx_, ks + 2, NF_);                                 \
         MOE_DTL_PART(ks + 2);                                                           \
       }                                                                                 \
-      MOE_DTL_MFMAS(wf1, tf1, NF_);                                                     \
+      MOE_MFMAS(wf1, tf1, NF_);                                                     \
     }                                                                                   \
   } while (0)
   // The K loop, specialised on the number of active token fragments (every
@@ -519,7 +513,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
 #endif
 }
 #undef MOE_DTL_FRAGS
-#undef MOE_DTL_MFMAS
 
 // ---------------------------------------------------------------------------
 // Register-staged kernel (router logits): 128-byte LDS rows, two buffers,
