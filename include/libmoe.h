@@ -237,6 +237,9 @@ MOE_API moe_status moe_grouped_gemm_gateup_swiglu_gather(const void* x, const in
  * expert's weights are streamed from HBM once and experts with no rows are
  * never read (article, "From Dense to Sparse": decode speed follows the
  * active parameters; section "Expert Backend": the small-batch strategy).
+ * The form follows the rows per expert: vector-ALU dot products up to 2,
+ * a split-K MFMA kernel above, and from 3 (gate/up) or 6 (down) the tile
+ * kernel of the grouped calls, which then streams the weights fastest.
  * rows > 1024 returns MOE_ERR_UNSUPPORTED.
  */
 MOE_API moe_status moe_decode_gateup_swiglu(const void* x_perm, const void* w_gate_up,

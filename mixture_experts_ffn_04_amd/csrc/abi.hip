@@ -13,6 +13,13 @@ moe_status decode_bf16(bool swiglu, const void* A, const void* B, const int32_t*
 namespace {
 
 constexpr int64_t kDecodeMaxRows = 1024;
+// Decode calls with several rows per expert on average run the grouped tile
+// kernel: with 3+ (gate/up) or 6+ (down) rows per expert its loads of whole
+// 128-byte row pieces into LDS stream the weights faster than the split-K
+// MFMA form (measured on 32 experts of 2880 x 2880: gate/up at T=24, 4 rows
+// per expert, 181 vs 194 us; down at T=64, 8 rows, 111 vs 122 us).
+constexpr int64_t kDecodeTileGateUpRows = 3;   // per expert
+constexpr int64_t kDecodeTileDownRows = 6;
 
 moe_status check_proj(const void* in, const void* w, const int32_t* offsets, int64_t rows, int64_t d, int64_t f,
                       int32_t E, moe_dtype dtype, const void* out) {
@@ -103,6 +110,8 @@ extern "C" moe_status moe_decode_gateup_swiglu(const void* x_perm, const void* w
   if (rows > kDecodeMaxRows) return MOE_ERR_UNSUPPORTED;
   if (dtype == MOE_F32)
     return gemm_f32_gateup_swiglu(proj_args(x_perm, w_gate_up, offsets, rows, d, f, E, h), as_stream(stream));
+  if (rows >= kDecodeTileGateUpRows * E)
+    return gemm_bf16_gateup_swiglu(proj_args(x_perm, w_gate_up, offsets, rows, d, f, E, h), as_stream(stream));
   return decode_bf16(true, x_perm, w_gate_up, offsets, rows, d, f, E, h, as_stream(stream));
 }
 
@@ -116,6 +125,13 @@ extern "C" moe_status moe_decode_gateup_swiglu_gather(const void* x, const int32
   if (rows == 0) return MOE_OK;
   if (!perm) return MOE_ERR_INVALID_ARG;
   if (rows > kDecodeMaxRows || dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (rows >= kDecodeTileGateUpRows * E) {
+    GemmArgs a = proj_args(x, w_gate_up, offsets, rows, d, f, E, h);
+    a.rowmap = perm;
+    a.kdiv = k;
+    a.a_rows = rows / k;
+    return gemm_bf16_gateup_swiglu(a, as_stream(stream));
+  }
   return decode_bf16(true, x, w_gate_up, offsets, rows, d, f, E, h, as_stream(stream), perm, k);
 }
 
@@ -126,5 +142,7 @@ extern "C" moe_status moe_decode_down(const void* h, const void* w_down, const i
   if (rows > kDecodeMaxRows) return MOE_ERR_UNSUPPORTED;
   if (dtype == MOE_F32)
     return gemm_f32_down(proj_args(h, w_down, offsets, rows, f, d, E, y_perm), as_stream(stream));
+  if (rows >= kDecodeTileDownRows * E)
+    return gemm_bf16_down(proj_args(h, w_down, offsets, rows, f, d, E, y_perm), as_stream(stream));
   return decode_bf16(false, h, w_down, offsets, rows, f, d, E, y_perm, as_stream(stream));
 }

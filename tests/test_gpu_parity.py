@@ -282,6 +282,26 @@ def test_decode_few_rows_per_expert(gpu, E, rows, K, N):
     U.assert_close(U.host_values(y), O.grouped_down(x64, W.values(dn, "bf16"), offsets), "bf16", "Y_perm")
 
 
+@pytest.mark.parametrize("rows", [24, 40, 64, 112])
+def test_decode_forms_by_rows_per_expert(gpu, rows):
+    """The decode calls pick their kernel by rows per expert (16 experts): the
+    vector-ALU form (24 rows), the split-K MFMA form (40), the tile kernel
+    for gate/up only (64) and for both projections (112)."""
+    E, K, N = 16, 1024, 192
+    offsets = _skewed_offsets(E, rows, seed=rows)
+    xs = W.gen_matrix((rows, K), seed=rows + 31)
+    gu = W.gen_matrix((E, 2 * N, K), seed=rows + 32, std=0.05)
+    dn = W.gen_matrix((E, N, K), seed=rows + 33, std=0.05)
+    h = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    y = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    B().gateup_swiglu(U.dev_tensor(xs, "bf16"), U.dev_tensor(gu, "bf16"), _i32(offsets), h, decode=True)
+    B().down(U.dev_tensor(xs, "bf16"), U.dev_tensor(dn, "bf16"), _i32(offsets), y, decode=True)
+    torch.cuda.synchronize()
+    x64 = W.values(xs, "bf16")
+    U.assert_close(U.host_values(h), O.grouped_gate_up_swiglu(x64, W.values(gu, "bf16"), offsets), "bf16", "H")
+    U.assert_close(U.host_values(y), O.grouped_down(x64, W.values(dn, "bf16"), offsets), "bf16", "Y_perm")
+
+
 def test_decode_few_rows_gather(gpu):
     """The vector-ALU form reading token rows through the sort."""
     T, E, k, K, N = 6, 32, 4, 2880, 256
