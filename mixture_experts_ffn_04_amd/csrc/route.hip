@@ -40,49 +40,68 @@ namespace {
 
 constexpr int kTokPerBlock = 4;   // one wave each
 
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// Order-preserving 32-bit key of a logit: unsigned comparison of keys is
+// the float comparison (-0 is taken as +0, so the two tie); 0 lies below
+// every real key and marks "no candidate".
+__device__ __forceinline__ unsigned logit_key(float f) {
+  unsigned u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_logit(unsigned k) {
+  return __uint_as_float((k >> 31) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Maximum over the wave, in every lane: an inclusive max-scan inside each
+// 16-lane row by DPP row shifts of 1, 2, 4, 8, then the row totals carried
+// across rows by row_bcast 15 and 31, so lane 63 holds the wave's maximum.
+__device__ __forceinline__ unsigned wave_max(unsigned v) {
+  int x = static_cast<int>(v);
+#define MOE_MAX_DPP(ctrl, rows)                                                                  \
+  x = static_cast<int>(max(static_cast<unsigned>(x),                                            \
+                           static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, x, ctrl, rows, 0xf, false))))
+  MOE_MAX_DPP(0x111, 0xf);   // row_shr:1
+  MOE_MAX_DPP(0x112, 0xf);   // row_shr:2
+  MOE_MAX_DPP(0x114, 0xf);   // row_shr:4
+  MOE_MAX_DPP(0x118, 0xf);   // row_shr:8
+  MOE_MAX_DPP(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
+  MOE_MAX_DPP(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
+#undef MOE_MAX_DPP
+  return static_cast<unsigned>(__builtin_amdgcn_readlane(x, 63));
 }
 
 // Selection and weights for one token, by one whole wave: row = the
-// token's E logits (global memory or LDS).
+// token's E logits (global memory or LDS).  Lane l holds candidates l,
+// l+64, l+128, l+192.  Each of the k rounds takes the largest key over the
+// wave, then the lowest index holding it (candidates of slot i all have
+// lower indices than those of slot i+1), and retires that candidate.
 __device__ __forceinline__ void topk_token(const float* row, int E, int k, int score, int32_t* __restrict__ ids,
                                            float* __restrict__ wts) {
   const int lane = threadIdx.x & 63;
-  float v[4];
-  bool live[4];
+  unsigned key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    live[i] = e < E;
-    v[i] = live[i] ? row[e] : 0.0f;
+    key[i] = e < E ? logit_key(row[e]) : 0u;
   }
   float sel_v[kMaxK];
   int sel_i[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j >= k) break;
-    // lane-local best
-    float bv = -__builtin_inff();
-    int bi = 0x7fffffff;
+    const unsigned m = wave_max(max(max(key[0], key[1]), max(key[2], key[3])));
+    int e = -1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (live[i] && (bi == 0x7fffffff || better(v[i], e, bv, bi))) { bv = v[i]; bi = e; }
+      const uint64_t b = __ballot(key[i] == m);
+      if (e < 0 && b != 0) e = 64 * i + static_cast<int>(__builtin_ctzll(b));
     }
-    // wave arg-max on (value, -index); lanes with nothing left carry index INT_MAX
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      const bool take = (oi != 0x7fffffff) && (bi == 0x7fffffff || better(ov, oi, bv, bi));
-      if (take) { bv = ov; bi = oi; }
-    }
-    sel_v[j] = bv;
-    sel_i[j] = bi;
+    sel_v[j] = key_logit(m);
+    sel_i[j] = e;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == bi) live[i] = false;
+      if (lane + 64 * i == e) key[i] = 0u;
   }
   if (lane == 0) {
     float w[kMaxK];
