@@ -91,9 +91,9 @@ def test_route(gpu, name):
 
 # router logits through each of its kernels, chosen by size: one wave per
 # (expert, few tokens) at d <= 4096 and d <= 8192, the streaming kernel with
-# 16- and 32-token blocks, the tiled GEMM
+# 16- and 32-token blocks, the tile kernel on 32- and 64-token tiles
 ROUTER_PATHS = [(40, 8, 4096, 2), (50, 16, 6144, 4), (300, 40, 1024, 4), (8192, 64, 256, 8), (1100, 96, 512, 6),
-                (1030, 8, 320, 2)]
+                (1030, 8, 320, 2), (16384, 128, 256, 8)]
 
 
 @pytest.mark.parametrize("T,E,d,k", ROUTER_PATHS)
