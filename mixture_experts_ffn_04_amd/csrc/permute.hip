@@ -95,22 +95,32 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t* __restrict__ cc, int
   if (e == E - 1) offsets[E] = excl + tot;
 }
 
-// One wave per chunk.
+// One wave per chunk.  The chunk's ids are all loaded (one memory round
+// trip) before the walk, which is then bound by ballots and LDS only.
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int P, int E,
                                                      int nbits, const int32_t* __restrict__ cc,
                                                      int32_t* __restrict__ perm,
                                                      int32_t* __restrict__ inv_perm) {
+  constexpr int kSteps = kChunk / 64;
   __shared__ int base[kMaxE];
   const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) base[e] = cc[static_cast<int64_t>(blockIdx.x) * E + e];
-  __syncthreads();
   const int p0 = blockIdx.x * kChunk;
   const int p1 = min(P, p0 + kChunk);
+  int idv[kSteps];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int p = p0 + 64 * i + lane;
+    idv[i] = p < p1 ? ids[p] : -1;
+  }
+  for (int e = lane; e < E; e += 64) base[e] = cc[static_cast<int64_t>(blockIdx.x) * E + e];
+  __syncthreads();
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  for (int s = p0; s < p1; s += 64) {
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int s = p0 + 64 * i;
+    if (s >= p1) break;
     const int p = s + lane;
-    int e = -1;
-    if (p < p1) e = ids[p];
+    const int e = idv[i];
     const bool ok = e >= 0 && e < E;
     uint64_t m = __ballot(ok);
 #pragma unroll 1
@@ -192,12 +202,19 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t* __res
   if (t == E - 1) offsets[E] = excl + c;
   __syncthreads();
   if (w != 0) return;
-  // stable scatter by the first wave, 64 pairs at a time in order
+  // stable scatter by the first wave, 64 pairs at a time in order, every id
+  // loaded before the walk
+  constexpr int kSteps = kChunk / 64;
+  int idv[kSteps];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) idv[i] = 64 * i + lane < P ? ids[64 * i + lane] : -1;
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  for (int s0 = 0; s0 < P; s0 += 64) {
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int s0 = 64 * i;
+    if (s0 >= P) break;
     const int p = s0 + lane;
-    int e = -1;
-    if (p < P) e = ids[p];
+    const int e = idv[i];
     const bool ok = e >= 0 && e < E;
     uint64_t m = __ballot(ok);
 #pragma unroll 1
