@@ -10,10 +10,12 @@
 //   2. scan       one workgroup: per expert, running sum over chunks (the
 //                 chunk's base inside the expert's group), then an exclusive
 //                 scan over experts -> counts, offsets, per-chunk bases
-//   3. scatter    one wave per chunk walks its pairs 64 at a time in order;
-//                 the rank of a pair among equal experts in the wave comes
-//                 from ballots on the bits of the expert id (a match-any), so
-//                 positions are stable without atomics on the ranks
+//   3. scatter    four waves per chunk, each walking a quarter of its pairs
+//                 64 at a time in order from its own base (the chunk's base
+//                 plus the counts of the waves before it); the rank of a pair
+//                 among equal experts in the wave comes from ballots on the
+//                 bits of the expert id (a match-any), so positions are
+//                 stable without atomics on the ranks
 //   4. gather     x_perm[r] = x[perm[r] / k], 16-byte loads and stores, one
 //                 wave per row
 #include "common.h"
@@ -95,30 +97,50 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t* __restrict__ cc, int
   if (e == E - 1) offsets[E] = excl + tot;
 }
 
-// One wave per chunk.  The chunk's ids are all loaded (one memory round
-// trip) before the walk, which is then bound by ballots and LDS only.
-__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int P, int E,
-                                                     int nbits, const int32_t* __restrict__ cc,
-                                                     int32_t* __restrict__ perm,
-                                                     int32_t* __restrict__ inv_perm) {
-  constexpr int kSteps = kChunk / 64;
-  __shared__ int base[kMaxE];
-  const int lane = threadIdx.x;
-  const int p0 = blockIdx.x * kChunk;
-  const int p1 = min(P, p0 + kChunk);
-  int idv[kSteps];
+// One workgroup of 4 waves per chunk; wave w takes the chunk's pairs
+// [256w, 256w + 256).  The waves first count their pairs per expert (LDS
+// atomics, order-free), thread e then turns the chunk's base in expert e's
+// group into one base per wave (the counts of the waves before it added),
+// and each wave walks its pairs 64 at a time in order.  Its ids are all
+// loaded before the walk.
+constexpr int kScatterWaves = 4;
+constexpr int kScatterSteps = kChunk / (64 * kScatterWaves);
+
+__global__ __launch_bounds__(64 * kScatterWaves) void scatter_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                                     int nbits, const int32_t* __restrict__ cc,
+                                                                     int32_t* __restrict__ perm,
+                                                                     int32_t* __restrict__ inv_perm) {
+  __shared__ int cnt[kScatterWaves][kMaxE];
+  __shared__ int base[kScatterWaves][kMaxE];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int p0 = blockIdx.x * kChunk + w * (64 * kScatterSteps);
+  const int pend = min(P, blockIdx.x * kChunk + kChunk);
+  int idv[kScatterSteps];
 #pragma unroll
-  for (int i = 0; i < kSteps; ++i) {
+  for (int i = 0; i < kScatterSteps; ++i) {
     const int p = p0 + 64 * i + lane;
-    idv[i] = p < p1 ? ids[p] : -1;
+    idv[i] = p < pend ? ids[p] : -1;
   }
-  for (int e = lane; e < E; e += 64) base[e] = cc[static_cast<int64_t>(blockIdx.x) * E + e];
+  for (int e = lane; e < E; e += 64) cnt[w][e] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kScatterSteps; ++i)
+    if (idv[i] >= 0 && idv[i] < E) atomicAdd(&cnt[w][idv[i]], 1);
+  __syncthreads();
+  if (t < E) {
+    int b = cc[static_cast<int64_t>(blockIdx.x) * E + t];
+#pragma unroll
+    for (int v = 0; v < kScatterWaves; ++v) {
+      base[v][t] = b;
+      b += cnt[v][t];
+    }
+  }
   __syncthreads();
   const uint64_t below = (uint64_t(1) << lane) - 1;
 #pragma unroll
-  for (int i = 0; i < kSteps; ++i) {
+  for (int i = 0; i < kScatterSteps; ++i) {
     const int s = p0 + 64 * i;
-    if (s >= p1) break;
+    if (s >= pend) break;
     const int p = s + lane;
     const int e = idv[i];
     const bool ok = e >= 0 && e < E;
@@ -131,21 +153,16 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
     }
     // m: lanes holding the same expert (valid lanes only)
     int pos = 0;
+    if (ok) pos = base[w][e] + __popcll(m & below);
+    __builtin_amdgcn_wave_barrier();   // every lane has read base[w] for this step
     if (ok) {
-      const int rank = __popcll(m & below);
-      pos = base[e] + rank;
-    }
-    __syncthreads();   // every lane has read base[] for this step
-    if (ok) {
-      const int cnt = __popcll(m);
-      const int leader = 63 - __clzll(m);          // highest lane of the group
-      if (lane == leader) base[e] += cnt;
+      if (lane == 63 - __clzll(m)) base[w][e] += __popcll(m);   // the group's highest lane
       perm[pos] = p;
       inv_perm[p] = pos;
-    } else if (p < p1) {
+    } else if (p < pend) {
       inv_perm[p] = -1;                            // routed to an expert not in this call
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -288,7 +305,7 @@ extern "C" moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_
   } else {
     hipLaunchKernelGGL(hist_kernel, dim3(chunks), dim3(256), 0, st, topk_ids, static_cast<int>(P), E, cc);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, st, cc, chunks, E, counts, offsets);
-    hipLaunchKernelGGL(scatter_kernel, dim3(chunks), dim3(64), 0, st, topk_ids, static_cast<int>(P), E, nbits,
+    hipLaunchKernelGGL(scatter_kernel, dim3(chunks), dim3(64 * kScatterWaves), 0, st, topk_ids, static_cast<int>(P), E, nbits,
                        cc, perm, inv_perm);
   }
   if (x_perm) {
