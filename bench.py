@@ -420,7 +420,7 @@ def main(argv=None):
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the layer runs on a single MI355X and this build has no "
+        print("bench.py measures one GPU only: the layer runs on a single MI355X and libmoe has no "
               "multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
