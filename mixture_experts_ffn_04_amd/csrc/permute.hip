@@ -46,55 +46,80 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   for (int e = threadIdx.x; e < E; e += 256) cc[static_cast<int64_t>(blockIdx.x) * E + e] = h[e];
 }
 
-// One workgroup of 256 threads (E <= 256): thread e owns expert e.
-__global__ __launch_bounds__(256) void scan_kernel(int32_t* __restrict__ cc, int chunks, int E,
-                                                   int32_t* __restrict__ counts,
-                                                   int32_t* __restrict__ offsets) {
+// One workgroup of kScanParts x 256 threads (E <= 256): thread (part, e)
+// owns expert e's counts in chunks [part*cq, (part+1)*cq), so each thread
+// walks a quarter of the chunks.  Pass 1 sums its chunks; the part sums
+// give each thread its base inside the expert's group, and an exclusive
+// scan over the experts' totals gives offsets; pass 2 rewrites every
+// chunk's count as that chunk's first row.  Loads of kScanBatch chunks are
+// issued together (one memory round trip per batch).
+constexpr int kScanParts = 4;
+
+__global__ __launch_bounds__(256 * kScanParts) void scan_kernel(int32_t* __restrict__ cc, int chunks, int E,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets) {
+  __shared__ int psum[kScanParts][kMaxE];
+  __shared__ int eoff[kMaxE];
   __shared__ int wsum[4];
-  const int e = threadIdx.x;
-  int tot = 0;
-  // Batches of kScanBatch chunks: the loads of a batch are independent, so
-  // they are all issued before the running sum (one memory round trip per
-  // batch instead of per chunk).
+  const int e = threadIdx.x & (kMaxE - 1);
+  const int part = threadIdx.x / kMaxE;
+  const int cq = (chunks + kScanParts - 1) / kScanParts;
+  const int c_lo = min(chunks, part * cq), c_hi = min(chunks, c_lo + cq);
+  int mine = 0;
   if (e < E) {
-    for (int c0 = 0; c0 < chunks; c0 += kScanBatch) {
+    for (int c0 = c_lo; c0 < c_hi; c0 += kScanBatch) {
       int v[kScanBatch];
 #pragma unroll
-      for (int j = 0; j < kScanBatch; ++j)
-        v[j] = c0 + j < chunks ? cc[static_cast<int64_t>(c0 + j) * E + e] : 0;
+      for (int j = 0; j < kScanBatch; ++j) v[j] = c0 + j < c_hi ? cc[static_cast<int64_t>(c0 + j) * E + e] : 0;
 #pragma unroll
-      for (int j = 0; j < kScanBatch; ++j) {
-        if (c0 + j < chunks) cc[static_cast<int64_t>(c0 + j) * E + e] = tot;   // base of the chunk in e's group
-        tot += v[j];
-      }
+      for (int j = 0; j < kScanBatch; ++j) mine += v[j];
     }
   }
-  const int lane = e & 63, w = e >> 6;
-  int v = tot;
+  psum[part][e] = mine;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int q = 0; q < kScanParts; ++q) {
+    before += q < part ? psum[q][e] : 0;
+    tot += psum[q][e];
+  }
+  // exclusive scan of the experts' totals, held by the first 256 threads
+  // (every thread takes part in the barriers)
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int v = (part == 0 && e < E) ? tot : 0;
+  const int c = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int u = __shfl_up(v, o, 64);
     if (lane >= o) v += u;
   }
-  if (lane == 63) wsum[w] = v;
+  if (part == 0 && lane == 63) wsum[w] = v;
   __syncthreads();
-  int base = 0;
-  for (int i = 0; i < w; ++i) base += wsum[i];
-  const int excl = base + v - tot;
+  if (part == 0) {
+    int base = 0;
+    for (int i = 0; i < w; ++i) base += wsum[i];
+    const int excl = base + v - c;
+    if (e < E) {
+      counts[e] = tot;
+      offsets[e] = excl;
+      eoff[e] = excl;
+    }
+    if (e == E - 1) offsets[E] = excl + tot;
+  }
+  __syncthreads();
   if (e < E) {
-    counts[e] = tot;
-    offsets[e] = excl;
-    for (int c0 = 0; c0 < chunks; c0 += kScanBatch) {
+    int run = eoff[e] + before;
+    for (int c0 = c_lo; c0 < c_hi; c0 += kScanBatch) {
       int v[kScanBatch];
 #pragma unroll
-      for (int j = 0; j < kScanBatch; ++j)
-        v[j] = c0 + j < chunks ? cc[static_cast<int64_t>(c0 + j) * E + e] : 0;
+      for (int j = 0; j < kScanBatch; ++j) v[j] = c0 + j < c_hi ? cc[static_cast<int64_t>(c0 + j) * E + e] : 0;
 #pragma unroll
-      for (int j = 0; j < kScanBatch; ++j)
-        if (c0 + j < chunks) cc[static_cast<int64_t>(c0 + j) * E + e] = v[j] + excl;
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (c0 + j < c_hi) cc[static_cast<int64_t>(c0 + j) * E + e] = run;   // first row of the chunk in e's group
+        run += v[j];
+      }
     }
   }
-  if (e == E - 1) offsets[E] = excl + tot;
 }
 
 // One workgroup of 4 waves per chunk; wave w takes the chunk's pairs
@@ -304,7 +329,7 @@ extern "C" moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_
                        counts, offsets, perm, inv_perm);
   } else {
     hipLaunchKernelGGL(hist_kernel, dim3(chunks), dim3(256), 0, st, topk_ids, static_cast<int>(P), E, cc);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, st, cc, chunks, E, counts, offsets);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256 * kScanParts), 0, st, cc, chunks, E, counts, offsets);
     hipLaunchKernelGGL(scatter_kernel, dim3(chunks), dim3(64 * kScatterWaves), 0, st, topk_ids, static_cast<int>(P), E, nbits,
                        cc, perm, inv_perm);
   }
