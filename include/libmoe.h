@@ -192,7 +192,8 @@ MOE_API moe_status moe_grouped_gemm_down(const void* h, const void* w_down,
  *   y_perm [T*k][d], y_shared [T][d] or NULL, y [T][d]  (dtype)
  *   inv_perm [T*k] int32, topk_w [T][k] fp32
  * A negative inv_perm entry (a pair handled by another expert-parallel
- * share) adds nothing; the others are clamped to [0, T*k).
+ * share) adds nothing and no y_perm row is read for it, so rows that no
+ * call wrote may hold anything; the others are clamped to [0, T*k).
  */
 MOE_API moe_status moe_unpermute_combine(const void* y_perm, const int32_t* inv_perm,
                                  const float* topk_w, const void* y_shared,

@@ -104,10 +104,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   for (int j = 0; j < KR; ++j) {
     if (KT == 0 && j >= kk) break;
     int r = inv[static_cast<int64_t>(t) * kk + j];
-    // a negative entry marks a pair handled elsewhere: it adds nothing
+    // a negative entry marks a pair handled elsewhere: no row of y_perm is
+    // read for it (y_perm may hold no written row at all), it adds zero
     wt[j] = r < 0 ? 0.0f : w[static_cast<int64_t>(t) * kk + j];
-    rows[j] = r < 0 ? 0 : (r >= P ? P - 1 : r);
+    rows[j] = r < 0 ? -1 : (r >= P ? P - 1 : r);
   }
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
   const uint4* ysr = ys ? ys + static_cast<int64_t>(t) * row_chunks : nullptr;
   uint4* yr = y + static_cast<int64_t>(t) * row_chunks;
   if (KT > 0) {
@@ -117,8 +119,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
       uint4 v0[KR], v1[KR], s0{}, s1{};
 #pragma unroll
       for (int j = 0; j < KR; ++j) {
-        v0[j] = load16<NT>(yp + static_cast<int64_t>(rows[j]) * row_chunks + c0);
-        v1[j] = load16<NT>(yp + static_cast<int64_t>(rows[j]) * row_chunks + c1);
+        v0[j] = rows[j] < 0 ? zero : load16<NT>(yp + static_cast<int64_t>(rows[j]) * row_chunks + c0);
+        v1[j] = rows[j] < 0 ? zero : load16<NT>(yp + static_cast<int64_t>(rows[j]) * row_chunks + c1);
       }
       if (ysr) {
         s0 = ysr[c0];
@@ -143,7 +145,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 #pragma unroll
       for (int j = 0; j < KR; ++j) {
         if (j >= kk) break;
-        add_scaled<BF16>(acc, load16<NT>(yp + static_cast<int64_t>(rows[j]) * row_chunks + c), wt[j]);
+        add_scaled<BF16>(acc, rows[j] < 0 ? zero : load16<NT>(yp + static_cast<int64_t>(rows[j]) * row_chunks + c),
+                         wt[j]);
       }
       if (ysr) add_plain<BF16>(acc, ysr[c]);
       store16<NT>(yr + c, pack_out<BF16>(acc));

@@ -27,9 +27,9 @@ moe_status decode_bf16_logits(const void* x, const void* w_router, const float* 
 //  - T*E <= kTinyRouteItems (d <= 8192): one wave per (expert row, few
 //    tokens), every load issued up front;
 //  - E <= kStreamRouteExperts or T <= kStreamRouteTokens: the streaming
-//    split-K kernel with the tokens split into blocks of 16 (32 once that
-//    makes at least kStreamRouteBlocks workgroups), one workgroup per
-//    (16 experts, token block);
+//    split-K kernel with the tokens split into blocks of 16 (32 once
+//    16-token blocks would make at least kStreamRouteBlocks workgroups),
+//    one workgroup per (16 experts, token block);
 //  - above: the tiled MFMA GEMM, which reuses tokens across 128 experts.
 constexpr int64_t kTinyRouteItems = 8192;
 constexpr int kStreamRouteExperts = 64;

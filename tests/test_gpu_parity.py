@@ -350,6 +350,37 @@ def test_combine_streaming(gpu, T, d, k, shared):
     U.assert_close(U.host_values(y), ref, "bf16", f"T={T} k={k} y")
 
 
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T,k,held", [(300, 4, 0.3), (257, 3, 0.5), (64, 8, 0.0), (40, 2, 1.0)])
+def test_combine_masked_pairs_read_no_row(gpu, T, k, held, dtype):
+    """Pairs handled by another expert-parallel share (inv_perm -1) add
+    nothing and read no row of y_perm: the rows that no held pair owns are
+    NaN here (with held = 0 no row at all was written) and the output stays
+    the sum over the held pairs.  k = 3 runs the any-k loop."""
+    rng = np.random.default_rng(T * 10 + k)
+    d = 512
+    P = T * k
+    mask = rng.random(P) < held
+    n = int(mask.sum())
+    inv = np.full(P, -1, np.int64)
+    inv[mask] = rng.permutation(n)
+    yp = np.full((P, d), np.nan)
+    yp[:n] = W.values(W.gen_matrix((n, d), seed=T + 1, dtype=dtype), dtype) if n else 0.0
+    ys = W.values(W.gen_matrix((T, d), seed=T + 2, dtype=dtype), dtype)
+    w = np.asarray(W.gen_matrix((T, k), seed=T + 3, dtype="f32"), np.float32)
+    tdt = U.torch_dtype(dtype)
+    y = torch.empty(T, d, dtype=tdt, device=gpu)
+    B().unpermute_combine(torch.from_numpy(yp).to(tdt).to(gpu), _i32(inv), _f32(w),
+                          torch.from_numpy(ys).to(tdt).to(gpu), y)
+    torch.cuda.synchronize()
+    # oracle on the held pairs only: masked pairs point at an appended zero row
+    yz = np.vstack([yp[:n], np.zeros((1, d))])
+    ref = O.unpermute_combine(yz, np.where(inv < 0, n, inv), w, ys)
+    got = U.host_values(y)
+    assert np.isfinite(got).all()
+    U.assert_close(got, ref, dtype, f"T={T} k={k} held={n}/{P} y")
+
 # ------------------------------------------------------------ whole layer
 
 def _layer_ref(wl, inp, x=None):
