@@ -78,6 +78,24 @@ def gateup_bytes(wl, active: int) -> float:
     return b * (2.0 * wl.f * wl.d * active + wl.P * wl.d + wl.P * wl.f)
 
 
+def tile_work(wl, counts) -> dict:
+    """MFMA work the grouped tile kernels issue, as a multiple of the
+    algorithmic work of each routed projection.  Rows are covered in 32-row
+    fragments (a fragment holding no row of its expert is skipped), columns
+    in whole output tiles (128 SwiGLU outputs for gate/up, 256 for down).
+    Padding each expert to whole 256-row tiles is given for comparison."""
+    c = np.asarray(counts, np.int64)
+    c = c[c > 0]
+    P = int(c.sum())
+    if P == 0:
+        return {"gateup": None, "down": None, "rows_at_256_row_tiles": None}
+    r32 = int((-(-c // 32) * 32).sum())
+    r256 = int((-(-c // 256) * 256).sum())
+    return {"gateup": r32 / P * (-(-wl.f // 128) * 128) / wl.f,
+            "down": r32 / P * (-(-wl.d // 256) * 256) / wl.d,
+            "rows_at_256_row_tiles": r256 / P}
+
+
 # ------------------------------------------------------------ setup
 
 def kernel_source_hash(kernel: str) -> str:
@@ -522,7 +540,8 @@ def main(argv=None):
                   "mfma_frac": layer_flops(wl) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                   "gbps": layer_bytes(wl, active) / (ms * 1e-3) / 1e9,
                   "hbm_frac": layer_bytes(wl, active) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                  "stage_ms": stage_ms, "wall_s": wall},
+                  "stage_ms": stage_ms, "wall_s": wall,
+                  "mfma_issued_over_algorithmic": None if decode else tile_work(wl, counts)},
         "cpu_baseline": None,
     }
     if not args.no_cpu:

@@ -38,3 +38,13 @@ def test_gateup_counts():
 def test_multi_gpu_request_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_tile_work():
+    wl = W.get("c2")
+    # 1000 rows -> 1024 at 32-row fragments and at 256-row tiles; 40 -> 64 and 256; 0 rows: no tiles
+    tw = bench.tile_work(wl, [1000, 40, 0])
+    assert tw["gateup"] == tw["down"] == 1088 / 1040            # f and d fill whole output tiles
+    assert tw["rows_at_256_row_tiles"] == 1280 / 1040
+    assert bench.tile_work(wl, [256, 512])["gateup"] == 1.0
+    assert bench.tile_work(wl, [0, 0])["down"] is None
