@@ -296,6 +296,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   constexpr int LDS_UNITS = 3 * WSTG + 2 * XSTG;
   static_assert(LDS_UNITS * 16 <= 160 * 1024, "LDS");
   static_assert(SP >= 1 && SP <= KS && LPS % SP == 0, "DMA spread");
+  static_assert(RPI * WN == 32 && LX == FM, "token load instruction i fills token fragment i of the wave's row block");
 
   __shared__ u32x4 lds[LDS_UNITS];
 
@@ -342,14 +343,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase), 0, arecords, kBufFlags);
 
   // Load instruction i of this wave fills RPI rows of a stage: the first LX
-  // instructions token rows, the rest weight rows.  Lane t -> row +t/CH,
-  // LDS slot t%CH, global chunk (t%CH) ^ swz(row).
+  // instructions token rows of the wave's own row block (instruction i
+  // into token fragment i, so the waves that read a fragment are the ones
+  // that load it), the rest weight rows.  Lane t -> row +t/CH, LDS slot
+  // t%CH, global chunk (t%CH) ^ swz(row).
   int voff[LPS];
   int dst[LPS];
 #pragma unroll
   for (int i = 0; i < LPS; ++i) {
     const bool tok = i < LX;
-    const int row0 = RPI * (wave + NW * (tok ? i : i - LX));
+    const int row0 = tok ? wm * TM + RPI * (wn + WN * i) : RPI * (wave + NW * (i - LX));
     const int r = row0 + lane / CH;
     const int c = (lane % CH) ^ swz<CH>(r);
     int64_t off;
@@ -409,11 +412,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   for (int i = LX; i < LPS; ++i) MOE_DTL_DMA(i, 1, (1 < last ? 1 : last), 0, 0);
   int cw = 0, cx = 0;                           // weight and token buffers of stage kt
   // Part p < SP of the loads of one stage (tokens first), issued after the
-  // fragment reads of K slice p.
-#define MOE_DTL_PART(p_)                                                                \
+  // fragment reads of K slice p.  Token fragments at or past NF_ are never
+  // read by the waves that load them, so their loads are left out.
+#define MOE_DTL_PART(p_, NF_)                                                           \
   if ((p_) < SP) {                                                                      \
     _Pragma("unroll") for (int i = (p_) * (LPS / SP); i < ((p_) + 1) * (LPS / SP); ++i) \
-      MOE_DTL_DMA(i, nbw, kw, nbx, kx);                                                 \
+      if (i >= LX || i < (NF_)) MOE_DTL_DMA(i, nbw, kw, nbx, kx);                       \
   }
   // All KS slices of one stage, the reads of slice ks+1 in flight during the
   // MFMAs of slice ks, the stage's loads spread over its first SP slices.
@@ -423,14 +427,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
     const u32x4* sx_ = lds + 3 * WSTG + cx * XSTG;                                      \
     bf16x8 wf0[FN], tf0[FM], wf1[FN], tf1[FM];                                          \
     MOE_DTL_FRAGS(wf0, tf0, sw_, sx_, 0, NF_);                                          \
-    MOE_DTL_PART(0);                                                                    \
+    MOE_DTL_PART(0, NF_);                                                               \
     _Pragma("unroll") for (int ks = 0; ks < KS; ks += 2) {                              \
       MOE_DTL_FRAGS(wf1, tf1, sw_, sx_, ks + 1, NF_);                                   \
-      MOE_DTL_PART(ks + 1);                                                             \
+      MOE_DTL_PART(ks + 1, NF_);                                                        \
       MOE_MFMAS(wf0, tf0, NF_);                                                     \
       if (ks + 2 < KS) {                                                                \
         MOE_DTL_FRAGS(wf0, tf0, sw_, sx_, ks + 2, NF_);                                 \
-        MOE_DTL_PART(ks + 2);                                                           \
+        MOE_DTL_PART(ks + 2, NF_);                                                      \
       }                                                                                 \
       MOE_MFMAS(wf1, tf1, NF_);                                                     \
     }                                                                                   \
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
       MOE_DTL_COMPUTE((NF_));                                                           \
       sched_stage<FN + (NF_), FN * ((NF_) > 0 ? (NF_) : 1), KS>();                \
     } else {                                                                            \
-      _Pragma("unroll") for (int i = 0; i < LPS; ++i) MOE_DTL_DMA(i, nbw, kw, nbx, kx); \
+      _Pragma("unroll") for (int i = LX; i < LPS; ++i) MOE_DTL_DMA(i, nbw, kw, nbx, kx); \
     }                                                                                   \
     cw = cw == 2 ? 0 : cw + 1;                                                          \
     cx ^= 1;                                                                            \
