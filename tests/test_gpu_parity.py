@@ -93,7 +93,10 @@ def test_route(gpu, name):
 # (expert, few tokens) at d <= 4096 and d <= 8192, the streaming kernel with
 # 16- and 32-token blocks, the tile kernel on 32- and 64-token tiles
 ROUTER_PATHS = [(40, 8, 4096, 2), (50, 16, 6144, 4), (300, 40, 1024, 4), (8192, 64, 256, 8), (1100, 96, 512, 6),
-                (1030, 8, 320, 2), (16384, 128, 256, 8)]
+                (1030, 8, 320, 2), (16384, 128, 256, 8),
+                # one or two 64-wide K stages on each path: one wave per expert row,
+                # split-K streaming, both flat tile shapes
+                (40, 8, 64, 2), (2000, 32, 64, 4), (2048, 128, 64, 8), (8192, 256, 64, 8), (1500, 256, 128, 8)]
 
 
 @pytest.mark.parametrize("T,E,d,k", ROUTER_PATHS)
@@ -248,6 +251,29 @@ def test_down_many_tiles(gpu, T, E, k, K, N):
     torch.cuda.synchronize()
     ref = O.grouped_down(W.values(h, "bf16"), W.values(dn, "bf16"), offsets)
     U.assert_close(U.host_values(y), ref, "bf16", f"T={T} E={E} K={K} N={N} Y_perm")
+
+
+@pytest.mark.parametrize("decode", [False, True], ids=["grouped", "decode"])
+@pytest.mark.parametrize("rows,E,K,N", [(300, 4, 64, 64), (300, 4, 128, 192), (40, 16, 64, 320),
+                                        (24, 16, 128, 64), (112, 16, 64, 192)])
+def test_short_k(gpu, rows, E, K, N, decode):
+    """K of one or two 64-wide stages (the tile kernel's prologue then
+    loads past the last stage, clamped) in every form: the tile kernel
+    (grouped, and decode with many rows per expert), the split-K MFMA form
+    (40 rows over 16 experts: some waves get no K step) and the vector-ALU
+    form (24 rows)."""
+    offsets = _skewed_offsets(E, rows, seed=K + N)
+    xs = W.gen_matrix((rows, K), seed=K + 41)
+    gu = W.gen_matrix((E, 2 * N, K), seed=K + 42, std=0.1)
+    dn = W.gen_matrix((E, N, K), seed=K + 43, std=0.1)
+    h = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    y = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    B().gateup_swiglu(U.dev_tensor(xs, "bf16"), U.dev_tensor(gu, "bf16"), _i32(offsets), h, decode=decode)
+    B().down(U.dev_tensor(xs, "bf16"), U.dev_tensor(dn, "bf16"), _i32(offsets), y, decode=decode)
+    torch.cuda.synchronize()
+    x64 = W.values(xs, "bf16")
+    U.assert_close(U.host_values(h), O.grouped_gate_up_swiglu(x64, W.values(gu, "bf16"), offsets), "bf16", "H")
+    U.assert_close(U.host_values(y), O.grouped_down(x64, W.values(dn, "bf16"), offsets), "bf16", "Y_perm")
 
 
 # decode calls with at most two rows per expert on average run the
