@@ -27,15 +27,12 @@ constexpr int kMC = 4;        // 16-row token chunks per pass (64 tokens)
 
 typedef __attribute__((address_space(1))) const u32x4 gu4;
 
-// token rows: reused by every weight tile of the expert, so cached loads
+// 16-byte load of token rows and weight rows alike.  Token rows are reused
+// by every weight tile of the expert.  Each weight load instruction touches
+// whole 128-byte lines of its 16 rows (every other 16 bytes); the other step
+// of the pair reads the rest from L2, so weights use cached loads too
+// (non-temporal weight loads measured about 10% slower).
 __device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *(const gu4*)p);
-}
-
-// weight rows: cached loads.  Each load instruction touches whole 128-byte
-// lines of its 16 rows (every other 16 bytes); the other step of the pair
-// reads the rest from L2.  Non-temporal loads measured about 10% slower.
-__device__ __forceinline__ bf16x8 ld8_stream(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *(const gu4*)p);
 }
 
@@ -70,8 +67,8 @@ __device__ __forceinline__ void decode_partial(const uint16_t* wg, const uint16_
     for (int u = 0; u < U; ++u) {
       const int su = s + u < s1 ? s + u : s1 - 1;
       const int64_t k0 = step_offset(su);
-      wgf[u] = ld8_stream(wg + k0);
-      if (SWIGLU) wuf[u] = ld8_stream(wu + k0);
+      wgf[u] = ld8(wg + k0);
+      if (SWIGLU) wuf[u] = ld8(wu + k0);
 #pragma unroll
       for (int mc = 0; mc < MC; ++mc) tf[u][mc] = ld8(xr[mc] + k0);
     }
