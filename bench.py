@@ -338,12 +338,16 @@ def summarize_trace(d: str, title: str, command: str, out: str):
     """rocprofv3 --kernel-trace --stats CSV -> a short markdown table."""
     rows = _read_csv(_find(d, "kernel_stats.csv"))
     lines = [f"# {title}", "", "Command:", "", "```", command, "```", "",
-             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+             "Part `layer` is libmoe's kernels.  Part `harness` is the benchmark's own work outside the timed "
+             "steps: weight uploads and read-backs (`copyBuffer`), buffer fills, and the cache-flush read "
+             "between decode steps (`reduce_kernel`).", "",
+             "| kernel | part | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"]
+        part = "layer" if "moe::" in name else "harness"
         if len(name) > 110:
             name = name[:107] + "..."
-        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+        lines.append(f"| `{name}` | {part} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
                      f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.1f} |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
