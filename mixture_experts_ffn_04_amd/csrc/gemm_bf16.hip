@@ -242,7 +242,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const TileLoc&
   for (int c = threadIdx.x; c < BM * NCH; c += NT) {
     const int r = c / NCH;
     const int ch = c - r * NCH;
-    if (r >= nrows) break;                     // rows past the group: never stored (c only grows)
+    if (r >= nrows) break;                     // rows past the tile's rows: never stored (c only grows)
     if (tl.n0 + ch * 8 >= N) continue;          // columns past N (N is a multiple of 64)
     const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * RB + ((ch ^ (r % NCH)) * 16));
     *reinterpret_cast<u32x4*>(C + static_cast<int64_t>(r) * N + ch * 8) = v;
@@ -315,13 +315,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   const int wn = wave % WN;
   const int64_t K = a.K;
   const int64_t N = a.N;
-  // token fragments of this wave holding at least one row of the group
+  // token fragments of this wave holding at least one row of the tile
   const int trows = min(tl.row_end - tl.row0, BM) - wm * TM;
   const int nfm = trows <= 0 ? 0 : min(FM, (trows + 31) / 32);
 
   // Buffer descriptors based at the tile's first weight row and first token
   // row; num_records is the valid extent, so rows past N or past the
-  // expert's last token read as zero (hardware bounds check) and every
+  // tile's last token row read as zero (hardware bounds check) and every
   // per-lane offset stays a small 32-bit byte offset.
   const int64_t rowb = K * 2;                          // bytes per row
   const char* wbase = static_cast<const char*>(a.B) +
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
         off = static_cast<int64_t>(r) * rowb;
       }
     } else if (gather) {
-      // rows past the group's end read row 0 (their results are never stored)
+      // rows past the tile's last row read row 0 (their results are never stored)
       const int grow = tl.row0 + r;
       const int src = grow < tl.row_end ? clamp_off(a.rowmap[grow], static_cast<int>(a.rows) - 1) / a.kdiv : 0;
       off = static_cast<int64_t>(src) * rowb;

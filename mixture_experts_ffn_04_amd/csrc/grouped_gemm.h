@@ -56,7 +56,7 @@ struct GemmArgs {
 struct TileLoc {
   int g;         // group
   int row0;      // first A/C row of the tile
-  int row_end;   // end of the group's rows
+  int row_end;   // end of the tile's rows (inside its group)
   int n0;        // first output column
 };
 
@@ -130,11 +130,19 @@ __device__ __forceinline__ TileLoc tile_coords(const GemmArgs& a, int g, int glo
     mt = r / snr;
     nt = nbf * SN + (r - mt * snr);
   }
+  // Row tile mt takes its share of the group's 32-row fragments: the F
+  // fragments are dealt as evenly as possible over the mt_g row tiles (the
+  // first F % mt_g take one more), so no tile of a ragged group is left
+  // with a sliver of rows that still streams a whole weight tile.
+  const int nf = (ghi - glo + 31) / 32;
+  const int fq = nf / mt_g, fr = nf - fq * mt_g;
+  const int f0 = mt * fq + min(mt, fr);
+  const int f1 = f0 + fq + (mt < fr ? 1 : 0);
   // workgroup-uniform: keep them in scalar registers
   TileLoc tl;
   tl.g = __builtin_amdgcn_readfirstlane(g);
-  tl.row0 = __builtin_amdgcn_readfirstlane(glo + mt * BM);
-  tl.row_end = __builtin_amdgcn_readfirstlane(ghi);
+  tl.row0 = __builtin_amdgcn_readfirstlane(glo + 32 * f0);
+  tl.row_end = __builtin_amdgcn_readfirstlane(min(ghi, glo + 32 * f1));
   tl.n0 = __builtin_amdgcn_readfirstlane(nt * BNO);
   return tl;
 }
