@@ -295,6 +295,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   constexpr int WSTG = BN * CH, XSTG = BM * CH;       // 16-byte units per weight / token stage
   constexpr int LDS_UNITS = 3 * WSTG + 2 * XSTG;
   static_assert(LDS_UNITS * 16 <= 160 * 1024, "LDS");
+  static_assert(locate_scratch_ints(NT) * 4 <= LDS_UNITS * 16, "tile scan scratch fits the stages");
   static_assert(SP >= 1 && SP <= KS && LPS % SP == 0, "DMA spread");
   static_assert(RPI * WN == 32 && LX == FM, "token load instruction i fills token fragment i of the wave's row block");
 
@@ -492,7 +493,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
 template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int SP = 1, int LDS_EPI = 0>
 moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  const int64_t grid = grouped_tile_bound(a.rows, a.G, BM, a.N, BNO);
+  // A launch of fewer than kAdaptRounds rounds of full tiles may pick
+  // smaller row tiles on the device; its grid then covers the smallest.
+  GemmArgs b = a;
+  b.adapt_rows = 0;
+  int64_t grid = grouped_tile_bound(a.rows, a.G, BM, a.N, BNO);
+  if (EPI != EPI_F32B && BM >= 32 * kRowChoices && grid < int64_t(kAdaptRounds) * kComputeUnits) {
+    b.adapt_rows = 1;
+    grid = grouped_tile_bound(a.rows, a.G, BM - 32 * (kRowChoices - 1), a.N, BNO);
+  }
   if (grid <= 0) return MOE_OK;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
   // byte offsets inside one expert's weights must fit the 32-bit descriptor range
@@ -501,7 +510,7 @@ moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
     return MOE_ERR_UNSUPPORTED;
   if (a.rowmap && (a.kdiv < 1 || a.a_rows * a.K * 2 >= (int64_t(1) << 31))) return MOE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, SP, LDS_EPI>), dim3(static_cast<unsigned>(grid)),
-                     dim3(64 * WM * WN), 0, st, a);
+                     dim3(64 * WM * WN), 0, st, b);
   return launch_status();
 }
 

@@ -51,7 +51,15 @@ struct GemmArgs {
   const int32_t* rowmap;
   int kdiv;
   int64_t a_rows;
+  // Set by the launcher, not by callers: the launch is short enough (fewer
+  // than kAdaptRounds rounds of full row tiles) for the tile rows to be
+  // chosen per launch, and its grid covers the smallest choice.
+  int adapt_rows;
 };
+
+constexpr int kComputeUnits = 256;   // MI355X: compute units, one tile workgroup each
+constexpr int kAdaptRounds = 4;
+constexpr int kRowChoices = 4;       // BM, BM - 32, BM - 64, BM - 96 rows per row tile
 
 struct TileLoc {
   int g;         // group
@@ -60,13 +68,64 @@ struct TileLoc {
   int n0;        // first output column
 };
 
+// Rows per row tile.  A launch of a few rounds of tiles leaves most CUs
+// idle in its last round, so with a.adapt_rows set every workgroup picks,
+// from the same offsets and so identically, the tile rows among BM,
+// BM - 32, BM - 64, BM - 96 that minimise (rounds of tiles) x (32-row
+// fragments of the largest tile), ties to more rows.  Measured on 8 experts
+// of ~1024 rows, K = 14336, N = 4096: 192 rows (752 tiles, 2.9 rounds) ran
+// 5% faster than 256 rows (592 tiles, 2.3 rounds); launches of more rounds
+// measured fastest with full 256-row tiles.  Contains one workgroup
+// barrier.  s_red: (kRowChoices + 1) * NT/64 ints of LDS.
+template <int NT, int BM, int BNO>
+__device__ __forceinline__ int tile_rows_for(const GemmArgs& a, int r, int ntiles, int* s_red) {
+  if (BM < 32 * kRowChoices || !a.adapt_rows) return BM;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int v[kRowChoices + 1];
+#pragma unroll
+  for (int c = 0; c < kRowChoices; ++c) v[c] = ((r + BM - 32 * c - 1) / (BM - 32 * c)) * ntiles;
+  v[kRowChoices] = r;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+    for (int c = 0; c < kRowChoices; ++c) v[c] += __shfl_xor(v[c], o, 64);
+    v[kRowChoices] = max(v[kRowChoices], __shfl_xor(v[kRowChoices], o, 64));
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int c = 0; c <= kRowChoices; ++c) s_red[c * (NT / 64) + w] = v[c];
+  }
+  __syncthreads();
+  int tot[kRowChoices + 1];
+#pragma unroll
+  for (int c = 0; c <= kRowChoices; ++c) {
+    tot[c] = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i)
+      tot[c] = c < kRowChoices ? tot[c] + s_red[c * (NT / 64) + i] : max(tot[c], s_red[c * (NT / 64) + i]);
+  }
+  const int maxf = (tot[kRowChoices] + 31) / 32;       // fragments of the largest group
+  int best = BM, best_cost = 0x7fffffff;
+#pragma unroll
+  for (int c = 0; c < kRowChoices; ++c) {
+    const int rows_c = BM - 32 * c;
+    const int cost = ((tot[c] + kComputeUnits - 1) / kComputeUnits) * min(rows_c / 32, maxf);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = rows_c;
+    }
+  }
+  return best;
+}
+
 // Tile counts of the groups and their exclusive scan, for all NT threads:
 // thread t < G gets its group's row range [lo, hi), tile count cnt and the
-// index excl of its first tile; every thread gets the total.  Contains one
-// workgroup barrier.
-// s_wsum: NT/64 ints of LDS.
+// index excl of its first tile; every thread gets the total and the rows
+// per row tile tr.  Contains one or two workgroup barriers.
+// s_wsum: NT/64 ints of LDS; s_red as for tile_rows_for.
 template <int NT, int BM, int BNO>
-__device__ __forceinline__ int scan_tiles(const GemmArgs& a, int& lo, int& hi, int& cnt, int& excl, int* s_wsum) {
+__device__ __forceinline__ int scan_tiles(const GemmArgs& a, int& lo, int& hi, int& cnt, int& excl, int& tr,
+                                          int* s_wsum, int* s_red) {
   static_assert(NT >= kMaxE, "one group per thread");
   const int t = threadIdx.x;
   const int rows = static_cast<int>(a.rows);
@@ -78,8 +137,9 @@ __device__ __forceinline__ int scan_tiles(const GemmArgs& a, int& lo, int& hi, i
     lo = a.off ? clamp_off(a.off[t], rows) : 0;
     hi = a.off ? clamp_off(a.off[t + 1], rows) : rows;
     if (hi < lo) hi = lo;
-    cnt = ((hi - lo + BM - 1) / BM) * ntiles;
   }
+  tr = tile_rows_for<NT, BM, BNO>(a, hi - lo, ntiles, s_red);
+  cnt = ((hi - lo + tr - 1) / tr) * ntiles;
   const int lane = t & 63, w = t >> 6;
   int v = cnt;
 #pragma unroll
@@ -113,10 +173,10 @@ __device__ __forceinline__ int tile_order(int bid, int total) {
 // Tile coordinates of logical tile `local` of group g (rows [glo, ghi)):
 // column blocks of SN tiles, row tiles within a block, a narrower last block
 // when SN does not divide the column tiles.
-template <int BM, int BNO, int SN>
-__device__ __forceinline__ TileLoc tile_coords(const GemmArgs& a, int g, int glo, int ghi, int local) {
+template <int BNO, int SN>
+__device__ __forceinline__ TileLoc tile_coords(const GemmArgs& a, int g, int glo, int ghi, int local, int tr) {
   const int ntiles = static_cast<int>((a.N + BNO - 1) / BNO);
-  const int mt_g = (ghi - glo + BM - 1) / BM;
+  const int mt_g = (ghi - glo + tr - 1) / tr;
   const int nbf = ntiles / SN;
   int mt, nt;
   if (local < nbf * mt_g * SN) {
@@ -147,16 +207,20 @@ __device__ __forceinline__ TileLoc tile_coords(const GemmArgs& a, int g, int glo
   return tl;
 }
 
+// LDS scratch of locate_tile, in ints.
+constexpr int locate_scratch_ints(int NT) { return NT / 64 * (kRowChoices + 2) + 4; }
+
 // Locate this workgroup's tile.  Must be called by all NT threads; returns
 // false (for the whole workgroup) when the block id is past the last tile.
 //   BM     rows per tile, BNO output columns per tile, SN column-block width
-//   scratch  NT/64 + 4 ints of LDS, free again once this returns and every
-//            thread has passed one more workgroup barrier
+//   scratch  locate_scratch_ints(NT) ints of LDS, free again once this
+//            returns and every thread has passed one more workgroup barrier
 template <int NT, int BM, int BNO, int SN>
 __device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl, int* scratch) {
-  int* s_hit = scratch + NT / 64;
-  int lo, hi, cnt, excl;
-  const int total = scan_tiles<NT, BM, BNO>(a, lo, hi, cnt, excl, scratch);
+  int* s_red = scratch + NT / 64;
+  int* s_hit = s_red + NT / 64 * (kRowChoices + 1);
+  int lo, hi, cnt, excl, tr;
+  const int total = scan_tiles<NT, BM, BNO>(a, lo, hi, cnt, excl, tr, scratch, s_red);
   const int bid = static_cast<int>(blockIdx.x);
   if (bid >= total) return false;     // uniform: total is the same in every thread
   const int L = tile_order(bid, total);
@@ -167,14 +231,14 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl, int*
     s_hit[3] = excl;
   }
   __syncthreads();
-  tl = tile_coords<BM, BNO, SN>(a, s_hit[0], s_hit[1], s_hit[2], L - s_hit[3]);
+  tl = tile_coords<BNO, SN>(a, s_hit[0], s_hit[1], s_hit[2], L - s_hit[3], tr);
   return true;
 }
 
 // The same with scratch of its own.
 template <int NT, int BM, int BNO, int SN>
 __device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl) {
-  __shared__ int scratch[NT / 64 + 4];
+  __shared__ int scratch[locate_scratch_ints(NT)];
   return locate_tile<NT, BM, BNO, SN>(a, tl, scratch);
 }
 
