@@ -334,20 +334,39 @@ def _find(d, suffix):
     raise FileNotFoundError(f"no *{suffix} under {d}")
 
 
-def summarize_trace(d: str, title: str, command: str, out: str):
-    """rocprofv3 --kernel-trace --stats CSV -> a short markdown table."""
+def summarize_trace(d: str, title: str, command: str, out: str, log: str = None):
+    """rocprofv3 --kernel-trace --stats CSV -> a short markdown table, with the
+    median of each kernel's dispatch durations from the per-dispatch trace.
+    With `log` (the profiled bench.py run's output), the bench's own figure
+    for its roofline kernel from the same run is quoted as well."""
     rows = _read_csv(_find(d, "kernel_stats.csv"))
+    durs = {}
+    for r in _read_csv(_find(d, "kernel_trace.csv")):
+        durs.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     lines = [f"# {title}", "", "Command:", "", "```", command, "```", "",
              "Part `layer` is libmoe's kernels.  Part `harness` is the benchmark's own work outside the timed "
              "steps: weight uploads and read-backs (`copyBuffer`), buffer fills, and the cache-flush read "
-             "between decode steps (`reduce_kernel`).", "",
-             "| kernel | part | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|---|"]
+             "between decode steps (`reduce_kernel`).  The averages include the warm-up calls and the "
+             "untimed per-stage pass; the medians are over all dispatches.", ""]
+    if log:
+        rec = None
+        for line in open(log, errors="replace"):
+            if line.startswith("{") and '"roofline"' in line:
+                rec = json.loads(line)
+        if rec is not None:
+            r = rec["roofline"]
+            lines += [f"bench.py in the same run: `{r['kernel']}` {r['kernel_ms'] * 1e3:.1f} us per call "
+                      f"(HIP events on the launch stream over the timed steps), {rec['ms_per_step']:.3f} ms per "
+                      f"step, {rec['value']:.4g} {rec['unit']}.", ""]
+    lines += ["| kernel | part | calls | avg us | median us | min us | max us | total % |",
+              "|---|---|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"]
         part = "layer" if "moe::" in name else "harness"
+        med = float(np.median(durs[name])) / 1e3 if name in durs else float("nan")
         if len(name) > 110:
             name = name[:107] + "..."
-        lines.append(f"| `{name}` | {part} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+        lines.append(f"| `{name}` | {part} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | {med:.2f} | "
                      f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.1f} |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -419,7 +438,8 @@ def main(argv=None):
     ap.add_argument("--copy-probe", type=int, default=0, help="run a plain copy of this many bytes and exit")
     ap.add_argument("--clock-probe", nargs=4, metavar=("WORKLOAD", "SECONDS", "COMMAND", "OUT"),
                     help="gate/up and hipBLASLt back to back while sampling clocks and power; write OUT")
-    ap.add_argument("--summarize-trace", nargs=4, metavar=("DIR", "TITLE", "COMMAND", "OUT"))
+    ap.add_argument("--summarize-trace", nargs="+", metavar="ARG",
+                    help="DIR TITLE COMMAND OUT [LOG]: summarise a rocprofv3 kernel trace")
     ap.add_argument("--summarize-traffic", nargs=11,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "MATCH", "KERNEL",
                              "WORKLOAD", "COPY_BYTES", "COMMAND", "OUT_MD", "OUT_JSON"))
