@@ -433,6 +433,45 @@ def test_layer(gpu, name, mode):
     U.assert_close(U.host_values(y)[same], out["y"][same], wl.dtype, f"{name} layer")
 
 
+
+def _random_workload(i):
+    """A seeded layer shape off the named workloads' grid: any expert count up
+    to 256, k up to 8, d and f any multiple of 64 up to 768, T up to 1500,
+    either score, with or without a Zipf bias and a shared expert."""
+    rng = np.random.default_rng(1000 + i)
+    E = int(rng.choice([1, 2, 5, 8, 16, 33, 64, 128, 256]))
+    k = int(rng.integers(1, min(8, E) + 1))
+    d = 64 * int(rng.integers(1, 13))
+    f = 64 * int(rng.integers(1, 13))
+    T = int(rng.integers(1, 1500))
+    score = "sigmoid" if rng.random() < 0.3 else "softmax"
+    zipf = None if rng.random() < 0.5 else float(rng.choice([0.8, 1.2]))
+    fs = 64 * int(rng.integers(1, 6)) if rng.random() < 0.3 else 0
+    return W.Workload(f"rand{i}", T, d, f, E, k, score, "bf16", zipf_s=zipf, f_shared=fs, seed=5000 + i,
+                      router_std=0.02 * (2048 / d) ** 0.5)
+
+
+@pytest.mark.parametrize("mode", ["grouped", "decode"])
+@pytest.mark.parametrize("i", range(16))
+def test_layer_random_shapes(gpu, i, mode):
+    """The whole layer on seeded random shapes against the oracle.  Short
+    launches like these pick their rows per row tile on the device, so this
+    also covers that choice on shapes no named workload has."""
+    wl = _random_workload(i)
+    if mode == "decode" and wl.P > 1024:
+        pytest.skip("decode calls take at most 1024 rows")
+    x = W.gen_x(wl)
+    wr, bias = W.gen_router(wl)
+    gu, dn = W.gen_all_experts(wl)
+    inp = dict(x=x, wr=wr, bias=bias, gu=gu, dn=dn, shared=W.gen_shared(wl))
+    layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score, mode=mode)
+    y = layer.forward(U.dev_tensor(x, wl.dtype))
+    torch.cuda.synchronize()
+    x64, wr64, out = _layer_ref(wl, inp)
+    same = U.routing_agreement(layer.ids.cpu().numpy(), out["logits"], x64, wr64, bias, wl.k)
+    U.assert_close(U.host_values(y)[same], out["y"][same], wl.dtype,
+                   f"{wl.name} T={wl.T} d={wl.d} f={wl.f} E={wl.E} k={wl.k} {wl.score} shared={wl.f_shared}")
+
 # ------------------------------------------------------- expert-parallel share
 
 def test_localize_ids(gpu):
