@@ -5,6 +5,8 @@
 namespace moe {
 moe_status gemm_bf16_gateup_swiglu(const GemmArgs& a, hipStream_t st);
 moe_status gemm_bf16_down(const GemmArgs& a, hipStream_t st);
+moe_status gemm_bf16_gateup_swiglu_few(const GemmArgs& a, hipStream_t st);
+moe_status gemm_bf16_down_few(const GemmArgs& a, hipStream_t st);
 moe_status gemm_f32_gateup_swiglu(const GemmArgs& a, hipStream_t st);
 moe_status gemm_f32_down(const GemmArgs& a, hipStream_t st);
 moe_status decode_bf16(bool swiglu, const void* A, const void* B, const int32_t* off, int64_t rows, int64_t K,
@@ -14,10 +16,11 @@ namespace {
 
 constexpr int64_t kDecodeMaxRows = 1024;
 // Decode calls with several rows per expert on average run the grouped tile
-// kernel: with 3+ (gate/up) or 6+ (down) rows per expert its loads of whole
-// 128-byte row pieces into LDS stream the weights faster than the split-K
-// MFMA form (measured on 32 experts of 2880 x 2880: gate/up at T=24, 4 rows
-// per expert, 181 vs 194 us; down at T=64, 8 rows, 111 vs 122 us).
+// kernel (in its 64-token shapes): with 3+ (gate/up) or 6+ (down) rows per
+// expert its loads of whole 128-byte row pieces into LDS stream the weights
+// faster than the split-K MFMA form (measured on 32 experts of 2880 x 2880:
+// gate/up at T=24, 3 rows per expert, 181 vs 194 us; down at T=48, 6 rows,
+// 104 vs 114 us, and level at 4 rows).
 constexpr int64_t kDecodeTileGateUpRows = 3;   // per expert
 constexpr int64_t kDecodeTileDownRows = 6;
 
@@ -111,7 +114,7 @@ extern "C" moe_status moe_decode_gateup_swiglu(const void* x_perm, const void* w
   if (dtype == MOE_F32)
     return gemm_f32_gateup_swiglu(proj_args(x_perm, w_gate_up, offsets, rows, d, f, E, h), as_stream(stream));
   if (rows >= kDecodeTileGateUpRows * E)
-    return gemm_bf16_gateup_swiglu(proj_args(x_perm, w_gate_up, offsets, rows, d, f, E, h), as_stream(stream));
+    return gemm_bf16_gateup_swiglu_few(proj_args(x_perm, w_gate_up, offsets, rows, d, f, E, h), as_stream(stream));
   return decode_bf16(true, x_perm, w_gate_up, offsets, rows, d, f, E, h, as_stream(stream));
 }
 
@@ -130,7 +133,7 @@ extern "C" moe_status moe_decode_gateup_swiglu_gather(const void* x, const int32
     a.rowmap = perm;
     a.kdiv = k;
     a.a_rows = rows / k;
-    return gemm_bf16_gateup_swiglu(a, as_stream(stream));
+    return gemm_bf16_gateup_swiglu_few(a, as_stream(stream));
   }
   return decode_bf16(true, x, w_gate_up, offsets, rows, d, f, E, h, as_stream(stream), perm, k);
 }
@@ -143,6 +146,6 @@ extern "C" moe_status moe_decode_down(const void* h, const void* w_down, const i
   if (dtype == MOE_F32)
     return gemm_f32_down(proj_args(h, w_down, offsets, rows, f, d, E, y_perm), as_stream(stream));
   if (rows >= kDecodeTileDownRows * E)
-    return gemm_bf16_down(proj_args(h, w_down, offsets, rows, f, d, E, y_perm), as_stream(stream));
+    return gemm_bf16_down_few(proj_args(h, w_down, offsets, rows, f, d, E, y_perm), as_stream(stream));
   return decode_bf16(false, h, w_down, offsets, rows, f, d, E, y_perm, as_stream(stream));
 }
