@@ -298,6 +298,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   static_assert(locate_scratch_ints(NT) * 4 <= LDS_UNITS * 16, "tile scan scratch fits the stages");
   static_assert(SP >= 1 && SP <= KS && LPS % SP == 0, "DMA spread");
   static_assert(RPI * WN == 32 && LX == FM, "token load instruction i fills token fragment i of the wave's row block");
+  // Fat tiles: an expert's last remainder of up to kFatExtraRows rows shared
+  // out over its other row tiles, BMF = BM + kFatExtraRows rows at most,
+  // with two stages of both operands (three weight stages no longer fit).
+  constexpr bool FAT_OK = BM == 256 && WM == 2 && EPI != EPI_F32B;
+  constexpr int BMF = BM + kFatExtraRows, TMF = BMF / WM, FMF = TMF / 32, LXF = BMF / (RPI * NW), LPF = LB + LXF;
+  constexpr int XSTGF = BMF * CH;
 
   __shared__ u32x4 lds[LDS_UNITS];
 
@@ -338,10 +344,105 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   // through rowmap, the descriptor then spanning all of A.
   const bool gather = a.rowmap != nullptr;
   const char* abase = static_cast<const char*>(a.A) + (gather ? 0 : static_cast<int64_t>(tl.row0) * rowb);
+  const int vrows = tl.row_end - tl.row0;             // at most BM, or BMF for a fat tile
   const int arecords = gather ? static_cast<int>(a.a_rows * rowb)
-                              : static_cast<int>(min(tl.row_end - tl.row0, BM) * rowb);
+                              : static_cast<int>(min(vrows, FAT_OK ? BMF : BM) * rowb);
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, wrecords, kBufFlags);
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase), 0, arecords, kBufFlags);
+
+  if constexpr (FAT_OK) {
+    if (vrows > BM) {
+      static_assert(2 * WSTG + 2 * XSTGF <= LDS_UNITS, "fat tile stages fit");
+      static_assert(!LDS_EPI || LDS_UNITS * 16 >= BMF * BNO * 2, "fat output tile fits the stages");
+      // Token instruction i of a wave fills fragment i of its 160-row block.
+      int voff[LPF];
+      int dst[LPF];
+#pragma unroll
+      for (int i = 0; i < LPF; ++i) {
+        const bool tok = i < LXF;
+        const int row0 = tok ? wm * TMF + RPI * (wn + WN * i) : RPI * (wave + NW * (i - LXF));
+        const int r = row0 + lane / CH;
+        const int c = (lane % CH) ^ swz<CH>(r);
+        int64_t off;
+        if (!tok) {
+          if (EPI == EPI_SWIGLU) {
+            const int half = r / (BN / 2);
+            off = (half * N + tl.n0 + (r - half * (BN / 2))) * rowb;
+          } else {
+            off = static_cast<int64_t>(r) * rowb;
+          }
+        } else if (gather) {
+          const int grow = tl.row0 + r;
+          const int src = grow < tl.row_end ? clamp_off(a.rowmap[grow], static_cast<int>(a.rows) - 1) / a.kdiv : 0;
+          off = static_cast<int64_t>(src) * rowb;
+        } else {
+          off = static_cast<int64_t>(r) * rowb;
+        }
+        voff[i] = static_cast<int>(off) + c * 16;
+        dst[i] = row0 * CH * 16;
+      }
+      const unsigned ldsw = lds_addr_of(lds);
+      const unsigned ldsxf = ldsw + 2u * WSTG * 16u;
+      auto stage_dma = [&](int b, int k) {
+#pragma unroll
+        for (int i = 0; i < LXF; ++i)
+          lds_dma16(ars, voff[i], k * (BK * 2),
+                    __builtin_amdgcn_readfirstlane(ldsxf + static_cast<unsigned>(b) * (XSTGF * 16) + dst[i]));
+#pragma unroll
+        for (int i = LXF; i < LPF; ++i)
+          lds_dma16(wrs, voff[i], k * (BK * 2),
+                    __builtin_amdgcn_readfirstlane(ldsw + static_cast<unsigned>(b) * (WSTG * 16) + dst[i]));
+      };
+      int wrow[FN];
+      weight_frag_rows<EPI, BN, TN, FN>(wn, wrow);
+      const int l32 = lane & 31;
+      const int khalf = lane >> 5;
+      const int sw = swz<CH>(l32);
+      f32x16 acc[FMF][FN];
+#pragma unroll
+      for (int i = 0; i < FMF; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+      const int nk = static_cast<int>(K / BK);
+      const int last = nk - 1;
+      // half 0 is full; half 1 holds more than 96 rows, so 4 or 5 fragments
+      const int nff = min(FMF, (vrows - wm * TMF + 31) / 32);
+      stage_dma(0, 0);
+      // Stage kt in buffers kt & 1: wait for this wave's loads of stage kt,
+      // then the barrier publishes them and frees the buffers of stage kt-1
+      // for stage kt+1's loads.
+#define MOE_FAT_LOOP(NF_)                                                                       \
+      for (int kt = 0; kt < nk; ++kt) {                                                         \
+        wait_stage_barrier<0>();                                                                \
+        stage_dma((kt + 1) & 1, kt + 1 < last ? kt + 1 : last);                                 \
+        const u32x4* sw_ = lds + (kt & 1) * WSTG;                                               \
+        const u32x4* sx_ = lds + 2 * WSTG + (kt & 1) * XSTGF;                                   \
+        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                     \
+          const int c_ = (ks * 2 + khalf) ^ sw;                                                 \
+          bf16x8 wf[FN], tf[FMF];                                                               \
+          _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                                     \
+            wf[fn] = __builtin_bit_cast(bf16x8, sw_[(wrow[fn] + l32) * CH + c_]);               \
+          _Pragma("unroll") for (int fm = 0; fm < (NF_); ++fm)                                  \
+            tf[fm] = __builtin_bit_cast(bf16x8, sx_[(wm * TMF + fm * 32 + l32) * CH + c_]);     \
+          MOE_MFMAS(wf, tf, (NF_));                                                             \
+        }                                                                                       \
+      }
+      if (nff == FMF) {
+        MOE_FAT_LOOP(FMF)
+      } else {
+        MOE_FAT_LOOP(FMF - 1)
+      }
+#undef MOE_FAT_LOOP
+      drain_vm();
+      if (LDS_EPI) {
+        __syncthreads();
+        store_tile_lds<EPI, FMF, FN, TMF, TN, BMF, BNO, NT>(a, tl, acc, wm, wn, l32, khalf, reinterpret_cast<char*>(lds));
+      } else {
+        store_tile<EPI, FMF, FN, TMF, TN>(a, tl, acc, wm, wn, l32, khalf);
+      }
+      return;
+    }
+  }
 
   // Load instruction i of this wave fills RPI rows of a stage: the first LX
   // instructions token rows of the wave's own row block (instruction i
@@ -490,6 +591,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
 
 #undef MOE_MFMAS
 
+// Fat tiles only for K >= kFatMinK.  Measured, outputs bit-identical: gate/up
+// of 8 experts of ~1024 rows at K = 4096 +2.9% (1.630 -> 1.584 ms) and of
+// 256 Zipf-loaded experts at K = 7168 +1%; at K = 2048 (128 Zipf-loaded
+// experts, gate/up; 256 experts, down) flat to 4% slower, where a fat
+// tile's longer critical path and its two-stage pipeline cost more than
+// the remainder tile it replaces.
+constexpr int64_t kFatMinK = 4096;
+
 template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int SP = 1, int LDS_EPI = 0>
 moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
@@ -497,16 +606,19 @@ moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   // smaller row tiles on the device; its grid then covers the smallest.
   GemmArgs b = a;
   b.adapt_rows = 0;
+  b.fat_rows = 0;
   int64_t grid = grouped_tile_bound(a.rows, a.G, BM, a.N, BNO);
   if (EPI != EPI_F32B && BM >= 32 * kRowChoices && grid < int64_t(kAdaptRounds) * kComputeUnits) {
     b.adapt_rows = 1;
     grid = grouped_tile_bound(a.rows, a.G, BM - 32 * (kRowChoices - 1), a.N, BNO);
+  } else if (BM == 256 && WM == 2 && EPI != EPI_F32B && a.K >= kFatMinK) {
+    b.fat_rows = 1;                              // fewer tiles than the bound at BM rows
   }
   if (grid <= 0) return MOE_OK;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
   // byte offsets inside one expert's weights must fit the 32-bit descriptor range
   const int64_t wbytes = ((EPI == EPI_SWIGLU) ? 2 : 1) * a.N * a.K * 2;
-  if (wbytes >= (int64_t(1) << 31) || static_cast<int64_t>(BM) * a.K * 2 >= (int64_t(1) << 31))
+  if (wbytes >= (int64_t(1) << 31) || static_cast<int64_t>(BM + kFatExtraRows) * a.K * 2 >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
   if (a.rowmap && (a.kdiv < 1 || a.a_rows * a.K * 2 >= (int64_t(1) << 31))) return MOE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, SP, LDS_EPI>), dim3(static_cast<unsigned>(grid)),

@@ -55,11 +55,16 @@ struct GemmArgs {
   // than kAdaptRounds rounds of full row tiles) for the tile rows to be
   // chosen per launch, and its grid covers the smallest choice.
   int adapt_rows;
+  // Set by the launcher, not by callers: a group's last remainder of at
+  // most kFatExtraRows rows is shared out over its other row tiles, which
+  // then hold up to BM + kFatExtraRows rows.
+  int fat_rows;
 };
 
 constexpr int kComputeUnits = 256;   // MI355X: compute units, one tile workgroup each
 constexpr int kAdaptRounds = 4;
 constexpr int kRowChoices = 4;       // BM, BM - 32, BM - 64, BM - 96 rows per row tile
+constexpr int kFatExtraRows = 64;
 
 struct TileLoc {
   int g;         // group
@@ -67,6 +72,15 @@ struct TileLoc {
   int row_end;   // end of the tile's rows (inside its group)
   int n0;        // first output column
 };
+
+// Row tiles of a group of r rows at tr rows per tile.  With fat tiles a
+// last remainder of at most kFatExtraRows rows is shared out over the
+// group's other row tiles instead of taking a row tile of its own.
+__device__ __forceinline__ int row_tiles(int r, int tr, int fat) {
+  int m = (r + tr - 1) / tr;
+  if (fat && m > 1 && r - (m - 1) * tr <= kFatExtraRows) --m;
+  return m;
+}
 
 // Rows per row tile.  A launch of a few rounds of tiles leaves most CUs
 // idle in its last round, so with a.adapt_rows set every workgroup picks,
@@ -139,7 +153,7 @@ __device__ __forceinline__ int scan_tiles(const GemmArgs& a, int& lo, int& hi, i
     if (hi < lo) hi = lo;
   }
   tr = tile_rows_for<NT, BM, BNO>(a, hi - lo, ntiles, s_red);
-  cnt = ((hi - lo + tr - 1) / tr) * ntiles;
+  cnt = row_tiles(hi - lo, tr, a.fat_rows) * ntiles;
   const int lane = t & 63, w = t >> 6;
   int v = cnt;
 #pragma unroll
@@ -176,7 +190,7 @@ __device__ __forceinline__ int tile_order(int bid, int total) {
 template <int BNO, int SN>
 __device__ __forceinline__ TileLoc tile_coords(const GemmArgs& a, int g, int glo, int ghi, int local, int tr) {
   const int ntiles = static_cast<int>((a.N + BNO - 1) / BNO);
-  const int mt_g = (ghi - glo + tr - 1) / tr;
+  const int mt_g = row_tiles(ghi - glo, tr, a.fat_rows);
   const int nbf = ntiles / SN;
   int mt, nt;
   if (local < nbf * mt_g * SN) {
