@@ -8,7 +8,9 @@
 // are K-contiguous rows, so a fragment (32 rows x 16 K) is one ds_read_b128
 // per lane.  Buffer loads go straight into LDS (no register staging); three
 // weight stages and two token stages of 64 K-elements, so weight loads run
-// two stages and token loads one stage ahead of the MFMAs.
+// two stages and token loads one stage ahead of the MFMAs (tiles of more
+// than 256 token rows, which absorb an expert's small remainder, keep two
+// stages of each).
 //
 // LDS layout: tile row r holds the 64 elements of one weight or token row
 // as 8 16-byte chunks; chunk c is stored at position c ^ swz(r).  gfx950
