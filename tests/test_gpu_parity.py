@@ -276,6 +276,53 @@ def test_short_k(gpu, rows, E, K, N, decode):
     U.assert_close(U.host_values(y), O.grouped_down(x64, W.values(dn, "bf16"), offsets), "bf16", "Y_perm")
 
 
+@pytest.mark.parametrize("kind", ["gateup", "gateup_gather", "down"])
+def test_fat_tiles(gpu, kind):
+    """K >= 4096 in a launch of more than 4 rounds of tiles (256 experts,
+    most of them empty): an expert whose rows overflow its 256-row tiles by
+    at most 64 rows shares the remainder out over its other row tiles (tiles
+    of up to 320 rows on their own two-stage loop).  Active experts of 300
+    rows (one fat tile), 530 and 1030 rows (remainders 18 and 6), exactly
+    256 and 100 rows, against the oracle on every row."""
+    E, K = 256, 4096
+    N = 1024 if kind == "down" else 512           # > 4 rounds of tiles at 256 rows
+    active = {3: 300, 17: 530, 100: 1030, 200: 256, 255: 100}
+    counts = np.zeros(E, np.int64)
+    for e, c in active.items():
+        counts[e] = c
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(counts.sum())
+    ids = sorted(active)
+    sub_off = np.concatenate([[0], np.cumsum([active[e] for e in ids])]).astype(np.int32)
+    wrows = N if kind == "down" else 2 * N
+    wsub = W.gen_matrix((len(ids), wrows, K), seed=73, std=0.02)
+    wdev = torch.zeros(E, wrows, K, dtype=torch.bfloat16, device=gpu)   # experts without rows: never read
+    wsub_dev = U.dev_tensor(wsub, "bf16")
+    for i, e in enumerate(ids):
+        wdev[e].copy_(wsub_dev[i])
+    out = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    if kind == "down":
+        hs = W.gen_matrix((rows, K), seed=71, std=0.5)
+        B().down(U.dev_tensor(hs, "bf16"), wdev, _i32(offsets), out)
+        torch.cuda.synchronize()
+        ref = O.grouped_down(W.values(hs, "bf16"), W.values(wsub, "bf16"), sub_off)
+        U.assert_close(U.host_values(out), ref, "bf16", "Y_perm (fat tiles)")
+        return
+    if kind == "gateup":
+        xs = W.gen_matrix((rows, K), seed=74)
+        B().gateup_swiglu(U.dev_tensor(xs, "bf16"), wdev, _i32(offsets), out)
+        x_rows = W.values(xs, "bf16")
+    else:
+        k = 2
+        xs = W.gen_matrix((rows // k, K), seed=75)
+        perm = np.random.default_rng(76).permutation(rows)
+        B().gateup_swiglu_gather(U.dev_tensor(xs, "bf16"), _i32(perm), k, wdev, _i32(offsets), out)
+        x_rows = W.values(xs, "bf16")[perm // k]
+    torch.cuda.synchronize()
+    ref = O.grouped_gate_up_swiglu(x_rows, W.values(wsub, "bf16"), sub_off)
+    U.assert_close(U.host_values(out), ref, "bf16", f"H (fat tiles, {kind})")
+
+
 # decode calls with at most two rows per expert on average run the
 # vector-ALU form: K up to 2048, 3072 and 4096 (its three register
 # layouts), one expert holding many of the rows, empty experts
