@@ -594,11 +594,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
 #undef MOE_MFMAS
 
 // Fat tiles only for K >= kFatMinK.  Measured, outputs bit-identical: gate/up
-// of 8 experts of ~1024 rows at K = 4096 +2.9% (1.630 -> 1.584 ms) and of
-// 256 Zipf-loaded experts at K = 7168 +1%; at K = 2048 (128 Zipf-loaded
-// experts, gate/up; 256 experts, down) flat to 4% slower, where a fat
-// tile's longer critical path and its two-stage pipeline cost more than
-// the remainder tile it replaces.
+// of 8 experts of ~1024 rows at K = 4096 +2.9% (1.630 -> 1.584 ms), their
+// down projection at K = 14336 +2% over the best smaller row tiles, and
+// gate/up of 256 Zipf-loaded experts at K = 7168 +1%; at K = 2048 (128
+// Zipf-loaded experts, gate/up; 256 experts, down) flat to 4% slower, where
+// a fat tile's longer critical path and its two-stage pipeline cost more
+// than the remainder tile it replaces.
 constexpr int64_t kFatMinK = 4096;
 
 template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int SP = 1, int LDS_EPI = 0>
@@ -608,13 +609,11 @@ moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   // smaller row tiles on the device; its grid then covers the smallest.
   GemmArgs b = a;
   b.adapt_rows = 0;
-  b.fat_rows = 0;
+  b.fat_rows = (BM == 256 && WM == 2 && EPI != EPI_F32B && a.K >= kFatMinK) ? 1 : 0;   // fat tiles: fewer tiles
   int64_t grid = grouped_tile_bound(a.rows, a.G, BM, a.N, BNO);
   if (EPI != EPI_F32B && BM >= 32 * kRowChoices && grid < int64_t(kAdaptRounds) * kComputeUnits) {
     b.adapt_rows = 1;
     grid = grouped_tile_bound(a.rows, a.G, BM - 32 * (kRowChoices - 1), a.N, BNO);
-  } else if (BM == 256 && WM == 2 && EPI != EPI_F32B && a.K >= kFatMinK) {
-    b.fat_rows = 1;                              // fewer tiles than the bound at BM rows
   }
   if (grid <= 0) return MOE_OK;
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;

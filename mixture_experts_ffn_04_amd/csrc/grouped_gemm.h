@@ -55,9 +55,9 @@ struct GemmArgs {
   // than kAdaptRounds rounds of full row tiles) for the tile rows to be
   // chosen per launch, and its grid covers the smallest choice.
   int adapt_rows;
-  // Set by the launcher, not by callers: a group's last remainder of at
-  // most kFatExtraRows rows is shared out over its other row tiles, which
-  // then hold up to BM + kFatExtraRows rows.
+  // Set by the launcher, not by callers: fat tiles are allowed, where a
+  // group's last remainder of at most kFatExtraRows rows is shared out over
+  // its other row tiles, which then hold up to BM + kFatExtraRows rows.
   int fat_rows;
 };
 
@@ -73,53 +73,73 @@ struct TileLoc {
   int n0;        // first output column
 };
 
-// Row tiles of a group of r rows at tr rows per tile.  With fat tiles a
-// last remainder of at most kFatExtraRows rows is shared out over the
-// group's other row tiles instead of taking a row tile of its own.
-__device__ __forceinline__ int row_tiles(int r, int tr, int fat) {
-  int m = (r + tr - 1) / tr;
-  if (fat && m > 1 && r - (m - 1) * tr <= kFatExtraRows) --m;
+// Row tiles of a group of r rows at tr rows per tile.  tr > BM means fat
+// tiles: BM-row tiles, with a last remainder of at most tr - BM rows shared
+// out over the group's other row tiles instead of taking a tile of its own.
+template <int BM>
+__device__ __forceinline__ int row_tiles(int r, int tr) {
+  if (tr <= BM) return (r + tr - 1) / tr;
+  int m = (r + BM - 1) / BM;
+  if (m > 1 && r - (m - 1) * BM <= tr - BM) --m;
   return m;
 }
 
-// Rows per row tile.  A launch of a few rounds of tiles leaves most CUs
-// idle in its last round, so with a.adapt_rows set every workgroup picks,
-// from the same offsets and so identically, the tile rows among BM,
-// BM - 32, BM - 64, BM - 96 that minimise (rounds of tiles) x (32-row
-// fragments of the largest tile), ties to more rows.  Measured on 8 experts
-// of ~1024 rows, K = 14336, N = 4096: 192 rows (752 tiles, 2.9 rounds) ran
-// 5% faster than 256 rows (592 tiles, 2.3 rounds); launches of more rounds
-// measured fastest with full 256-row tiles.  Contains one workgroup
-// barrier.  s_red: (kRowChoices + 1) * NT/64 ints of LDS.
+// Rows per row tile (a value above BM means fat tiles, see row_tiles).
+// Without a.adapt_rows: BM, or fat tiles where the launcher allows them.  A
+// launch of a few rounds of tiles leaves most CUs idle in its last round,
+// so with a.adapt_rows set every workgroup picks, from the same offsets and
+// so identically, among BM, BM - 32, BM - 64, BM - 96 rows and (where
+// allowed) fat tiles, the choice that minimises (rounds of tiles) x (32-row
+// fragments of the largest tile), ties to fat tiles, then to more rows.
+// Measured on 8 experts of ~1024 rows, K = 14336, N = 4096: 192 rows (752
+// tiles, 2.9 rounds) ran 5% faster than 256 rows (592 tiles, 2.3 rounds),
+// and fat tiles (512 tiles, 2 rounds) 2% faster again; launches of more
+// rounds measured fastest with 256-row (or fat) tiles.  Contains one
+// workgroup barrier.  s_red: kRowReduce * NT/64 ints of LDS.
+constexpr int kRowReduce = kRowChoices + 3;
 template <int NT, int BM, int BNO>
 __device__ __forceinline__ int tile_rows_for(const GemmArgs& a, int r, int ntiles, int* s_red) {
-  if (BM < 32 * kRowChoices || !a.adapt_rows) return BM;
+  constexpr int FAT = BM + kFatExtraRows;
+  if (BM < 32 * kRowChoices || !a.adapt_rows) return a.fat_rows ? FAT : BM;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int v[kRowChoices + 1];
+  // per candidate tile counts; then the largest group's rows, the fat tile
+  // count and the fragments of the largest fat-mode tile
+  int v[kRowReduce];
 #pragma unroll
   for (int c = 0; c < kRowChoices; ++c) v[c] = ((r + BM - 32 * c - 1) / (BM - 32 * c)) * ntiles;
   v[kRowChoices] = r;
+  const int mf = r > 0 ? row_tiles<BM>(r, FAT) : 1;
+  v[kRowChoices + 1] = r > 0 ? mf * ntiles : 0;
+  v[kRowChoices + 2] = ((r + 31) / 32 + mf - 1) / mf;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
 #pragma unroll
-    for (int c = 0; c < kRowChoices; ++c) v[c] += __shfl_xor(v[c], o, 64);
-    v[kRowChoices] = max(v[kRowChoices], __shfl_xor(v[kRowChoices], o, 64));
+    for (int c = 0; c < kRowReduce; ++c) {
+      const int u = __shfl_xor(v[c], o, 64);
+      v[c] = (c == kRowChoices || c == kRowChoices + 2) ? max(v[c], u) : v[c] + u;
+    }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int c = 0; c <= kRowChoices; ++c) s_red[c * (NT / 64) + w] = v[c];
+    for (int c = 0; c < kRowReduce; ++c) s_red[c * (NT / 64) + w] = v[c];
   }
   __syncthreads();
-  int tot[kRowChoices + 1];
+  int tot[kRowReduce];
 #pragma unroll
-  for (int c = 0; c <= kRowChoices; ++c) {
+  for (int c = 0; c < kRowReduce; ++c) {
     tot[c] = 0;
 #pragma unroll
-    for (int i = 0; i < NT / 64; ++i)
-      tot[c] = c < kRowChoices ? tot[c] + s_red[c * (NT / 64) + i] : max(tot[c], s_red[c * (NT / 64) + i]);
+    for (int i = 0; i < NT / 64; ++i) {
+      const int u = s_red[c * (NT / 64) + i];
+      tot[c] = (c == kRowChoices || c == kRowChoices + 2) ? max(tot[c], u) : tot[c] + u;
+    }
   }
   const int maxf = (tot[kRowChoices] + 31) / 32;       // fragments of the largest group
   int best = BM, best_cost = 0x7fffffff;
+  if (a.fat_rows) {
+    best = FAT;
+    best_cost = ((tot[kRowChoices + 1] + kComputeUnits - 1) / kComputeUnits) * tot[kRowChoices + 2];
+  }
 #pragma unroll
   for (int c = 0; c < kRowChoices; ++c) {
     const int rows_c = BM - 32 * c;
@@ -153,7 +173,7 @@ __device__ __forceinline__ int scan_tiles(const GemmArgs& a, int& lo, int& hi, i
     if (hi < lo) hi = lo;
   }
   tr = tile_rows_for<NT, BM, BNO>(a, hi - lo, ntiles, s_red);
-  cnt = row_tiles(hi - lo, tr, a.fat_rows) * ntiles;
+  cnt = row_tiles<BM>(hi - lo, tr) * ntiles;
   const int lane = t & 63, w = t >> 6;
   int v = cnt;
 #pragma unroll
@@ -187,10 +207,10 @@ __device__ __forceinline__ int tile_order(int bid, int total) {
 // Tile coordinates of logical tile `local` of group g (rows [glo, ghi)):
 // column blocks of SN tiles, row tiles within a block, a narrower last block
 // when SN does not divide the column tiles.
-template <int BNO, int SN>
+template <int BM, int BNO, int SN>
 __device__ __forceinline__ TileLoc tile_coords(const GemmArgs& a, int g, int glo, int ghi, int local, int tr) {
   const int ntiles = static_cast<int>((a.N + BNO - 1) / BNO);
-  const int mt_g = row_tiles(ghi - glo, tr, a.fat_rows);
+  const int mt_g = row_tiles<BM>(ghi - glo, tr);
   const int nbf = ntiles / SN;
   int mt, nt;
   if (local < nbf * mt_g * SN) {
@@ -222,7 +242,7 @@ __device__ __forceinline__ TileLoc tile_coords(const GemmArgs& a, int g, int glo
 }
 
 // LDS scratch of locate_tile, in ints.
-constexpr int locate_scratch_ints(int NT) { return NT / 64 * (kRowChoices + 2) + 4; }
+constexpr int locate_scratch_ints(int NT) { return NT / 64 * (kRowReduce + 1) + 4; }
 
 // Locate this workgroup's tile.  Must be called by all NT threads; returns
 // false (for the whole workgroup) when the block id is past the last tile.
@@ -232,7 +252,7 @@ constexpr int locate_scratch_ints(int NT) { return NT / 64 * (kRowChoices + 2) +
 template <int NT, int BM, int BNO, int SN>
 __device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl, int* scratch) {
   int* s_red = scratch + NT / 64;
-  int* s_hit = s_red + NT / 64 * (kRowChoices + 1);
+  int* s_hit = s_red + NT / 64 * kRowReduce;
   int lo, hi, cnt, excl, tr;
   const int total = scan_tiles<NT, BM, BNO>(a, lo, hi, cnt, excl, tr, scratch, s_red);
   const int bid = static_cast<int>(blockIdx.x);
@@ -245,7 +265,7 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl, int*
     s_hit[3] = excl;
   }
   __syncthreads();
-  tl = tile_coords<BNO, SN>(a, s_hit[0], s_hit[1], s_hit[2], L - s_hit[3], tr);
+  tl = tile_coords<BM, BNO, SN>(a, s_hit[0], s_hit[1], s_hit[2], L - s_hit[3], tr);
   return true;
 }
 
