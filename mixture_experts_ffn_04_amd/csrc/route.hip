@@ -8,10 +8,10 @@
 // grouped GEMM kernels as a single group with a "+ bias, fp32" epilogue, or
 // for small batches by the split-K streaming kernel of the decode path.
 //
-// Selection: one wave per token.  Lane l holds logits l, l+64, l+128, l+192
-// (E <= 256).  k rounds of a wave-wide arg-max on the key (logit, -index)
-// -- larger logit first, equal logits to the lower index -- each round
-// removing the winner from its lane.  The k winners, in selection order,
+// Selection: one wave per token.  Lane l holds logits l, l+64, ... in 1, 2
+// or 4 slots (E <= 64, 128, 256).  k rounds of a wave-wide arg-max on the
+// key (logit, -index) -- larger logit first, equal logits to the lower
+// index -- each round removing the winner from its lane.  The k winners, in selection order,
 // give the weights: a softmax over the selected logits, or sigmoid scores
 // divided by their sum.
 #include "grouped_gemm.h"
@@ -73,15 +73,17 @@ __device__ __forceinline__ unsigned wave_max(unsigned v) {
 
 // Selection and weights for one token, by one whole wave: row = the
 // token's E logits (global memory or LDS).  Lane l holds candidates l,
-// l+64, l+128, l+192.  Each of the k rounds takes the largest key over the
-// wave, then the lowest index holding it (candidates of slot i all have
-// lower indices than those of slot i+1), and retires that candidate.
+// l+64, ... in S slots (E <= 64 S).  Each of the k rounds takes the largest
+// key over the wave, then the lowest index holding it (candidates of slot i
+// all have lower indices than those of slot i+1), and retires that
+// candidate.
+template <int S>
 __device__ __forceinline__ void topk_token(const float* row, int E, int k, int score, int32_t* __restrict__ ids,
                                            float* __restrict__ wts) {
   const int lane = threadIdx.x & 63;
-  unsigned key[4];
+  unsigned key[S];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < S; ++i) {
     const int e = lane + 64 * i;
     key[i] = e < E ? logit_key(row[e]) : 0u;
   }
@@ -90,17 +92,20 @@ __device__ __forceinline__ void topk_token(const float* row, int E, int k, int s
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j >= k) break;
-    const unsigned m = wave_max(max(max(key[0], key[1]), max(key[2], key[3])));
+    unsigned lm = key[0];
+#pragma unroll
+    for (int i = 1; i < S; ++i) lm = max(lm, key[i]);
+    const unsigned m = wave_max(lm);
     int e = -1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < S; ++i) {
       const uint64_t b = __ballot(key[i] == m);
       if (e < 0 && b != 0) e = 64 * i + static_cast<int>(__builtin_ctzll(b));
     }
     sel_v[j] = key_logit(m);
     sel_i[j] = e;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < S; ++i)
       if (lane + 64 * i == e) key[i] = 0u;
   }
   if (lane == 0) {
@@ -132,13 +137,14 @@ __device__ __forceinline__ void topk_token(const float* row, int E, int k, int s
   }
 }
 
+template <int S>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                    int score, int32_t* __restrict__ ids,
                                                    float* __restrict__ wts) {
   const int tok = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
   if (tok >= T) return;
-  topk_token(logits + static_cast<int64_t>(tok) * E, E, k, score, ids + static_cast<int64_t>(tok) * k,
-             wts + static_cast<int64_t>(tok) * k);
+  topk_token<S>(logits + static_cast<int64_t>(tok) * E, E, k, score, ids + static_cast<int64_t>(tok) * k,
+                wts + static_cast<int64_t>(tok) * k);
 }
 
 // Small batches (bf16): router logits with one wave per (expert, block of
@@ -222,8 +228,17 @@ moe_status check_topk_args(int64_t T, int32_t E, int32_t k, moe_score score) {
 moe_status launch_topk(const float* logits, int64_t T, int32_t E, int32_t k, moe_score score,
                        int32_t* ids, float* w, hipStream_t st) {
   const int64_t blocks = ceil_div(T, kTokPerBlock);
-  hipLaunchKernelGGL(topk_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, logits,
-                     static_cast<int>(T), E, k, static_cast<int>(score), ids, w);
+  // candidate slots per lane: 1 (E <= 64), 2 (E <= 128) or 4
+#define MOE_TOPK(S_)                                                                                  \
+  hipLaunchKernelGGL(topk_kernel<S_>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, logits, \
+                     static_cast<int>(T), E, k, static_cast<int>(score), ids, w)
+  if (E <= 64)
+    MOE_TOPK(1);
+  else if (E <= 128)
+    MOE_TOPK(2);
+  else
+    MOE_TOPK(4);
+#undef MOE_TOPK
   return launch_status();
 }
 
