@@ -498,6 +498,34 @@ def _random_workload(i):
                       router_std=0.02 * (2048 / d) ** 0.5)
 
 
+# d = 4096 layers: gate/up runs at K = 4096, where fat tiles (an expert's
+# remainder of at most 64 rows past a multiple of 256 folded into its other
+# row tiles) are allowed.  These launches are short, so every workgroup
+# weighs fat tiles against smaller row tiles on the device.  With k = E every
+# token picks every expert, so each expert gets exactly T rows (290, 300,
+# 560, 1050: sizes with a foldable remainder); the last two shapes are
+# many-expert layers.
+DEEP_LAYERS = [(290, 1, 1, 256), (300, 2, 2, 384), (560, 4, 4, 256), (1050, 2, 2, 192),
+               (1300, 16, 4, 512), (700, 64, 2, 320)]
+
+
+@pytest.mark.parametrize("T,E,k,f", DEEP_LAYERS)
+def test_layer_deep_shapes(gpu, T, E, k, f):
+    wl = W.Workload(f"deep_{T}_{E}_{k}_{f}", T, 4096, f, E, k, "softmax", "bf16", seed=6000 + T + E,
+                    router_std=0.02 * (2048 / 4096) ** 0.5)
+    x = W.gen_x(wl)
+    wr, bias = W.gen_router(wl)
+    gu, dn = W.gen_all_experts(wl)
+    inp = dict(x=x, wr=wr, bias=bias, gu=gu, dn=dn, shared=None)
+    layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score, mode="grouped")
+    y = layer.forward(U.dev_tensor(x, wl.dtype))
+    torch.cuda.synchronize()
+    x64, wr64, out = _layer_ref(wl, inp)
+    same = U.routing_agreement(layer.ids.cpu().numpy(), out["logits"], x64, wr64, bias, wl.k)
+    U.assert_close(U.host_values(y)[same], out["y"][same], wl.dtype,
+                   f"{wl.name} T={wl.T} f={wl.f} E={wl.E} k={wl.k}")
+
+
 @pytest.mark.parametrize("mode", ["grouped", "decode"])
 @pytest.mark.parametrize("i", range(16))
 def test_layer_random_shapes(gpu, i, mode):
