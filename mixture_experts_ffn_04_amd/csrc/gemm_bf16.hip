@@ -251,6 +251,44 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const TileLoc&
   }
 }
 
+// Per-lane byte offsets (from the tile's buffer descriptors) and LDS byte
+// offsets inside a stage of a wave's NL load instructions.  The first NX
+// fill token rows of the wave's own row block, instruction i its token
+// fragment i (rows tm * wm + RPI (wn + WN i) ...), so the waves that read a
+// fragment are the ones that load it; the rest fill RPI weight rows each.
+// Lane t covers row +t/CH, LDS slot t%CH and global chunk (t%CH) ^ swz(row).
+// With a row map, token rows past the tile's last row read row 0 (their
+// results are never stored).
+template <int EPI, int BN, int CH, int RPI, int NW, int WN, int NX, int NL>
+__device__ __forceinline__ void dma_offsets(const GemmArgs& a, const TileLoc& tl, int64_t rowb, bool gather, int wave,
+                                            int wm, int wn, int lane, int tm, int (&voff)[NL], int (&dst)[NL]) {
+  const int64_t N = a.N;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const bool tok = i < NX;
+    const int row0 = tok ? wm * tm + RPI * (wn + WN * i) : RPI * (wave + NW * (i - NX));
+    const int r = row0 + lane / CH;
+    const int c = (lane % CH) ^ swz<CH>(r);
+    int64_t off;
+    if (!tok) {
+      if (EPI == EPI_SWIGLU) {
+        const int half = r / (BN / 2);
+        off = (half * N + tl.n0 + (r - half * (BN / 2))) * rowb;
+      } else {
+        off = static_cast<int64_t>(r) * rowb;
+      }
+    } else if (gather) {
+      const int grow = tl.row0 + r;
+      const int src = grow < tl.row_end ? clamp_off(a.rowmap[grow], static_cast<int>(a.rows) - 1) / a.kdiv : 0;
+      off = static_cast<int64_t>(src) * rowb;
+    } else {
+      off = static_cast<int64_t>(r) * rowb;
+    }
+    voff[i] = static_cast<int>(off) + c * 16;
+    dst[i] = row0 * CH * 16;
+  }
+}
+
 // Fragment reads of K slice ks (16 wide) -- the FN weight fragments from
 // weight stage sw_ and the first NF_ token fragments from token stage sx_
 // (their MFMAs are MOE_MFMAS).
@@ -359,30 +397,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
       // Token instruction i of a wave fills fragment i of its 160-row block.
       int voff[LPF];
       int dst[LPF];
-#pragma unroll
-      for (int i = 0; i < LPF; ++i) {
-        const bool tok = i < LXF;
-        const int row0 = tok ? wm * TMF + RPI * (wn + WN * i) : RPI * (wave + NW * (i - LXF));
-        const int r = row0 + lane / CH;
-        const int c = (lane % CH) ^ swz<CH>(r);
-        int64_t off;
-        if (!tok) {
-          if (EPI == EPI_SWIGLU) {
-            const int half = r / (BN / 2);
-            off = (half * N + tl.n0 + (r - half * (BN / 2))) * rowb;
-          } else {
-            off = static_cast<int64_t>(r) * rowb;
-          }
-        } else if (gather) {
-          const int grow = tl.row0 + r;
-          const int src = grow < tl.row_end ? clamp_off(a.rowmap[grow], static_cast<int>(a.rows) - 1) / a.kdiv : 0;
-          off = static_cast<int64_t>(src) * rowb;
-        } else {
-          off = static_cast<int64_t>(r) * rowb;
-        }
-        voff[i] = static_cast<int>(off) + c * 16;
-        dst[i] = row0 * CH * 16;
-      }
+      dma_offsets<EPI, BN, CH, RPI, NW, WN, LXF, LPF>(a, tl, rowb, gather, wave, wm, wn, lane, TMF, voff, dst);
       const unsigned ldsw = lds_addr_of(lds);
       const unsigned ldsxf = ldsw + 2u * WSTG * 16u;
       auto stage_dma = [&](int b, int k) {
@@ -446,38 +461,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
     }
   }
 
-  // Load instruction i of this wave fills RPI rows of a stage: the first LX
-  // instructions token rows of the wave's own row block (instruction i
-  // into token fragment i, so the waves that read a fragment are the ones
-  // that load it), the rest weight rows.  Lane t -> row +t/CH, LDS slot
-  // t%CH, global chunk (t%CH) ^ swz(row).
+  // Load instruction i of this wave: the first LX fill its token fragments,
+  // the rest weight rows (dma_offsets).
   int voff[LPS];
   int dst[LPS];
-#pragma unroll
-  for (int i = 0; i < LPS; ++i) {
-    const bool tok = i < LX;
-    const int row0 = tok ? wm * TM + RPI * (wn + WN * i) : RPI * (wave + NW * (i - LX));
-    const int r = row0 + lane / CH;
-    const int c = (lane % CH) ^ swz<CH>(r);
-    int64_t off;
-    if (!tok) {
-      if (EPI == EPI_SWIGLU) {
-        const int half = r / (BN / 2);
-        off = (half * N + tl.n0 + (r - half * (BN / 2))) * rowb;
-      } else {
-        off = static_cast<int64_t>(r) * rowb;
-      }
-    } else if (gather) {
-      // rows past the tile's last row read row 0 (their results are never stored)
-      const int grow = tl.row0 + r;
-      const int src = grow < tl.row_end ? clamp_off(a.rowmap[grow], static_cast<int>(a.rows) - 1) / a.kdiv : 0;
-      off = static_cast<int64_t>(src) * rowb;
-    } else {
-      off = static_cast<int64_t>(r) * rowb;
-    }
-    voff[i] = static_cast<int>(off) + c * 16;
-    dst[i] = row0 * CH * 16;                           // byte offset inside a stage
-  }
+  dma_offsets<EPI, BN, CH, RPI, NW, WN, LX, LPS>(a, tl, rowb, gather, wave, wm, wn, lane, TM, voff, dst);
   const unsigned ldsw = lds_addr_of(lds);                          // weight stages 0..2
   const unsigned ldsx = ldsw + 3u * WSTG * 16u;                    // token stages 0..1
 
