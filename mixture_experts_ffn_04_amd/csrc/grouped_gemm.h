@@ -28,6 +28,14 @@
 // -- and column blocks of 2 to 16: two halves with 16-wide blocks was the
 // fastest, by 2-11% over one stretch per XCD, although it fetches more
 // from beyond L2.)
+//
+// Row tiles.  A group's rows are dealt to its row tiles in whole 32-row
+// fragments, as evenly as possible (row_tiles, tile_coords).  The rows per
+// row tile are BM, or BM with a group's small last remainder folded into its
+// other tiles (fat tiles, where the launcher allows them), or -- in a
+// launch of only a few rounds of tiles -- a per-launch choice that every
+// workgroup makes identically from the offsets (tile_rows_for).  Which rows
+// a tile holds never changes a result: each output keeps its K order.
 #pragma once
 
 #include "common.h"
