@@ -283,9 +283,10 @@ def test_fat_tiles(gpu, kind):
     at most 64 rows shares the remainder out over its other row tiles (tiles
     of up to 320 rows on their own two-stage loop).  Active experts of 300
     rows (one fat tile), 530 and 1030 rows (remainders 18 and 6), exactly
-    256 and 100 rows, against the oracle on every row."""
+    256 and 100 rows, against the oracle on every row and column."""
     E, K = 256, 4096
-    N = 1024 if kind == "down" else 512           # > 4 rounds of tiles at 256 rows
+    # > 4 rounds of tiles at 256 rows, and a ragged last column tile
+    N = 1088 if kind == "down" else 576
     active = {3: 300, 17: 530, 100: 1030, 200: 256, 255: 100}
     counts = np.zeros(E, np.int64)
     for e, c in active.items():
