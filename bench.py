@@ -1,6 +1,6 @@
 """Benchmark of the routed MoE FFN layer (libmoe) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
 
 A step is one pass of the whole layer -- router logits + top-k, sort by
 expert, grouped gate/up + SwiGLU, grouped down projection, (shared expert),
@@ -9,10 +9,12 @@ one JSON line: layer tokens/s for the workload, the roofline position of
 its dominant kernel (timed with HIP events on the launch stream), and the
 CPU oracle timed on a bounded sample of the same workload.
 
-The default workload is the Mixtral-shaped prefill layer (T=4096, d=4096,
-f=14336, E=8, top-2, bf16).  The other workloads (c3_t1 ... c3_t64 decode,
-c4, c5) can be selected with --workload; decode workloads evict the caches
-between steps and are timed per step with events.
+The default workload is the largest layer that fits one GPU, the
+DeepSeek-V3-shaped one (T=16384, d=7168, f=2048, E=256 routed experts,
+top-8 sigmoid router with a Zipf(1.0) popularity bias, one shared expert of
+f=2048, bf16).  The other workloads (c2 Mixtral-shaped, c3_t1 ... c3_t64
+decode, c4 fine-grained) can be selected with --workload; decode workloads
+evict the caches between steps and are timed per step with events.
 """
 from __future__ import annotations
 
@@ -96,6 +98,44 @@ def tile_work(wl, counts) -> dict:
             "rows_at_256_row_tiles": r256 / P}
 
 
+def down_bytes(wl, active: int) -> float:
+    """Down kernel: active experts' [d, f] weights + H rows in + Y_perm out."""
+    b = wl.elem_bytes
+    return b * (wl.d * wl.f * active + wl.P * wl.f + wl.P * wl.d)
+
+
+def kernel_rooflines(wl, active: int, kern_ms: dict, decode: bool) -> dict:
+    """Roofline position of each projection kernel from its mean duration
+    (HIP events on the launch stream over the timed steps).  Grouped
+    workloads: algorithmic FLOPs (gate/up 4 d f, down 2 d f per routed row;
+    the shared expert's per token) against dense bf16 MFMA peak.  Decode
+    workloads: algorithmic bytes (active experts' weights once, rows in and
+    out) against HBM peak."""
+    out = {}
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    work = {
+        "gateup": (gateup_flops(wl), gateup_bytes(wl, active)),
+        "down": (2.0 * wl.P * wl.d * wl.f, down_bytes(wl, active)),
+    }
+    if wl.f_shared:
+        fs, b = wl.f_shared, wl.elem_bytes
+        work["shared_gateup"] = (4.0 * wl.T * wl.d * fs, b * (2.0 * fs * wl.d + wl.T * wl.d + wl.T * fs))
+        work["shared_down"] = (2.0 * wl.T * wl.d * fs, b * (fs * wl.d + wl.T * fs + wl.T * wl.d))
+    for name, (flops, nbytes) in work.items():
+        if name not in kern_ms:
+            continue
+        s = kern_ms[name] * 1e-3
+        if decode:
+            a = nbytes / s / 1e9
+            out[name] = {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": a / PEAK_HBM_GBPS, "kernel_ms": kern_ms[name], "algorithmic_bytes": nbytes}
+        else:
+            a = flops / s / 1e12
+            out[name] = {"bound": "mfma", "achieved": a, "peak": peak, "unit": "TFLOP/s", "frac": a / peak,
+                         "kernel_ms": kern_ms[name], "algorithmic_flops": flops}
+    return out
+
+
 # ------------------------------------------------------------ setup
 
 def kernel_source_hash(kernel: str) -> str:
@@ -121,7 +161,10 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def setup(wl, device):
+def setup(wl, device, keep_host: bool = True):
+    """Upload the workload's seeded inputs to the GPU and build the layer.
+    With keep_host, the storage-format expert weights stay in host memory
+    too (for the CPU oracle leg; the DeepSeek-shaped layer holds 22.5 GB)."""
     import torch
     from mixture_experts_ffn_04_amd import MoeLayer, MoeWeights
 
@@ -138,11 +181,10 @@ def setup(wl, device):
     gu = torch.empty(wl.E, 2 * wl.f, wl.d, dtype=tdt, device=device)
     dn = torch.empty(wl.E, wl.d, wl.f, dtype=tdt, device=device)
     host_experts = {}
-    keep = wl.E * 3 * wl.d * wl.f * wl.elem_bytes <= (4 << 30)
     for e, g, w in W.iter_experts(wl):
         gu[e].copy_(dev(g))
         dn[e].copy_(dev(w))
-        if keep:
+        if keep_host:
             host_experts[e] = (g, w)
     sh = W.gen_shared(wl)
     weights = MoeWeights(dev(wr), None if bias is None else torch.from_numpy(bias).to(device), gu, dn,
@@ -155,11 +197,16 @@ def setup(wl, device):
 # ------------------------------------------------------------ CPU oracle
 
 def cpu_baseline(wl, host, sample_tokens: int, target_s: float = 15.0):
-    """Time the CPU oracle (router + eager expert loop, float64) on the first
+    """Time the CPU oracle (float64 router + eager expert loop) on the first
     `sample_tokens` tokens of the workload; when that takes well under
     target_s seconds, time it again on enough tokens (at most T) to take
-    about target_s.  Input generation is excluded; decoding the stored bf16
-    values for the oracle is included."""
+    about target_s.
+
+    Every input is generated before the clock starts (setup() keeps the
+    storage-format weights in host memory).  The oracle takes float64
+    values, so the bf16 -> float64 decode of each expert's weights, which
+    the oracle's expert loop asks for one expert at a time, is timed on its
+    own and subtracted: the figure is the oracle's arithmetic only."""
     from oracle import moe_oracle as O
     try:
         import threadpoolctl
@@ -169,33 +216,42 @@ def cpu_baseline(wl, host, sample_tokens: int, target_s: float = 15.0):
         cores = os.cpu_count() or 1
     S = min(sample_tokens, wl.T)
     experts = host["experts"]
+    if len(experts) != wl.E:
+        raise RuntimeError("cpu_baseline needs the expert weights in host memory (setup(keep_host=True))")
+    decode_s = [0.0]
 
     def fetch(e):
-        if e in experts:
-            g, w = experts[e]
-        else:
-            g, w = W.gen_expert(wl, e)
-        return W.values(g, wl.dtype), W.values(w, wl.dtype)
+        t = time.perf_counter()
+        g, w = experts[e]
+        out = W.values(g, wl.dtype), W.values(w, wl.dtype)
+        decode_s[0] += time.perf_counter() - t
+        return out
+
+    x_all = host["x"]
+    wr = W.values(host["wr"], wl.dtype)
+    sh = host["shared"]
+    shared = None if sh is None else (W.values(sh[0], wl.dtype), W.values(sh[1], wl.dtype))
 
     def run(S):
+        x = W.values(x_all[:S], wl.dtype)
+        decode_s[0] = 0.0
         t0 = time.perf_counter()
-        x = W.values(host["x"][:S], wl.dtype)
-        L = O.router_logits(x, W.values(host["wr"], wl.dtype), host["bias"])
+        L = O.router_logits(x, wr, host["bias"])
         ids, w = O.route(L, wl.k, wl.score)
-        sh = host["shared"]
-        shared = None if sh is None else (W.values(sh[0], wl.dtype), W.values(sh[1], wl.dtype))
         O.moe_layer_eager(x, ids, w, fetch, wl.E, shared)
-        return time.perf_counter() - t0, ids
+        wall = time.perf_counter() - t0
+        return wall - decode_s[0], wall, decode_s[0], ids
 
-    dt, ids = run(S)
+    dt, wall, dec, ids = run(S)
     if target_s and dt < 0.5 * target_s and S < wl.T:
         # a bounded sample of about target_s seconds of CPU work
         S = min(wl.T, max(S + 1, int(S * target_s / dt)))
-        dt, ids = run(S)
+        dt, wall, dec, ids = run(S)
     return {"value": S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {S} of {wl.T} tokens of workload {wl.name}: float64 router + eager "
                       f"per-expert loop over the {len(np.unique(ids))} experts they select; "
-                      f"{dt:.1f} s wall"}
+                      f"{dt:.1f} s of oracle arithmetic ({wall:.1f} s wall, of which {dec:.1f} s decoding "
+                      f"bf16 weights to float64, subtracted); inputs generated beforehand"}
 
 
 # ------------------------------------------------------------ profiles
@@ -334,20 +390,32 @@ def _find(d, suffix):
     raise FileNotFoundError(f"no *{suffix} under {d}")
 
 
+def _grid(r) -> str:
+    """Grid size of a dispatch (work-items) from a rocprofv3 trace row."""
+    for key in ("Grid_Size_X", "Grid_Size", "Grid_Size_x"):
+        if r.get(key) not in (None, ""):
+            g = [r.get(key)] + [r.get(key[:-1] + c) for c in "YZ" if key.endswith("X") and r.get(key[:-1] + c)]
+            return "x".join(x for x in g if x not in (None, "", "1")) or "1"
+    return "?"
+
+
 def summarize_trace(d: str, title: str, command: str, out: str, log: str = None):
-    """rocprofv3 --kernel-trace --stats CSV -> a short markdown table, with the
-    median of each kernel's dispatch durations from the per-dispatch trace.
-    With `log` (the profiled bench.py run's output), the bench's own figure
-    for its roofline kernel from the same run is quoted as well."""
-    rows = _read_csv(_find(d, "kernel_stats.csv"))
+    """rocprofv3 --kernel-trace CSV -> a short markdown table, one row per
+    (kernel, grid size): the same tile kernel serves the routed projections
+    and the shared expert (and both projections), which differ in grid size.
+    With `log` (the profiled bench.py run's output), the bench's own figures
+    for its projection kernels from the same run are quoted as well."""
     durs = {}
     for r in _read_csv(_find(d, "kernel_trace.csv")):
-        durs.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        key = (r["Kernel_Name"], _grid(r))
+        durs.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    total = float(sum(sum(v) for v in durs.values())) or 1.0
     lines = [f"# {title}", "", "Command:", "", "```", command, "```", "",
              "Part `layer` is libmoe's kernels.  Part `harness` is the benchmark's own work outside the timed "
              "steps: weight uploads and read-backs (`copyBuffer`), buffer fills, and the cache-flush read "
-             "between decode steps (`reduce_kernel`).  The averages include the warm-up calls and the "
-             "untimed per-stage pass; the medians are over all dispatches.", ""]
+             "between decode steps (`reduce_kernel`).  One row per kernel and grid size (work-items): the "
+             "tile kernel runs the routed projections and the shared expert with different grids.  The "
+             "averages include the warm-up calls and the untimed per-stage pass.", ""]
     if log:
         rec = None
         for line in open(log, errors="replace"):
@@ -355,30 +423,69 @@ def summarize_trace(d: str, title: str, command: str, out: str, log: str = None)
                 rec = json.loads(line)
         if rec is not None:
             r = rec["roofline"]
-            lines += [f"bench.py in the same run: `{r['kernel']}` {r['kernel_ms'] * 1e3:.1f} us per call "
-                      f"(HIP events on the launch stream over the timed steps), {rec['ms_per_step']:.3f} ms per "
-                      f"step, {rec['value']:.4g} {rec['unit']}.", ""]
-    lines += ["| kernel | part | calls | avg us | median us | min us | max us | total % |",
-              "|---|---|---|---|---|---|---|---|"]
-    for r in rows:
-        name = r["Name"]
+            lines += [f"bench.py in the same run: {rec['ms_per_step']:.3f} ms per step, "
+                      f"{rec['value']:.4g} {rec['unit']}; per call (HIP events on the launch stream over the "
+                      f"timed steps):"]
+            for name, k in rec.get("layer", {}).get("kernels", {}).items():
+                lines.append(f"- `{name}` {k['kernel_ms'] * 1e3:.1f} us, {k['achieved']:.4g} {k['unit']} "
+                             f"({100 * k['frac']:.1f}% of {k['peak']:.0f})")
+            lines.append("")
+    lines += ["| kernel | grid | part | calls | avg us | median us | min us | max us | total % |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    for (name, grid), v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
         part = "layer" if "moe::" in name else "harness"
-        med = float(np.median(durs[name])) / 1e3 if name in durs else float("nan")
-        if len(name) > 110:
-            name = name[:107] + "..."
-        lines.append(f"| `{name}` | {part} | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | {med:.2f} | "
-                     f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | {float(r['Percentage']):.1f} |")
+        a = np.asarray(v, np.float64) / 1e3
+        short = name if len(name) <= 110 else name[:107] + "..."
+        lines.append(f"| `{short}` | {grid} | {part} | {len(v)} | {a.mean():.2f} | {np.median(a):.2f} | "
+                     f"{a.min():.2f} | {a.max():.2f} | {100.0 * sum(v) / total:.1f} |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(out)
 
 
 def _pmc_by_kernel(d: str):
+    """counter_collection.csv -> {"kernel name@grid": {counter: [values]}}."""
     import collections
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in _read_csv(_find(d, "counter_collection.csv")):
-        acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        acc[f"{r['Kernel_Name']}@{_grid(r)}"][r["Counter_Name"]].append(float(r["Counter_Value"]))
     return acc
+
+
+def summarize_pmc(d: str, title: str, command: str, out: str, n_cu: int = 256):
+    """One rocprofv3 --pmc pass -> the median of every counter per (kernel,
+    grid size), and where the counters are present:
+      MFMA FLOPs issued = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 (one MOP is
+                          512 bf16 FLOPs)
+      MFMA busy        = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs x 4)
+                          (the share of SIMD cycles the matrix cores are busy
+                          while the GPU is active)."""
+    import collections
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _read_csv(_find(d, "counter_collection.csv")):
+        acc[(r["Kernel_Name"], _grid(r))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for v in acc.values() for c in v})
+    lines = [f"# {title}", "", "Command:", "", "```", command, "```", "",
+             "Medians over the dispatches of each (kernel, grid size).  Derived: MFMA FLOPs issued = 512 x "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x "
+             f"{n_cu} CUs x 4 SIMDs).", "",
+             "| kernel | grid | dispatches | " + " | ".join(names) + " | MFMA TFLOP issued | MFMA busy |",
+             "|---|---|---|" + "---|" * len(names) + "---|---|"]
+    for (name, grid), cs in sorted(acc.items(), key=lambda kv: kv[0]):
+        if "moe::" not in name:
+            continue
+        med = {c: float(np.median(v)) for c, v in cs.items()}
+        n = max(len(v) for v in cs.values())
+        fl = med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        busy = med.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        gui = med.get("GRBM_GUI_ACTIVE")
+        short = name if len(name) <= 90 else name[:87] + "..."
+        lines.append(f"| `{short}` | {grid} | {n} | " + " | ".join(f"{med[c]:.6g}" if c in med else "" for c in names)
+                     + f" | {'' if fl is None else f'{512 * fl / 1e12:.4g}'}"
+                     + f" | {'' if busy is None or not gui else f'{busy / (gui * n_cu * 4):.3f}'} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out)
 
 
 def summarize_traffic(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
@@ -394,7 +501,11 @@ def summarize_traffic(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_
     cw = _pmc_by_kernel(copy_write_dir)
 
     def per_dispatch(tab, match, counter):
-        vals = [v for k, c in tab.items() if match in k for v in c.get(counter, [])]
+        # match: a substring of the kernel name, optionally "...@grid" to pick
+        # one grid size (the routed and shared-expert launches of one kernel)
+        name, _, grid = match.partition("@")
+        vals = [v for k, c in tab.items() if name in k.rpartition("@")[0] and (not grid or k.rpartition("@")[2] == grid)
+                for v in c.get(counter, [])]
         if not vals:
             raise ValueError(f"no {counter} for {match}")
         return float(np.median(vals)) * 1024.0
@@ -431,7 +542,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--workload", default="c5")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernels", action="store_true", help="also print per-stage times to stderr")
@@ -440,6 +551,8 @@ def main(argv=None):
                     help="gate/up and hipBLASLt back to back while sampling clocks and power; write OUT")
     ap.add_argument("--summarize-trace", nargs="+", metavar="ARG",
                     help="DIR TITLE COMMAND OUT [LOG]: summarise a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("DIR", "TITLE", "COMMAND", "OUT"),
+                    help="summarise one rocprofv3 --pmc pass per kernel and grid")
     ap.add_argument("--summarize-traffic", nargs=11,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "MATCH", "KERNEL",
                              "WORKLOAD", "COPY_BYTES", "COMMAND", "OUT_MD", "OUT_JSON"))
@@ -447,6 +560,9 @@ def main(argv=None):
 
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return 0
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
         return 0
     if args.summarize_traffic:
         a = list(args.summarize_traffic)
@@ -472,8 +588,11 @@ def main(argv=None):
     wl = W.get(args.workload)
     decode = args.workload.startswith("c3")
 
-    layer, x, host = setup(wl, device)
+    layer, x, host = setup(wl, device, keep_host=not args.no_cpu)
     st = torch.cuda.current_stream()
+    # the projection kernels are timed by events on the launch stream inside
+    # the timed steps (an event pair per call costs a few microseconds)
+    timed = ("gateup", "down", "shared_gateup", "shared_down")
 
     for _ in range(args.warmup):
         layer.forward(x)
@@ -497,7 +616,7 @@ def main(argv=None):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(st)
-            layer.forward(x, marks=marks, stages=("gateup",))
+            layer.forward(x, marks=marks, stages=timed)
             e1.record(st)
             step_ev.append((e0, e1))
         torch.cuda.synchronize()
@@ -507,11 +626,11 @@ def main(argv=None):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            layer.forward(x, marks=marks, stages=("gateup",))
+            layer.forward(x, marks=marks, stages=timed)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms = wall * 1e3 / args.steps
-    gateup_ms = float(np.mean([a.elapsed_time(b) for a, b in marks["gateup"]]))
+    kern_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in marks.items()}
 
     # per-stage breakdown (reported, not part of the timed steps)
     brk = {}
@@ -521,24 +640,13 @@ def main(argv=None):
         layer.forward(x, marks=brk)
     torch.cuda.synchronize()
     stage_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in brk.items()}
-    stage_ms["gateup"] = gateup_ms
+    stage_ms.update(kern_ms)
     tokens_per_s = wl.T / (ms * 1e-3)
 
-    if decode:
-        kname = "decode_gateup"
-        alg = gateup_bytes(wl, active)
-        achieved = alg / (stage_ms["gateup"] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBPS}
-    else:
-        kname = "gateup"
-        alg = gateup_flops(wl)
-        peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
-        achieved = alg / (stage_ms["gateup"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak}
+    kernels = kernel_rooflines(wl, active, kern_ms, decode)
+    kname = "decode_gateup" if decode else "gateup"
+    roof = dict(kernels["gateup"])
     roof["kernel"] = kname
-    roof["kernel_ms"] = stage_ms["gateup"]
     roof["traffic"] = load_traffic(kname, wl.name)
 
     out = {
@@ -564,7 +672,7 @@ def main(argv=None):
                   "mfma_frac": layer_flops(wl) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                   "gbps": layer_bytes(wl, active) / (ms * 1e-3) / 1e9,
                   "hbm_frac": layer_bytes(wl, active) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                  "stage_ms": stage_ms, "wall_s": wall,
+                  "stage_ms": stage_ms, "wall_s": wall, "kernels": kernels,
                   "mfma_issued_over_algorithmic": None if decode else tile_work(wl, counts)},
         "cpu_baseline": None,
     }

@@ -1,5 +1,6 @@
 """Helpers shared by the GPU tests: moving storage-format arrays to and from
-the device, tolerances, and near-tie aware routing comparison."""
+the device, tolerances, near-tie aware routing comparison and whole-layer
+parity on every token."""
 from __future__ import annotations
 
 import functools
@@ -82,6 +83,39 @@ def routing_agreement(gpu_ids, ref_logits, x, w_router, bias, k, max_frac=1e-3):
             assert L[sel[j]] + bt[sel[j]] >= L[sel[j + 1]] - bt[sel[j + 1]], f"token {t}: order"
     assert (~same).mean() <= max_frac, f"{(~same).sum()} of {same.size} tokens route differently"
     return same
+
+
+def check_layer(layer, wl, x, wr, bias, expert_weights, shared, y, what: str, tokens=None):
+    """Whole-layer parity with no token left out.
+
+    1. The GPU's fp32 logits lie within the fp32 dot-product error bound of
+       the float64 oracle's (every token).
+    2. The GPU's ids are a valid top-k of the float64 logits: bit-exact away
+       from near-ties, any order consistent with the bound at a near-tie
+       (routing_agreement).
+    3. The oracle routes from the GPU's own logits ("given the same
+       logits"): its ids must equal the GPU's bit for bit, its weights match
+       within 1e-6, and the layer output y of every token (or of `tokens`)
+       is compared with the oracle's eager expert loop on that routing.
+
+    x, wr, bias: float64 inputs; expert_weights(e) -> float64 (w_gate_up[e],
+    w_down[e]); shared: float64 shared-expert weights or None; y: device
+    output.  Returns the oracle's (ids, w) from the GPU logits."""
+    k, score = wl.k, wl.score
+    g_logits = layer.logits.cpu().numpy().astype(np.float64)
+    g_ids = layer.ids.cpu().numpy()
+    g_w = layer.wts.cpu().numpy().astype(np.float64)
+    L = O.router_logits(x, wr, bias)
+    bound = O.logit_error_bound(x, wr, bias)
+    assert (np.abs(g_logits - L) <= bound).all(), f"{what}: router logits outside the fp32 error bound"
+    routing_agreement(g_ids, L, x, wr, bias, k)
+    ids, w = O.route(g_logits, k, score)
+    assert (ids == g_ids).all(), f"{what}: ids differ from the oracle's on the same logits"
+    assert np.abs(g_w - w).max() <= 1e-6, f"{what}: routing weights"
+    sel = np.arange(wl.T) if tokens is None else np.asarray(tokens)
+    ref = O.moe_layer_eager(x[sel], ids[sel], w[sel], expert_weights, wl.E, shared)
+    assert_close(host_values(y)[sel], ref, wl.dtype, f"{what} layer")
+    return ids, w
 
 
 @functools.lru_cache(maxsize=None)

@@ -335,4 +335,28 @@ def pin_margin_and_error_bound():
     assert (np.abs(f32 - exact) <= O.logit_error_bound(x, wr, bias)).all()
 
 
+def pin_logit_error_bound_is_attained():
+    """The logit bound is the worst-case error of an fp32 dot product summed
+    in any order, so some order must come close to it.  Sum 1 and then d-1
+    products of exactly 2^-24 (x = w = 2^-12) one by one in fp32: every
+    partial sum lies exactly halfway between 1 and the next fp32 number above
+    it, and the tie goes to the even neighbour, 1.0, so every step rounds
+    down and the error is (d-1) 2^-24 against an exact sum of 1 + (d-1) 2^-24.
+    The bound must cover that error (lower side) and exceed it by under 10%
+    (upper side: a looser bound would accept wrong GPU logits and excuse
+    routing differences that are not near-ties)."""
+    for d in (64, 256, 1024, 4096):
+        x = np.full((1, d), 2.0 ** -12)
+        w = np.full((1, d), 2.0 ** -12)
+        x[0, 0] = w[0, 0] = 1.0
+        acc = np.float32(0.0)
+        for i in range(d):
+            acc = np.float32(acc + np.float32(x[0, i]) * np.float32(w[0, i]))
+        exact = 1.0 + (d - 1) * 2.0 ** -24
+        err = abs(float(acc) - exact)
+        assert float(acc) == 1.0 and err == (d - 1) * 2.0 ** -24
+        b = O.logit_error_bound(x, w)[0, 0]
+        assert err <= b <= 1.1 * err, (d, err, b)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

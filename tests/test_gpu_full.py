@@ -1,17 +1,23 @@
 """GPU parity at the full workload sizes (Mixtral-, gpt-oss- and
 DeepSeek-shaped layers and the fine-grained Zipf layer), through the C ABI.
 
-What is compared:
-  * router logits for every token against the float64 oracle, within the
-    fp32 dot-product error bound;
-  * routing for every token (bit-exact away from near-ties, valid top-k at
-    near-ties);
-  * the sort by expert, bit-exact against the oracle, on the oracle's own
-    routing of the same inputs;
-  * properties of every GPU output that hold at any size (counts, offsets,
-    bijective stable permutation, weights summing to 1);
-  * sampled rows / tokens of H, Y_perm and y against the oracle evaluated
-    one row or token at a time.
+What is compared, on the layer's own launches:
+  * router logits of every token against the float64 oracle, within the
+    fp32 dot-product error bound, and the GPU's routing as a valid top-k of
+    the float64 logits (bit-exact away from near-ties);
+  * the oracle's routing from the GPU's own logits ("given the same
+    logits"): ids of every token bit-exact, weights within 1e-6;
+  * the sort by expert (counts, offsets, perm, inv_perm) bit-exact;
+  * H (gate/up + SwiGLU) and Y_perm (down) against the oracle's per-expert
+    float64 products -- every element of every row for the Mixtral-shaped,
+    gpt-oss-shaped and fine-grained layers; for the DeepSeek-shaped layer
+    every row of a set of whole experts (the largest, the smallest, one with
+    a remainder of 1-64 rows past a multiple of 256, one with at most 32
+    rows, and a few more) and every element of the shared expert's H and
+    output;
+  * the layer output y of every token (DeepSeek-shaped: 1024 tokens, which
+    use nearly every expert).
+The oracle's Y_perm is computed from its own H, not from the GPU's.
 """
 import sys
 import time
@@ -28,8 +34,10 @@ from tests import gpu_util as U
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 FULL = ["c2", "c3_t1", "c3_t8", "c3_t32", "c3_t64", "c4", "c5"]
-SAMPLE_TOKENS = {"c2": 24, "c4": 64, "c5": 16}
-SAMPLE_ROWS = {"c2": 24, "c4": 64, "c5": 24}
+# workloads whose every row and token is compared; the others compare whole
+# experts and a token sample
+EVERY_ROW = {"c2", "c3_t1", "c3_t8", "c3_t32", "c3_t64", "c4"}
+C5_TOKENS = 1024
 
 
 def log(*a):
@@ -37,147 +45,174 @@ def log(*a):
     sys.stdout.flush()
 
 
-def _i32(a):
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
-
-
 def _upload(wl):
-    """Generate the workload (experts in a thread pool) straight to the GPU."""
-    from mixture_experts_ffn_04_amd import MoeLayer, MoeWeights
+    """Generate the workload (experts in a thread pool) straight to the GPU,
+    keeping the storage-format expert weights on the host for the oracle."""
+    from mixture_experts_ffn_04_amd import MoeWeights
     dt = wl.dtype
     x = W.gen_x(wl)
     wr, bias = W.gen_router(wl)
     tdt = U.torch_dtype(dt)
     gu = torch.empty(wl.E, 2 * wl.f, wl.d, dtype=tdt, device="cuda")
     dn = torch.empty(wl.E, wl.d, wl.f, dtype=tdt, device="cuda")
+    stored = {}
     for e, g, w in W.iter_experts(wl):
         gu[e].copy_(U.dev_tensor(g, dt))
         dn[e].copy_(U.dev_tensor(w, dt))
+        stored[e] = (g, w)
     sh = W.gen_shared(wl)
     weights = MoeWeights(U.dev_tensor(wr, dt), None if bias is None else torch.from_numpy(bias).cuda(), gu, dn,
                          None if sh is None else U.dev_tensor(sh[0], dt),
                          None if sh is None else U.dev_tensor(sh[1], dt))
-    return x, wr, bias, sh, weights
+    return x, wr, bias, sh, weights, stored
 
 
-def _fetch_many(wl, experts):
-    """Oracle-side expert weights regenerated from the seeds, kept in their
-    2-byte storage format (decoded to float64 one expert at a time by
-    _f64_expert, so the DeepSeek-shaped layer fits in host memory)."""
-    with ThreadPoolExecutor(W.default_threads()) as ex:
-        return dict(zip(experts, ex.map(lambda e: W.gen_expert(wl, e), experts)))
+class _Decoded:
+    """float64 expert weights for the oracle's expert loop, decoded from the
+    stored bf16 a few experts ahead in a thread pool (the loop asks for the
+    experts in increasing order)."""
+
+    def __init__(self, wl, stored, order, ahead=12):
+        self.wl, self.stored, self.order = wl, stored, list(order)
+        self.ex = ThreadPoolExecutor(8)
+        self.fut = {}
+        self.next = 0
+        self.ahead = ahead
+        self._fill()
+
+    def _dec(self, e):
+        g, w = self.stored[e]
+        return W.values(g, self.wl.dtype), W.values(w, self.wl.dtype)
+
+    def _fill(self):
+        while self.next < len(self.order) and len(self.fut) < self.ahead:
+            e = self.order[self.next]
+            self.fut[e] = self.ex.submit(self._dec, e)
+            self.next += 1
+
+    def __call__(self, e):
+        f = self.fut.pop(e, None)
+        out = f.result() if f is not None else self._dec(e)
+        self._fill()
+        return out
+
+    def close(self):
+        self.ex.shutdown(wait=True)
 
 
-def _f64_expert(wl, stored, e):
-    g, w = stored[e]
-    return W.values(g, wl.dtype), W.values(w, wl.dtype)
+def _c5_experts(counts):
+    """Whole experts to compare on the DeepSeek-shaped layer: the largest,
+    the smallest with rows, the largest one whose rows overflow a multiple of
+    256 by 1-64 (a fat tile at K = 7168), one with at most 32 rows (else the
+    next smallest), and three more spread over the order."""
+    c = np.asarray(counts)
+    act = np.nonzero(c > 0)[0]
+    pick = {int(act[np.argmax(c[act])]), int(act[np.argmin(c[act])])}
+    rem = [e for e in act if c[e] > 256 and 1 <= c[e] % 256 <= 64]
+    if rem:
+        pick.add(int(max(rem, key=lambda e: c[e])))
+    small = [e for e in act if c[e] <= 32 and e not in pick]
+    by_size = sorted(act, key=lambda e: c[e])
+    pick.add(int(small[0]) if small else int(next(e for e in by_size if e not in pick)))
+    for e in act[[len(act) // 4, len(act) // 2, 3 * len(act) // 4]]:
+        pick.add(int(e))
+    return sorted(pick), bool(rem), bool(small)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
 def test_full_size(gpu, name):
-    from mixture_experts_ffn_04_amd import MoeLayer, binding as B
+    from mixture_experts_ffn_04_amd import binding as B
     wl = W.get(name)
     t0 = time.time()
     log(f"[{name}] generating and uploading")
-    x, wr, bias, sh, weights = _upload(wl)
+    x, wr, bias, sh, weights, stored = _upload(wl)
     x_dev = U.dev_tensor(x, wl.dtype)
     x64 = W.values(x, wl.dtype)
     wr64 = W.values(wr, wl.dtype)
-    log(f"[{name}] oracle routing ({time.time() - t0:.1f}s)")
-    L = O.router_logits(x64, wr64, bias)
-    ids_ref, w_ref = O.route(L, wl.k, wl.score)
     E, k, T, P = wl.E, wl.k, wl.T, wl.P
 
-    # ---- the layer on the GPU (decode calls for the small-batch workload)
-    log(f"[{name}] GPU layer")
+    log(f"[{name}] GPU layer ({time.time() - t0:.1f}s)")
     layer = B.MoeLayer(weights, k, wl.score)
     y = layer.forward(x_dev)
     torch.cuda.synchronize()
     g_logits = layer.logits.cpu().numpy().astype(np.float64)
     g_ids = layer.ids.cpu().numpy()
     g_w = layer.wts.cpu().numpy().astype(np.float64)
-    g_counts = layer.counts.cpu().numpy()
-    g_off = layer.offsets.cpu().numpy()
-    g_perm = layer.perm.cpu().numpy().astype(np.int64)
-    g_inv = layer.inv_perm.cpu().numpy().astype(np.int64)
-    g_y = U.host_values(y)
 
     # logits and routing, every token
-    bound = O.logit_error_bound(x64, wr64, bias)
-    assert (np.abs(g_logits - L) <= bound).all(), "router logits outside the fp32 error bound"
+    L = O.router_logits(x64, wr64, bias)
+    assert (np.abs(g_logits - L) <= O.logit_error_bound(x64, wr64, bias)).all(), \
+        "router logits outside the fp32 error bound"
     same = U.routing_agreement(g_ids, L, x64, wr64, bias, k)
-    log(f"[{name}] routing: {int((~same).sum())} near-tie tokens differ of {T}")
-    assert np.abs(g_w[same] - w_ref[same]).max() <= U.WEIGHT_ABS
-    assert np.abs(g_w.sum(1) - 1).max() <= 1e-6
+    log(f"[{name}] routing on the float64 logits: {int((~same).sum())} near-tie tokens differ of {T}")
+    ids, w = O.route(g_logits, k, wl.score)
+    assert (ids == g_ids).all(), "ids differ from the oracle's on the same logits"
+    assert np.abs(g_w - w).max() <= 1e-6
 
-    # properties of the GPU sort at full size
-    flat = g_ids.reshape(-1).astype(np.int64)
-    assert (g_counts == np.bincount(flat, minlength=E)).all()
-    assert g_off[0] == 0 and (np.diff(g_off) == g_counts).all() and g_off[-1] == P
-    assert (np.sort(g_perm) == np.arange(P)).all() and (g_inv[g_perm] == np.arange(P)).all()
-    grp = flat[g_perm]
-    assert (np.diff(grp) >= 0).all()
-    same_grp = np.diff(grp) == 0
-    assert (np.diff(g_perm)[same_grp] > 0).all(), "sort is not stable"
+    # the sort, bit-exact
+    rc, ro, rp, ri = O.permute(ids, E)
+    assert (layer.counts.cpu().numpy() == rc).all() and (layer.offsets.cpu().numpy() == ro).all()
+    assert (layer.perm.cpu().numpy() == rp).all() and (layer.inv_perm.cpu().numpy() == ri).all()
 
-    # ---- the sort on the oracle's routing: bit-exact
-    log(f"[{name}] permute on oracle routing")
-    rc, ro, rp, ri = O.permute(ids_ref, E)
-    counts = torch.empty(E, dtype=torch.int32, device="cuda")
-    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
-    perm = torch.empty(P, dtype=torch.int32, device="cuda")
-    inv = torch.empty(P, dtype=torch.int32, device="cuda")
-    xp = torch.empty(P, wl.d, dtype=x_dev.dtype, device="cuda")
-    ws = torch.empty(B.permute_workspace_size(T, k, E), dtype=torch.uint8, device="cuda")
-    B.permute(_i32(ids_ref), x_dev, E, counts, offsets, perm, inv, xp, ws)
-    torch.cuda.synchronize()
-    assert (counts.cpu().numpy() == rc).all() and (offsets.cpu().numpy() == ro).all()
-    assert (perm.cpu().numpy() == rp).all() and (inv.cpu().numpy() == ri).all()
-    rng = np.random.default_rng(7)
-    chk = rng.choice(P, size=min(P, 512), replace=False)
-    assert (U.host_bits(xp[torch.from_numpy(chk).cuda()]) == np.asarray(x)[rp[chk] // k]).all()
+    # H and Y_perm, whole experts
+    if name in EVERY_ROW:
+        experts = [e for e in range(E) if rc[e] > 0]
+    else:
+        experts, has_rem, has_small = _c5_experts(rc)
+        log(f"[{name}] whole experts {experts} with rows {[int(rc[e]) for e in experts]}"
+            f" (fat-tile remainder: {has_rem}, <= 32 rows: {has_small})")
+        assert has_rem, "no expert with a 1-64 row remainder past a multiple of 256"
+    rows = np.concatenate([np.arange(ro[e], ro[e + 1]) for e in experts])
+    h_gpu = U.host_values(layer.h[torch.from_numpy(rows).cuda()])
+    yp_gpu = U.host_values(layer.y_perm[torch.from_numpy(rows).cuda()])
+    h_ref = np.empty_like(h_gpu)
+    yp_ref = np.empty_like(yp_gpu)
+    dec = _Decoded(wl, stored, experts)
+    i = 0
+    for e in experts:
+        n = int(rc[e])
+        gu64, dn64 = dec(e)
+        xe = x64[rp[ro[e]:ro[e + 1]] // k]
+        h_ref[i:i + n] = O.gate_up_swiglu(xe, gu64)
+        yp_ref[i:i + n] = O.down(h_ref[i:i + n], dn64)
+        i += n
+    dec.close()
+    log(f"[{name}] H / Y_perm: {rows.size} rows of {len(experts)} experts ({time.time() - t0:.1f}s)")
+    U.assert_close(h_gpu, h_ref, wl.dtype, f"{name} H")
+    U.assert_close(yp_gpu, yp_ref, wl.dtype, f"{name} Y_perm")
 
-    # ---- the projections on that (oracle-routed) grouping, sampled rows
-    decode = layer.use_decode(T)
-    h = torch.empty(P, wl.f, dtype=x_dev.dtype, device="cuda")
-    yp = torch.empty(P, wl.d, dtype=x_dev.dtype, device="cuda")
-    B.gateup_swiglu(xp, weights.w_gate_up, offsets, h, decode)
-    B.down(h, weights.w_down, offsets, yp, decode)
-    torch.cuda.synchronize()
-    nrows = SAMPLE_ROWS.get(name, P)
-    rows = np.sort(rng.choice(P, size=min(P, nrows), replace=False))
-    row_e = np.searchsorted(ro, rows, side="right") - 1
-    wts = _fetch_many(wl, sorted(set(row_e.tolist())))
-    log(f"[{name}] sampled rows: {rows.size} over {len(wts)} experts ({time.time() - t0:.1f}s)")
-    h_rows = U.host_values(h[torch.from_numpy(rows).cuda()])
-    h_ref = np.empty_like(h_rows)
-    y_ref = np.empty((rows.size, wl.d))
-    for e in sorted(set(row_e.tolist())):
-        gu64, dn64 = _f64_expert(wl, wts, e)
-        for i in np.nonzero(row_e == e)[0]:
-            h_ref[i] = O.gate_up_swiglu(x64[rp[rows[i]] // k][None], gu64)[0]
-            y_ref[i] = O.down(h_ref[i][None], dn64)[0]          # the oracle's own H
-        del gu64, dn64
-    U.assert_close(h_rows, h_ref, wl.dtype, f"{name} H rows")
-    U.assert_close(U.host_values(yp[torch.from_numpy(rows).cuda()]), y_ref, wl.dtype, f"{name} Y_perm rows")
+    # the shared expert, every element
+    shared = None
+    if sh is not None:
+        shared = (W.values(sh[0], wl.dtype), W.values(sh[1], wl.dtype))
+        hs_ref = O.gate_up_swiglu(x64, shared[0][0])
+        U.assert_close(U.host_values(layer.s_h), hs_ref, wl.dtype, f"{name} shared H")
+        U.assert_close(U.host_values(layer.s_y), O.down(hs_ref, shared[1][0]), wl.dtype, f"{name} shared output")
+        del hs_ref
+        log(f"[{name}] shared expert ({time.time() - t0:.1f}s)")
 
-    # ---- whole layer, sampled tokens with identical routing
-    ntok = SAMPLE_TOKENS.get(name, T)
-    cand = np.nonzero(same)[0]
-    toks = np.sort(rng.choice(cand, size=min(cand.size, ntok), replace=False))
-    need = sorted(set(ids_ref[toks].reshape(-1).tolist()))
-    wts = _fetch_many(wl, need)
-    shared = None if sh is None else (W.values(sh[0], wl.dtype), W.values(sh[1], wl.dtype))
-    y_ref = O.moe_layer_eager(x64[toks], ids_ref[toks], w_ref[toks], lambda e: _f64_expert(wl, wts, e), E, shared)
-    log(f"[{name}] sampled tokens: {toks.size} ({time.time() - t0:.1f}s)")
-    U.assert_close(g_y[toks], y_ref, wl.dtype, f"{name} layer")
+    # the layer output
+    g_y = U.host_values(y)
+    if name in EVERY_ROW:
+        # the oracle's grouped intermediates are whole here: combine them
+        y_ref = O.unpermute_combine(yp_ref, ri, w)
+        U.assert_close(g_y, y_ref, wl.dtype, f"{name} layer, every token")
+    else:
+        toks = np.sort(np.random.default_rng(7).choice(T, size=C5_TOKENS, replace=False))
+        need = sorted(set(ids[toks].reshape(-1).tolist()))
+        dec = _Decoded(wl, stored, need)
+        y_ref = O.moe_layer_eager(x64[toks], ids[toks], w[toks], dec, E, shared)
+        dec.close()
+        log(f"[{name}] y on {toks.size} tokens using {len(need)} experts ({time.time() - t0:.1f}s)")
+        U.assert_close(g_y[toks], y_ref, wl.dtype, f"{name} layer, {toks.size} tokens")
 
-    # ---- decode workloads: the decode and grouped calls agree
-    if decode:
+    # decode workloads: the decode and grouped calls agree
+    if layer.use_decode(T):
         grouped = B.MoeLayer(weights, k, wl.score, mode="grouped")
         yg = U.host_values(grouped.forward(x_dev))
         torch.cuda.synchronize()
         U.assert_close(g_y, yg, wl.dtype, f"{name} decode vs grouped")
     log(f"[{name}] done ({time.time() - t0:.1f}s)")
-    del weights, layer, xp, h, yp
+    del weights, layer, stored
     torch.cuda.empty_cache()

@@ -85,8 +85,11 @@ def test_route(gpu, name):
     torch.cuda.synchronize()
     gl = logits.cpu().numpy().astype(np.float64)
     assert (np.abs(gl - L) <= O.logit_error_bound(x, wr, inp["bias"])).all()
-    same = U.routing_agreement(ids.cpu().numpy(), L, x, wr, inp["bias"], k)
-    assert np.abs(w.cpu().numpy()[same] - ref_w[same]).max() <= U.WEIGHT_ABS
+    U.routing_agreement(ids.cpu().numpy(), L, x, wr, inp["bias"], k)
+    # the same logits: every token's ids bit-exact, weights within 1e-6
+    own_ids, own_w = O.route(gl, k, wl.score)
+    assert (ids.cpu().numpy() == own_ids).all()
+    assert np.abs(w.cpu().numpy() - own_w).max() <= 1e-6
 
 
 # router logits through each of its kernels, chosen by size: one wave per
@@ -114,8 +117,10 @@ def test_router_logit_paths(gpu, T, E, d, k):
     torch.cuda.synchronize()
     gl = logits.cpu().numpy().astype(np.float64)
     assert (np.abs(gl - L) <= O.logit_error_bound(x, wr, bias)).all()
-    same = U.routing_agreement(ids.cpu().numpy(), L, x, wr, bias, k)
-    assert np.abs(w.cpu().numpy()[same] - ref_w[same]).max() <= U.WEIGHT_ABS
+    U.routing_agreement(ids.cpu().numpy(), L, x, wr, bias, k)
+    own_ids, own_w = O.route(gl, k, "softmax")
+    assert (ids.cpu().numpy() == own_ids).all()
+    assert np.abs(w.cpu().numpy() - own_w).max() <= 1e-6
 
 
 # ---------------------------------------------------------------- permute
@@ -324,6 +329,47 @@ def test_fat_tiles(gpu, kind):
     U.assert_close(U.host_values(out), ref, "bf16", f"H (fat tiles, {kind})")
 
 
+@pytest.mark.parametrize("kind", ["gateup", "gateup_gather", "down"])
+def test_fat_tiles_short_launch(gpu, kind):
+    """A launch of under 4 rounds of tiles at K = 4096 whose per-launch
+    choice of rows per row tile falls on fat tiles (the host replay of that
+    choice says so): 8 experts of 1072 = 4 x 256 + 48 rows, 8 column tiles,
+    so 256 fat tiles in one round against 320 tiles in two at 256 rows.
+    Every row and column against the oracle."""
+    from tests.tile_model import choose_rows
+    E, K, c = 8, 4096, 1072
+    N = 2048 if kind == "down" else 1024
+    counts = np.full(E, c)
+    rows = E * c
+    tr, tiles, adapt = choose_rows(counts, rows, K, N, swiglu=kind != "down")
+    assert (tr, tiles, adapt) == (320, 256, True), (tr, tiles, adapt)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    wrows = N if kind == "down" else 2 * N
+    wts = W.gen_matrix((E, wrows, K), seed=81, std=0.02)
+    out = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    if kind == "down":
+        hs = W.gen_matrix((rows, K), seed=82, std=0.5)
+        B().down(U.dev_tensor(hs, "bf16"), U.dev_tensor(wts, "bf16"), _i32(offsets), out)
+        torch.cuda.synchronize()
+        ref = O.grouped_down(W.values(hs, "bf16"), W.values(wts, "bf16"), offsets)
+        U.assert_close(U.host_values(out), ref, "bf16", "Y_perm (fat tiles, short launch)")
+        return
+    if kind == "gateup":
+        xs = W.gen_matrix((rows, K), seed=83)
+        B().gateup_swiglu(U.dev_tensor(xs, "bf16"), U.dev_tensor(wts, "bf16"), _i32(offsets), out)
+        x_rows = W.values(xs, "bf16")
+    else:
+        k = 4
+        xs = W.gen_matrix((rows // k, K), seed=84)
+        perm = np.random.default_rng(85).permutation(rows)
+        B().gateup_swiglu_gather(U.dev_tensor(xs, "bf16"), _i32(perm), k, U.dev_tensor(wts, "bf16"),
+                                 _i32(offsets), out)
+        x_rows = W.values(xs, "bf16")[perm // k]
+    torch.cuda.synchronize()
+    ref = O.grouped_gate_up_swiglu(x_rows, W.values(wts, "bf16"), offsets)
+    U.assert_close(U.host_values(out), ref, "bf16", f"H (fat tiles, short launch, {kind})")
+
+
 # decode calls with at most two rows per expert on average run the
 # vector-ALU form: K up to 2048, 3072 and 4096 (its three register
 # layouts), one expert holding many of the rows, empty experts
@@ -457,6 +503,17 @@ def test_combine_masked_pairs_read_no_row(gpu, T, k, held, dtype):
 
 # ------------------------------------------------------------ whole layer
 
+def _check_layer(layer, wl, inp, y, what, x=None):
+    """Every token of the layer against the oracle routed from the GPU's own
+    logits (see gpu_util.check_layer)."""
+    x64 = W.values(inp["x"] if x is None else x, wl.dtype)
+    wr = W.values(inp["wr"], wl.dtype)
+    gu = W.values(inp["gu"], wl.dtype)
+    dn = W.values(inp["dn"], wl.dtype)
+    sh = None if inp["shared"] is None else tuple(W.values(a, wl.dtype) for a in inp["shared"])
+    return U.check_layer(layer, wl, x64, wr, inp["bias"], lambda e: (gu[e], dn[e]), sh, y, what)
+
+
 def _layer_ref(wl, inp, x=None):
     x64 = W.values(inp["x"] if x is None else x, wl.dtype)
     wr = W.values(inp["wr"], wl.dtype)
@@ -476,9 +533,7 @@ def test_layer(gpu, name, mode):
     layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score, mode=mode)
     y = layer.forward(U.dev_tensor(inp["x"], wl.dtype))
     torch.cuda.synchronize()
-    x64, wr, out = _layer_ref(wl, inp)
-    same = U.routing_agreement(layer.ids.cpu().numpy(), out["logits"], x64, wr, inp["bias"], wl.k)
-    U.assert_close(U.host_values(y)[same], out["y"][same], wl.dtype, f"{name} layer")
+    _check_layer(layer, wl, inp, y, f"{name} {mode}")
 
 
 
@@ -502,10 +557,11 @@ def _random_workload(i):
 # d = 4096 layers: gate/up runs at K = 4096, where fat tiles (an expert's
 # remainder of at most 64 rows past a multiple of 256 folded into its other
 # row tiles) are allowed.  These launches are short, so every workgroup
-# weighs fat tiles against smaller row tiles on the device.  With k = E every
-# token picks every expert, so each expert gets exactly T rows (290, 300,
-# 560, 1050: sizes with a foldable remainder); the last two shapes are
-# many-expert layers.
+# weighs fat tiles against smaller row tiles on the device; on these shapes
+# the choice mostly falls on smaller row tiles (fat tiles in a short launch
+# are covered by test_fat_tiles_short_launch).  With k = E every token picks
+# every expert, so each expert gets exactly T rows (290, 300, 560, 1050);
+# the last two shapes are many-expert layers.
 DEEP_LAYERS = [(290, 1, 1, 256), (300, 2, 2, 384), (560, 4, 4, 256), (1050, 2, 2, 192),
                (1300, 16, 4, 512), (700, 64, 2, 320)]
 
@@ -521,10 +577,7 @@ def test_layer_deep_shapes(gpu, T, E, k, f):
     layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score, mode="grouped")
     y = layer.forward(U.dev_tensor(x, wl.dtype))
     torch.cuda.synchronize()
-    x64, wr64, out = _layer_ref(wl, inp)
-    same = U.routing_agreement(layer.ids.cpu().numpy(), out["logits"], x64, wr64, bias, wl.k)
-    U.assert_close(U.host_values(y)[same], out["y"][same], wl.dtype,
-                   f"{wl.name} T={wl.T} f={wl.f} E={wl.E} k={wl.k}")
+    _check_layer(layer, wl, inp, y, f"{wl.name} T={wl.T} f={wl.f} E={wl.E} k={wl.k}")
 
 
 @pytest.mark.parametrize("mode", ["grouped", "decode"])
@@ -543,10 +596,8 @@ def test_layer_random_shapes(gpu, i, mode):
     layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score, mode=mode)
     y = layer.forward(U.dev_tensor(x, wl.dtype))
     torch.cuda.synchronize()
-    x64, wr64, out = _layer_ref(wl, inp)
-    same = U.routing_agreement(layer.ids.cpu().numpy(), out["logits"], x64, wr64, bias, wl.k)
-    U.assert_close(U.host_values(y)[same], out["y"][same], wl.dtype,
-                   f"{wl.name} T={wl.T} d={wl.d} f={wl.f} E={wl.E} k={wl.k} {wl.score} shared={wl.f_shared}")
+    _check_layer(layer, wl, inp, y,
+                 f"{wl.name} T={wl.T} d={wl.d} f={wl.f} E={wl.E} k={wl.k} {wl.score} shared={wl.f_shared}")
 
 # ------------------------------------------------------- expert-parallel share
 
@@ -600,7 +651,7 @@ def test_expert_parallel_partition_sum(gpu, name, mode):
     n = 4
     ec = wl.E // n
     total = np.zeros((wl.T, wl.d))
-    ids = None
+    first = None
     for g in range(n):
         w = B().MoeWeights(full.w_router, full.bias, full.w_gate_up[g * ec:(g + 1) * ec],
                            full.w_down[g * ec:(g + 1) * ec],
@@ -609,11 +660,21 @@ def test_expert_parallel_partition_sum(gpu, name, mode):
         y = layer.forward(x)
         torch.cuda.synchronize()
         total += U.host_values(y)
-        if ids is None:
-            ids = layer.ids.cpu().numpy()
-    x64, wr, out = _layer_ref(wl, inp)
-    same = U.routing_agreement(ids, out["logits"], x64, wr, inp["bias"], wl.k)
-    U.assert_close(total[same], out["y"][same], wl.dtype, f"{name} sum of {n} expert-parallel shares")
+        if first is None:
+            first = layer
+    # every share routes all tokens identically: the oracle routes from share
+    # 0's logits, and the summed partial outputs are compared on every token
+    x64 = W.values(inp["x"], wl.dtype)
+    wr = W.values(inp["wr"], wl.dtype)
+    g_logits = first.logits.cpu().numpy().astype(np.float64)
+    assert (np.abs(g_logits - O.router_logits(x64, wr, inp["bias"])) <= O.logit_error_bound(x64, wr, inp["bias"])).all()
+    ids, w = O.route(g_logits, wl.k, wl.score)
+    assert (ids == first.ids.cpu().numpy()).all()
+    gu = W.values(inp["gu"], wl.dtype)
+    dn = W.values(inp["dn"], wl.dtype)
+    sh = None if inp["shared"] is None else tuple(W.values(a, wl.dtype) for a in inp["shared"])
+    ref = O.moe_layer_eager(x64, ids, w, lambda e: (gu[e], dn[e]), wl.E, sh)
+    U.assert_close(total, ref, wl.dtype, f"{name} sum of {n} expert-parallel shares")
 
 
 def test_layer_deterministic_and_token_equivariant(gpu):

@@ -98,6 +98,14 @@ def _route_decides_in_f64(logits, k, score, decide_dtype=np.float32):
     return _orig["route"](logits, k, score, np.float64)
 
 
+def _bound_too_loose(x, w_router, bias=None):
+    return 1000.0 * _orig["logit_error_bound"](x, w_router, bias)
+
+
+def _bound_too_tight(x, w_router, bias=None):
+    return 0.25 * _orig["logit_error_bound"](x, w_router, bias)
+
+
 MUTATIONS = {
     "logits drop bias": ("router_logits", _logits_no_bias),
     "logits bias sign": ("router_logits", _logits_neg_bias),
@@ -117,6 +125,8 @@ MUTATIONS = {
     "combine drops shared": ("unpermute_combine", _combine_drops_shared),
     "eager wrong slot weight": ("moe_layer_eager", _eager_wrong_slot_weight),
     "eager drops shared": ("moe_layer_eager", _eager_drops_shared),
+    "logit bound x1000": ("logit_error_bound", _bound_too_loose),
+    "logit bound /4": ("logit_error_bound", _bound_too_tight),
 }
 
 
