@@ -17,6 +17,8 @@
  *   moe_topk                         top-k + weights from given logits
  *   moe_permute                      sort by expert ID (histogram, scan,
  *                                    stable scatter) + gather of the rows
+ *   moe_permute_noalloc              the same with the library's own scratch
+ *                                    (for callers that cannot allocate)
  *   moe_grouped_gemm_gateup_swiglu   per-expert gate/up projection + SwiGLU
  *   moe_grouped_gemm_gateup_swiglu_gather  the same, reading the rows
  *                                    through the sort instead of x_perm
@@ -53,8 +55,9 @@
  *   - Index tensors are int32; routing weights and logits are fp32; the
  *     activation / weight element type is given by `dtype` (bf16 or fp32).
  *     bf16 paths accumulate in fp32 and round results to bf16 (RNE).
- *   - The library keeps no state: concurrent calls on different streams with
- *     disjoint buffers are allowed.
+ *   - The library keeps no state, apart from the per-GPU scratch of
+ *     moe_permute_noalloc: concurrent calls on different streams with
+ *     disjoint buffers are allowed (moe_permute_noalloc excepted).
  */
 #ifndef LIBMOE_H
 #define LIBMOE_H
@@ -150,6 +153,29 @@ MOE_API moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_t T
                        int32_t E, int32_t k, moe_dtype dtype, int32_t* counts,
                        int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                        void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_permute for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same outputs, but the per-chunk counts live in a scratch
+ * array the library holds on each GPU (MOE_PERMUTE_SCRATCH_BYTES bytes,
+ * held until the process ends) instead of a caller workspace.  The call
+ * allocates nothing; its first call on a device looks up that device's
+ * scratch address, with the device current (the current device must be the
+ * one `stream` belongs to).  Sizes whose moe_permute_workspace_size()
+ * exceeds MOE_PERMUTE_SCRATCH_BYTES (with E = 256 experts: more than
+ * 1 048 576 pairs) return MOE_ERR_WORKSPACE, launching nothing.  Every call
+ * on one GPU uses the same scratch, which keeps the last call's contents
+ * (each call writes all of the part it reads first): calls that overlap on
+ * one GPU (different streams, or other threads) race and must be
+ * serialised by the caller.
+ */
+#define MOE_PERMUTE_SCRATCH_BYTES (1u << 20)
+
+MOE_API moe_status moe_permute_noalloc(const int32_t* topk_ids, const void* x, int64_t T, int64_t d,
+                                       int32_t E, int32_t k, moe_dtype dtype, int32_t* counts,
+                                       int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                                       void* x_perm, void* stream);
 
 /*
  * Grouped gate/up projection with SwiGLU, one group per expert:

@@ -26,7 +26,7 @@ EXPORTS = (
     "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_gateup_swiglu",
     "moe_grouped_gemm_down", "moe_unpermute_combine", "moe_decode_gateup_swiglu",
     "moe_decode_down", "moe_decode_gateup_swiglu_gather", "moe_grouped_gemm_gateup_swiglu_gather",
-    "moe_localize_ids",
+    "moe_localize_ids", "moe_permute_noalloc",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -49,6 +49,7 @@ _SIGS = {
     "moe_grouped_gemm_gateup_swiglu_gather": ([P, P, I32, P, P, I64, I64, I64, I32, ctypes.c_int, P, P],
                                               ctypes.c_int),
     "moe_localize_ids": ([P, I64, I32, I32, P, P], ctypes.c_int),
+    "moe_permute_noalloc": ([P, P, I64, I64, I32, I32, ctypes.c_int, P, P, P, P, P, P], ctypes.c_int),
 }
 
 
@@ -142,6 +143,16 @@ def permute(topk_ids, x, E: int, counts, offsets, perm, inv_perm, x_perm, ws, st
                                              _ptr(offsets), _ptr(perm), _ptr(inv_perm), _ptr(x_perm),
                                              _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0,
                                              _stream(stream)))
+
+
+def permute_noalloc(topk_ids, x, E: int, counts, offsets, perm, inv_perm, x_perm, stream=None):
+    """moe_permute with the library's own per-GPU scratch (no workspace)."""
+    T, k = topk_ids.shape
+    d = x.shape[1] if x is not None else 0
+    dt = _dt(x) if x is not None else MOE_BF16
+    _check("moe_permute_noalloc", load().moe_permute_noalloc(
+        _ptr(topk_ids), _ptr(x), T, d, E, k, dt, _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(inv_perm),
+        _ptr(x_perm), _stream(stream)))
 
 
 def gateup_swiglu(x_perm, w_gate_up, offsets, h, decode: bool = False, stream=None):
@@ -389,6 +400,7 @@ moe_route = route
 moe_topk = topk
 moe_permute_workspace_size = permute_workspace_size
 moe_permute = permute
+moe_permute_noalloc = permute_noalloc
 moe_grouped_gemm_gateup_swiglu = gateup_swiglu
 moe_grouped_gemm_down = down
 moe_unpermute_combine = unpermute_combine

@@ -18,6 +18,8 @@
 //                 stable without atomics on the ranks
 //   4. gather     x_perm[r] = x[perm[r] / k], 16-byte loads and stores, one
 //                 wave per row
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -294,10 +296,18 @@ extern "C" size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t E) {
   return ws_bytes_for(T * k, E);
 }
 
-extern "C" moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_t T, int64_t d,
-                                  int32_t E, int32_t k, moe_dtype dtype, int32_t* counts,
-                                  int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_perm,
-                                  void* ws, size_t ws_bytes, void* stream) {
+namespace moe {
+namespace {
+
+// The sort, with its per-chunk counts in a workspace of ws_bytes bytes
+// (ws_given: there is one).  Shared by moe_permute (the caller's workspace)
+// and moe_permute_noalloc (the library's static scratch).  `ws_of` yields
+// the workspace's device address; it is called only once every check has
+// passed, so a rejected call touches neither the workspace nor the GPU.
+template <class WsOf>
+moe_status permute_impl(const int32_t* topk_ids, const void* x, int64_t T, int64_t d, int32_t E, int32_t k,
+                        moe_dtype dtype, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                        void* x_perm, size_t ws_bytes, bool ws_given, WsOf ws_of, void* stream) {
   // k may exceed E: with an expert-parallel share, the pairs of experts held
   // elsewhere carry ids outside [0, E)
   if (T < 0 || d < 0 || E < 1 || k < 1 || k > kMaxK) return MOE_ERR_INVALID_ARG;
@@ -318,8 +328,9 @@ extern "C" moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_
   }
   if (!topk_ids || !perm || !inv_perm) return MOE_ERR_INVALID_ARG;
   const size_t need = ws_bytes_for(P, E);
-  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
-  int32_t* cc = static_cast<int32_t*>(ws);
+  if (!ws_given || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  int32_t* cc = nullptr;
+  if (moe_status s = ws_of(cc); s != MOE_OK) return s;
   const int chunks = static_cast<int>(ceil_div(P, kChunk));
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
@@ -340,6 +351,51 @@ extern "C" moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_
                        k, row_chunks, static_cast<uint4*>(x_perm));
   }
   return launch_status();
+}
+
+// Scratch of moe_permute_noalloc: the per-chunk expert counts, in device
+// memory the library owns (one copy per GPU, held until the process ends).
+// Its name is a host-side stand-in: host code uses only the device address
+// that hipGetSymbolAddress returns for the current device.
+__device__ __align__(256) int32_t scratch[MOE_PERMUTE_SCRATCH_BYTES / sizeof(int32_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+moe_status scratch_on_current_device(int32_t*& out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_permute(const int32_t* topk_ids, const void* x, int64_t T, int64_t d,
+                                  int32_t E, int32_t k, moe_dtype dtype, int32_t* counts,
+                                  int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_perm,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return permute_impl(topk_ids, x, T, d, E, k, dtype, counts, offsets, perm, inv_perm, x_perm, ws_bytes,
+                      ws != nullptr, [ws](int32_t*& cc) { cc = static_cast<int32_t*>(ws); return MOE_OK; },
+                      stream);
+}
+
+extern "C" moe_status moe_permute_noalloc(const int32_t* topk_ids, const void* x, int64_t T, int64_t d,
+                                          int32_t E, int32_t k, moe_dtype dtype, int32_t* counts,
+                                          int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_perm,
+                                          void* stream) {
+  return permute_impl(topk_ids, x, T, d, E, k, dtype, counts, offsets, perm, inv_perm, x_perm,
+                      MOE_PERMUTE_SCRATCH_BYTES, true, scratch_on_current_device, stream);
 }
 
 // ---------------------------------------------------------------------------
