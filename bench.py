@@ -42,7 +42,9 @@ PEAK_HBM_GBPS = 8000.0
 
 KERNEL_SOURCES = {
     "gateup": ["gemm_bf16.hip", "grouped_gemm.h", "common.h"],
+    "down": ["gemm_bf16.hip", "grouped_gemm.h", "common.h"],
     "decode_gateup": ["decode.hip", "common.h"],
+    "decode_down": ["decode.hip", "common.h"],
 }
 
 
@@ -161,7 +163,7 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def setup(wl, device, keep_host: bool = True):
+def setup(wl, device, keep_host: bool = True, mode: str = "auto"):
     """Upload the workload's seeded inputs to the GPU and build the layer.
     With keep_host, the storage-format expert weights stay in host memory
     too (for the CPU oracle leg; the DeepSeek-shaped layer holds 22.5 GB)."""
@@ -189,7 +191,7 @@ def setup(wl, device, keep_host: bool = True):
     sh = W.gen_shared(wl)
     weights = MoeWeights(dev(wr), None if bias is None else torch.from_numpy(bias).to(device), gu, dn,
                          None if sh is None else dev(sh[0]), None if sh is None else dev(sh[1]))
-    layer = MoeLayer(weights, wl.k, wl.score)
+    layer = MoeLayer(weights, wl.k, wl.score, mode=mode)
     host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=sh)
     return layer, dev(x), host
 
@@ -452,25 +454,38 @@ def _pmc_by_kernel(d: str):
     return acc
 
 
-def summarize_pmc(d: str, title: str, command: str, out: str, n_cu: int = 256):
-    """One rocprofv3 --pmc pass -> the median of every counter per (kernel,
-    grid size), and where the counters are present:
-      MFMA FLOPs issued = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 (one MOP is
-                          512 bf16 FLOPs)
-      MFMA busy        = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs x 4)
-                          (the share of SIMD cycles the matrix cores are busy
-                          while the GPU is active)."""
+def summarize_pmc(d: str, title: str, command: str, out: str, n_simd: int = 1024, n_xcd: int = 8):
+    """One rocprofv3 --pmc pass (with --kernel-trace for the durations) ->
+    the median of every counter per (kernel, grid size), and where the
+    counters are present:
+      MFMA FLOPs issued = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 (one MOP is 512
+                          bf16 FLOPs)
+      cycles            = GRBM_GUI_ACTIVE / 8 (the counter is summed over the
+                          8 XCDs, each counting the kernel's active cycles)
+      MFMA busy         = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)
+                          (the busy counter is summed over all SIMDs; it reads
+                          32 cycles per v_mfma_f32_32x32x16_bf16)
+      clock             = cycles / the dispatch's duration"""
     import collections
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in _read_csv(_find(d, "counter_collection.csv")):
         acc[(r["Kernel_Name"], _grid(r))][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    durs = collections.defaultdict(list)
+    try:
+        for r in _read_csv(_find(d, "kernel_trace.csv")):
+            durs[(r["Kernel_Name"], _grid(r))].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    except FileNotFoundError:
+        pass
     names = sorted({c for v in acc.values() for c in v})
     lines = [f"# {title}", "", "Command:", "", "```", command, "```", "",
-             "Medians over the dispatches of each (kernel, grid size).  Derived: MFMA FLOPs issued = 512 x "
-             "SQ_INSTS_VALU_MFMA_MOPS_BF16; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x "
-             f"{n_cu} CUs x 4 SIMDs).", "",
-             "| kernel | grid | dispatches | " + " | ".join(names) + " | MFMA TFLOP issued | MFMA busy |",
-             "|---|---|---|" + "---|" * len(names) + "---|---|"]
+             "Medians over the dispatches of each (kernel, grid size).  Derived: MFMA TFLOP issued = 512 x "
+             f"SQ_INSTS_VALU_MFMA_MOPS_BF16; cycles = GRBM_GUI_ACTIVE / {n_xcd} (summed over the {n_xcd} XCDs); "
+             f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {n_simd} SIMDs) (the busy counter is summed over "
+             "the SIMDs and reads 32 cycles per 32x32x16 bf16 MFMA); clock = cycles / dispatch duration "
+             "(kernel trace of the same run; the profiler serialises dispatches).", "",
+             "| kernel | grid | dispatches | " + " | ".join(names) +
+             " | MFMA TFLOP issued | cycles | MFMA busy | us | clock MHz |",
+             "|---|---|---|" + "---|" * len(names) + "---|---|---|---|---|"]
     for (name, grid), cs in sorted(acc.items(), key=lambda kv: kv[0]):
         if "moe::" not in name:
             continue
@@ -479,10 +494,15 @@ def summarize_pmc(d: str, title: str, command: str, out: str, n_cu: int = 256):
         fl = med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
         busy = med.get("SQ_VALU_MFMA_BUSY_CYCLES")
         gui = med.get("GRBM_GUI_ACTIVE")
+        cyc = gui / n_xcd if gui else None
+        us = float(np.median(durs[(name, grid)])) / 1e3 if durs.get((name, grid)) else None
         short = name if len(name) <= 90 else name[:87] + "..."
         lines.append(f"| `{short}` | {grid} | {n} | " + " | ".join(f"{med[c]:.6g}" if c in med else "" for c in names)
                      + f" | {'' if fl is None else f'{512 * fl / 1e12:.4g}'}"
-                     + f" | {'' if busy is None or not gui else f'{busy / (gui * n_cu * 4):.3f}'} |")
+                     + f" | {'' if cyc is None else f'{cyc:.4g}'}"
+                     + f" | {'' if busy is None or not cyc else f'{busy / (cyc * n_simd):.3f}'}"
+                     + f" | {'' if us is None else f'{us:.1f}'}"
+                     + f" | {'' if us is None or not cyc else f'{cyc / us:.0f}'} |")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(out)
@@ -543,6 +563,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c5")
+    ap.add_argument("--mode", default="auto", choices=("auto", "grouped", "decode", "batched"),
+                    help="layer strategy (auto: decode calls up to 256 routed rows, grouped above)")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernels", action="store_true", help="also print per-stage times to stderr")
@@ -586,13 +608,15 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     device = torch.device("cuda:0")
     wl = W.get(args.workload)
-    decode = args.workload.startswith("c3")
+    decode = args.workload.startswith("c3")   # weight streaming: timed per step after a cache flush
 
-    layer, x, host = setup(wl, device, keep_host=not args.no_cpu)
+    layer, x, host = setup(wl, device, keep_host=not args.no_cpu, mode=args.mode)
     st = torch.cuda.current_stream()
     # the projection kernels are timed by events on the launch stream inside
-    # the timed steps (an event pair per call costs a few microseconds)
-    timed = ("gateup", "down", "shared_gateup", "shared_down")
+    # the timed steps; an event pair costs a few microseconds, so the
+    # microsecond-scale decode steps carry one only around the dominant
+    # kernel (the others come from the untimed per-stage pass)
+    timed = ("gateup",) if decode else ("gateup", "down", "shared_gateup", "shared_down")
 
     for _ in range(args.warmup):
         layer.forward(x)
@@ -641,6 +665,9 @@ def main(argv=None):
     torch.cuda.synchronize()
     stage_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in brk.items()}
     stage_ms.update(kern_ms)
+    for name in ("down", "shared_gateup", "shared_down"):
+        if name in stage_ms and name not in kern_ms:
+            kern_ms[name] = stage_ms[name]          # from the per-stage pass
     tokens_per_s = wl.T / (ms * 1e-3)
 
     kernels = kernel_rooflines(wl, active, kern_ms, decode)
@@ -664,7 +691,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.f, "experts": wl.E,
                    "top_k": wl.k, "score": wl.score, "zipf_s": wl.zipf_s, "shared_d_ff": wl.f_shared,
-                   "active_experts": active, "parallelism": "single GPU",
+                   "active_experts": active, "parallelism": "single GPU", "strategy": args.mode,
                    "timing": "per-step events, caches flushed by a 1 GiB read between steps" if decode
                    else "wall clock over the timed steps"},
         "roofline": roof,

@@ -30,6 +30,9 @@
  *   moe_decode_gateup_swiglu_gather  the active experts' weights (the
  *   moe_decode_down                  _gather form reads the rows through
  *                                    the sort instead of x_perm)
+ *   moe_batched_gateup_swiglu        the small-batch "batched_mm" strategy:
+ *   moe_batched_down_combine         per (token, slot) pair, no sort; the
+ *                                    down call also applies the weights
  *
  * All experts of a layer share one packed buffer per projection, the layout
  * the article's "Dynamic Weight Loading with WeightConverter" subsection
@@ -190,6 +193,10 @@ MOE_API moe_status moe_permute_noalloc(const int32_t* topk_ids, const void* x, i
  *   offsets[E] <= rows.  Rows past offsets[E] are not written.  Offsets are
  *   clamped to [0, rows] on the device, so malformed offsets give wrong
  *   results but no out-of-bounds access.
+ * bf16 tile loads address memory through 32-bit byte offsets from the
+ * tile's base: one expert's w_gate_up[e] (2f * d * 2 bytes) must stay under
+ * 2 GiB, else MOE_ERR_UNSUPPORTED (a Mixtral-shaped expert's is 235 MB).
+ * The whole packed tensor and x_perm may be larger.
  */
 MOE_API moe_status moe_grouped_gemm_gateup_swiglu(const void* x_perm, const void* w_gate_up,
                                           const int32_t* offsets, int64_t rows,
@@ -201,6 +208,8 @@ MOE_API moe_status moe_grouped_gemm_gateup_swiglu(const void* x_perm, const void
  *   y_perm[r][c] = h[r] . w_down[e][c]   for r in expert e's rows, c < d
  *
  *   h [rows][f], w_down [E][d][f], y_perm [rows][d]  (dtype); offsets as above.
+ * bf16: one expert's w_down[e] (d * f * 2 bytes) must stay under 2 GiB, else
+ * MOE_ERR_UNSUPPORTED (32-bit tile offsets, as for the gate/up call).
  */
 MOE_API moe_status moe_grouped_gemm_down(const void* h, const void* w_down,
                                  const int32_t* offsets, int64_t rows, int64_t d,
@@ -290,6 +299,39 @@ MOE_API moe_status moe_decode_gateup_swiglu_gather(const void* x, const int32_t*
                                            const void* w_gate_up, const int32_t* offsets,
                                            int64_t rows, int64_t d, int64_t f, int32_t E,
                                            moe_dtype dtype, void* h, void* stream);
+
+/*
+ * The "batched_mm" strategy (article, section "Expert Backend": for small
+ * batches, each token is multiplied with the weights of the experts it
+ * selected, in one batched product, without sorting the tokens by expert).
+ * The pairs p = t*k + j are taken in token order; each reads its expert's
+ * weights in place (nothing is copied), so an expert chosen by several
+ * pairs is read once per pair.  No moe_permute is needed.
+ *
+ * moe_batched_gateup_swiglu:
+ *   h[p][n] = silu(x[t] . w_gate_up[e][n]) * (x[t] . w_gate_up[e][f + n]),
+ *   e = topk_ids[p], t = p / k
+ *   x [T][d], w_gate_up [E][2f][d], h [T*k][f]  (bf16); topk_ids [T][k] int32
+ * moe_batched_down_combine:
+ *   y[t][c] = sum_{j<k} topk_w[t][j] * (h[t*k+j] . w_down[e_tj][c])
+ *             (+ y_shared[t][c] when y_shared is not NULL)
+ *   summed in fp32 in increasing j, then the shared row, rounded once (the
+ *   down products are not rounded to bf16 before the sum, unlike the
+ *   grouped path's y_perm).  Deterministic: no atomics.
+ *   h [T*k][f], w_down [E][d][f], y_shared [T][d] or NULL, y [T][d] (bf16);
+ *   topk_w [T][k] fp32.
+ * Pairs whose id is outside [0, E) (another expert-parallel share's, see
+ * moe_localize_ids) get no h row and add nothing to y.  bf16 only
+ * (MOE_ERR_UNSUPPORTED for fp32); T*k <= 1024 (else MOE_ERR_UNSUPPORTED).
+ */
+MOE_API moe_status moe_batched_gateup_swiglu(const void* x, const int32_t* topk_ids, const void* w_gate_up,
+                                             int64_t T, int64_t d, int64_t f, int32_t E, int32_t k,
+                                             moe_dtype dtype, void* h, void* stream);
+
+MOE_API moe_status moe_batched_down_combine(const void* h, const int32_t* topk_ids, const float* topk_w,
+                                            const void* w_down, const void* y_shared, int64_t T, int64_t d,
+                                            int64_t f, int32_t E, int32_t k, moe_dtype dtype, void* y,
+                                            void* stream);
 
 #ifdef __cplusplus
 }

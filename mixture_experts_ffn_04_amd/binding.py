@@ -26,7 +26,7 @@ EXPORTS = (
     "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_gateup_swiglu",
     "moe_grouped_gemm_down", "moe_unpermute_combine", "moe_decode_gateup_swiglu",
     "moe_decode_down", "moe_decode_gateup_swiglu_gather", "moe_grouped_gemm_gateup_swiglu_gather",
-    "moe_localize_ids", "moe_permute_noalloc",
+    "moe_localize_ids", "moe_permute_noalloc", "moe_batched_gateup_swiglu", "moe_batched_down_combine",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -50,6 +50,8 @@ _SIGS = {
                                               ctypes.c_int),
     "moe_localize_ids": ([P, I64, I32, I32, P, P], ctypes.c_int),
     "moe_permute_noalloc": ([P, P, I64, I64, I32, I32, ctypes.c_int, P, P, P, P, P, P], ctypes.c_int),
+    "moe_batched_gateup_swiglu": ([P, P, P, I64, I64, I64, I32, I32, ctypes.c_int, P, P], ctypes.c_int),
+    "moe_batched_down_combine": ([P, P, P, P, P, I64, I64, I64, I32, I32, ctypes.c_int, P, P], ctypes.c_int),
 }
 
 
@@ -182,6 +184,24 @@ def down(h, w_down, offsets, y_perm, decode: bool = False, stream=None):
                                    _ptr(y_perm), _stream(stream)))
 
 
+def batched_gateup_swiglu(x, topk_ids, w_gate_up, h, stream=None):
+    """The "batched_mm" gate/up: h [T*k, f] in pair order, no sort."""
+    T, d = x.shape
+    k = topk_ids.shape[1]
+    E, f2, _ = w_gate_up.shape
+    _check("moe_batched_gateup_swiglu", load().moe_batched_gateup_swiglu(
+        _ptr(x), _ptr(topk_ids), _ptr(w_gate_up), T, d, f2 // 2, E, k, _dt(x), _ptr(h), _stream(stream)))
+
+
+def batched_down_combine(h, topk_ids, topk_w, w_down, y_shared, y, stream=None):
+    """The "batched_mm" down projection with the weighted combine folded in."""
+    T, k = topk_ids.shape
+    E, d, f = w_down.shape
+    _check("moe_batched_down_combine", load().moe_batched_down_combine(
+        _ptr(h), _ptr(topk_ids), _ptr(topk_w), _ptr(w_down), _ptr(y_shared), T, d, f, E, k, _dt(h), _ptr(y),
+        _stream(stream)))
+
+
 def unpermute_combine(y_perm, inv_perm, topk_w, y_shared, y, stream=None):
     T, k = topk_w.shape
     d = y.shape[1]
@@ -209,6 +229,12 @@ class MoeLayer:
     gate/up + SwiGLU and down projections (grouped, or decode variants for
     small batches), the shared expert when present, and the weighted
     combine.  Buffers are allocated once per token count and reused.
+
+    mode: "grouped" (sort by expert, grouped GEMMs), "decode" (sort, then
+    the decode calls that stream only the active experts' weights),
+    "batched" (the small-batch "batched_mm" strategy: per (token, slot)
+    pair, no sort, the combine folded into the down call) or "auto"
+    (decode up to DECODE_MAX_ROWS routed rows, grouped above).
 
     experts=(e_begin, e_count) makes it one expert-parallel share: the
     router (weights.w_router) covers all experts, weights.w_gate_up and
@@ -273,7 +299,7 @@ class MoeLayer:
     def use_decode(self, T: int) -> bool:
         if self.mode == "decode":
             return True
-        if self.mode == "grouped":
+        if self.mode in ("grouped", "batched"):
             return False
         return T * self.k <= self.DECODE_MAX_ROWS
 
@@ -284,6 +310,8 @@ class MoeLayer:
         T = x.shape[0]
         self._alloc(T)
         w = self.w
+        if self.mode == "batched":
+            return self._batched_stages(x, st)
         dec = self.use_decode(T)
         # bf16 gate/up reads the token rows through the sort (no x_perm copy)
         gather = self.dtype == torch.bfloat16
@@ -307,6 +335,27 @@ class MoeLayer:
             out.append(("shared_down", down, (self.s_h, w.shared_down, self.s_off, self.s_y, sdec, st)))
             ys = self.s_y
         out.append(("combine", unpermute_combine, (self.y_perm, self.inv_perm, self.wts, ys, self.y, st)))
+        return out
+
+    def _batched_stages(self, x: torch.Tensor, st) -> list:
+        """The "batched_mm" strategy: route, then per (token, slot) pair the
+        gate/up projection and the down projection with the weighted
+        combine folded in; no sort.  The shared expert runs on the decode
+        calls before the down projection, which adds its output."""
+        T = x.shape[0]
+        w = self.w
+        out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st))]
+        ids = self.ids
+        if self.e_begin is not None:
+            out.append(("localize", localize_ids, (self.ids, self.e_begin, self.E_loc, self.lids, st)))
+            ids = self.lids
+        ys = None
+        if w.shared_gate_up is not None:
+            out.append(("shared_gateup", gateup_swiglu, (x, w.shared_gate_up, self.s_off, self.s_h, True, st)))
+            out.append(("shared_down", down, (self.s_h, w.shared_down, self.s_off, self.s_y, True, st)))
+            ys = self.s_y
+        out.append(("gateup", batched_gateup_swiglu, (x, ids, w.w_gate_up, self.h, st)))
+        out.append(("down", batched_down_combine, (self.h, ids, self.wts, w.w_down, ys, self.y, st)))
         return out
 
     def forward(self, x: torch.Tensor, stream=None, marks: Optional[dict] = None,

@@ -34,6 +34,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+typedef __bf16 bfx2 __attribute__((ext_vector_type(2)));
+
+// acc + w.x (two bf16 pairs, fp32 accumulate: v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2(unsigned w, unsigned x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bfx2, w), __builtin_bit_cast(bfx2, x), acc, false);
+}
+
+// acc + w.x over 16 bytes (8 bf16) of each
+__device__ __forceinline__ float dot8(const u32x4& w, const u32x4& x, float acc) {
+  acc = dot2(w.x, x.x, acc);
+  acc = dot2(w.y, x.y, acc);
+  acc = dot2(w.z, x.z, acc);
+  return dot2(w.w, x.w, acc);
+}
+
 // ---------------------------------------------------------------- waves
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

@@ -247,19 +247,6 @@ moe_status launch_decode(const void* A, const void* B, const int32_t* off, const
 // the sums held 24 more VGPRs, one wave less per SIMD, and measured 2-5%
 // slower at 1-6 rows per expert.)
 
-typedef __bf16 bfx2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2(unsigned w, unsigned x, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bfx2, w), __builtin_bit_cast(bfx2, x), acc, false);
-}
-
-__device__ __forceinline__ float dot8(const u32x4& w, const u32x4& x, float acc) {
-  acc = dot2(w.x, x.x, acc);
-  acc = dot2(w.y, x.y, acc);
-  acc = dot2(w.z, x.z, acc);
-  return dot2(w.w, x.w, acc);
-}
-
 template <int EPI, int CI>
 __global__ __launch_bounds__(256) void decode_rows_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                           const int32_t* __restrict__ off,

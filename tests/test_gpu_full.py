@@ -207,12 +207,18 @@ def test_full_size(gpu, name):
         log(f"[{name}] y on {toks.size} tokens using {len(need)} experts ({time.time() - t0:.1f}s)")
         U.assert_close(g_y[toks], y_ref, wl.dtype, f"{name} layer, {toks.size} tokens")
 
-    # decode workloads: the decode and grouped calls agree
+    # decode workloads: the decode and grouped calls agree, and the
+    # "batched_mm" strategy matches the oracle on every token
     if layer.use_decode(T):
         grouped = B.MoeLayer(weights, k, wl.score, mode="grouped")
         yg = U.host_values(grouped.forward(x_dev))
         torch.cuda.synchronize()
         U.assert_close(g_y, yg, wl.dtype, f"{name} decode vs grouped")
+        batched = B.MoeLayer(weights, k, wl.score, mode="batched")
+        yb = U.host_values(batched.forward(x_dev))
+        torch.cuda.synchronize()
+        assert (batched.ids.cpu().numpy() == g_ids).all()
+        U.assert_close(yb, y_ref, wl.dtype, f"{name} batched layer, every token")
     log(f"[{name}] done ({time.time() - t0:.1f}s)")
     del weights, layer, stored
     torch.cuda.empty_cache()
