@@ -1,0 +1,119 @@
+"""The C ABI's host-side argument validation under AddressSanitizer (CPU
+only): every csrc/*.hip is rebuilt with ASan on its host pass (the device
+code is compiled as usual and never run), and a C client built with the same
+compiler's ASan runtime calls every entry point with invalid or empty
+arguments.  Each call must return its documented status before any HIP call,
+and ASan must report nothing."""
+import os
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mixture_experts_ffn_04_amd", "csrc")
+INC = os.path.join(ROOT, "include")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CLANG = "/opt/rocm/llvm/bin/clang"
+
+CLIENT = r"""
+#include <stdio.h>
+#include "libmoe.h"
+#define EXPECT(call, want) do { moe_status s_ = (call); if (s_ != (want)) { \
+    printf("line %d: got %d want %d\n", __LINE__, (int)s_, (int)(want)); return 1; } } while (0)
+int main(void) {
+  static char buf[1 << 16];
+  void* p = (void*)((((unsigned long)buf) + 4095) & ~4095ul);     /* aligned, never dereferenced */
+  void* q = (char*)p + 2;                                            /* misaligned */
+  const int B = MOE_BF16, F = MOE_F32;
+  /* router */
+  EXPECT(moe_route(p, p, NULL, 10, 100, 8, 2, B, MOE_SCORE_SOFTMAX, p, p, p, NULL), MOE_ERR_ALIGNMENT);
+  EXPECT(moe_route(q, p, NULL, 10, 128, 8, 2, B, MOE_SCORE_SOFTMAX, p, p, p, NULL), MOE_ERR_ALIGNMENT);
+  EXPECT(moe_route(NULL, p, NULL, 10, 128, 8, 2, B, MOE_SCORE_SOFTMAX, p, p, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_route(p, p, NULL, 10, 128, 8, 9, B, MOE_SCORE_SOFTMAX, p, p, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_route(p, p, NULL, 10, 128, 300, 2, B, MOE_SCORE_SOFTMAX, p, p, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_route(NULL, NULL, NULL, 0, 128, 8, 2, B, MOE_SCORE_SOFTMAX, NULL, NULL, NULL, NULL), MOE_OK);
+  EXPECT(moe_topk(p, 10, 8, 0, MOE_SCORE_SOFTMAX, p, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_topk(p, 10, 8, 17, MOE_SCORE_SOFTMAX, p, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_topk(p, 10, 8, 2, (moe_score)7, p, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_topk(NULL, 0, 8, 2, MOE_SCORE_SIGMOID, NULL, NULL, NULL), MOE_OK);
+  /* sort */
+  size_t need = moe_permute_workspace_size(1000, 4, 32);
+  if (need < 4 * 32 || moe_permute_workspace_size(10, 0, 8) != 0) return 2;
+  EXPECT(moe_permute(p, p, 1000, 128, 32, 4, B, p, p, p, p, p, p, need - 1, NULL), MOE_ERR_WORKSPACE);
+  EXPECT(moe_permute(p, p, 1000, 128, 32, 4, B, p, p, p, p, p, NULL, need, NULL), MOE_ERR_WORKSPACE);
+  EXPECT(moe_permute(p, p, 1000, 100, 32, 4, B, p, p, p, p, p, p, need, NULL), MOE_ERR_ALIGNMENT);
+  EXPECT(moe_permute(p, p, 1000, 128, 300, 4, B, p, p, p, p, p, p, need, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_permute(p, p, 1000, 128, 32, 17, B, p, p, p, p, p, p, need, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_permute_noalloc(p, NULL, 131073, 0, 256, 8, B, p, p, p, p, NULL, NULL), MOE_ERR_WORKSPACE);
+  EXPECT(moe_permute_noalloc(p, p, 1000, 100, 32, 4, B, p, p, p, p, p, NULL), MOE_ERR_ALIGNMENT);
+  EXPECT(moe_permute_noalloc(p, p, 1000, 128, 32, 4, B, NULL, p, p, p, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_localize_ids(p, 10, 0, 0, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_localize_ids(p, 10, 0, 257, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_localize_ids(NULL, 0, 0, 4, NULL, NULL), MOE_OK);
+  /* projections */
+  moe_status (*proj[4])(const void*, const void*, const int32_t*, int64_t, int64_t, int64_t, int32_t, moe_dtype,
+                        void*, void*) = {moe_grouped_gemm_gateup_swiglu, moe_grouped_gemm_down,
+                                         moe_decode_gateup_swiglu, moe_decode_down};
+  for (int i = 0; i < 4; ++i) {
+    EXPECT(proj[i](p, p, p, 100, 128, 96, 8, B, p, NULL), MOE_ERR_ALIGNMENT);
+    EXPECT(proj[i](p, p, p, 100, 128, 128, 0, B, p, NULL), MOE_ERR_INVALID_ARG);
+    EXPECT(proj[i](p, p, p, 100, 128, 128, 257, B, p, NULL), MOE_ERR_UNSUPPORTED);
+    EXPECT(proj[i](p, p, NULL, 100, 128, 128, 8, B, p, NULL), MOE_ERR_INVALID_ARG);
+    EXPECT(proj[i](q, p, p, 100, 128, 128, 8, B, p, NULL), MOE_ERR_ALIGNMENT);
+    EXPECT(proj[i](p, p, p, 100, 128, 128, 8, (moe_dtype)3, p, NULL), MOE_ERR_INVALID_ARG);
+    EXPECT(proj[i](NULL, NULL, NULL, 0, 128, 128, 8, B, NULL, NULL), MOE_OK);
+  }
+  EXPECT(moe_decode_down(p, p, p, 1025, 128, 128, 8, B, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_grouped_gemm_gateup_swiglu_gather(p, p, 3, p, p, 100, 128, 128, 8, B, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_grouped_gemm_gateup_swiglu_gather(p, NULL, 2, p, p, 100, 128, 128, 8, B, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_grouped_gemm_gateup_swiglu_gather(p, p, 2, p, p, 100, 128, 128, 8, F, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_decode_gateup_swiglu_gather(p, p, 2, p, p, 1026, 128, 128, 8, B, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_decode_gateup_swiglu_gather(p, p, 0, p, p, 100, 128, 128, 8, B, p, NULL), MOE_ERR_INVALID_ARG);
+  /* combine and the batched strategy */
+  EXPECT(moe_unpermute_combine(p, p, p, NULL, 10, 100, 2, B, p, NULL), MOE_ERR_ALIGNMENT);
+  EXPECT(moe_unpermute_combine(p, p, p, NULL, 10, 128, 0, B, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_unpermute_combine(NULL, NULL, NULL, NULL, 0, 128, 2, B, NULL, NULL), MOE_OK);
+  EXPECT(moe_batched_gateup_swiglu(p, p, p, 257, 64, 64, 8, 4, B, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_batched_gateup_swiglu(p, p, p, 8, 64, 64, 8, 4, F, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_batched_gateup_swiglu(p, p, p, 8, 64, 96, 8, 4, B, p, NULL), MOE_ERR_ALIGNMENT);
+  EXPECT(moe_batched_down_combine(p, p, NULL, p, NULL, 8, 64, 64, 8, 4, B, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_batched_down_combine(NULL, NULL, NULL, NULL, NULL, 0, 64, 64, 8, 4, B, NULL, NULL), MOE_OK);
+  for (int s = -1; s < 8; ++s)
+    if (!moe_status_string((moe_status)s)) return 3;
+  printf("ok\n");
+  return 0;
+}
+"""
+
+
+def _compile(src, obj):
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-fPIC", "-std=c++17", f"-I{INC}", f"-I{CSRC}",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_host_validation_under_asan(tmp_path):
+    if not (os.path.exists(HIPCC) and os.path.exists(CLANG)):
+        pytest.skip("ROCm compilers not found")
+    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    objs = [str(tmp_path / (os.path.basename(s)[:-4] + ".o")) for s in srcs]
+    with ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
+        list(ex.map(_compile, srcs, objs))
+    lib = tmp_path / "libmoe_asan.so"
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+                    *objs, "-o", str(lib)], check=True, capture_output=True)
+    nm = subprocess.run(["nm", "-D", str(lib)], capture_output=True, text=True).stdout
+    assert "__asan_report" in nm, "the host code is not instrumented"
+    src = tmp_path / "client.c"
+    src.write_text(CLIENT)
+    exe = tmp_path / "client"
+    subprocess.run([CLANG, "-fsanitize=address", "-g", "-std=c99", f"-I{INC}", str(src), f"-L{tmp_path}",
+                    "-l:libmoe_asan.so", f"-Wl,-rpath,{tmp_path}", "-o", str(exe)], check=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=0")
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", (out.returncode, out.stdout, out.stderr[-3000:])
+    assert "AddressSanitizer" not in out.stderr
