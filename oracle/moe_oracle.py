@@ -47,6 +47,10 @@ notes with its reason):
   * the routing weight is applied after the down projection, in the combine;
     a shared expert (when present) is added unweighted.
 
+Expert weights may also come in the MXFP4 format (OCP Microscaling
+Formats Specification v1.0): mxfp4_dequantize gives their float64 values,
+and the layer is then the same sum with those weights.
+
 Every function below is pinned by CPU tests against something other than
 itself: brute force on tiny inputs, closed forms, library routines
 (numpy.argsort, torch.nn.functional) and invariants (weights sum to 1,
@@ -278,6 +282,60 @@ def moe_layer(x, w_router, bias, w_gate_up, w_down, k: int, score: str,
     E = np.shape(w_router)[0]
     y = moe_layer_eager(x, ids, w, lambda e: (w_gate_up[e], w_down[e]), E, shared)
     return dict(logits=L, ids=ids, w=w, y=y)
+
+
+# ------------------------------------------------------- mxfp4 expert weights
+
+# The article's section "From Dense to Sparse" remarks that decoding would be
+# faster still with kernels for the native mxfp4 format of the model's
+# experts, and its section "Where Quantization Fits In" quantises weights per
+# expert while they are loaded.  The format itself is the OCP Microscaling
+# (MX) Formats Specification v1.0: an MXFP4 block holds 32 FP4 (E2M1)
+# elements and one shared E8M0 scale; element i of a block stands for
+# X * P_i, X = 2^(scale - 127) (scale code 255 is NaN), P_i the element's
+# E2M1 value.
+MX_BLOCK = 32
+
+
+def e2m1_value(code: int) -> float:
+    """The value of a 4-bit E2M1 element from its fields: sign bit 3,
+    exponent bits 2..1 (bias 1), mantissa bit 0.  Exponent 0 is subnormal,
+    0.M x 2^(1 - bias); otherwise 1.M x 2^(E - bias).  No Inf or NaN."""
+    code = int(code)
+    sign = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return sign * (m * 0.5) * 2.0 ** (1 - 1)
+    return sign * (1.0 + m * 0.5) * 2.0 ** (e - 1)
+
+
+def e8m0_value(code: int) -> float:
+    """An E8M0 scale: 2^(code - 127); code 255 is NaN."""
+    code = int(code)
+    return float("nan") if code == 255 else 2.0 ** (code - 127)
+
+
+def mxfp4_dequantize(q, scales) -> np.ndarray:
+    """float64 values of MXFP4 rows.
+
+    q       [..., K/2] uint8: two elements per byte, element 2i in the low
+            nibble and element 2i+1 in the high nibble (the byte order of the
+            packed layout; the specification leaves packing open)
+    scales  [..., K/32] uint8 E8M0 codes, one per block of 32 consecutive
+            elements along the row
+    """
+    q = np.asarray(q, np.uint8)
+    scales = np.asarray(scales, np.uint8)
+    table = np.array([e2m1_value(c) for c in range(16)], F64)
+    lo = table[q & 0x0F]
+    hi = table[q >> 4]
+    elems = np.stack([lo, hi], axis=-1).reshape(*q.shape[:-1], q.shape[-1] * 2)
+    K = elems.shape[-1]
+    if scales.shape[-1] * MX_BLOCK != K:
+        raise ValueError("one scale per 32 elements")
+    sv = np.array([e8m0_value(c) for c in range(256)], F64)[scales]
+    return (elems.reshape(*elems.shape[:-1], K // MX_BLOCK, MX_BLOCK) * sv[..., None]).reshape(elems.shape)
 
 
 def topk_margin(logits, k: int) -> np.ndarray:

@@ -359,4 +359,51 @@ def pin_logit_error_bound_is_attained():
         assert err <= b <= 1.1 * err, (d, err, b)
 
 
+# ------------------------------------------------------------- mxfp4 weights
+
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
+
+
+def pin_mxfp4_element_table():
+    """The 16 E2M1 codes decode to the table of the OCP MX specification
+    (tests/golden/mxfp4_e2m1_values.json), signed zero included."""
+    import json
+    ref = json.load(open(__import__("os").path.join(GOLDEN, "mxfp4_e2m1_values.json")))["values"]
+    for c in range(16):
+        v = O.e2m1_value(c)
+        assert v == ref[c] and math.copysign(1.0, v) == math.copysign(1.0, ref[c]), (c, v, ref[c])
+
+
+def pin_mxfp4_scale_library():
+    """E8M0 scale codes against torch's float8_e8m0fnu decoding (every code:
+    powers of two 2^-127 .. 2^127, and NaN for 255)."""
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = np.array([O.e8m0_value(c) for c in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert (got[:255] == ref[:255]).all()
+
+
+def pin_mxfp4_dequantize_layout():
+    """Closed forms of the packed layout: element 2i in the low nibble, one
+    scale per 32 consecutive elements along the row."""
+    q = np.zeros((2, 32), np.uint8)              # 2 rows of 64 elements
+    q[0, 0], q[0, 1] = 0x21, 0xF7                # 0.5, 1.0, 6, -6
+    q[0, 15] = 0x20                              # element 31 (last of block 0): 1.0
+    q[1, 16] = 0x3A                              # element 32: -1.0, element 33: 1.5
+    s = np.array([[128, 120], [127, 130]], np.uint8)
+    v = O.mxfp4_dequantize(q, s)
+    assert v.shape == (2, 64)
+    assert list(v[0, :4]) == [1.0, 2.0, 12.0, -12.0]        # x 2^(128-127)
+    assert v[0, 31] == 2.0                                    # still block 0's scale
+    assert (v[0, 4:31] == 0).all() and (v[0, 32:] == 0).all()
+    assert list(v[1, 32:34]) == [-8.0, 12.0]                  # second block x 2^(130-127)
+    assert (v[1, :32] == 0).all() and (v[1, 34:] == 0).all()
+    # every code in every nibble position, scale 1: the element table in order
+    q = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    v = O.mxfp4_dequantize(q, np.full((8, 2), 127, np.uint8)).reshape(-1)
+    table = [O.e2m1_value(c) for c in range(16)]
+    assert all(v[2 * b] == table[b & 15] and v[2 * b + 1] == table[b >> 4] for b in range(256))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

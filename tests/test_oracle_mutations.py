@@ -106,6 +106,38 @@ def _bound_too_tight(x, w_router, bias=None):
     return 0.25 * _orig["logit_error_bound"](x, w_router, bias)
 
 
+def _e2m1_bias0(code):
+    v = _orig["e2m1_value"](code)
+    return v if (int(code) >> 1) & 3 == 0 else 2.0 * v
+
+
+def _e2m1_no_subnormal(code):
+    code = int(code)
+    if (code >> 1) & 3 == 0 and code & 1:
+        return (-1.0 if code & 8 else 1.0) * 0.75
+    return _orig["e2m1_value"](code)
+
+
+def _e8m0_off_by_one(code):
+    return _orig["e8m0_value"](code) / 2.0 if int(code) != 255 else float("nan")
+
+
+def _mx_nibbles_swapped(q, scales):
+    q = np.asarray(q, np.uint8)
+    return _orig["mxfp4_dequantize"](((q & 0x0F) << 4) | (q >> 4), scales)
+
+
+def _mx_block16(q, scales):
+    v = _orig["mxfp4_dequantize"](q, np.repeat(np.asarray(scales, np.uint8), 1, axis=-1))
+    s = np.asarray(scales, np.uint8)
+    # scale of block b applied to elements [16b, 16b + 16)
+    sv = np.array([_orig["e8m0_value"](c) for c in range(256)])[s]
+    base = _orig["mxfp4_dequantize"](q, np.full_like(s, 127))
+    K = base.shape[-1]
+    idx = np.minimum(np.arange(K) // 16, s.shape[-1] - 1)
+    return base * sv[..., idx]
+
+
 MUTATIONS = {
     "logits drop bias": ("router_logits", _logits_no_bias),
     "logits bias sign": ("router_logits", _logits_neg_bias),
@@ -127,6 +159,11 @@ MUTATIONS = {
     "eager drops shared": ("moe_layer_eager", _eager_drops_shared),
     "logit bound x1000": ("logit_error_bound", _bound_too_loose),
     "logit bound /4": ("logit_error_bound", _bound_too_tight),
+    "e2m1 exponent bias 0": ("e2m1_value", _e2m1_bias0),
+    "e2m1 subnormal as normal": ("e2m1_value", _e2m1_no_subnormal),
+    "e8m0 bias 128": ("e8m0_value", _e8m0_off_by_one),
+    "mxfp4 nibbles swapped": ("mxfp4_dequantize", _mx_nibbles_swapped),
+    "mxfp4 blocks of 16": ("mxfp4_dequantize", _mx_block16),
 }
 
 
