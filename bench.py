@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "down": ["gemm_bf16.hip", "grouped_gemm.h", "common.h"],
     "decode_gateup": ["decode.hip", "common.h"],
     "decode_down": ["decode.hip", "common.h"],
+    "decode_mx_gateup": ["decode_mx.hip", "common.h"],
 }
 
 
@@ -68,7 +69,8 @@ def layer_bytes(wl, active: int) -> float:
     """Algorithmic HBM bytes of one layer call: each active expert's weights
     once, the router weights, x read and y written once (+ shared expert)."""
     b = wl.elem_bytes
-    return b * (3.0 * wl.d * wl.f * active + wl.d * wl.E + 2.0 * wl.T * wl.d + 3.0 * wl.d * wl.f_shared)
+    return (wl.expert_weight_bytes * 3.0 * wl.d * wl.f * active
+            + b * (wl.d * wl.E + 2.0 * wl.T * wl.d + 3.0 * wl.d * wl.f_shared))
 
 
 def gateup_flops(wl) -> float:
@@ -77,9 +79,10 @@ def gateup_flops(wl) -> float:
 
 
 def gateup_bytes(wl, active: int) -> float:
-    """Gate/up kernel: active experts' [2f, d] weights + routed rows in + H out."""
+    """Gate/up kernel: active experts' [2f, d] weights (as stored: MXFP4 at
+    4.25 bits per weight) + routed rows in + H out."""
     b = wl.elem_bytes
-    return b * (2.0 * wl.f * wl.d * active + wl.P * wl.d + wl.P * wl.f)
+    return wl.expert_weight_bytes * 2.0 * wl.f * wl.d * active + b * (wl.P * wl.d + wl.P * wl.f)
 
 
 def tile_work(wl, counts) -> dict:
@@ -101,9 +104,10 @@ def tile_work(wl, counts) -> dict:
 
 
 def down_bytes(wl, active: int) -> float:
-    """Down kernel: active experts' [d, f] weights + H rows in + Y_perm out."""
+    """Down kernel: active experts' [d, f] weights (as stored) + H rows in +
+    Y_perm out."""
     b = wl.elem_bytes
-    return b * (wl.d * wl.f * active + wl.P * wl.f + wl.P * wl.d)
+    return wl.expert_weight_bytes * wl.d * wl.f * active + b * (wl.P * wl.f + wl.P * wl.d)
 
 
 def kernel_rooflines(wl, active: int, kern_ms: dict, decode: bool) -> dict:
@@ -180,6 +184,14 @@ def setup(wl, device, keep_host: bool = True, mode: str = "auto"):
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     x = W.gen_x(wl)
     wr, bias = W.gen_router(wl)
+    if wl.experts == "mxfp4":
+        gq, gs, dq, ds = W.gen_all_experts_mxfp4(wl)
+        u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
+        weights = MoeWeights(dev(wr), None if bias is None else torch.from_numpy(bias).to(device), u8(gq), u8(dq),
+                             w_gate_up_scales=u8(gs), w_down_scales=u8(ds))
+        host_experts = {e: (gq[e], gs[e], dq[e], ds[e]) for e in range(wl.E)} if keep_host else {}
+        host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=None)
+        return MoeLayer(weights, wl.k, wl.score, mode=mode), dev(x), host
     gu = torch.empty(wl.E, 2 * wl.f, wl.d, dtype=tdt, device=device)
     dn = torch.empty(wl.E, wl.d, wl.f, dtype=tdt, device=device)
     host_experts = {}
@@ -224,8 +236,12 @@ def cpu_baseline(wl, host, sample_tokens: int, target_s: float = 15.0):
 
     def fetch(e):
         t = time.perf_counter()
-        g, w = experts[e]
-        out = W.values(g, wl.dtype), W.values(w, wl.dtype)
+        if wl.experts == "mxfp4":
+            gq, gs, dq, ds = experts[e]
+            out = O.mxfp4_dequantize(gq, gs), O.mxfp4_dequantize(dq, ds)
+        else:
+            g, w = experts[e]
+            out = W.values(g, wl.dtype), W.values(w, wl.dtype)
         decode_s[0] += time.perf_counter() - t
         return out
 
@@ -609,6 +625,9 @@ def main(argv=None):
     device = torch.device("cuda:0")
     wl = W.get(args.workload)
     decode = args.workload.startswith("c3")   # weight streaming: timed per step after a cache flush
+    if wl.experts == "mxfp4" and args.mode not in ("auto", "decode"):
+        print("MXFP4 experts run on the decode calls only", file=sys.stderr)
+        return 2
 
     layer, x, host = setup(wl, device, keep_host=not args.no_cpu, mode=args.mode)
     st = torch.cuda.current_stream()
@@ -671,7 +690,7 @@ def main(argv=None):
     tokens_per_s = wl.T / (ms * 1e-3)
 
     kernels = kernel_rooflines(wl, active, kern_ms, decode)
-    kname = "decode_gateup" if decode else "gateup"
+    kname = ("decode_mx_gateup" if wl.experts == "mxfp4" else "decode_gateup") if decode else "gateup"
     roof = dict(kernels["gateup"])
     roof["kernel"] = kname
     roof["traffic"] = load_traffic(kname, wl.name)
@@ -687,7 +706,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": "mxfp4 weights, bf16 activations" if wl.experts == "mxfp4" else wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.f, "experts": wl.E,
                    "top_k": wl.k, "score": wl.score, "zipf_s": wl.zipf_s, "shared_d_ff": wl.f_shared,

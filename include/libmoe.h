@@ -30,6 +30,8 @@
  *   moe_decode_gateup_swiglu_gather  the active experts' weights (the
  *   moe_decode_down                  _gather form reads the rows through
  *                                    the sort instead of x_perm)
+ *   moe_decode_gateup_swiglu_mxfp4   decode calls for MXFP4 expert weights
+ *   moe_decode_down_mxfp4            (OCP MX: E2M1 codes, E8M0 block scales)
  *   moe_batched_gateup_swiglu        the small-batch "batched_mm" strategy:
  *   moe_batched_down_combine         per (token, slot) pair, no sort; the
  *                                    down call also applies the weights
@@ -299,6 +301,40 @@ MOE_API moe_status moe_decode_gateup_swiglu_gather(const void* x, const int32_t*
                                            const void* w_gate_up, const int32_t* offsets,
                                            int64_t rows, int64_t d, int64_t f, int32_t E,
                                            moe_dtype dtype, void* h, void* stream);
+
+/*
+ * Decode calls with MXFP4 expert weights and bf16 activations (article,
+ * section "From Dense to Sparse": decoding would be faster still with
+ * kernels for the native mxfp4 format of the model's experts; section
+ * "Where Quantization Fits In": weights quantised per expert).  MXFP4 is
+ * the OCP Microscaling (MX) v1.0 format: blocks of 32 consecutive elements
+ * along a weight row share one E8M0 scale code s (value 2^(s - 127), 255 =
+ * NaN); each element is an FP4 E2M1 code (sign, 2 exponent bits with bias
+ * 1, 1 mantissa bit), two per byte with element 2i in the low nibble.
+ * Weight w[r][i] = 2^(s[r][i/32] - 127) * E2M1(code of element i of row r).
+ *
+ *   moe_decode_gateup_swiglu_mxfp4: as moe_decode_gateup_swiglu with
+ *     wq_gate_up [E][2f][d/2] uint8 codes, ws_gate_up [E][2f][d/32] uint8
+ *     scale codes (gate rows [0, f), up rows [f, 2f)); input row r is
+ *     x[perm[r] / k] (x [rows/k][d], perm from moe_permute, 1 <= k <= 16,
+ *     rows % k == 0), or x[r] when perm is NULL (x = x_perm [rows][d]);
+ *     h [rows][f] bf16.
+ *   moe_decode_down_mxfp4: as moe_decode_down with wq_down [E][d][f/2],
+ *     ws_down [E][d][f/32]; h [rows][f], y_perm [rows][d] bf16.
+ * Activations are bf16; products accumulate in fp32 (each block's sum is
+ * scaled by its power of two, exact for scale codes 1..254 unless the
+ * result overflows).  rows <= 1024, K (d for gate/up, f for down) <= 8192,
+ * else MOE_ERR_UNSUPPORTED; codes, activations and outputs 16-byte
+ * aligned.  Experts with no rows are never read.
+ */
+MOE_API moe_status moe_decode_gateup_swiglu_mxfp4(const void* x, const int32_t* perm, int32_t k,
+                                                  const void* wq_gate_up, const void* ws_gate_up,
+                                                  const int32_t* offsets, int64_t rows, int64_t d,
+                                                  int64_t f, int32_t E, void* h, void* stream);
+
+MOE_API moe_status moe_decode_down_mxfp4(const void* h, const void* wq_down, const void* ws_down,
+                                         const int32_t* offsets, int64_t rows, int64_t d, int64_t f,
+                                         int32_t E, void* y_perm, void* stream);
 
 /*
  * The "batched_mm" strategy (article, section "Expert Backend": for small

@@ -27,6 +27,7 @@ EXPORTS = (
     "moe_grouped_gemm_down", "moe_unpermute_combine", "moe_decode_gateup_swiglu",
     "moe_decode_down", "moe_decode_gateup_swiglu_gather", "moe_grouped_gemm_gateup_swiglu_gather",
     "moe_localize_ids", "moe_permute_noalloc", "moe_batched_gateup_swiglu", "moe_batched_down_combine",
+    "moe_decode_gateup_swiglu_mxfp4", "moe_decode_down_mxfp4",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -52,6 +53,8 @@ _SIGS = {
     "moe_permute_noalloc": ([P, P, I64, I64, I32, I32, ctypes.c_int, P, P, P, P, P, P], ctypes.c_int),
     "moe_batched_gateup_swiglu": ([P, P, P, I64, I64, I64, I32, I32, ctypes.c_int, P, P], ctypes.c_int),
     "moe_batched_down_combine": ([P, P, P, P, P, I64, I64, I64, I32, I32, ctypes.c_int, P, P], ctypes.c_int),
+    "moe_decode_gateup_swiglu_mxfp4": ([P, P, I32, P, P, P, I64, I64, I64, I32, P, P], ctypes.c_int),
+    "moe_decode_down_mxfp4": ([P, P, P, P, I64, I64, I64, I32, P, P], ctypes.c_int),
 }
 
 
@@ -202,6 +205,24 @@ def batched_down_combine(h, topk_ids, topk_w, w_down, y_shared, y, stream=None):
         _stream(stream)))
 
 
+def gateup_swiglu_mxfp4(x, perm, k: int, wq_gate_up, ws_gate_up, offsets, h, stream=None):
+    """Decode gate/up + SwiGLU with MXFP4 expert weights: row r is
+    x[perm[r] // k], or x[r] when perm is None."""
+    rows, f = h.shape
+    E, _, dh = wq_gate_up.shape
+    _check("moe_decode_gateup_swiglu_mxfp4", load().moe_decode_gateup_swiglu_mxfp4(
+        _ptr(x), _ptr(perm), k, _ptr(wq_gate_up), _ptr(ws_gate_up), _ptr(offsets), rows, 2 * dh, f, E, _ptr(h),
+        _stream(stream)))
+
+
+def down_mxfp4(h, wq_down, ws_down, offsets, y_perm, stream=None):
+    """Decode down projection with MXFP4 expert weights."""
+    rows, f = h.shape
+    E, d, _ = wq_down.shape
+    _check("moe_decode_down_mxfp4", load().moe_decode_down_mxfp4(
+        _ptr(h), _ptr(wq_down), _ptr(ws_down), _ptr(offsets), rows, d, f, E, _ptr(y_perm), _stream(stream)))
+
+
 def unpermute_combine(y_perm, inv_perm, topk_w, y_shared, y, stream=None):
     T, k = topk_w.shape
     d = y.shape[1]
@@ -220,6 +241,14 @@ class MoeWeights:
     w_down: torch.Tensor             # [E, d, f]
     shared_gate_up: Optional[torch.Tensor] = None   # [1, 2f_s, d]
     shared_down: Optional[torch.Tensor] = None      # [1, d, f_s]
+    # MXFP4 experts: w_gate_up / w_down then hold uint8 codes ([E, 2f, d/2],
+    # [E, d, f/2]) and these their E8M0 block scales ([E, 2f, d/32], [E, d, f/32])
+    w_gate_up_scales: Optional[torch.Tensor] = None
+    w_down_scales: Optional[torch.Tensor] = None
+
+    @property
+    def mxfp4(self) -> bool:
+        return self.w_gate_up_scales is not None
 
 
 class MoeLayer:
@@ -264,9 +293,12 @@ class MoeLayer:
             if e_count != self.E_loc or e_begin < 0 or e_begin + e_count > self.E:
                 raise ValueError("experts=(e_begin, e_count) does not match the expert weights")
             self.e_begin = int(e_begin)
-        self.f = weights.w_down.shape[2]
+        self.mx = weights.mxfp4
+        self.f = weights.w_down.shape[2] * (2 if self.mx else 1)
         self.dev = weights.w_router.device
-        self.dtype = weights.w_gate_up.dtype
+        self.dtype = weights.w_router.dtype             # activations
+        if self.mx and mode not in ("auto", "decode"):
+            raise ValueError("MXFP4 experts run on the decode calls only")
         self._T = None
 
     def _alloc(self, T: int):
@@ -313,6 +345,8 @@ class MoeLayer:
         if self.mode == "batched":
             return self._batched_stages(x, st)
         dec = self.use_decode(T)
+        if self.mx and T * self.k > 1024:
+            raise ValueError("MXFP4 experts: at most 1024 routed rows (the decode calls)")
         # bf16 gate/up reads the token rows through the sort (no x_perm copy)
         gather = self.dtype == torch.bfloat16
         out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st))]
@@ -328,6 +362,12 @@ class MoeLayer:
             ("gateup", gateup_swiglu, (self.x_perm, w.w_gate_up, self.offsets, self.h, dec, st)),
             ("down", down, (self.h, w.w_down, self.offsets, self.y_perm, dec, st)),
         ]
+        if self.mx:
+            out[-2:] = [
+                ("gateup", gateup_swiglu_mxfp4, (x, self.perm, self.k, w.w_gate_up, w.w_gate_up_scales, self.offsets,
+                                                 self.h, st)),
+                ("down", down_mxfp4, (self.h, w.w_down, w.w_down_scales, self.offsets, self.y_perm, st)),
+            ]
         ys = None
         if w.shared_gate_up is not None:
             sdec = dec and T <= self.DECODE_MAX_ROWS

@@ -56,6 +56,29 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 // Clamp an offsets entry read from device memory to [0, rows].
 __device__ __forceinline__ int clamp_off(int v, int rows) { return v < 0 ? 0 : (v > rows ? rows : v); }
 
+// Index of the j-th group with rows (in group order), or -1; all 256
+// threads of the workgroup call it (G <= 256).  A decode batch of P < G
+// rows touches at most P groups, so the grid then covers only P groups and
+// no workgroup is spent on an expert without tokens (with P >= G the grid
+// covers every group and empty ones exit at once, which measured faster
+// than the search).
+__device__ __forceinline__ int nth_active_group(const int32_t* __restrict__ off, int G, int rows, int j) {
+  __shared__ int s_cnt[4];
+  __shared__ int s_g;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  bool act = false;
+  if (t < G) act = clamp_off(off[t + 1], rows) > clamp_off(off[t], rows);
+  const uint64_t m = __ballot(act);
+  if (lane == 0) s_cnt[w] = __popcll(m);
+  if (t == 0) s_g = -1;
+  __syncthreads();
+  int rank = __popcll(m & ((uint64_t(1) << lane) - 1));
+  for (int i = 0; i < w; ++i) rank += s_cnt[i];
+  if (act && rank == j) s_g = t;
+  __syncthreads();
+  return s_g;
+}
+
 // ---------------------------------------------------------------- host
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -86,29 +86,6 @@ __device__ __forceinline__ void decode_partial(const uint16_t* wg, const uint16_
   }
 }
 
-// Index of the j-th group with rows (in group order), or -1; all 256
-// threads of the workgroup call it (G <= 256).  A decode batch of P < G
-// rows touches at most P groups, so the grid then covers only P groups and
-// no workgroup is spent on an expert without tokens (with P >= G the grid
-// covers every group and empty ones exit at once, which measured faster
-// than the search).
-__device__ __forceinline__ int nth_active_group(const int32_t* __restrict__ off, int G, int rows, int j) {
-  __shared__ int s_cnt[4];
-  __shared__ int s_g;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  bool act = false;
-  if (t < G) act = clamp_off(off[t + 1], rows) > clamp_off(off[t], rows);
-  const uint64_t m = __ballot(act);
-  if (lane == 0) s_cnt[w] = __popcll(m);
-  if (t == 0) s_g = -1;
-  __syncthreads();
-  int rank = __popcll(m & ((uint64_t(1) << lane) - 1));
-  for (int i = 0; i < w; ++i) rank += s_cnt[i];
-  if (act && rank == j) s_g = t;
-  __syncthreads();
-  return s_g;
-}
-
 // EPI: 0 = bf16 store, 1 = SwiGLU pairs (bf16), 2 = fp32 + bias (router
 // logits for small batches; N need not be a multiple of 16 there).
 // rowmap (may be NULL): input row r is A[rowmap[r] / kdiv] (rowmap entries

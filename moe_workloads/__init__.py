@@ -17,6 +17,9 @@ gpt-oss-20b uses 4 of 32 experts, DeepSeek-V3 stores 256 experts per layer):
   c4      fine-grained    T=8192   d=2048 f=768   E=128 k=8  softmax  Zipf(1.1)
   c5      DeepSeek-shaped T=16384  d=7168 f=2048  E=256 k=8  sigmoid  Zipf(1.0)
                                                         + shared expert f_s=2048
+  c3mx_tN the gpt-oss-shaped decode layer with MXFP4 expert weights (the
+          format gpt-oss ships its experts in; article section "From Dense
+          to Sparse" remarks that native mxfp4 kernels would decode faster)
 
 Storage layout (the packed per-layer expert tensors the article's weight
 loading produces, see its "Dynamic Weight Loading with WeightConverter"
@@ -64,6 +67,7 @@ class Workload:
     f_shared: int = 0
     seed: int = 0
     router_std: float = 0.02   # scaled-down shapes raise it to keep the full-size logit spread
+    experts: str = "dense"     # expert weight storage: "dense" (dtype) | "mxfp4"
 
     @property
     def P(self) -> int:
@@ -73,6 +77,12 @@ class Workload:
     @property
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
+
+    @property
+    def expert_weight_bytes(self) -> float:
+        """Bytes per expert weight element as stored (MXFP4: half a byte per
+        element plus one scale byte per 32 elements)."""
+        return 0.5 + 1.0 / 32 if self.experts == "mxfp4" else float(self.elem_bytes)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -85,6 +95,10 @@ WORKLOADS = {
     "c3_t8": Workload("c3_t8", 8, 2880, 2880, 32, 4, "softmax", "bf16", seed=38),
     "c3_t32": Workload("c3_t32", 32, 2880, 2880, 32, 4, "softmax", "bf16", seed=332),
     "c3_t64": Workload("c3_t64", 64, 2880, 2880, 32, 4, "softmax", "bf16", seed=364),
+    "c3mx_t1": Workload("c3mx_t1", 1, 2880, 2880, 32, 4, "softmax", "bf16", seed=41, experts="mxfp4"),
+    "c3mx_t8": Workload("c3mx_t8", 8, 2880, 2880, 32, 4, "softmax", "bf16", seed=48, experts="mxfp4"),
+    "c3mx_t32": Workload("c3mx_t32", 32, 2880, 2880, 32, 4, "softmax", "bf16", seed=432, experts="mxfp4"),
+    "c3mx_t64": Workload("c3mx_t64", 64, 2880, 2880, 32, 4, "softmax", "bf16", seed=464, experts="mxfp4"),
     "c4": Workload("c4", 8192, 2048, 768, 128, 8, "softmax", "bf16", zipf_s=1.1, seed=4),
     "c5": Workload("c5", 16384, 7168, 2048, 256, 8, "sigmoid", "bf16", zipf_s=1.0,
                    f_shared=2048, seed=5),
@@ -102,6 +116,10 @@ SMALL_WORKLOADS = {
                        router_std=0.02 * (2880 / 576) ** 0.5),
     "c3s_t37": Workload("c3s_t37", 37, 576, 640, 32, 4, "softmax", "bf16", seed=137,
                         router_std=0.02 * (2880 / 576) ** 0.5),
+    "c3mxs_t1": Workload("c3mxs_t1", 1, 576, 640, 32, 4, "softmax", "bf16", seed=141,
+                         router_std=0.02 * (2880 / 576) ** 0.5, experts="mxfp4"),
+    "c3mxs_t37": Workload("c3mxs_t37", 37, 576, 640, 32, 4, "softmax", "bf16", seed=147,
+                          router_std=0.02 * (2880 / 576) ** 0.5, experts="mxfp4"),
     "c4s": Workload("c4s", 517, 256, 192, 128, 8, "softmax", "bf16", zipf_s=1.1, seed=104,
                     router_std=0.02 * (2048 / 256) ** 0.5),
     "c5s": Workload("c5s", 301, 448, 128, 256, 8, "sigmoid", "bf16", zipf_s=1.0,
@@ -190,6 +208,35 @@ def gen_expert(wl: Workload, e: int):
     gu = _encode(_normal(_rng(wl, _WGU, e), (2 * wl.f, wl.d), WEIGHT_STD), wl.dtype)
     dn = _encode(_normal(_rng(wl, _WD, e), (wl.d, wl.f), WEIGHT_STD), wl.dtype)
     return gu, dn
+
+
+# MXFP4 scale codes are drawn from MX_SCALE_CODE + {-1, 0, 1}: with codes
+# uniform over the 16 E2M1 values (root mean square 2.93), 2^(120 - 127)
+# gives an element spread of about 0.023, close to the dense weights' 0.02.
+MX_SCALE_CODE = 120
+
+
+def _mx_rows(rng: np.random.Generator, rows: int, K: int):
+    """Random MXFP4 rows: codes [rows, K/2] uint8 (two E2M1 codes per byte,
+    every code equally likely) and E8M0 scale codes [rows, K/32] uint8."""
+    q = rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+    s = (MX_SCALE_CODE + rng.integers(-1, 2, size=(rows, K // 32))).astype(np.uint8)
+    return q, s
+
+
+def gen_expert_mxfp4(wl: Workload, e: int):
+    """MXFP4 storage of expert e: (gate_up codes [2f, d/2], gate_up scales
+    [2f, d/32], down codes [d, f/2], down scales [d, f/32]); the blocks of
+    32 run along each row's input dimension (d for gate/up, f for down)."""
+    gq, gs = _mx_rows(_rng(wl, _WGU, e), 2 * wl.f, wl.d)
+    dq, ds = _mx_rows(_rng(wl, _WD, e), wl.d, wl.f)
+    return gq, gs, dq, ds
+
+
+def gen_all_experts_mxfp4(wl: Workload):
+    """Packed MXFP4 experts: codes and scales stacked over the experts."""
+    parts = [gen_expert_mxfp4(wl, e) for e in range(wl.E)]
+    return tuple(np.stack([p[i] for p in parts]) for i in range(4))
 
 
 def gen_shared(wl: Workload):

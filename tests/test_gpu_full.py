@@ -222,3 +222,47 @@ def test_full_size(gpu, name):
     log(f"[{name}] done ({time.time() - t0:.1f}s)")
     del weights, layer, stored
     torch.cuda.empty_cache()
+
+
+MX_FULL = ["c3mx_t1", "c3mx_t8", "c3mx_t32", "c3mx_t64"]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", MX_FULL)
+def test_full_size_mxfp4(gpu, name):
+    """The gpt-oss-shaped decode layer with MXFP4 experts at full size: every
+    row of H and Y_perm and every token of y against the oracle with the
+    dequantised experts."""
+    from mixture_experts_ffn_04_amd import binding as B
+    wl = W.get(name)
+    t0 = time.time()
+    log(f"[{name}] generating and uploading")
+    x = W.gen_x(wl)
+    wr, bias = W.gen_router(wl)
+    gq, gs, dq, ds = W.gen_all_experts_mxfp4(wl)
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    weights = B.MoeWeights(U.dev_tensor(wr, "bf16"), None, u8(gq), u8(dq), w_gate_up_scales=u8(gs),
+                           w_down_scales=u8(ds))
+    layer = B.MoeLayer(weights, wl.k, wl.score)
+    y = layer.forward(U.dev_tensor(x, "bf16"))
+    torch.cuda.synchronize()
+    x64, wr64 = W.values(x, "bf16"), W.values(wr, "bf16")
+    g_logits = layer.logits.cpu().numpy().astype(np.float64)
+    assert (np.abs(g_logits - O.router_logits(x64, wr64, bias)) <= O.logit_error_bound(x64, wr64, bias)).all()
+    ids, w = O.route(g_logits, wl.k, wl.score)
+    assert (ids == layer.ids.cpu().numpy()).all()
+    rc, ro, rp, ri = O.permute(ids, wl.E)
+    assert (layer.perm.cpu().numpy() == rp).all() and (layer.offsets.cpu().numpy() == ro).all()
+    h_ref = np.zeros((wl.P, wl.f))
+    yp_ref = np.zeros((wl.P, wl.d))
+    for e in range(wl.E):
+        if rc[e] == 0:
+            continue
+        gu64 = O.mxfp4_dequantize(gq[e], gs[e])
+        dn64 = O.mxfp4_dequantize(dq[e], ds[e])
+        h_ref[ro[e]:ro[e + 1]] = O.gate_up_swiglu(x64[rp[ro[e]:ro[e + 1]] // wl.k], gu64)
+        yp_ref[ro[e]:ro[e + 1]] = O.down(h_ref[ro[e]:ro[e + 1]], dn64)
+    U.assert_close(U.host_values(layer.h), h_ref, "bf16", f"{name} H")
+    U.assert_close(U.host_values(layer.y_perm), yp_ref, "bf16", f"{name} Y_perm")
+    U.assert_close(U.host_values(y), O.unpermute_combine(yp_ref, ri, w), "bf16", f"{name} layer, every token")
+    log(f"[{name}] done ({time.time() - t0:.1f}s)")

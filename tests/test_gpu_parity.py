@@ -667,6 +667,85 @@ def test_batched_rejects_large_or_f32(gpu):
     assert lib.moe_batched_down_combine(p, p, None, p, None, 8, 64, 64, 8, 4, Bd.MOE_BF16, p, None) == \
         Bd.MOE_ERR_INVALID_ARG
 
+# ------------------------------------------------------ MXFP4 expert weights
+
+def _mx_dev(a, gpu):
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(gpu)
+
+
+@pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37"])
+def test_mxfp4_projections(gpu, name):
+    """MXFP4 decode calls against the oracle's projections with the
+    dequantised weights, every element: gate/up reading the rows through
+    the sort and from x_perm (bit-identical), and down."""
+    wl, inp = U.small_inputs(name)
+    _, _, _, ids, w = _oracle_routing(wl, inp)
+    counts, offsets, perm, inv = O.permute(ids, wl.E)
+    gq, gs, dq, ds = W.gen_all_experts_mxfp4(wl)
+    P = wl.P
+    h = torch.empty(P, wl.f, dtype=torch.bfloat16, device=gpu)
+    B().gateup_swiglu_mxfp4(U.dev_tensor(inp["x"], "bf16"), _i32(perm), wl.k, _mx_dev(gq, gpu), _mx_dev(gs, gpu),
+                            _i32(offsets), h)
+    x_perm = np.asarray(inp["x"])[perm // wl.k]
+    hp = torch.empty_like(h)
+    B().gateup_swiglu_mxfp4(U.dev_tensor(x_perm, "bf16"), None, 1, _mx_dev(gq, gpu), _mx_dev(gs, gpu),
+                            _i32(offsets), hp)
+    hs = W.gen_matrix((P, wl.f), seed=wl.seed + 7, std=0.5)
+    y = torch.empty(P, wl.d, dtype=torch.bfloat16, device=gpu)
+    B().down_mxfp4(U.dev_tensor(hs, "bf16"), _mx_dev(dq, gpu), _mx_dev(ds, gpu), _i32(offsets), y)
+    torch.cuda.synchronize()
+    gu64 = O.mxfp4_dequantize(gq, gs)
+    dn64 = O.mxfp4_dequantize(dq, ds)
+    ref_h = O.grouped_gate_up_swiglu(W.values(x_perm, "bf16"), gu64, offsets)
+    U.assert_close(U.host_values(h), ref_h, "bf16", f"{name} mxfp4 H")
+    assert (U.host_bits(h) == U.host_bits(hp)).all()
+    U.assert_close(U.host_values(y), O.grouped_down(W.values(hs, "bf16"), dn64, offsets), "bf16", f"{name} mxfp4 Y")
+
+
+# K of one, two and four 64-block columns per lane (2048, 4096, 8192), rows
+# from 1 to 64 per expert with empty experts in between
+@pytest.mark.parametrize("E,rows,K,N", [(16, 40, 2048, 192), (64, 300, 4096, 128), (8, 200, 8192, 64),
+                                         (256, 24, 1024, 320)])
+def test_mxfp4_shapes(gpu, E, rows, K, N):
+    offsets = _skewed_offsets(E, rows, seed=K + N)
+    xs = W.gen_matrix((rows, K), seed=K + 51)
+    rng = np.random.default_rng(K + N)
+    gq = rng.integers(0, 256, size=(E, 2 * N, K // 2), dtype=np.uint8)
+    gs = rng.integers(118, 123, size=(E, 2 * N, K // 32)).astype(np.uint8)
+    dq = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ds = rng.integers(118, 123, size=(E, N, K // 32)).astype(np.uint8)
+    h = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    y = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    xd = U.dev_tensor(xs, "bf16")
+    B().gateup_swiglu_mxfp4(xd, None, 1, _mx_dev(gq, gpu), _mx_dev(gs, gpu), _i32(offsets), h)
+    # the down call on the same activations: its K is the rows' length
+    B().down_mxfp4(xd, _mx_dev(dq, gpu), _mx_dev(ds, gpu), _i32(offsets), y)
+    torch.cuda.synchronize()
+    x64 = W.values(xs, "bf16")
+    U.assert_close(U.host_values(h), O.grouped_gate_up_swiglu(x64, O.mxfp4_dequantize(gq, gs), offsets), "bf16",
+                   f"mxfp4 H E={E} K={K}")
+    U.assert_close(U.host_values(y), O.grouped_down(x64, O.mxfp4_dequantize(dq, ds), offsets), "bf16",
+                   f"mxfp4 Y E={E} K={K}")
+
+
+@pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37"])
+def test_layer_mxfp4(gpu, name):
+    """The whole layer with MXFP4 experts against the oracle's eager loop
+    over the dequantised experts, every token."""
+    wl, inp = U.small_inputs(name)
+    gq, gs, dq, ds = W.gen_all_experts_mxfp4(wl)
+    dev = U.device_weights(wl, inp)
+    weights = B().MoeWeights(dev.w_router, dev.bias, _mx_dev(gq, gpu), _mx_dev(dq, gpu),
+                             w_gate_up_scales=_mx_dev(gs, gpu), w_down_scales=_mx_dev(ds, gpu))
+    layer = B().MoeLayer(weights, wl.k, wl.score)
+    y = layer.forward(U.dev_tensor(inp["x"], "bf16"))
+    torch.cuda.synchronize()
+    gu64 = O.mxfp4_dequantize(gq, gs)
+    dn64 = O.mxfp4_dequantize(dq, ds)
+    U.check_layer(layer, wl, W.values(inp["x"], "bf16"), W.values(inp["wr"], "bf16"), inp["bias"],
+                  lambda e: (gu64[e], dn64[e]), None, y, f"{name} mxfp4 layer")
+
+
 # ------------------------------------------------------- expert-parallel share
 
 def test_localize_ids(gpu):
