@@ -54,7 +54,7 @@ __device__ __forceinline__ float dot8(const u32x4& w, const u32x4& x, float acc)
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Clamp an offsets entry read from device memory to [0, rows].
-__device__ __forceinline__ int clamp_off(int v, int rows) { return v < 0 ? 0 : (v > rows ? rows : v); }
+__host__ __device__ __forceinline__ int clamp_off(int v, int rows) { return v < 0 ? 0 : (v > rows ? rows : v); }
 
 // Index of the j-th group with rows (in group order), or -1; all 256
 // threads of the workgroup call it (G <= 256).  A decode batch of P < G
@@ -77,6 +77,14 @@ __device__ __forceinline__ int nth_active_group(const int32_t* __restrict__ off,
   if (act && rank == j) s_g = t;
   __syncthreads();
   return s_g;
+}
+
+// MXFP4 (OCP Microscaling): E8M0 scale code -> 2^(code - 127) as fp32
+// (code 0: 2^-127, a denormal; code 255: NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
+  if (code == 0) return __uint_as_float(0x00400000u);
+  if (code == 255) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float(code << 23);
 }
 
 // ---------------------------------------------------------------- host

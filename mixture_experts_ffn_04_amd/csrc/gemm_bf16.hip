@@ -34,7 +34,7 @@ constexpr int kBufFlags = 0x00020000;
 // 128-byte bank halves, and the 8 same-parity rows among 16 need 8 distinct
 // positions.
 template <int CH>
-__device__ __forceinline__ int swz(int r) {
+__host__ __device__ __forceinline__ int swz(int r) {
   static_assert(CH == 8, "128-byte tile rows");
   return (r & 7) ^ ((r >> 3) & 1);
 }
@@ -260,7 +260,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const TileLoc&
 // With a row map, token rows past the tile's last row read row 0 (their
 // results are never stored).
 template <int EPI, int BN, int CH, int RPI, int NW, int WN, int NX, int NL>
-__device__ __forceinline__ void dma_offsets(const GemmArgs& a, const TileLoc& tl, int64_t rowb, bool gather, int wave,
+__host__ __device__ __forceinline__ void dma_offsets(const GemmArgs& a, const TileLoc& tl, int64_t rowb, bool gather, int wave,
                                             int wm, int wn, int lane, int tm, int (&voff)[NL], int (&dst)[NL]) {
   const int64_t N = a.N;
 #pragma unroll
@@ -287,6 +287,66 @@ __device__ __forceinline__ void dma_offsets(const GemmArgs& a, const TileLoc& tl
     voff[i] = static_cast<int>(off) + c * 16;
     dst[i] = row0 * CH * 16;
   }
+}
+
+// The tile kernel's shape constants: wave layout, fragments, load
+// instructions per wave and stage, and LDS stage sizes (16-byte units).
+template <int BM, int BN, int WM, int WN, int EPI, int BK>
+struct DtlShape {
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = 64 * NW;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int CH = BK / 8;                   // 16-byte chunks per tile row
+  static constexpr int KS = BK / 16;                  // 16-wide K slices per stage
+  static constexpr int RPI = 64 / CH;                 // tile rows per 1 KB load instruction
+  static constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  static constexpr int LB = BN / (RPI * NW);          // weight load instructions per wave per stage
+  static constexpr int LX = BM / (RPI * NW);          // token load instructions
+  static constexpr int LPS = LB + LX;
+  static constexpr int WSTG = BN * CH, XSTG = BM * CH;   // units per weight / token stage
+  static constexpr int LDS_UNITS = 3 * WSTG + 2 * XSTG;
+  // Fat tiles: an expert's last remainder of up to kFatExtraRows rows shared
+  // out over its other row tiles, BMF = BM + kFatExtraRows rows at most,
+  // with two stages of both operands (three weight stages no longer fit).
+  static constexpr bool FAT_OK = BM == 256 && WM == 2 && EPI != EPI_F32B;
+  static constexpr int BMF = BM + kFatExtraRows, TMF = BMF / WM, FMF = TMF / 32;
+  static constexpr int LXF = BMF / (RPI * NW), LPF = LB + LXF;
+  static constexpr int XSTGF = BMF * CH;
+};
+
+// Byte offsets from a.B and a.A of the tile's two buffer descriptors, their
+// extents (num_records), and the tile's valid token rows.  Weights: expert
+// g's rows (gate/up: all 2N rows; down: from the tile's first output
+// column on).  Tokens: the tile's own rows of A, or with a row map all of A.
+// num_records is the valid extent, so rows past N or past the tile's last
+// token row read as zero (hardware bounds check).
+struct TileBuffers {
+  int64_t wbase;
+  int wrecords;
+  int64_t abase;
+  int arecords;
+  int vrows;
+};
+
+template <int EPI, int BM, bool FAT_OK, int BMF>
+__host__ __device__ __forceinline__ TileBuffers tile_buffers(const GemmArgs& a, const TileLoc& tl) {
+  const int64_t N = a.N;
+  const int64_t rowb = a.K * 2;                       // bytes per row
+  TileBuffers b;
+  b.wbase = static_cast<int64_t>(tl.g) * ((EPI == EPI_SWIGLU) ? 2 * N : N) * rowb;
+  if (EPI == EPI_SWIGLU) {
+    b.wrecords = static_cast<int>(2 * N * rowb);      // gate rows [0, N), up rows [N, 2N)
+  } else {
+    b.wbase += tl.n0 * rowb;
+    b.wrecords = static_cast<int>((N - tl.n0) * rowb);
+  }
+  const bool gather = a.rowmap != nullptr;
+  b.abase = gather ? 0 : static_cast<int64_t>(tl.row0) * rowb;
+  b.vrows = tl.row_end - tl.row0;                     // at most BM, or BMF for a fat tile
+  const int cap = FAT_OK ? BMF : BM;
+  b.arecords = gather ? static_cast<int>(a.a_rows * rowb) : static_cast<int>((b.vrows < cap ? b.vrows : cap) * rowb);
+  return b;
 }
 
 // Fragment reads of K slice ks (16 wide) -- the FN weight fragments from
@@ -316,34 +376,22 @@ __device__ __forceinline__ void dma_offsets(const GemmArgs& a, const TileLoc& tl
 template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int SP, int LDS_EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the body uses device-only types; the host pass needs only the stub
-  constexpr int NW = WM * WN;
-  constexpr int NT = 64 * NW;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 32, FN = TN / 32;
+  typedef DtlShape<BM, BN, WM, WN, EPI, BK> S;
+  constexpr int NW = S::NW, NT = S::NT, TM = S::TM, TN = S::TN, FM = S::FM, FN = S::FN;
   static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "fragment shape");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
   static_assert(BK == 64, "stage width");
   static_assert(FM <= 4, "active-fragment specialisations cover up to 4 token fragments");
-  constexpr int CH = BK / 8;                          // 16-byte chunks per tile row
-  constexpr int KS = BK / 16;                         // 16-wide K slices per stage
-  constexpr int RPI = 64 / CH;                        // tile rows per 1 KB load instruction
-  constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  constexpr int CH = S::CH, KS = S::KS, RPI = S::RPI, BNO = S::BNO;
   static_assert(BN % (RPI * NW) == 0 && BM % (RPI * NW) == 0, "rows per wave");
-  constexpr int LB = BN / (RPI * NW);                 // weight load instructions per wave per stage
-  constexpr int LX = BM / (RPI * NW);                 // token load instructions
-  constexpr int LPS = LB + LX;
-  constexpr int WSTG = BN * CH, XSTG = BM * CH;       // 16-byte units per weight / token stage
-  constexpr int LDS_UNITS = 3 * WSTG + 2 * XSTG;
+  constexpr int LB = S::LB, LX = S::LX, LPS = S::LPS;
+  constexpr int WSTG = S::WSTG, XSTG = S::XSTG, LDS_UNITS = S::LDS_UNITS;
   static_assert(LDS_UNITS * 16 <= 160 * 1024, "LDS");
   static_assert(locate_scratch_ints(NT) * 4 <= LDS_UNITS * 16, "tile scan scratch fits the stages");
   static_assert(SP >= 1 && SP <= KS && LPS % SP == 0, "DMA spread");
   static_assert(RPI * WN == 32 && LX == FM, "token load instruction i fills token fragment i of the wave's row block");
-  // Fat tiles: an expert's last remainder of up to kFatExtraRows rows shared
-  // out over its other row tiles, BMF = BM + kFatExtraRows rows at most,
-  // with two stages of both operands (three weight stages no longer fit).
-  constexpr bool FAT_OK = BM == 256 && WM == 2 && EPI != EPI_F32B;
-  constexpr int BMF = BM + kFatExtraRows, TMF = BMF / WM, FMF = TMF / 32, LXF = BMF / (RPI * NW), LPF = LB + LXF;
-  constexpr int XSTGF = BMF * CH;
+  constexpr bool FAT_OK = S::FAT_OK;
+  constexpr int BMF = S::BMF, TMF = S::TMF, FMF = S::FMF, LXF = S::LXF, LPF = S::LPF, XSTGF = S::XSTGF;
 
   __shared__ u32x4 lds[LDS_UNITS];
 
@@ -367,28 +415,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   const int nfm = trows <= 0 ? 0 : min(FM, (trows + 31) / 32);
 
   // Buffer descriptors based at the tile's first weight row and first token
-  // row; num_records is the valid extent, so rows past N or past the
-  // tile's last token row read as zero (hardware bounds check) and every
-  // per-lane offset stays a small 32-bit byte offset.
+  // row (or all of A with a row map), so every per-lane offset stays a
+  // small 32-bit byte offset (tile_buffers).
   const int64_t rowb = K * 2;                          // bytes per row
-  const char* wbase = static_cast<const char*>(a.B) +
-      static_cast<int64_t>(tl.g) * ((EPI == EPI_SWIGLU) ? 2 * N : N) * rowb;
-  int wrecords;
-  if (EPI == EPI_SWIGLU) {
-    wrecords = static_cast<int>(2 * N * rowb);         // gate rows [0, N), up rows [N, 2N)
-  } else {
-    wbase += tl.n0 * rowb;
-    wrecords = static_cast<int>((N - tl.n0) * rowb);
-  }
-  // Token rows: the tile's own rows of A, or (row gather) rows of A picked
-  // through rowmap, the descriptor then spanning all of A.
   const bool gather = a.rowmap != nullptr;
-  const char* abase = static_cast<const char*>(a.A) + (gather ? 0 : static_cast<int64_t>(tl.row0) * rowb);
-  const int vrows = tl.row_end - tl.row0;             // at most BM, or BMF for a fat tile
-  const int arecords = gather ? static_cast<int>(a.a_rows * rowb)
-                              : static_cast<int>(min(vrows, FAT_OK ? BMF : BM) * rowb);
-  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, wrecords, kBufFlags);
-  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase), 0, arecords, kBufFlags);
+  const TileBuffers tb = tile_buffers<EPI, BM, FAT_OK, BMF>(a, tl);
+  const int vrows = tb.vrows;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(a.B) + tb.wbase), 0, tb.wrecords, kBufFlags);
+  const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(a.A) + tb.abase), 0, tb.arecords, kBufFlags);
 
   if constexpr (FAT_OK) {
     if (vrows > BM) {

@@ -85,7 +85,7 @@ struct TileLoc {
 // tiles: BM-row tiles, with a last remainder of at most tr - BM rows shared
 // out over the group's other row tiles instead of taking a tile of its own.
 template <int BM>
-__device__ __forceinline__ int row_tiles(int r, int tr) {
+__host__ __device__ __forceinline__ int row_tiles(int r, int tr) {
   if (tr <= BM) return (r + tr - 1) / tr;
   int m = (r + BM - 1) / BM;
   if (m > 1 && r - (m - 1) * BM <= tr - BM) --m;
@@ -212,6 +212,20 @@ __device__ __forceinline__ int tile_order(int bid, int total) {
   return (bid < (q << 1)) ? ((bid & 1) * q + (bid >> 1)) : bid;
 }
 
+// Rows [row0, row_end) of row tile mt of a group with rows [glo, ghi) cut
+// into mt_g row tiles: the group's 32-row fragments are dealt as evenly as
+// possible over its row tiles (the first F % mt_g take one more), so no
+// tile of a ragged group is left with a sliver of rows that still streams a
+// whole weight tile.
+__host__ __device__ __forceinline__ void tile_rows(int glo, int ghi, int mt, int mt_g, int& row0, int& row_end) {
+  const int nf = (ghi - glo + 31) / 32;
+  const int fq = nf / mt_g, fr = nf - fq * mt_g;
+  const int f0 = mt * fq + (mt < fr ? mt : fr);
+  const int f1 = f0 + fq + (mt < fr ? 1 : 0);
+  row0 = glo + 32 * f0;
+  row_end = ghi < glo + 32 * f1 ? ghi : glo + 32 * f1;
+}
+
 // Tile coordinates of logical tile `local` of group g (rows [glo, ghi)):
 // column blocks of SN tiles, row tiles within a block, a narrower last block
 // when SN does not divide the column tiles.
@@ -232,19 +246,13 @@ __device__ __forceinline__ TileLoc tile_coords(const GemmArgs& a, int g, int glo
     mt = r / snr;
     nt = nbf * SN + (r - mt * snr);
   }
-  // Row tile mt takes its share of the group's 32-row fragments: the F
-  // fragments are dealt as evenly as possible over the mt_g row tiles (the
-  // first F % mt_g take one more), so no tile of a ragged group is left
-  // with a sliver of rows that still streams a whole weight tile.
-  const int nf = (ghi - glo + 31) / 32;
-  const int fq = nf / mt_g, fr = nf - fq * mt_g;
-  const int f0 = mt * fq + min(mt, fr);
-  const int f1 = f0 + fq + (mt < fr ? 1 : 0);
+  int row0, row_end;
+  tile_rows(glo, ghi, mt, mt_g, row0, row_end);
   // workgroup-uniform: keep them in scalar registers
   TileLoc tl;
   tl.g = __builtin_amdgcn_readfirstlane(g);
-  tl.row0 = __builtin_amdgcn_readfirstlane(glo + 32 * f0);
-  tl.row_end = __builtin_amdgcn_readfirstlane(min(ghi, glo + 32 * f1));
+  tl.row0 = __builtin_amdgcn_readfirstlane(row0);
+  tl.row_end = __builtin_amdgcn_readfirstlane(row_end);
   tl.n0 = __builtin_amdgcn_readfirstlane(nt * BNO);
   return tl;
 }
