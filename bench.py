@@ -167,7 +167,7 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def setup(wl, device, keep_host: bool = True, mode: str = "auto"):
+def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared: bool = False):
     """Upload the workload's seeded inputs to the GPU and build the layer.
     With keep_host, the storage-format expert weights stay in host memory
     too (for the CPU oracle leg; the DeepSeek-shaped layer holds 22.5 GB)."""
@@ -203,7 +203,7 @@ def setup(wl, device, keep_host: bool = True, mode: str = "auto"):
     sh = W.gen_shared(wl)
     weights = MoeWeights(dev(wr), None if bias is None else torch.from_numpy(bias).to(device), gu, dn,
                          None if sh is None else dev(sh[0]), None if sh is None else dev(sh[1]))
-    layer = MoeLayer(weights, wl.k, wl.score, mode=mode)
+    layer = MoeLayer(weights, wl.k, wl.score, mode=mode, overlap_shared=overlap_shared)
     host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=sh)
     return layer, dev(x), host
 
@@ -581,6 +581,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="c5")
     ap.add_argument("--mode", default="auto", choices=("auto", "grouped", "decode", "batched"),
                     help="layer strategy (auto: decode calls up to 256 routed rows, grouped above)")
+    ap.add_argument("--overlap-shared", action="store_true",
+                    help="run the shared expert on a second stream beside the router, the sort and the routed "
+                         "experts (measured no faster on the DeepSeek-shaped layer; default: after them)")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernels", action="store_true", help="also print per-stage times to stderr")
@@ -629,7 +632,8 @@ def main(argv=None):
         print("MXFP4 experts run on the decode calls only", file=sys.stderr)
         return 2
 
-    layer, x, host = setup(wl, device, keep_host=not args.no_cpu, mode=args.mode)
+    layer, x, host = setup(wl, device, keep_host=not args.no_cpu, mode=args.mode,
+                           overlap_shared=args.overlap_shared)
     st = torch.cuda.current_stream()
     # the projection kernels are timed by events on the launch stream inside
     # the timed steps; an event pair costs a few microseconds, so the
@@ -640,7 +644,11 @@ def main(argv=None):
     for _ in range(args.warmup):
         layer.forward(x)
     torch.cuda.synchronize()
-    counts = layer.counts.cpu().numpy()
+    if layer.use_batched(wl.T):
+        # no sort: the experts the pairs chose
+        counts = np.bincount(layer.ids.cpu().numpy().reshape(-1), minlength=wl.E)
+    else:
+        counts = layer.counts.cpu().numpy()
     active = int((counts > 0).sum())
 
     marks = {}
@@ -711,6 +719,8 @@ def main(argv=None):
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.f, "experts": wl.E,
                    "top_k": wl.k, "score": wl.score, "zipf_s": wl.zipf_s, "shared_d_ff": wl.f_shared,
                    "active_experts": active, "parallelism": "single GPU", "strategy": args.mode,
+                   "shared_expert": None if not wl.f_shared else
+                   ("second stream beside the routed experts" if args.overlap_shared else "after the routed experts"),
                    "timing": "per-step events, caches flushed by a 1 GiB read between steps" if decode
                    else "wall clock over the timed steps"},
         "roofline": roof,

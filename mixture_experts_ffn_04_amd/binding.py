@@ -263,7 +263,8 @@ class MoeLayer:
     the decode calls that stream only the active experts' weights),
     "batched" (the small-batch "batched_mm" strategy: per (token, slot)
     pair, no sort, the combine folded into the down call) or "auto"
-    (decode up to DECODE_MAX_ROWS routed rows, grouped above).
+    ("batched" for one bf16 token, decode up to DECODE_MAX_ROWS routed
+    rows, grouped above).
 
     experts=(e_begin, e_count) makes it one expert-parallel share: the
     router (weights.w_router) covers all experts, weights.w_gate_up and
@@ -276,9 +277,15 @@ class MoeLayer:
     DECODE_MAX_ROWS = 256
 
     def __init__(self, weights: MoeWeights, k: int, score: str, mode: str = "auto",
-                 experts: Optional[tuple] = None):
+                 experts: Optional[tuple] = None, overlap_shared: bool = False):
         load()
         self.w = weights
+        # the shared expert does not depend on the routing: with
+        # overlap_shared (grouped calls) it runs on a second stream from the
+        # start of the layer, beside the router, the sort and the routed
+        # projections, and the combine waits for it
+        self.overlap_shared = overlap_shared
+        self._side = None
         self.k = k
         self.score = score
         self.mode = mode
@@ -304,6 +311,9 @@ class MoeLayer:
     def _alloc(self, T: int):
         if self._T == T:
             return
+        if self._side is not None:
+            # buffers the second stream may still use are about to be freed
+            torch.cuda.current_stream(self.dev).wait_stream(self._side)
         dev, dt, k, E, d, f = self.dev, self.dtype, self.k, self.E, self.d, self.f
         P = T * k
         i32 = torch.int32
@@ -328,6 +338,15 @@ class MoeLayer:
             self.s_y = torch.empty(T, d, device=dev, dtype=dt)
         self._T = T
 
+    def use_batched(self, T: int) -> bool:
+        """The "batched_mm" strategy: when asked for, and in "auto" for a
+        single bf16 token (its k experts are distinct, so each expert's
+        weights are read once either way, and the sort and the combine
+        launches are saved)."""
+        if self.mode == "batched":
+            return True
+        return self.mode == "auto" and T == 1 and not self.mx and self.dtype == torch.bfloat16
+
     def use_decode(self, T: int) -> bool:
         if self.mode == "decode":
             return True
@@ -342,7 +361,7 @@ class MoeLayer:
         T = x.shape[0]
         self._alloc(T)
         w = self.w
-        if self.mode == "batched":
+        if self.use_batched(T):
             return self._batched_stages(x, st)
         dec = self.use_decode(T)
         if self.mx and T * self.k > 1024:
@@ -371,9 +390,15 @@ class MoeLayer:
         ys = None
         if w.shared_gate_up is not None:
             sdec = dec and T <= self.DECODE_MAX_ROWS
-            out.append(("shared_gateup", gateup_swiglu, (x, w.shared_gate_up, self.s_off, self.s_h, sdec, st)))
-            out.append(("shared_down", down, (self.s_h, w.shared_down, self.s_off, self.s_y, sdec, st)))
+            ss = st
+            if self.overlap_shared and not sdec:
+                if self._side is None:
+                    self._side = torch.cuda.Stream(device=self.dev)     # default priority
+                ss = self._side
+            sh = [("shared_gateup", gateup_swiglu, (x, w.shared_gate_up, self.s_off, self.s_h, sdec, ss)),
+                  ("shared_down", down, (self.s_h, w.shared_down, self.s_off, self.s_y, sdec, ss))]
             ys = self.s_y
+            out = sh + out if ss is not st else out + sh
         out.append(("combine", unpermute_combine, (self.y_perm, self.inv_perm, self.wts, ys, self.y, st)))
         return out
 
@@ -405,17 +430,24 @@ class MoeLayer:
         stages named in `stages`) and is appended to marks[stage].  With
         `run`, only the stages named there are enqueued."""
         st = torch.cuda.current_stream() if stream is None else stream
+        side = None
         for name, fn, a in self.stages(x, st):
             if run is not None and name not in run:
                 continue
+            s = a[-1]                                # the stage's launch stream
+            if s is not st and side is None:
+                side = s
+                side.wait_stream(st)                 # x and the buffers are ready
+            if name == "combine" and side is not None:
+                st.wait_stream(side)                 # the shared expert's output is ready
             if marks is None or (stages is not None and name not in stages):
                 fn(*a)
                 continue
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(st)
+            e0.record(s)
             fn(*a)
-            e1.record(st)
+            e1.record(s)
             marks.setdefault(name, []).append((e0, e1))
         return self.y
 

@@ -31,14 +31,9 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 constexpr int kMxRows = 4;            // weight rows per wave
 constexpr int64_t kMxMaxRows = 1024;  // routed rows per call (decode sizes)
-
-// E8M0 scale code -> 2^(code - 127) as fp32 (code 0: 2^-127, a denormal;
-// code 255: NaN).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
-  if (code == 0) return __uint_as_float(0x00400000u);
-  if (code == 255) return __uint_as_float(0x7fc00000u);
-  return __uint_as_float(code << 23);
-}
+// Above this many rows per expert on average the split-K MFMA form runs:
+// the vector form re-reads each activation row for every 4 weight rows.
+constexpr int64_t kMxVectorRowsPerExpert = 1;
 
 // Elements 2B and 2B + 1 of a code dword (byte B) as bf16, times x's pair.
 template <int B>
@@ -136,6 +131,186 @@ __global__ __launch_bounds__(256) void decode_mx_kernel(const uint16_t* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// Several rows per expert: the split-K MFMA form (v_mfma_f32_16x16x32_bf16,
+// weight rows as the 16-row operand, tokens as the 16-column one).
+//
+// K is walked in quads of 128 elements.  In quad j, lane (row i = lane % 16,
+// part q = lane / 16) holds elements 128j + 32q + [0, 32) of its row: one
+// whole MX block, so a single 16-byte load brings its codes and one byte its
+// scale.  MFMA m (0..3) of the quad takes elements 128j + 32q + 8m + [0, 8)
+// from every lane, of the weights and of the tokens alike, which only
+// permutes the order of the reduction over K.  The gfx950 FP4 conversion
+// applies the block's power of two while decoding, so the bf16 operand is
+// the weight's value.  A last half quad (K % 128 == 64) leaves parts 2 and 3
+// without elements: their weights and tokens load as zeros.
+//
+// Workgroup = (expert g, 16 output columns), 4 waves splitting the quads;
+// each wave issues all loads of a batch of U quads before its MFMAs; the
+// four partial sums meet in LDS.
+template <bool SWIGLU, int MC, int U>
+__device__ __forceinline__ void mx_partial(const uint8_t* wq_g, const uint8_t* ws_g, const uint8_t* wq_u,
+                                           const uint8_t* ws_u, const uint16_t* const* xr, int q0, int q1, int part,
+                                           int KB, f32x4* ag, f32x4* au) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int mc = 0; mc < MC; ++mc) {
+    ag[mc] = f32x4{};
+    au[mc] = f32x4{};
+  }
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int qb = q0; qb < q1; qb += U) {
+    u32x4 cg[U], cu[U], tk[U][MC][4];
+    uint32_t sg[U], su[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = (qb + u) * 4 + part;             // this lane's block
+      const bool ok = qb + u < q1 && b < KB;
+      cg[u] = ok ? *(const gu4*)(wq_g + b * 16) : zero;
+      sg[u] = ok ? ws_g[b] : 127u;
+      if (SWIGLU) {
+        cu[u] = ok ? *(const gu4*)(wq_u + b * 16) : zero;
+        su[u] = ok ? ws_u[b] : 127u;
+      }
+#pragma unroll
+      for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) tk[u][mc][c] = ok ? *(const gu4*)(xr[mc] + b * 32 + c * 8) : zero;
+    }
+    __builtin_amdgcn_sched_barrier(0);   // the whole batch of loads is issued before any MFMA waits
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float xg = e8m0_to_f32(sg[u]);
+      const float xu = SWIGLU ? e8m0_to_f32(su[u]) : 0.0f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        u32x4 wg, wu;
+        wg[0] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cg[u][m], xg, 0));
+        wg[1] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cg[u][m], xg, 1));
+        wg[2] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cg[u][m], xg, 2));
+        wg[3] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cg[u][m], xg, 3));
+        if (SWIGLU) {
+          wu[0] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cu[u][m], xu, 0));
+          wu[1] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cu[u][m], xu, 1));
+          wu[2] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cu[u][m], xu, 2));
+          wu[3] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cu[u][m], xu, 3));
+        }
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) {
+          const bf16x8 t = __builtin_bit_cast(bf16x8, tk[u][mc][m]);
+          ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wg), t, ag[mc], 0, 0, 0);
+          if (SWIGLU)
+            au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wu), t, au[mc], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void decode_mx_mfma_kernel(const uint16_t* __restrict__ A,
+                                                             const uint8_t* __restrict__ Bq,
+                                                             const uint8_t* __restrict__ Bs,
+                                                             const int32_t* __restrict__ off,
+                                                             const int32_t* __restrict__ rowmap, int kdiv, int rows,
+                                                             int K, int N, int G, uint16_t* __restrict__ C) {
+  constexpr int MCX = 4;                              // 16-token chunks per pass (64 tokens)
+  constexpr int NH = SWIGLU ? 2 : 1;
+  __shared__ float red[4][MCX][NH][4][64];
+  const int ntiles = N / 16;
+  const int j = blockIdx.x / ntiles;
+  const int n0 = (blockIdx.x - j * ntiles) * 16;
+  const int g = (rows < G) ? nth_active_group(off, G, rows, j) : j;
+  if (g < 0 || g >= G) return;
+  const int lo = clamp_off(off[g], rows);
+  const int hi = clamp_off(off[g + 1], rows);
+  if (hi <= lo) return;                               // expert without rows: its weights are never read
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, part = lane >> 4;
+  const int KB = K / 32;
+  const int64_t brows = SWIGLU ? 2 * static_cast<int64_t>(N) : N;
+  const int64_t wrow = n0 + i16;                      // N is a multiple of 16: always a valid row
+  const int64_t urow = SWIGLU ? N + wrow : wrow;
+  const uint8_t* Bqg = Bq + static_cast<int64_t>(g) * brows * (K / 2);
+  const uint8_t* Bsg = Bs + static_cast<int64_t>(g) * brows * KB;
+  const uint8_t* wq_g = Bqg + wrow * (K / 2);
+  const uint8_t* wq_u = Bqg + urow * (K / 2);
+  const uint8_t* ws_g = Bsg + wrow * KB;
+  const uint8_t* ws_u = Bsg + urow * KB;
+  // contiguous quads per wave
+  const int quads = (KB + 3) / 4;
+  const int per = (quads + 3) / 4;
+  const int q0 = min(quads, wave * per);
+  const int q1 = min(quads, q0 + per);
+  for (int m0 = lo; m0 < hi; m0 += 16 * MCX) {
+    const int mcn = min(MCX, (hi - m0 + 15) / 16);
+    const uint16_t* xr[MCX];
+#pragma unroll
+    for (int mc = 0; mc < MCX; ++mc) {
+      const int row = m0 + mc * 16 + i16;             // rows past the group read a valid row; never stored
+      int src = row < hi ? row : lo;
+      if (rowmap) src = clamp_off(rowmap[src], rows - 1) / kdiv;
+      xr[mc] = A + static_cast<int64_t>(src) * K;
+    }
+    f32x4 ag[MCX], au[MCX];
+    if (mcn == 1) {
+      mx_partial<SWIGLU, 1, 4>(wq_g, ws_g, wq_u, ws_u, xr, q0, q1, part, KB, ag, au);
+    } else if (mcn == 2) {
+      mx_partial<SWIGLU, 2, 2>(wq_g, ws_g, wq_u, ws_u, xr, q0, q1, part, KB, ag, au);
+    } else {
+      mx_partial<SWIGLU, 4, 1>(wq_g, ws_g, wq_u, ws_u, xr, q0, q1, part, KB, ag, au);
+    }
+#pragma unroll
+    for (int mc = 0; mc < MCX; ++mc) {
+      if (mc < mcn) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          red[wave][mc][0][r][lane] = ag[mc][r];
+          if (SWIGLU) red[wave][mc][NH - 1][r][lane] = au[mc][r];
+        }
+      }
+    }
+    __syncthreads();
+    if (wave < mcn) {
+      const int mc = wave;
+      const int row = m0 + mc * 16 + i16;
+      if (row < hi) {
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float gs = red[0][mc][0][r][lane] + red[1][mc][0][r][lane] + red[2][mc][0][r][lane] +
+                     red[3][mc][0][r][lane];
+          if (SWIGLU) {
+            const float us = red[0][mc][NH - 1][r][lane] + red[1][mc][NH - 1][r][lane] +
+                             red[2][mc][NH - 1][r][lane] + red[3][mc][NH - 1][r][lane];
+            gs = silu(gs) * us;
+          }
+          o[r] = gs;
+        }
+        uint2 v;
+        v.x = pack_bf16x2(o[0], o[1]);
+        v.y = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * N + n0 + 4 * part) = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <bool SWIGLU>
+moe_status launch_mx_mfma(const void* A, const void* Bq, const void* Bs, const int32_t* off, const int32_t* rowmap,
+                          int kdiv, int64_t rows, int64_t K, int64_t N, int G, void* C, hipStream_t st) {
+  const int64_t groups = G < rows ? G : rows;
+  const int64_t grid = groups * (N / 16);
+  if (grid == 0) return MOE_OK;
+  if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((decode_mx_mfma_kernel<SWIGLU>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Bq), static_cast<const uint8_t*>(Bs),
+                     off, rowmap, kdiv, static_cast<int>(rows), static_cast<int>(K), static_cast<int>(N), G,
+                     static_cast<uint16_t*>(C));
+  return launch_status();
+}
+
 template <bool SWIGLU>
 moe_status launch_mx(const void* A, const void* Bq, const void* Bs, const int32_t* off, const int32_t* rowmap,
                      int kdiv, int64_t rows, int64_t K, int64_t N, int G, void* C, hipStream_t st) {
@@ -180,6 +355,9 @@ extern "C" moe_status moe_decode_gateup_swiglu_mxfp4(const void* x, const int32_
   moe_status s = check_mx(x, wq_gate_up, ws_gate_up, offsets, rows, d, f, E, h, d);
   if (s != MOE_OK || rows == 0) return s;
   if (perm && (k < 1 || k > kMaxK || rows % k != 0)) return MOE_ERR_INVALID_ARG;
+  if (rows > kMxVectorRowsPerExpert * E)
+    return launch_mx_mfma<true>(x, wq_gate_up, ws_gate_up, offsets, perm, perm ? k : 1, rows, d, f, E, h,
+                                as_stream(stream));
   return launch_mx<true>(x, wq_gate_up, ws_gate_up, offsets, perm, perm ? k : 1, rows, d, f, E, h, as_stream(stream));
 }
 
@@ -188,5 +366,7 @@ extern "C" moe_status moe_decode_down_mxfp4(const void* h, const void* wq_down, 
                                             void* y_perm, void* stream) {
   moe_status s = check_mx(h, wq_down, ws_down, offsets, rows, d, f, E, y_perm, f);
   if (s != MOE_OK || rows == 0) return s;
+  if (rows > kMxVectorRowsPerExpert * E)
+    return launch_mx_mfma<false>(h, wq_down, ws_down, offsets, nullptr, 1, rows, f, d, E, y_perm, as_stream(stream));
   return launch_mx<false>(h, wq_down, ws_down, offsets, nullptr, 1, rows, f, d, E, y_perm, as_stream(stream));
 }

@@ -133,7 +133,9 @@ def test_full_size(gpu, name):
     E, k, T, P = wl.E, wl.k, wl.T, wl.P
 
     log(f"[{name}] GPU layer ({time.time() - t0:.1f}s)")
-    layer = B.MoeLayer(weights, k, wl.score)
+    # the sort-based strategies (grouped, or the decode calls for small
+    # batches); the "batched_mm" strategy is checked further down
+    layer = B.MoeLayer(weights, k, wl.score, mode="decode" if P <= B.MoeLayer.DECODE_MAX_ROWS else "grouped")
     y = layer.forward(x_dev)
     torch.cuda.synchronize()
     g_logits = layer.logits.cpu().numpy().astype(np.float64)

@@ -824,6 +824,26 @@ def test_expert_parallel_partition_sum(gpu, name, mode):
     U.assert_close(total, ref, wl.dtype, f"{name} sum of {n} expert-parallel shares")
 
 
+@pytest.mark.parametrize("T", [301, 40])
+def test_shared_expert_on_second_stream(gpu, T):
+    """The shared expert launched on a second stream beside the router, the
+    sort and the routed projections gives the same bits as the serial layer,
+    step after step (and across a change of token count)."""
+    wl, inp = U.small_inputs("c5s")
+    weights = U.device_weights(wl, inp)
+    x = U.dev_tensor(np.asarray(inp["x"])[:T], wl.dtype)
+    serial = B().MoeLayer(weights, wl.k, wl.score, mode="grouped")
+    ref = U.host_bits(serial.forward(x).clone())
+    over = B().MoeLayer(weights, wl.k, wl.score, mode="grouped", overlap_shared=True)
+    for _ in range(3):
+        y = over.forward(x)
+    torch.cuda.synchronize()
+    assert (U.host_bits(y) == ref).all()
+    y2 = over.forward(x[:T // 2].contiguous())
+    torch.cuda.synchronize()
+    assert (U.host_bits(y2) == U.host_bits(serial.forward(x[:T // 2].contiguous()))).all()
+
+
 def test_layer_deterministic_and_token_equivariant(gpu):
     wl, inp = U.small_inputs("c4s")
     layer = B().MoeLayer(U.device_weights(wl, inp), wl.k, wl.score)
