@@ -46,6 +46,9 @@ KERNEL_SOURCES = {
     "decode_gateup": ["decode.hip", "common.h"],
     "decode_down": ["decode.hip", "common.h"],
     "decode_mx_gateup": ["decode_mx.hip", "common.h"],
+    "decode_mx_down": ["decode_mx.hip", "common.h"],
+    "batched_gateup": ["batched.hip", "common.h"],
+    "batched_down": ["batched.hip", "common.h"],
 }
 
 
@@ -698,7 +701,12 @@ def main(argv=None):
     tokens_per_s = wl.T / (ms * 1e-3)
 
     kernels = kernel_rooflines(wl, active, kern_ms, decode)
-    kname = ("decode_mx_gateup" if wl.experts == "mxfp4" else "decode_gateup") if decode else "gateup"
+    if layer.use_batched(wl.T):
+        kname = "batched_gateup"
+    elif decode:
+        kname = "decode_mx_gateup" if wl.experts == "mxfp4" else "decode_gateup"
+    else:
+        kname = "gateup"
     roof = dict(kernels["gateup"])
     roof["kernel"] = kname
     roof["traffic"] = load_traffic(kname, wl.name)
