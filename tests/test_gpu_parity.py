@@ -99,7 +99,10 @@ ROUTER_PATHS = [(40, 8, 4096, 2), (50, 16, 6144, 4), (300, 40, 1024, 4), (8192, 
                 (1030, 8, 320, 2), (16384, 128, 256, 8),
                 # one or two 64-wide K stages on each path: one wave per expert row,
                 # split-K streaming, both flat tile shapes
-                (40, 8, 64, 2), (2000, 32, 64, 4), (2048, 128, 64, 8), (8192, 256, 64, 8), (1500, 256, 128, 8)]
+                (40, 8, 64, 2), (2000, 32, 64, 4), (2048, 128, 64, 8), (8192, 256, 64, 8), (1500, 256, 128, 8),
+                # a few tokens, E up to 128
+                (1, 32, 2880, 4), (3, 64, 4096, 8), (4, 16, 8192, 2), (2, 8, 64, 2), (1, 40, 192, 16),
+                (4, 64, 2880, 4), (1, 128, 2880, 4)]
 
 
 @pytest.mark.parametrize("T,E,d,k", ROUTER_PATHS)

@@ -51,3 +51,36 @@ def test_permute_noalloc_rejects_sizes_past_its_scratch(gpu):
     T, k = 1024 * 1024 // 8 + 1, 8
     st = lib.moe_permute_noalloc(P, None, T, 0, 256, k, B.MOE_BF16, P, P, P, P, None, None)
     assert st == B.MOE_ERR_WORKSPACE
+
+
+def test_permute_noalloc_in_a_graph(gpu):
+    """The call its callers need: captured in a HIP graph (no allocation, no
+    memset inside) and replayed several times with new ids and other work on
+    the stream in between; every replay equals the workspace form."""
+    from mixture_experts_ffn_04_amd import binding as B
+    T, E, k = 3000, 64, 4
+    x = torch.from_numpy(W.gen_matrix((T, 64), seed=5).view(np.int16)).to(gpu).view(torch.bfloat16)
+    ids_d = torch.from_numpy(W.gen_ids(T, E, k, seed=1)).to(gpu)
+    P = T * k
+    outs = [torch.empty(E, dtype=torch.int32, device=gpu), torch.empty(E + 1, dtype=torch.int32, device=gpu),
+            torch.empty(P, dtype=torch.int32, device=gpu), torch.empty(P, dtype=torch.int32, device=gpu)]
+    xp = torch.empty(P, 64, dtype=torch.bfloat16, device=gpu)
+    side = torch.cuda.Stream(device=gpu)
+    side.wait_stream(torch.cuda.current_stream(gpu))
+    with torch.cuda.stream(side):
+        B.permute_noalloc(ids_d, x, E, *outs, xp)          # the device's scratch address is looked up here
+    torch.cuda.current_stream(gpu).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        B.permute_noalloc(ids_d, x, E, *outs, xp)
+    for rep in range(4):
+        ids = W.gen_ids(T, E, k, seed=10 + rep, zipf_s=1.2 if rep % 2 else None)
+        ids_d.copy_(torch.from_numpy(ids))
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.cpu().numpy() for t in outs] + [xp.view(torch.int16).cpu().numpy()]
+        ref = _run(B, "ws", ids, x, E, gpu)
+        for name, a, b in zip(("counts", "offsets", "perm", "inv_perm", "x_perm"), ref, got):
+            assert (a == b).all(), f"replay {rep}: {name} differs"
+        torch.sum(x.float())                                  # other work between replays
