@@ -49,6 +49,8 @@ KERNEL_SOURCES = {
     "decode_mx_down": ["decode_mx.hip", "common.h"],
     "batched_gateup": ["batched.hip", "common.h"],
     "batched_down": ["batched.hip", "common.h"],
+    "batched_mx_gateup": ["decode_mx.hip", "common.h"],
+    "batched_mx_down": ["decode_mx.hip", "common.h"],
 }
 
 
@@ -631,8 +633,8 @@ def main(argv=None):
     device = torch.device("cuda:0")
     wl = W.get(args.workload)
     decode = args.workload.startswith("c3")   # weight streaming: timed per step after a cache flush
-    if wl.experts == "mxfp4" and args.mode not in ("auto", "decode"):
-        print("MXFP4 experts run on the decode calls only", file=sys.stderr)
+    if wl.experts == "mxfp4" and args.mode not in ("auto", "decode", "batched"):
+        print("MXFP4 experts run on the decode or the batched calls", file=sys.stderr)
         return 2
 
     layer, x, host = setup(wl, device, keep_host=not args.no_cpu, mode=args.mode,
@@ -702,7 +704,7 @@ def main(argv=None):
 
     kernels = kernel_rooflines(wl, active, kern_ms, decode)
     if layer.use_batched(wl.T):
-        kname = "batched_gateup"
+        kname = "batched_mx_gateup" if wl.experts == "mxfp4" else "batched_gateup"
     elif decode:
         kname = "decode_mx_gateup" if wl.experts == "mxfp4" else "decode_gateup"
     else:

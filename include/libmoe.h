@@ -35,6 +35,8 @@
  *   moe_batched_gateup_swiglu        the small-batch "batched_mm" strategy:
  *   moe_batched_down_combine         per (token, slot) pair, no sort; the
  *                                    down call also applies the weights
+ *   moe_batched_gateup_swiglu_mxfp4  the same with MXFP4 expert weights
+ *   moe_batched_down_combine_mxfp4
  *
  * All experts of a layer share one packed buffer per projection, the layout
  * the article's "Dynamic Weight Loading with WeightConverter" subsection
@@ -368,6 +370,29 @@ MOE_API moe_status moe_batched_down_combine(const void* h, const int32_t* topk_i
                                             const void* w_down, const void* y_shared, int64_t T, int64_t d,
                                             int64_t f, int32_t E, int32_t k, moe_dtype dtype, void* y,
                                             void* stream);
+
+/*
+ * "batched_mm" with MXFP4 expert weights (the two sections above together:
+ * the article's small-batch strategy on the MXFP4 layout of the
+ * moe_decode_*_mxfp4 calls), bf16 activations and outputs, fp32
+ * accumulation:
+ *   moe_batched_gateup_swiglu_mxfp4: h[p] as moe_batched_gateup_swiglu with
+ *     wq_gate_up [E][2f][d/2], ws_gate_up [E][2f][d/32].
+ *   moe_batched_down_combine_mxfp4: y as moe_batched_down_combine with
+ *     wq_down [E][d][f/2], ws_down [E][d][f/32] (y_shared may be NULL).
+ * Pairs whose id is outside [0, E) get no h row and add nothing to y.
+ * T*k <= 1024 and d, f <= 8192, else MOE_ERR_UNSUPPORTED; x, h, codes
+ * 16-byte aligned.
+ */
+MOE_API moe_status moe_batched_gateup_swiglu_mxfp4(const void* x, const int32_t* topk_ids,
+                                                   const void* wq_gate_up, const void* ws_gate_up, int64_t T,
+                                                   int64_t d, int64_t f, int32_t E, int32_t k, void* h,
+                                                   void* stream);
+
+MOE_API moe_status moe_batched_down_combine_mxfp4(const void* h, const int32_t* topk_ids, const float* topk_w,
+                                                  const void* wq_down, const void* ws_down, const void* y_shared,
+                                                  int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, void* y,
+                                                  void* stream);
 
 #ifdef __cplusplus
 }

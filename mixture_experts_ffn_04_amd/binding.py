@@ -27,7 +27,8 @@ EXPORTS = (
     "moe_grouped_gemm_down", "moe_unpermute_combine", "moe_decode_gateup_swiglu",
     "moe_decode_down", "moe_decode_gateup_swiglu_gather", "moe_grouped_gemm_gateup_swiglu_gather",
     "moe_localize_ids", "moe_permute_noalloc", "moe_batched_gateup_swiglu", "moe_batched_down_combine",
-    "moe_decode_gateup_swiglu_mxfp4", "moe_decode_down_mxfp4",
+    "moe_decode_gateup_swiglu_mxfp4", "moe_decode_down_mxfp4", "moe_batched_gateup_swiglu_mxfp4",
+    "moe_batched_down_combine_mxfp4",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -55,6 +56,8 @@ _SIGS = {
     "moe_batched_down_combine": ([P, P, P, P, P, I64, I64, I64, I32, I32, ctypes.c_int, P, P], ctypes.c_int),
     "moe_decode_gateup_swiglu_mxfp4": ([P, P, I32, P, P, P, I64, I64, I64, I32, P, P], ctypes.c_int),
     "moe_decode_down_mxfp4": ([P, P, P, P, I64, I64, I64, I32, P, P], ctypes.c_int),
+    "moe_batched_gateup_swiglu_mxfp4": ([P, P, P, P, I64, I64, I64, I32, I32, P, P], ctypes.c_int),
+    "moe_batched_down_combine_mxfp4": ([P, P, P, P, P, P, I64, I64, I64, I32, I32, P, P], ctypes.c_int),
 }
 
 
@@ -223,6 +226,26 @@ def down_mxfp4(h, wq_down, ws_down, offsets, y_perm, stream=None):
         _ptr(h), _ptr(wq_down), _ptr(ws_down), _ptr(offsets), rows, d, f, E, _ptr(y_perm), _stream(stream)))
 
 
+def batched_gateup_swiglu_mxfp4(x, topk_ids, wq_gate_up, ws_gate_up, h, stream=None):
+    """The "batched_mm" gate/up with MXFP4 expert weights: h [T*k, f] in
+    pair order, no sort."""
+    T, d = x.shape
+    k = topk_ids.shape[1]
+    E, f2, _ = wq_gate_up.shape
+    _check("moe_batched_gateup_swiglu_mxfp4", load().moe_batched_gateup_swiglu_mxfp4(
+        _ptr(x), _ptr(topk_ids), _ptr(wq_gate_up), _ptr(ws_gate_up), T, d, f2 // 2, E, k, _ptr(h), _stream(stream)))
+
+
+def batched_down_combine_mxfp4(h, topk_ids, topk_w, wq_down, ws_down, y_shared, y, stream=None):
+    """The "batched_mm" down projection with MXFP4 expert weights and the
+    weighted combine folded in."""
+    T, k = topk_ids.shape
+    E, d, fh = wq_down.shape
+    _check("moe_batched_down_combine_mxfp4", load().moe_batched_down_combine_mxfp4(
+        _ptr(h), _ptr(topk_ids), _ptr(topk_w), _ptr(wq_down), _ptr(ws_down), _ptr(y_shared), T, d, 2 * fh, E, k,
+        _ptr(y), _stream(stream)))
+
+
 def unpermute_combine(y_perm, inv_perm, topk_w, y_shared, y, stream=None):
     T, k = topk_w.shape
     d = y.shape[1]
@@ -304,8 +327,8 @@ class MoeLayer:
         self.f = weights.w_down.shape[2] * (2 if self.mx else 1)
         self.dev = weights.w_router.device
         self.dtype = weights.w_router.dtype             # activations
-        if self.mx and mode not in ("auto", "decode"):
-            raise ValueError("MXFP4 experts run on the decode calls only")
+        if self.mx and mode not in ("auto", "decode", "batched"):
+            raise ValueError("MXFP4 experts run on the decode or the batched calls")
         self._T = None
 
     def _alloc(self, T: int):
@@ -340,12 +363,12 @@ class MoeLayer:
 
     def use_batched(self, T: int) -> bool:
         """The "batched_mm" strategy: when asked for, and in "auto" for a
-        single bf16 token (its k experts are distinct, so each expert's
-        weights are read once either way, and the sort and the combine
-        launches are saved)."""
+        single token with bf16 activations, bf16 or MXFP4 experts (its k
+        experts are distinct, so each expert's weights are read once either
+        way, and the sort and the combine launches are saved)."""
         if self.mode == "batched":
             return True
-        return self.mode == "auto" and T == 1 and not self.mx and self.dtype == torch.bfloat16
+        return self.mode == "auto" and T == 1 and self.dtype == torch.bfloat16
 
     def use_decode(self, T: int) -> bool:
         if self.mode == "decode":
@@ -419,8 +442,15 @@ class MoeLayer:
             out.append(("shared_gateup", gateup_swiglu, (x, w.shared_gate_up, self.s_off, self.s_h, True, st)))
             out.append(("shared_down", down, (self.s_h, w.shared_down, self.s_off, self.s_y, True, st)))
             ys = self.s_y
-        out.append(("gateup", batched_gateup_swiglu, (x, ids, w.w_gate_up, self.h, st)))
-        out.append(("down", batched_down_combine, (self.h, ids, self.wts, w.w_down, ys, self.y, st)))
+        if self.mx:
+            if T * self.k > 1024:
+                raise ValueError("MXFP4 experts: at most 1024 routed rows (the batched calls)")
+            out.append(("gateup", batched_gateup_swiglu_mxfp4, (x, ids, w.w_gate_up, w.w_gate_up_scales, self.h, st)))
+            out.append(("down", batched_down_combine_mxfp4, (self.h, ids, self.wts, w.w_down, w.w_down_scales, ys,
+                                                             self.y, st)))
+        else:
+            out.append(("gateup", batched_gateup_swiglu, (x, ids, w.w_gate_up, self.h, st)))
+            out.append(("down", batched_down_combine, (self.h, ids, self.wts, w.w_down, ys, self.y, st)))
         return out
 
     def forward(self, x: torch.Tensor, stream=None, marks: Optional[dict] = None,

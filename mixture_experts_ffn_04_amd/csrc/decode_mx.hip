@@ -56,6 +56,75 @@ __device__ __forceinline__ float block_dot(const u32x4& q, const u32x4 (&x)[4]) 
   return s;
 }
 
+// The codes and scales of the kMxRows weight rows wr[] of one expert (Bqg,
+// Bsg: its codes [rows][K/2] and scales [rows][K/32]): lane l holds blocks
+// l, l + 64, ... (CI of them).
+template <int CI>
+__device__ __forceinline__ void mx_load_rows(const uint8_t* Bqg, const uint8_t* Bsg, const int (&wr)[kMxRows], int K,
+                                             int KB, int lane, u32x4 (&wq)[kMxRows][CI], float (&ws)[kMxRows][CI]) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int r = 0; r < kMxRows; ++r) {
+#pragma unroll
+    for (int i = 0; i < CI; ++i) {
+      const int b = lane + 64 * i;
+      const bool ok = b < KB;
+      wq[r][i] = ok ? *(const gu4*)(Bqg + static_cast<int64_t>(wr[r]) * (K / 2) + b * 16) : zero;
+      ws[r][i] = ok ? e8m0_to_f32(Bsg[static_cast<int64_t>(wr[r]) * KB + b]) : 0.0f;
+    }
+  }
+}
+
+// The wave's dot products of one activation row xr (bf16, K long) with its
+// kMxRows weight rows, in every lane: per lane, each block's sum times the
+// block's scale, accumulated over the lane's blocks in order, then summed
+// across the wave.
+template <int CI>
+__device__ __forceinline__ void mx_dot_rows(const u32x4 (&wq)[kMxRows][CI], const float (&ws)[kMxRows][CI],
+                                            const uint16_t* xr, int KB, int lane, float (&acc)[kMxRows]) {
+#pragma unroll
+  for (int r = 0; r < kMxRows; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CI; ++i) {
+    const int b = lane + 64 * i;
+    if (b < KB) {
+      u32x4 xv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xv[c] = *(const gu4*)(xr + b * 32 + c * 8);
+#pragma unroll
+      for (int r = 0; r < kMxRows; ++r) acc[r] = fmaf(block_dot(wq[r][i], xv), ws[r][i], acc[r]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+    for (int r = 0; r < kMxRows; ++r) acc[r] += __shfl_xor(acc[r], o, 64);
+  }
+}
+
+// The wave's outputs (lane 0 stores them at crow): SwiGLU of rows (0, 2)
+// and (1, 3) -- the gate and up rows of two columns -- or the four rows.
+template <bool SWIGLU>
+__device__ __forceinline__ void mx_store(const float (&acc)[kMxRows], int lane, uint16_t* crow) {
+  if (lane != 0) return;
+  if (SWIGLU) {
+    *reinterpret_cast<uint32_t*>(crow) = pack_bf16x2(silu(acc[0]) * acc[2], silu(acc[1]) * acc[3]);
+  } else {
+    uint2 v;
+    v.x = pack_bf16x2(acc[0], acc[1]);
+    v.y = pack_bf16x2(acc[2], acc[3]);
+    *reinterpret_cast<uint2*>(crow) = v;
+  }
+}
+
+// Weight rows of the wave's output columns n0, n0 + 1 (SwiGLU: gate rows n0,
+// n0 + 1 and up rows N + n0, N + n0 + 1) or n0 .. n0 + 3.
+template <bool SWIGLU>
+__device__ __forceinline__ void mx_wave_rows(int n0, int N, int (&wr)[kMxRows]) {
+#pragma unroll
+  for (int r = 0; r < kMxRows; ++r) wr[r] = SWIGLU ? (r < 2 ? n0 + r : N + n0 + r - 2) : n0 + r;
+}
+
 // SWIGLU: C = h [rows][N], B = gate/up [G][2N][K/2] codes + [G][2N][K/32]
 // scales; else C = y_perm [rows][N], B = down [G][N][K/2] + [G][N][K/32].
 // A: activation rows [.][K] bf16; with rowmap, row r reads A[rowmap[r] /
@@ -79,55 +148,103 @@ __global__ __launch_bounds__(256) void decode_mx_kernel(const uint16_t* __restri
   const int n0 = cb * CPB + wave * CPW;
   const int KB = K / 32;                                 // blocks per row
   const int64_t brows = SWIGLU ? 2 * static_cast<int64_t>(N) : N;
-  const uint8_t* Bqg = Bq + static_cast<int64_t>(g) * brows * (K / 2);
-  const uint8_t* Bsg = Bs + static_cast<int64_t>(g) * brows * KB;
   int wr[kMxRows];
-#pragma unroll
-  for (int r = 0; r < kMxRows; ++r) wr[r] = SWIGLU ? (r < 2 ? n0 + r : N + n0 + r - 2) : n0 + r;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  mx_wave_rows<SWIGLU>(n0, N, wr);
   u32x4 wq[kMxRows][CI];
   float ws[kMxRows][CI];
-#pragma unroll
-  for (int r = 0; r < kMxRows; ++r) {
-#pragma unroll
-    for (int i = 0; i < CI; ++i) {
-      const int b = lane + 64 * i;
-      const bool ok = b < KB;
-      wq[r][i] = ok ? *(const gu4*)(Bqg + static_cast<int64_t>(wr[r]) * (K / 2) + b * 16) : zero;
-      ws[r][i] = ok ? e8m0_to_f32(Bsg[static_cast<int64_t>(wr[r]) * KB + b]) : 0.0f;
-    }
-  }
+  mx_load_rows<CI>(Bq + static_cast<int64_t>(g) * brows * (K / 2), Bs + static_cast<int64_t>(g) * brows * KB, wr, K,
+                   KB, lane, wq, ws);
   for (int m = lo; m < hi; ++m) {
     const int src = rowmap ? clamp_off(rowmap[m], rows - 1) / kdiv : m;
-    const uint16_t* xr = A + static_cast<int64_t>(src) * K;
+    float acc[kMxRows];
+    mx_dot_rows<CI>(wq, ws, A + static_cast<int64_t>(src) * K, KB, lane, acc);
+    mx_store<SWIGLU>(acc, lane, C + static_cast<int64_t>(m) * N + n0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The "batched_mm" strategy with MXFP4 experts (the article's section
+// "Expert Backend"): every (token, slot) pair p multiplies the weights of
+// its expert ids[p] in place, with no sort; the down call applies the
+// routing weights and sums a token's slots.  The per-row arithmetic is that
+// of decode_mx_kernel, so a pair's h row equals the one the decode call's
+// vector form computes, bit for bit.
+
+// h[p][n] for p < P: workgroup = (pair p, 8 output columns), two per wave.
+template <int CI>
+__global__ __launch_bounds__(256) void batched_mx_gateup_kernel(const uint16_t* __restrict__ x,
+                                                                const int32_t* __restrict__ ids,
+                                                                const uint8_t* __restrict__ Bq,
+                                                                const uint8_t* __restrict__ Bs, int P, int k, int E,
+                                                                int K, int N, uint16_t* __restrict__ h) {
+  constexpr int CPW = kMxRows / 2, CPB = 4 * CPW;
+  const int ncb = N / CPB;
+  const int p = blockIdx.x / ncb;
+  const int cb = blockIdx.x - p * ncb;
+  if (p >= P) return;
+  const int e = ids[p];
+  if (e < 0 || e >= E) return;                           // a pair of an expert held elsewhere
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = cb * CPB + wave * CPW;
+  const int KB = K / 32;
+  int wr[kMxRows];
+  mx_wave_rows<true>(n0, N, wr);
+  u32x4 wq[kMxRows][CI];
+  float ws[kMxRows][CI];
+  mx_load_rows<CI>(Bq + static_cast<int64_t>(e) * 2 * N * (K / 2), Bs + static_cast<int64_t>(e) * 2 * N * KB, wr, K,
+                   KB, lane, wq, ws);
+  float acc[kMxRows];
+  mx_dot_rows<CI>(wq, ws, x + static_cast<int64_t>(p / k) * K, KB, lane, acc);
+  mx_store<true>(acc, lane, h + static_cast<int64_t>(p) * N + n0);
+}
+
+// y[t][c] = sum_j w[t][j] * (h[t*k+j] . Wd[e_tj][c])  (+ y_shared[t][c]),
+// in fp32 in increasing j, then the shared row, rounded once.  Workgroup =
+// (token t, 4 output columns); wave w takes slots j = w, w + 4, ..., each
+// slot's four dot products go to LDS, and one thread per column sums them
+// in slot order.  Slots with an id outside [0, E) add nothing.
+template <int CI>
+__global__ __launch_bounds__(256) void batched_mx_down_combine_kernel(
+    const uint16_t* __restrict__ h, const int32_t* __restrict__ ids, const float* __restrict__ wts,
+    const uint8_t* __restrict__ Bq, const uint8_t* __restrict__ Bs, const uint16_t* __restrict__ ys, int T, int k,
+    int E, int K, int N, uint16_t* __restrict__ y) {
+  __shared__ float part[kMaxK][kMxRows];
+  const int ncb = N / kMxRows;
+  const int t = blockIdx.x / ncb;
+  const int c0 = (blockIdx.x - t * ncb) * kMxRows;
+  if (t >= T) return;                                    // uniform over the workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int KB = K / 32;
+  for (int j = wave; j < k; j += 4) {
+    const int64_t p = static_cast<int64_t>(t) * k + j;
+    const int e = ids[p];
     float acc[kMxRows] = {};
-#pragma unroll
-    for (int i = 0; i < CI; ++i) {
-      const int b = lane + 64 * i;
-      if (b < KB) {
-        u32x4 xv[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) xv[c] = *(const gu4*)(xr + b * 32 + c * 8);
-#pragma unroll
-        for (int r = 0; r < kMxRows; ++r) acc[r] = fmaf(block_dot(wq[r][i], xv), ws[r][i], acc[r]);
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-#pragma unroll
-      for (int r = 0; r < kMxRows; ++r) acc[r] += __shfl_xor(acc[r], o, 64);
+    if (e >= 0 && e < E) {
+      int wr[kMxRows];
+      mx_wave_rows<false>(c0, N, wr);
+      u32x4 wq[kMxRows][CI];
+      float ws[kMxRows][CI];
+      mx_load_rows<CI>(Bq + static_cast<int64_t>(e) * N * (K / 2), Bs + static_cast<int64_t>(e) * N * KB, wr, K, KB,
+                       lane, wq, ws);
+      mx_dot_rows<CI>(wq, ws, h + p * K, KB, lane, acc);
     }
     if (lane == 0) {
-      uint16_t* crow = C + static_cast<int64_t>(m) * N + n0;
-      if (SWIGLU) {
-        *reinterpret_cast<uint32_t*>(crow) = pack_bf16x2(silu(acc[0]) * acc[2], silu(acc[1]) * acc[3]);
-      } else {
-        uint2 v;
-        v.x = pack_bf16x2(acc[0], acc[1]);
-        v.y = pack_bf16x2(acc[2], acc[3]);
-        *reinterpret_cast<uint2*>(crow) = v;
-      }
+#pragma unroll
+      for (int r = 0; r < kMxRows; ++r) part[j][r] = acc[r];
     }
+  }
+  __syncthreads();
+  if (threadIdx.x < kMxRows) {
+    const int c = c0 + threadIdx.x;
+    float acc = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int64_t p = static_cast<int64_t>(t) * k + j;
+      const int e = ids[p];
+      if (e >= 0 && e < E) acc = fmaf(wts[p], part[j][threadIdx.x], acc);
+    }
+    const int64_t o = static_cast<int64_t>(t) * N + c;
+    if (ys) acc += bf16_to_f32(ys[o]);
+    y[o] = f32_to_bf16(acc);
   }
 }
 
@@ -343,10 +460,64 @@ moe_status check_mx(const void* in, const void* wq, const void* ws, const int32_
   return MOE_OK;
 }
 
+constexpr int64_t kMxBatchedMaxPairs = 1024;
+
+moe_status check_batched_mx(const void* in, const int32_t* ids, const void* wq, const void* ws, int64_t T, int64_t d,
+                            int64_t f, int32_t E, int32_t k, const void* out) {
+  if (T < 0 || d <= 0 || f <= 0 || E < 1 || k < 1 || k > kMaxK) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE || T * k > kMxBatchedMaxPairs || d > 8192 || f > 8192) return MOE_ERR_UNSUPPORTED;
+  if (d % 64 != 0 || f % 64 != 0) return MOE_ERR_ALIGNMENT;
+  if (T == 0) return MOE_OK;
+  if (!in || !ids || !wq || !ws || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(in) || !aligned16(wq)) return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" moe_status moe_batched_gateup_swiglu_mxfp4(const void* x, const int32_t* topk_ids, const void* wq_gate_up,
+                                                      const void* ws_gate_up, int64_t T, int64_t d, int64_t f,
+                                                      int32_t E, int32_t k, void* h, void* stream) {
+  moe_status s = check_batched_mx(x, topk_ids, wq_gate_up, ws_gate_up, T, d, f, E, k, h);
+  if (s != MOE_OK || T == 0) return s;
+  const int64_t P = T * k;
+  const int KB = static_cast<int>(d / 32);
+  const dim3 grid(static_cast<unsigned>(P * (f / (2 * kMxRows))));
+#define MOE_BMX_GU(CI_)                                                                                          \
+  hipLaunchKernelGGL((batched_mx_gateup_kernel<CI_>), grid, dim3(256), 0, as_stream(stream),                     \
+                     static_cast<const uint16_t*>(x), topk_ids, static_cast<const uint8_t*>(wq_gate_up),          \
+                     static_cast<const uint8_t*>(ws_gate_up), static_cast<int>(P), k, E, static_cast<int>(d),      \
+                     static_cast<int>(f), static_cast<uint16_t*>(h))
+  if (KB <= 64) MOE_BMX_GU(1);
+  else if (KB <= 128) MOE_BMX_GU(2);
+  else MOE_BMX_GU(4);
+#undef MOE_BMX_GU
+  return launch_status();
+}
+
+extern "C" moe_status moe_batched_down_combine_mxfp4(const void* h, const int32_t* topk_ids, const float* topk_w,
+                                                     const void* wq_down, const void* ws_down, const void* y_shared,
+                                                     int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, void* y,
+                                                     void* stream) {
+  moe_status s = check_batched_mx(h, topk_ids, wq_down, ws_down, T, d, f, E, k, y);
+  if (s != MOE_OK || T == 0) return s;
+  if (!topk_w) return MOE_ERR_INVALID_ARG;
+  const int KB = static_cast<int>(f / 32);
+  const dim3 grid(static_cast<unsigned>(T * (d / kMxRows)));
+#define MOE_BMX_DN(CI_)                                                                                          \
+  hipLaunchKernelGGL((batched_mx_down_combine_kernel<CI_>), grid, dim3(256), 0, as_stream(stream),              \
+                     static_cast<const uint16_t*>(h), topk_ids, topk_w, static_cast<const uint8_t*>(wq_down),     \
+                     static_cast<const uint8_t*>(ws_down), static_cast<const uint16_t*>(y_shared),                \
+                     static_cast<int>(T), k, E, static_cast<int>(f), static_cast<int>(d), static_cast<uint16_t*>(y))
+  if (KB <= 64) MOE_BMX_DN(1);
+  else if (KB <= 128) MOE_BMX_DN(2);
+  else MOE_BMX_DN(4);
+#undef MOE_BMX_DN
+  return launch_status();
+}
 
 extern "C" moe_status moe_decode_gateup_swiglu_mxfp4(const void* x, const int32_t* perm, int32_t k,
                                                      const void* wq_gate_up, const void* ws_gate_up,

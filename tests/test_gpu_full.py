@@ -234,7 +234,9 @@ MX_FULL = ["c3mx_t1", "c3mx_t8", "c3mx_t32", "c3mx_t64"]
 def test_full_size_mxfp4(gpu, name):
     """The gpt-oss-shaped decode layer with MXFP4 experts at full size: every
     row of H and Y_perm and every token of y against the oracle with the
-    dequantised experts."""
+    dequantised experts, on the decode calls; then the "batched" mode (no
+    sort) on the same layer: every row of H in pair order and every token
+    of y."""
     from mixture_experts_ffn_04_amd import binding as B
     wl = W.get(name)
     t0 = time.time()
@@ -245,7 +247,7 @@ def test_full_size_mxfp4(gpu, name):
     u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     weights = B.MoeWeights(U.dev_tensor(wr, "bf16"), None, u8(gq), u8(dq), w_gate_up_scales=u8(gs),
                            w_down_scales=u8(ds))
-    layer = B.MoeLayer(weights, wl.k, wl.score)
+    layer = B.MoeLayer(weights, wl.k, wl.score, mode="decode")
     y = layer.forward(U.dev_tensor(x, "bf16"))
     torch.cuda.synchronize()
     x64, wr64 = W.values(x, "bf16"), W.values(wr, "bf16")
@@ -266,5 +268,12 @@ def test_full_size_mxfp4(gpu, name):
         yp_ref[ro[e]:ro[e + 1]] = O.down(h_ref[ro[e]:ro[e + 1]], dn64)
     U.assert_close(U.host_values(layer.h), h_ref, "bf16", f"{name} H")
     U.assert_close(U.host_values(layer.y_perm), yp_ref, "bf16", f"{name} Y_perm")
-    U.assert_close(U.host_values(y), O.unpermute_combine(yp_ref, ri, w), "bf16", f"{name} layer, every token")
+    y_ref = O.unpermute_combine(yp_ref, ri, w)
+    U.assert_close(U.host_values(y), y_ref, "bf16", f"{name} layer, every token")
+    bl = B.MoeLayer(weights, wl.k, wl.score, mode="batched")
+    yb = bl.forward(U.dev_tensor(x, "bf16"))
+    torch.cuda.synchronize()
+    assert (bl.ids.cpu().numpy() == ids).all()
+    U.assert_close(U.host_values(bl.h), h_ref[ri], "bf16", f"{name} batched H, pair order")
+    U.assert_close(U.host_values(yb), y_ref, "bf16", f"{name} batched layer, every token")
     log(f"[{name}] done ({time.time() - t0:.1f}s)")

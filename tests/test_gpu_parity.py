@@ -731,22 +731,116 @@ def test_mxfp4_shapes(gpu, E, rows, K, N):
                    f"mxfp4 Y E={E} K={K}")
 
 
+@pytest.mark.parametrize("mode", ["auto", "decode"])
 @pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37"])
-def test_layer_mxfp4(gpu, name):
+def test_layer_mxfp4(gpu, name, mode):
     """The whole layer with MXFP4 experts against the oracle's eager loop
-    over the dequantised experts, every token."""
+    over the dequantised experts, every token (auto: the batched calls for
+    one token, the decode calls for more)."""
     wl, inp = U.small_inputs(name)
     gq, gs, dq, ds = W.gen_all_experts_mxfp4(wl)
     dev = U.device_weights(wl, inp)
     weights = B().MoeWeights(dev.w_router, dev.bias, _mx_dev(gq, gpu), _mx_dev(dq, gpu),
                              w_gate_up_scales=_mx_dev(gs, gpu), w_down_scales=_mx_dev(ds, gpu))
-    layer = B().MoeLayer(weights, wl.k, wl.score)
+    layer = B().MoeLayer(weights, wl.k, wl.score, mode=mode)
     y = layer.forward(U.dev_tensor(inp["x"], "bf16"))
     torch.cuda.synchronize()
     gu64 = O.mxfp4_dequantize(gq, gs)
     dn64 = O.mxfp4_dequantize(dq, ds)
     U.check_layer(layer, wl, W.values(inp["x"], "bf16"), W.values(inp["wr"], "bf16"), inp["bias"],
-                  lambda e: (gu64[e], dn64[e]), None, y, f"{name} mxfp4 layer")
+                  lambda e: (gu64[e], dn64[e]), None, y, f"{name} mxfp4 layer ({mode})")
+
+
+@pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37"])
+def test_layer_mxfp4_batched(gpu, name):
+    """The layer with MXFP4 experts in the "batched" mode (no sort; the down
+    call applies the routing weights) against the oracle on every token."""
+    wl, inp = U.small_inputs(name)
+    gq, gs, dq, ds = W.gen_all_experts_mxfp4(wl)
+    dev = U.device_weights(wl, inp)
+    weights = B().MoeWeights(dev.w_router, dev.bias, _mx_dev(gq, gpu), _mx_dev(dq, gpu),
+                             w_gate_up_scales=_mx_dev(gs, gpu), w_down_scales=_mx_dev(ds, gpu))
+    layer = B().MoeLayer(weights, wl.k, wl.score, mode="batched")
+    y = layer.forward(U.dev_tensor(inp["x"], "bf16"))
+    torch.cuda.synchronize()
+    gu64 = O.mxfp4_dequantize(gq, gs)
+    dn64 = O.mxfp4_dequantize(dq, ds)
+    U.check_layer(layer, wl, W.values(inp["x"], "bf16"), W.values(inp["wr"], "bf16"), inp["bias"],
+                  lambda e: (gu64[e], dn64[e]), None, y, f"{name} mxfp4 batched layer")
+
+
+# (T, E, k, d, f): one, two and four 64-block columns per lane, slot counts
+# that give a wave one to four slots, a single token over 256 experts
+MX_BATCHED = [(3, 16, 6, 2048, 192), (9, 64, 16, 4096, 128), (2, 8, 2, 8192, 64), (1, 256, 8, 1024, 320),
+              (37, 32, 4, 576, 640)]
+
+
+@pytest.mark.parametrize("T,E,k,d,f", MX_BATCHED)
+def test_batched_mxfp4_calls(gpu, T, E, k, d, f):
+    """The "batched_mm" calls with MXFP4 experts, every element: gate/up rows
+    in pair order against the oracle's projection of each pair with the
+    dequantised expert, and bit for bit against the row the sorted decode
+    call computes for the same pair when that call takes its vector form
+    (within the bf16 tolerance otherwise); the down call with the weighted
+    combine folded in against the oracle, a third of the pairs masked as
+    another share's, with and without a shared-expert row."""
+    rng = np.random.default_rng(T * 1000 + E + d)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(1, keepdims=True)
+    P = T * k
+    xs = W.gen_matrix((T, d), seed=d + T)
+    gq = rng.integers(0, 256, size=(E, 2 * f, d // 2), dtype=np.uint8)
+    gs = rng.integers(118, 123, size=(E, 2 * f, d // 32)).astype(np.uint8)
+    dq = rng.integers(0, 256, size=(E, d, f // 2), dtype=np.uint8)
+    ds = rng.integers(118, 123, size=(E, d, f // 32)).astype(np.uint8)
+    gqd, gsd, dqd, dsd = (_mx_dev(a, gpu) for a in (gq, gs, dq, ds))
+    xd = U.dev_tensor(xs, "bf16")
+    h = torch.empty(P, f, dtype=torch.bfloat16, device=gpu)
+    B().batched_gateup_swiglu_mxfp4(xd, _i32(ids), gqd, gsd, h)
+    # the sorted decode call on the same pairs
+    counts, offsets, perm, inv = O.permute(ids, E)
+    hd = torch.empty(P, f, dtype=torch.bfloat16, device=gpu)
+    B().gateup_swiglu_mxfp4(xd, _i32(perm), k, gqd, gsd, _i32(offsets), hd)
+    torch.cuda.synchronize()
+    flat = ids.reshape(-1)
+    x64 = W.values(xs, "bf16")
+    used = np.unique(flat)
+    gu64 = {e: O.mxfp4_dequantize(gq[e], gs[e]) for e in used}
+    dn64 = {e: O.mxfp4_dequantize(dq[e], ds[e]) for e in used}
+    h_ref = np.stack([O.gate_up_swiglu(x64[p // k][None], gu64[flat[p]])[0] for p in range(P)])
+    U.assert_close(U.host_values(h), h_ref, "bf16", f"mxfp4 batched H T={T} E={E} k={k}")
+    if P <= E:      # the decode call's vector form (at most one row per expert on average): same arithmetic
+        assert (U.host_bits(h) == U.host_bits(hd)[inv]).all(), "batched and decode gate/up rows differ"
+    else:
+        U.assert_close(U.host_values(h), U.host_values(hd)[inv], "bf16", "mxfp4 batched vs decode H")
+    hs = W.gen_matrix((P, f), seed=f + P, std=0.5)
+    h64 = W.values(hs, "bf16")
+    masked = rng.random(P) < 0.3
+    mids = np.where(masked, -1, flat).reshape(T, k).astype(np.int32)
+    yk = np.stack([np.zeros(d) if masked[p] else O.down(h64[p][None], dn64[flat[p]])[0] for p in range(P)])
+    wm = np.where(masked.reshape(T, k), 0.0, w)
+    ys = W.gen_matrix((T, d), seed=d + 3, std=0.05)
+    for shared in (None, ys):
+        y = torch.empty(T, d, dtype=torch.bfloat16, device=gpu)
+        B().batched_down_combine_mxfp4(U.dev_tensor(hs, "bf16"), _i32(mids), _f32(w), dqd, dsd,
+                                       None if shared is None else U.dev_tensor(shared, "bf16"), y)
+        torch.cuda.synchronize()
+        ref = O.unpermute_combine(yk, np.arange(P), wm, None if shared is None else W.values(shared, "bf16"))
+        U.assert_close(U.host_values(y), ref, "bf16", f"mxfp4 batched down + combine T={T} (shared={shared is not None})")
+
+
+def test_batched_mxfp4_rejects(gpu):
+    from mixture_experts_ffn_04_amd import binding as Bd
+    lib = Bd.load()
+    p = 4096
+    assert lib.moe_batched_gateup_swiglu_mxfp4(p, p, p, p, 257, 64, 64, 8, 4, p, None) == Bd.MOE_ERR_UNSUPPORTED
+    assert lib.moe_batched_down_combine_mxfp4(p, p, p, p, p, None, 1, 16384, 64, 8, 4, p, None) == \
+        Bd.MOE_ERR_UNSUPPORTED
+    assert lib.moe_batched_gateup_swiglu_mxfp4(p, p, p, p, 1, 96, 64, 8, 4, p, None) == Bd.MOE_ERR_ALIGNMENT
+    assert lib.moe_batched_down_combine_mxfp4(p, p, None, p, p, None, 1, 64, 64, 8, 4, p, None) == \
+        Bd.MOE_ERR_INVALID_ARG
+    assert lib.moe_batched_gateup_swiglu_mxfp4(p, p, p, p, 0, 64, 64, 8, 4, p, None) == Bd.MOE_OK
 
 
 # ------------------------------------------------------- expert-parallel share
