@@ -37,6 +37,8 @@
  *                                    down call also applies the weights
  *   moe_batched_gateup_swiglu_mxfp4  the same with MXFP4 expert weights
  *   moe_batched_down_combine_mxfp4
+ *   moe_batched_gateup_swiglu_select        batched gate/up that also selects
+ *   moe_batched_gateup_swiglu_mxfp4_select  the experts from the logits
  *
  * All experts of a layer share one packed buffer per projection, the layout
  * the article's "Dynamic Weight Loading with WeightConverter" subsection
@@ -117,6 +119,9 @@ MOE_API const char* moe_status_string(moe_status s);
  *   x        [T][d]  dtype          w_router [E][d] dtype
  *   bias     [E] fp32, may be NULL  logits   [T][E] fp32 (output)
  *   topk_ids [T][k] int32 (output)  topk_w   [T][k] fp32 (output)
+ *   With topk_ids and topk_w both NULL only the logits are computed (the
+ *   batched_mm "_select" calls then choose the experts); one of them NULL
+ *   alone is MOE_ERR_INVALID_ARG.
  */
 MOE_API moe_status moe_route(const void* x, const void* w_router, const float* bias,
                      int64_t T, int64_t d, int32_t E, int32_t k, moe_dtype dtype,
@@ -388,6 +393,27 @@ MOE_API moe_status moe_batched_gateup_swiglu_mxfp4(const void* x, const int32_t*
                                                    const void* wq_gate_up, const void* ws_gate_up, int64_t T,
                                                    int64_t d, int64_t f, int32_t E, int32_t k, void* h,
                                                    void* stream);
+
+/*
+ * The batched_mm gate/up calls with the expert selection folded in, for a
+ * router whose logits were computed by moe_route with NULL ids and weights:
+ * every workgroup selects its token's experts from logits [T][E] (fp32)
+ * with the selection and weights of moe_topk (ids and weights bit for bit
+ * the same), writes topk_ids [T][k] and topk_w [T][k] (for the down call),
+ * and computes h as moe_batched_gateup_swiglu / _mxfp4 do.  The saving is
+ * the top-k launch, which at one token costs about as much as the
+ * selection itself.
+ */
+MOE_API moe_status moe_batched_gateup_swiglu_select(const void* x, const float* logits, const void* w_gate_up,
+                                                    int64_t T, int64_t d, int64_t f, int32_t E, int32_t k,
+                                                    moe_score score, moe_dtype dtype, int32_t* topk_ids,
+                                                    float* topk_w, void* h, void* stream);
+
+MOE_API moe_status moe_batched_gateup_swiglu_mxfp4_select(const void* x, const float* logits,
+                                                          const void* wq_gate_up, const void* ws_gate_up,
+                                                          int64_t T, int64_t d, int64_t f, int32_t E, int32_t k,
+                                                          moe_score score, int32_t* topk_ids, float* topk_w,
+                                                          void* h, void* stream);
 
 MOE_API moe_status moe_batched_down_combine_mxfp4(const void* h, const int32_t* topk_ids, const float* topk_w,
                                                   const void* wq_down, const void* ws_down, const void* y_shared,

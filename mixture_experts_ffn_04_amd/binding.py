@@ -28,7 +28,7 @@ EXPORTS = (
     "moe_decode_down", "moe_decode_gateup_swiglu_gather", "moe_grouped_gemm_gateup_swiglu_gather",
     "moe_localize_ids", "moe_permute_noalloc", "moe_batched_gateup_swiglu", "moe_batched_down_combine",
     "moe_decode_gateup_swiglu_mxfp4", "moe_decode_down_mxfp4", "moe_batched_gateup_swiglu_mxfp4",
-    "moe_batched_down_combine_mxfp4",
+    "moe_batched_down_combine_mxfp4", "moe_batched_gateup_swiglu_select", "moe_batched_gateup_swiglu_mxfp4_select",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -58,6 +58,10 @@ _SIGS = {
     "moe_decode_down_mxfp4": ([P, P, P, P, I64, I64, I64, I32, P, P], ctypes.c_int),
     "moe_batched_gateup_swiglu_mxfp4": ([P, P, P, P, I64, I64, I64, I32, I32, P, P], ctypes.c_int),
     "moe_batched_down_combine_mxfp4": ([P, P, P, P, P, P, I64, I64, I64, I32, I32, P, P], ctypes.c_int),
+    "moe_batched_gateup_swiglu_select": ([P, P, P, I64, I64, I64, I32, I32, ctypes.c_int, ctypes.c_int, P, P, P, P],
+                                         ctypes.c_int),
+    "moe_batched_gateup_swiglu_mxfp4_select": ([P, P, P, P, I64, I64, I64, I32, I32, ctypes.c_int, P, P, P, P],
+                                               ctypes.c_int),
 }
 
 
@@ -197,6 +201,26 @@ def batched_gateup_swiglu(x, topk_ids, w_gate_up, h, stream=None):
     E, f2, _ = w_gate_up.shape
     _check("moe_batched_gateup_swiglu", load().moe_batched_gateup_swiglu(
         _ptr(x), _ptr(topk_ids), _ptr(w_gate_up), T, d, f2 // 2, E, k, _dt(x), _ptr(h), _stream(stream)))
+
+
+def batched_gateup_swiglu_select(x, logits, k: int, score: str, w_gate_up, topk_ids, topk_w, h, stream=None):
+    """The "batched_mm" gate/up that selects each token's experts from the
+    router logits itself (writing topk_ids / topk_w for the down call)."""
+    T, d = x.shape
+    E, f2, _ = w_gate_up.shape
+    _check("moe_batched_gateup_swiglu_select", load().moe_batched_gateup_swiglu_select(
+        _ptr(x), _ptr(logits), _ptr(w_gate_up), T, d, f2 // 2, E, k, SCORES[score], _dt(x), _ptr(topk_ids),
+        _ptr(topk_w), _ptr(h), _stream(stream)))
+
+
+def batched_gateup_swiglu_mxfp4_select(x, logits, k: int, score: str, wq_gate_up, ws_gate_up, topk_ids, topk_w, h,
+                                       stream=None):
+    """The same with MXFP4 expert weights."""
+    T, d = x.shape
+    E, f2, _ = wq_gate_up.shape
+    _check("moe_batched_gateup_swiglu_mxfp4_select", load().moe_batched_gateup_swiglu_mxfp4_select(
+        _ptr(x), _ptr(logits), _ptr(wq_gate_up), _ptr(ws_gate_up), T, d, f2 // 2, E, k, SCORES[score],
+        _ptr(topk_ids), _ptr(topk_w), _ptr(h), _stream(stream)))
 
 
 def batched_down_combine(h, topk_ids, topk_w, w_down, y_shared, y, stream=None):
@@ -426,16 +450,24 @@ class MoeLayer:
         return out
 
     def _batched_stages(self, x: torch.Tensor, st) -> list:
-        """The "batched_mm" strategy: route, then per (token, slot) pair the
-        gate/up projection and the down projection with the weighted
-        combine folded in; no sort.  The shared expert runs on the decode
-        calls before the down projection, which adds its output."""
+        """The "batched_mm" strategy: the router logits, then per (token,
+        slot) pair the gate/up projection, which also selects the experts
+        from the logits (the router's top-k launch saved), and the down
+        projection with the weighted combine folded in; no sort.  On an
+        expert-parallel share the router selects and the ids are localised
+        first.  The shared expert runs on the decode calls before the down
+        projection, which adds its output."""
         T = x.shape[0]
         w = self.w
-        out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st))]
+        if self.mx and T * self.k > 1024:
+            raise ValueError("MXFP4 experts: at most 1024 routed rows (the batched calls)")
+        select = self.e_begin is None
         ids = self.ids
-        if self.e_begin is not None:
-            out.append(("localize", localize_ids, (self.ids, self.e_begin, self.E_loc, self.lids, st)))
+        if select:
+            out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, None, None, st))]
+        else:
+            out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st)),
+                   ("localize", localize_ids, (self.ids, self.e_begin, self.E_loc, self.lids, st))]
             ids = self.lids
         ys = None
         if w.shared_gate_up is not None:
@@ -443,13 +475,21 @@ class MoeLayer:
             out.append(("shared_down", down, (self.s_h, w.shared_down, self.s_off, self.s_y, True, st)))
             ys = self.s_y
         if self.mx:
-            if T * self.k > 1024:
-                raise ValueError("MXFP4 experts: at most 1024 routed rows (the batched calls)")
-            out.append(("gateup", batched_gateup_swiglu_mxfp4, (x, ids, w.w_gate_up, w.w_gate_up_scales, self.h, st)))
+            if select:
+                out.append(("gateup", batched_gateup_swiglu_mxfp4_select,
+                            (x, self.logits, self.k, self.score, w.w_gate_up, w.w_gate_up_scales, self.ids, self.wts,
+                             self.h, st)))
+            else:
+                out.append(("gateup", batched_gateup_swiglu_mxfp4,
+                            (x, ids, w.w_gate_up, w.w_gate_up_scales, self.h, st)))
             out.append(("down", batched_down_combine_mxfp4, (self.h, ids, self.wts, w.w_down, w.w_down_scales, ys,
                                                              self.y, st)))
         else:
-            out.append(("gateup", batched_gateup_swiglu, (x, ids, w.w_gate_up, self.h, st)))
+            if select:
+                out.append(("gateup", batched_gateup_swiglu_select,
+                            (x, self.logits, self.k, self.score, w.w_gate_up, self.ids, self.wts, self.h, st)))
+            else:
+                out.append(("gateup", batched_gateup_swiglu, (x, ids, w.w_gate_up, self.h, st)))
             out.append(("down", batched_down_combine, (self.h, ids, self.wts, w.w_down, ys, self.y, st)))
         return out
 

@@ -14,6 +14,7 @@
 // 16-byte loads (1 KB per load instruction, a plain streaming read) and
 // reduces their dot products with the pair's activation row across the wave.
 #include "common.h"
+#include "select.h"
 
 namespace moe {
 namespace {
@@ -58,16 +59,33 @@ __device__ __forceinline__ void wave_sum2(float& a, float& b) {
 // h[p][n] = silu(x[p/k] . Wg[e][n]) * (x[p/k] . Wu[e][n]), e = ids[p].
 // Workgroup = (pair p, 4 output columns), one column (its gate and up
 // rows) per wave.  Pairs with an id outside [0, E) get no row.
+// S > 0: the experts are selected here from the router logits [T][E] (every
+// wave runs its token's selection, S candidate slots per lane), and the
+// first workgroup of each token writes the token's ids and weights.
+template <int S>
 __global__ __launch_bounds__(256) void batched_gateup_kernel(const u32x4* __restrict__ x,
-                                                             const int32_t* __restrict__ ids,
+                                                             int32_t* __restrict__ ids, const float* __restrict__ logits,
+                                                             int score, float* __restrict__ wts,
                                                              const u32x4* __restrict__ W, int P, int k, int E,
                                                              int K, int N, uint16_t* __restrict__ h) {
   const int ncb = N / 4;
   const int p = blockIdx.x / ncb;
-  const int n = (blockIdx.x - p * ncb) * 4 + (threadIdx.x >> 6);
+  const int cb = blockIdx.x - p * ncb;
+  const int n = cb * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (p >= P) return;
-  const int e = ids[p];
+  int e;
+  if constexpr (S > 0) {
+    const int t = p / k, j = p - t * k;
+    float sel_v[kMaxK];
+    int sel_i[kMaxK];
+    topk_select<S>(logits + static_cast<int64_t>(t) * E, E, k, sel_v, sel_i);
+    if (j == 0 && cb == 0 && threadIdx.x == 0)
+      topk_store(sel_v, sel_i, k, score, ids + static_cast<int64_t>(t) * k, wts + static_cast<int64_t>(t) * k);
+    e = topk_slot(sel_i, k, j);
+  } else {
+    e = ids[p];
+  }
   if (e < 0 || e >= E) return;                       // a pair of an expert held elsewhere
   const int KC = K / 8;
   const gu4* We = (const gu4*)W + static_cast<int64_t>(e) * 2 * N * KC;
@@ -149,9 +167,33 @@ extern "C" moe_status moe_batched_gateup_swiglu(const void* x, const int32_t* to
   moe_status s = check_batched(x, topk_ids, w_gate_up, T, d, f, E, k, dtype, h);
   if (s != MOE_OK || T == 0) return s;
   const int64_t P = T * k;
-  hipLaunchKernelGGL(batched_gateup_kernel, dim3(static_cast<unsigned>(P * (f / 4))), dim3(256), 0,
-                     as_stream(stream), static_cast<const u32x4*>(x), topk_ids, static_cast<const u32x4*>(w_gate_up),
-                     static_cast<int>(P), k, E, static_cast<int>(d), static_cast<int>(f), static_cast<uint16_t*>(h));
+  hipLaunchKernelGGL(batched_gateup_kernel<0>, dim3(static_cast<unsigned>(P * (f / 4))), dim3(256), 0,
+                     as_stream(stream), static_cast<const u32x4*>(x), const_cast<int32_t*>(topk_ids), nullptr, 0,
+                     nullptr, static_cast<const u32x4*>(w_gate_up), static_cast<int>(P), k, E, static_cast<int>(d),
+                     static_cast<int>(f), static_cast<uint16_t*>(h));
+  return launch_status();
+}
+
+extern "C" moe_status moe_batched_gateup_swiglu_select(const void* x, const float* logits, const void* w_gate_up,
+                                                       int64_t T, int64_t d, int64_t f, int32_t E, int32_t k,
+                                                       moe_score score, moe_dtype dtype, int32_t* topk_ids,
+                                                       float* topk_w, void* h, void* stream) {
+  moe_status s = check_batched(x, logits ? topk_ids : nullptr, w_gate_up, T, d, f, E, k, dtype, h);
+  if (s != MOE_OK || T == 0) return s;
+  if (!topk_w || (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)) return MOE_ERR_INVALID_ARG;
+  const int64_t P = T * k;
+#define MOE_BGU_SEL(S_)                                                                                          \
+  hipLaunchKernelGGL(batched_gateup_kernel<S_>, dim3(static_cast<unsigned>(P * (f / 4))), dim3(256), 0,            \
+                     as_stream(stream), static_cast<const u32x4*>(x), topk_ids, logits, static_cast<int>(score),    \
+                     topk_w, static_cast<const u32x4*>(w_gate_up), static_cast<int>(P), k, E, static_cast<int>(d),   \
+                     static_cast<int>(f), static_cast<uint16_t*>(h))
+  if (E <= 64)
+    MOE_BGU_SEL(1);
+  else if (E <= 128)
+    MOE_BGU_SEL(2);
+  else
+    MOE_BGU_SEL(4);
+#undef MOE_BGU_SEL
   return launch_status();
 }
 

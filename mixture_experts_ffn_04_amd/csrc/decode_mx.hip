@@ -22,6 +22,7 @@
 // for scale codes 1..254 short of overflow) and the wave sums its lanes.
 // Experts without rows are never read.
 #include "common.h"
+#include "select.h"
 
 namespace moe {
 namespace {
@@ -171,9 +172,14 @@ __global__ __launch_bounds__(256) void decode_mx_kernel(const uint16_t* __restri
 // vector form computes, bit for bit.
 
 // h[p][n] for p < P: workgroup = (pair p, 8 output columns), two per wave.
-template <int CI>
+// S > 0: the experts are selected here from the router logits [T][E] (every
+// wave runs its token's selection), and the first workgroup of each token
+// writes the token's ids and weights.
+template <int CI, int S>
 __global__ __launch_bounds__(256) void batched_mx_gateup_kernel(const uint16_t* __restrict__ x,
-                                                                const int32_t* __restrict__ ids,
+                                                                int32_t* __restrict__ ids,
+                                                                const float* __restrict__ logits, int score,
+                                                                float* __restrict__ wts,
                                                                 const uint8_t* __restrict__ Bq,
                                                                 const uint8_t* __restrict__ Bs, int P, int k, int E,
                                                                 int K, int N, uint16_t* __restrict__ h) {
@@ -182,7 +188,18 @@ __global__ __launch_bounds__(256) void batched_mx_gateup_kernel(const uint16_t* 
   const int p = blockIdx.x / ncb;
   const int cb = blockIdx.x - p * ncb;
   if (p >= P) return;
-  const int e = ids[p];
+  int e;
+  if constexpr (S > 0) {
+    const int t = p / k, j = p - t * k;
+    float sel_v[kMaxK];
+    int sel_i[kMaxK];
+    topk_select<S>(logits + static_cast<int64_t>(t) * E, E, k, sel_v, sel_i);
+    if (j == 0 && cb == 0 && threadIdx.x == 0)
+      topk_store(sel_v, sel_i, k, score, ids + static_cast<int64_t>(t) * k, wts + static_cast<int64_t>(t) * k);
+    e = topk_slot(sel_i, k, j);
+  } else {
+    e = ids[p];
+  }
   if (e < 0 || e >= E) return;                           // a pair of an expert held elsewhere
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = cb * CPB + wave * CPW;
@@ -487,14 +504,46 @@ extern "C" moe_status moe_batched_gateup_swiglu_mxfp4(const void* x, const int32
   const int KB = static_cast<int>(d / 32);
   const dim3 grid(static_cast<unsigned>(P * (f / (2 * kMxRows))));
 #define MOE_BMX_GU(CI_)                                                                                          \
-  hipLaunchKernelGGL((batched_mx_gateup_kernel<CI_>), grid, dim3(256), 0, as_stream(stream),                     \
-                     static_cast<const uint16_t*>(x), topk_ids, static_cast<const uint8_t*>(wq_gate_up),          \
-                     static_cast<const uint8_t*>(ws_gate_up), static_cast<int>(P), k, E, static_cast<int>(d),      \
-                     static_cast<int>(f), static_cast<uint16_t*>(h))
+  hipLaunchKernelGGL((batched_mx_gateup_kernel<CI_, 0>), grid, dim3(256), 0, as_stream(stream),                  \
+                     static_cast<const uint16_t*>(x), const_cast<int32_t*>(topk_ids), nullptr, 0, nullptr,       \
+                     static_cast<const uint8_t*>(wq_gate_up), static_cast<const uint8_t*>(ws_gate_up),           \
+                     static_cast<int>(P), k, E, static_cast<int>(d), static_cast<int>(f), static_cast<uint16_t*>(h))
   if (KB <= 64) MOE_BMX_GU(1);
   else if (KB <= 128) MOE_BMX_GU(2);
   else MOE_BMX_GU(4);
 #undef MOE_BMX_GU
+  return launch_status();
+}
+
+extern "C" moe_status moe_batched_gateup_swiglu_mxfp4_select(const void* x, const float* logits,
+                                                             const void* wq_gate_up, const void* ws_gate_up,
+                                                             int64_t T, int64_t d, int64_t f, int32_t E, int32_t k,
+                                                             moe_score score, int32_t* topk_ids, float* topk_w,
+                                                             void* h, void* stream) {
+  moe_status s = check_batched_mx(x, logits ? topk_ids : nullptr, wq_gate_up, ws_gate_up, T, d, f, E, k, h);
+  if (s != MOE_OK || T == 0) return s;
+  if (!topk_w || (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)) return MOE_ERR_INVALID_ARG;
+  const int64_t P = T * k;
+  const int KB = static_cast<int>(d / 32);
+  const dim3 grid(static_cast<unsigned>(P * (f / (2 * kMxRows))));
+#define MOE_BMX_GUS(CI_, S_)                                                                                     \
+  hipLaunchKernelGGL((batched_mx_gateup_kernel<CI_, S_>), grid, dim3(256), 0, as_stream(stream),                 \
+                     static_cast<const uint16_t*>(x), topk_ids, logits, static_cast<int>(score), topk_w,          \
+                     static_cast<const uint8_t*>(wq_gate_up), static_cast<const uint8_t*>(ws_gate_up),           \
+                     static_cast<int>(P), k, E, static_cast<int>(d), static_cast<int>(f), static_cast<uint16_t*>(h))
+#define MOE_BMX_GUS_CI(S_)            \
+  if (KB <= 64) MOE_BMX_GUS(1, S_);   \
+  else if (KB <= 128) MOE_BMX_GUS(2, S_); \
+  else MOE_BMX_GUS(4, S_)
+  if (E <= 64) {
+    MOE_BMX_GUS_CI(1);
+  } else if (E <= 128) {
+    MOE_BMX_GUS_CI(2);
+  } else {
+    MOE_BMX_GUS_CI(4);
+  }
+#undef MOE_BMX_GUS_CI
+#undef MOE_BMX_GUS
   return launch_status();
 }
 

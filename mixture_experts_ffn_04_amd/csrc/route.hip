@@ -8,13 +8,10 @@
 // grouped GEMM kernels as a single group with a "+ bias, fp32" epilogue, or
 // for small batches by the split-K streaming kernel of the decode path.
 //
-// Selection: one wave per token.  Lane l holds logits l, l+64, ... in 1, 2
-// or 4 slots (E <= 64, 128, 256).  k rounds of a wave-wide arg-max on the
-// key (logit, -index) -- larger logit first, equal logits to the lower
-// index -- each round removing the winner from its lane.  The k winners, in selection order,
-// give the weights: a softmax over the selected logits, or sigmoid scores
-// divided by their sum.
+// Selection and weights: one wave per token (select.h), with 1, 2 or 4
+// candidate slots per lane for E <= 64, 128, 256.
 #include "grouped_gemm.h"
+#include "select.h"
 
 namespace moe {
 
@@ -40,111 +37,17 @@ namespace {
 
 constexpr int kTokPerBlock = 4;   // one wave each
 
-// Order-preserving 32-bit key of a logit: unsigned comparison of keys is
-// the float comparison (-0 is taken as +0, so the two tie); 0 lies below
-// every real key and marks "no candidate".
-__device__ __forceinline__ unsigned logit_key(float f) {
-  unsigned u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;
-  return (u >> 31) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_logit(unsigned k) {
-  return __uint_as_float((k >> 31) ? (k & 0x7fffffffu) : ~k);
-}
-
-// Maximum over the wave, in every lane: an inclusive max-scan inside each
-// 16-lane row by DPP row shifts of 1, 2, 4, 8, then the row totals carried
-// across rows by row_bcast 15 and 31, so lane 63 holds the wave's maximum.
-__device__ __forceinline__ unsigned wave_max(unsigned v) {
-  int x = static_cast<int>(v);
-#define MOE_MAX_DPP(ctrl, rows)                                                                  \
-  x = static_cast<int>(max(static_cast<unsigned>(x),                                            \
-                           static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, x, ctrl, rows, 0xf, false))))
-  MOE_MAX_DPP(0x111, 0xf);   // row_shr:1
-  MOE_MAX_DPP(0x112, 0xf);   // row_shr:2
-  MOE_MAX_DPP(0x114, 0xf);   // row_shr:4
-  MOE_MAX_DPP(0x118, 0xf);   // row_shr:8
-  MOE_MAX_DPP(0x142, 0xa);   // row_bcast:15 into rows 1 and 3
-  MOE_MAX_DPP(0x143, 0xc);   // row_bcast:31 into rows 2 and 3
-#undef MOE_MAX_DPP
-  return static_cast<unsigned>(__builtin_amdgcn_readlane(x, 63));
-}
-
-// Selection and weights for one token, by one whole wave: row = the
-// token's E logits (global memory or LDS).  Lane l holds candidates l,
-// l+64, ... in S slots (E <= 64 S).  Each of the k rounds takes the largest
-// key over the wave, then the lowest index holding it (candidates of slot i
-// all have lower indices than those of slot i+1), and retires that
-// candidate.
-template <int S>
-__device__ __forceinline__ void topk_token(const float* row, int E, int k, int score, int32_t* __restrict__ ids,
-                                           float* __restrict__ wts) {
-  const int lane = threadIdx.x & 63;
-  unsigned key[S];
-#pragma unroll
-  for (int i = 0; i < S; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? logit_key(row[e]) : 0u;
-  }
-  float sel_v[kMaxK];
-  int sel_i[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j >= k) break;
-    unsigned lm = key[0];
-#pragma unroll
-    for (int i = 1; i < S; ++i) lm = max(lm, key[i]);
-    const unsigned m = wave_max(lm);
-    int e = -1;
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-      const uint64_t b = __ballot(key[i] == m);
-      if (e < 0 && b != 0) e = 64 * i + static_cast<int>(__builtin_ctzll(b));
-    }
-    sel_v[j] = key_logit(m);
-    sel_i[j] = e;
-#pragma unroll
-    for (int i = 0; i < S; ++i)
-      if (lane + 64 * i == e) key[i] = 0u;
-  }
-  if (lane == 0) {
-    float w[kMaxK];
-    float s = 0.0f;
-    if (score == MOE_SCORE_SOFTMAX) {
-      const float m = sel_v[0];
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (j >= k) break;
-        w[j] = expf(sel_v[j] - m);
-        s += w[j];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kMaxK; ++j) {
-        if (j >= k) break;
-        w[j] = 1.0f / (1.0f + expf(-sel_v[j]));
-        s += w[j];
-      }
-    }
-    const float inv = 1.0f / s;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j >= k) break;
-      ids[j] = sel_i[j];
-      wts[j] = w[j] * inv;
-    }
-  }
-}
-
 template <int S>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                    int score, int32_t* __restrict__ ids,
                                                    float* __restrict__ wts) {
   const int tok = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
   if (tok >= T) return;
-  topk_token<S>(logits + static_cast<int64_t>(tok) * E, E, k, score, ids + static_cast<int64_t>(tok) * k,
-                wts + static_cast<int64_t>(tok) * k);
+  float sel_v[kMaxK];
+  int sel_i[kMaxK];
+  topk_select<S>(logits + static_cast<int64_t>(tok) * E, E, k, sel_v, sel_i);
+  if ((threadIdx.x & 63) == 0)
+    topk_store(sel_v, sel_i, k, score, ids + static_cast<int64_t>(tok) * k, wts + static_cast<int64_t>(tok) * k);
 }
 
 // Small batches (bf16): router logits with one wave per (expert, block of
@@ -264,7 +167,7 @@ extern "C" moe_status moe_route(const void* x, const void* w_router, const float
   if (!valid_dtype(dtype) || d <= 0) return MOE_ERR_INVALID_ARG;
   if (d % 64 != 0) return MOE_ERR_ALIGNMENT;
   if (T == 0) return MOE_OK;
-  if (!x || !w_router || !logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!x || !w_router || !logits || (!topk_ids) != (!topk_w)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits)) return MOE_ERR_ALIGNMENT;
   GemmArgs a{};
   a.A = x;
@@ -289,6 +192,6 @@ extern "C" moe_status moe_route(const void* x, const void* w_router, const float
   } else {
     s = (dtype == MOE_BF16) ? gemm_bf16_logits(a, st) : gemm_f32_logits(a, st);
   }
-  if (s != MOE_OK) return s;
+  if (s != MOE_OK || !topk_ids) return s;                 // logits only
   return launch_topk(logits, T, E, k, score, topk_ids, topk_w, st);
 }
