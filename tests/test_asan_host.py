@@ -80,6 +80,36 @@ int main(void) {
   EXPECT(moe_batched_gateup_swiglu(p, p, p, 8, 64, 96, 8, 4, B, p, NULL), MOE_ERR_ALIGNMENT);
   EXPECT(moe_batched_down_combine(p, p, NULL, p, NULL, 8, 64, 64, 8, 4, B, p, NULL), MOE_ERR_INVALID_ARG);
   EXPECT(moe_batched_down_combine(NULL, NULL, NULL, NULL, NULL, 0, 64, 64, 8, 4, B, NULL, NULL), MOE_OK);
+  /* the router's logits alone: both selection outputs NULL, never one */
+  EXPECT(moe_route(p, p, NULL, 10, 128, 8, 2, B, MOE_SCORE_SOFTMAX, p, p, NULL, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_route(p, p, NULL, 10, 128, 8, 2, B, MOE_SCORE_SOFTMAX, p, NULL, p, NULL), MOE_ERR_INVALID_ARG);
+  /* batched gate/up with the selection folded in */
+  EXPECT(moe_batched_gateup_swiglu_select(p, NULL, p, 8, 64, 64, 8, 4, MOE_SCORE_SOFTMAX, B, p, p, p, NULL),
+         MOE_ERR_INVALID_ARG);
+  EXPECT(moe_batched_gateup_swiglu_select(p, p, p, 8, 64, 64, 8, 4, (moe_score)7, B, p, p, p, NULL),
+         MOE_ERR_INVALID_ARG);
+  EXPECT(moe_batched_gateup_swiglu_select(p, p, p, 8, 64, 64, 8, 4, MOE_SCORE_SOFTMAX, F, p, p, p, NULL),
+         MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_batched_gateup_swiglu_select(p, p, p, 8, 64, 64, 8, 4, MOE_SCORE_SOFTMAX, B, p, NULL, p, NULL),
+         MOE_ERR_INVALID_ARG);
+  EXPECT(moe_batched_gateup_swiglu_mxfp4_select(p, p, p, p, 257, 64, 64, 8, 4, MOE_SCORE_SIGMOID, p, p, p, NULL),
+         MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_batched_gateup_swiglu_mxfp4_select(p, NULL, p, p, 8, 64, 64, 8, 4, MOE_SCORE_SIGMOID, p, p, p, NULL),
+         MOE_ERR_INVALID_ARG);
+  /* MXFP4 expert weights: decode and batched calls */
+  EXPECT(moe_decode_gateup_swiglu_mxfp4(p, NULL, 1, p, p, p, 2000, 128, 128, 8, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_decode_gateup_swiglu_mxfp4(p, NULL, 1, p, p, p, 10, 96, 128, 8, p, NULL), MOE_ERR_ALIGNMENT);
+  EXPECT(moe_decode_gateup_swiglu_mxfp4(p, NULL, 1, p, p, NULL, 10, 128, 128, 8, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_decode_gateup_swiglu_mxfp4(p, p, 3, p, p, p, 10, 128, 128, 8, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_decode_gateup_swiglu_mxfp4(NULL, NULL, 1, NULL, NULL, NULL, 0, 128, 128, 8, NULL, NULL), MOE_OK);
+  EXPECT(moe_decode_down_mxfp4(p, p, p, p, 10, 128, 16384, 8, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_decode_down_mxfp4(q, p, p, p, 10, 128, 128, 8, p, NULL), MOE_ERR_ALIGNMENT);
+  EXPECT(moe_batched_gateup_swiglu_mxfp4(p, p, p, p, 257, 64, 64, 8, 4, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_batched_gateup_swiglu_mxfp4(p, p, p, p, 8, 96, 64, 8, 4, p, NULL), MOE_ERR_ALIGNMENT);
+  EXPECT(moe_batched_gateup_swiglu_mxfp4(p, p, p, NULL, 8, 64, 64, 8, 4, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_batched_down_combine_mxfp4(p, p, NULL, p, p, NULL, 8, 64, 64, 8, 4, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_batched_down_combine_mxfp4(p, p, p, p, p, NULL, 1, 16384, 64, 8, 4, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_batched_down_combine_mxfp4(NULL, NULL, NULL, NULL, NULL, NULL, 0, 64, 64, 8, 4, NULL, NULL), MOE_OK);
   for (int s = -1; s < 8; ++s)
     if (!moe_status_string((moe_status)s)) return 3;
   printf("ok\n");
