@@ -63,10 +63,12 @@ def decode_tokens_per_s(bandwidth_bytes_per_s: float, active_params: float, byte
     return bandwidth_bytes_per_s / (active_params * bytes_per_param)
 
 
-def layer_flops(wl) -> float:
+def layer_flops(wl, P=None) -> float:
     """Algorithmic FLOPs of one layer call: router + 3 expert GEMMs per
-    routed pair (+ the shared expert on every token)."""
-    return (2.0 * wl.T * wl.d * wl.E + 6.0 * wl.T * wl.k * wl.d * wl.f
+    routed pair (+ the shared expert on every token).  P: the routed pairs
+    computed here (an expert-parallel share's), else all T*k."""
+    P = wl.P if P is None else P
+    return (2.0 * wl.T * wl.d * wl.E + 6.0 * P * wl.d * wl.f
             + 6.0 * wl.T * wl.d * wl.f_shared)
 
 
@@ -78,16 +80,17 @@ def layer_bytes(wl, active: int) -> float:
             + b * (wl.d * wl.E + 2.0 * wl.T * wl.d + 3.0 * wl.d * wl.f_shared))
 
 
-def gateup_flops(wl) -> float:
+def gateup_flops(wl, P=None) -> float:
     """Grouped gate/up projection: 2 x (2f) x d FLOPs per routed row."""
-    return 4.0 * wl.P * wl.d * wl.f
+    return 4.0 * (wl.P if P is None else P) * wl.d * wl.f
 
 
-def gateup_bytes(wl, active: int) -> float:
+def gateup_bytes(wl, active: int, P=None) -> float:
     """Gate/up kernel: active experts' [2f, d] weights (as stored: MXFP4 at
     4.25 bits per weight) + routed rows in + H out."""
     b = wl.elem_bytes
-    return wl.expert_weight_bytes * 2.0 * wl.f * wl.d * active + b * (wl.P * wl.d + wl.P * wl.f)
+    P = wl.P if P is None else P
+    return wl.expert_weight_bytes * 2.0 * wl.f * wl.d * active + b * (P * wl.d + P * wl.f)
 
 
 def tile_work(wl, counts) -> dict:
@@ -108,14 +111,15 @@ def tile_work(wl, counts) -> dict:
             "rows_at_256_row_tiles": r256 / P}
 
 
-def down_bytes(wl, active: int) -> float:
+def down_bytes(wl, active: int, P=None) -> float:
     """Down kernel: active experts' [d, f] weights (as stored) + H rows in +
     Y_perm out."""
     b = wl.elem_bytes
-    return wl.expert_weight_bytes * wl.d * wl.f * active + b * (wl.P * wl.f + wl.P * wl.d)
+    P = wl.P if P is None else P
+    return wl.expert_weight_bytes * wl.d * wl.f * active + b * (P * wl.f + P * wl.d)
 
 
-def kernel_rooflines(wl, active: int, kern_ms: dict, decode: bool) -> dict:
+def kernel_rooflines(wl, active: int, kern_ms: dict, decode: bool, P=None) -> dict:
     """Roofline position of each projection kernel from its mean duration
     (HIP events on the launch stream over the timed steps).  Grouped
     workloads: algorithmic FLOPs (gate/up 4 d f, down 2 d f per routed row;
@@ -125,8 +129,8 @@ def kernel_rooflines(wl, active: int, kern_ms: dict, decode: bool) -> dict:
     out = {}
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
     work = {
-        "gateup": (gateup_flops(wl), gateup_bytes(wl, active)),
-        "down": (2.0 * wl.P * wl.d * wl.f, down_bytes(wl, active)),
+        "gateup": (gateup_flops(wl, P), gateup_bytes(wl, active, P)),
+        "down": (2.0 * (wl.P if P is None else P) * wl.d * wl.f, down_bytes(wl, active, P)),
     }
     if wl.f_shared:
         fs, b = wl.f_shared, wl.elem_bytes
@@ -172,10 +176,12 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared: bool = False):
+def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared: bool = False, share: int = 1):
     """Upload the workload's seeded inputs to the GPU and build the layer.
     With keep_host, the storage-format expert weights stay in host memory
-    too (for the CPU oracle leg; the DeepSeek-shaped layer holds 22.5 GB)."""
+    too (for the CPU oracle leg; the DeepSeek-shaped layer holds 22.5 GB).
+    share > 1: one GPU's expert-parallel share of the layer -- experts
+    [0, E/share) and the shared expert -- with every token routed."""
     import torch
     from mixture_experts_ffn_04_amd import MoeLayer, MoeWeights
 
@@ -197,10 +203,11 @@ def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared
         host_experts = {e: (gq[e], gs[e], dq[e], ds[e]) for e in range(wl.E)} if keep_host else {}
         host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=None)
         return MoeLayer(weights, wl.k, wl.score, mode=mode), dev(x), host
-    gu = torch.empty(wl.E, 2 * wl.f, wl.d, dtype=tdt, device=device)
-    dn = torch.empty(wl.E, wl.d, wl.f, dtype=tdt, device=device)
+    E_loc = wl.E // share
+    gu = torch.empty(E_loc, 2 * wl.f, wl.d, dtype=tdt, device=device)
+    dn = torch.empty(E_loc, wl.d, wl.f, dtype=tdt, device=device)
     host_experts = {}
-    for e, g, w in W.iter_experts(wl):
+    for e, g, w in W.iter_experts(wl, range(E_loc)):
         gu[e].copy_(dev(g))
         dn[e].copy_(dev(w))
         if keep_host:
@@ -208,7 +215,8 @@ def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared
     sh = W.gen_shared(wl)
     weights = MoeWeights(dev(wr), None if bias is None else torch.from_numpy(bias).to(device), gu, dn,
                          None if sh is None else dev(sh[0]), None if sh is None else dev(sh[1]))
-    layer = MoeLayer(weights, wl.k, wl.score, mode=mode, overlap_shared=overlap_shared)
+    layer = MoeLayer(weights, wl.k, wl.score, mode=mode, overlap_shared=overlap_shared,
+                     experts=None if share == 1 else (0, E_loc))
     host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=sh)
     return layer, dev(x), host
 
@@ -589,6 +597,9 @@ def main(argv=None):
     ap.add_argument("--overlap-shared", action="store_true",
                     help="run the shared expert on a second stream beside the router, the sort and the routed "
                          "experts (measured no faster on the DeepSeek-shaped layer; default: after them)")
+    ap.add_argument("--ep-share", type=int, default=1, metavar="N",
+                    help="time one GPU's expert-parallel share of N (experts [0, E/N) and the shared expert, "
+                         "every token routed, local pairs only); prefill workloads")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernels", action="store_true", help="also print per-stage times to stderr")
@@ -636,9 +647,15 @@ def main(argv=None):
     if wl.experts == "mxfp4" and args.mode not in ("auto", "decode", "batched"):
         print("MXFP4 experts run on the decode or the batched calls", file=sys.stderr)
         return 2
+    share = args.ep_share
+    if share > 1:
+        if decode or wl.experts == "mxfp4" or wl.E % share or args.mode not in ("auto", "grouped"):
+            print("--ep-share: prefill workloads with E divisible by N, grouped calls", file=sys.stderr)
+            return 2
+        args.no_cpu = True          # the oracle leg needs every expert
 
     layer, x, host = setup(wl, device, keep_host=not args.no_cpu, mode=args.mode,
-                           overlap_shared=args.overlap_shared)
+                           overlap_shared=args.overlap_shared, share=share)
     st = torch.cuda.current_stream()
     # the projection kernels are timed by events on the launch stream inside
     # the timed steps; an event pair costs a few microseconds, so the
@@ -657,6 +674,7 @@ def main(argv=None):
     else:
         counts = layer.counts.cpu().numpy()
     active = int((counts > 0).sum())
+    P_here = int(counts.sum()) if share > 1 else None     # an expert-parallel share's routed pairs
 
     marks = {}
     if decode:
@@ -707,7 +725,7 @@ def main(argv=None):
             kern_ms[name] = stage_ms[name]          # from the per-stage pass
     tokens_per_s = wl.T / (ms * 1e-3)
 
-    kernels = kernel_rooflines(wl, active, kern_ms, decode)
+    kernels = kernel_rooflines(wl, active, kern_ms, decode, P_here)
     if layer.use_batched(wl.T):
         kname = "batched_mx_gateup" if wl.experts == "mxfp4" else "batched_gateup"
     elif decode:
@@ -716,7 +734,7 @@ def main(argv=None):
         kname = "gateup"
     roof = dict(kernels["gateup"])
     roof["kernel"] = kname
-    roof["traffic"] = load_traffic(kname, wl.name)
+    roof["traffic"] = load_traffic(kname, wl.name) if share == 1 else None   # taken on the whole layer
 
     out = {
         "metric": METRIC,
@@ -733,15 +751,19 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.f, "experts": wl.E,
                    "top_k": wl.k, "score": wl.score, "zipf_s": wl.zipf_s, "shared_d_ff": wl.f_shared,
-                   "active_experts": active, "parallelism": "single GPU", "strategy": args.mode,
+                   "active_experts": active, "strategy": args.mode,
+                   "parallelism": "single GPU" if share == 1 else
+                   f"one GPU's expert-parallel share of {share}: experts 0..{wl.E // share - 1}"
+                   f"{' and the shared expert' if wl.f_shared else ''}, every token routed, {P_here} of {wl.P} "
+                   f"routed pairs here (the sum over shares is not run)",
                    "shared_expert": None if not wl.f_shared else
                    ("second stream beside the routed experts" if args.overlap_shared else "after the routed experts"),
                    "timing": "per-step events, caches flushed by a 1 GiB read between steps; the dominant "
                              "kernel's events on every other step, the step time over the others" if decode
                    else "wall clock over the timed steps"},
         "roofline": roof,
-        "layer": {"tflops": layer_flops(wl) / (ms * 1e-3) / 1e12,
-                  "mfma_frac": layer_flops(wl) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "layer": {"tflops": layer_flops(wl, P_here) / (ms * 1e-3) / 1e12,
+                  "mfma_frac": layer_flops(wl, P_here) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                   "gbps": layer_bytes(wl, active) / (ms * 1e-3) / 1e9,
                   "hbm_frac": layer_bytes(wl, active) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                   "stage_ms": stage_ms, "wall_s": wall, "kernels": kernels,
