@@ -583,15 +583,16 @@ def test_layer_deep_shapes(gpu, T, E, k, f):
     _check_layer(layer, wl, inp, y, f"{wl.name} T={wl.T} f={wl.f} E={wl.E} k={wl.k}")
 
 
-@pytest.mark.parametrize("mode", ["grouped", "decode"])
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("mode", ["grouped", "decode", "batched"])
+@pytest.mark.parametrize("i", range(32))
 def test_layer_random_shapes(gpu, i, mode):
-    """The whole layer on seeded random shapes against the oracle.  Short
-    launches like these pick their rows per row tile on the device, so this
-    also covers that choice on shapes no named workload has."""
+    """The whole layer on seeded random shapes against the oracle, in each
+    strategy whose size limit the shape meets.  Short launches like these
+    pick their rows per row tile on the device, so this also covers that
+    choice on shapes no named workload has."""
     wl = _random_workload(i)
-    if mode == "decode" and wl.P > 1024:
-        pytest.skip("decode calls take at most 1024 rows")
+    if mode in ("decode", "batched") and wl.P > 1024:
+        pytest.skip(f"{mode} calls take at most 1024 routed rows")
     x = W.gen_x(wl)
     wr, bias = W.gen_router(wl)
     gu, dn = W.gen_all_experts(wl)
