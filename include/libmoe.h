@@ -400,7 +400,8 @@ MOE_API moe_status moe_batched_gateup_swiglu_mxfp4(const void* x, const int32_t*
  * every workgroup selects its token's experts from logits [T][E] (fp32)
  * with the selection and weights of moe_topk (ids and weights bit for bit
  * the same), writes topk_ids [T][k] and topk_w [T][k] (for the down call),
- * and computes h as moe_batched_gateup_swiglu / _mxfp4 do.  The saving is
+ * and computes h as moe_batched_gateup_swiglu / _mxfp4 do (k <= E, else
+ * MOE_ERR_INVALID_ARG, as for moe_topk).  The saving is
  * the top-k launch, which at one token costs about as much as the
  * selection itself.
  */

@@ -180,7 +180,7 @@ extern "C" moe_status moe_batched_gateup_swiglu_select(const void* x, const floa
                                                        float* topk_w, void* h, void* stream) {
   moe_status s = check_batched(x, logits ? topk_ids : nullptr, w_gate_up, T, d, f, E, k, dtype, h);
   if (s != MOE_OK || T == 0) return s;
-  if (!topk_w || (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)) return MOE_ERR_INVALID_ARG;
+  if (!topk_w || k > E || (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)) return MOE_ERR_INVALID_ARG;
   const int64_t P = T * k;
 #define MOE_BGU_SEL(S_)                                                                                          \
   hipLaunchKernelGGL(batched_gateup_kernel<S_>, dim3(static_cast<unsigned>(P * (f / 4))), dim3(256), 0,            \

@@ -522,7 +522,7 @@ extern "C" moe_status moe_batched_gateup_swiglu_mxfp4_select(const void* x, cons
                                                              void* h, void* stream) {
   moe_status s = check_batched_mx(x, logits ? topk_ids : nullptr, wq_gate_up, ws_gate_up, T, d, f, E, k, h);
   if (s != MOE_OK || T == 0) return s;
-  if (!topk_w || (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)) return MOE_ERR_INVALID_ARG;
+  if (!topk_w || k > E || (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)) return MOE_ERR_INVALID_ARG;
   const int64_t P = T * k;
   const int KB = static_cast<int>(d / 32);
   const dim3 grid(static_cast<unsigned>(P * (f / (2 * kMxRows))));

@@ -92,6 +92,10 @@ int main(void) {
          MOE_ERR_UNSUPPORTED);
   EXPECT(moe_batched_gateup_swiglu_select(p, p, p, 8, 64, 64, 8, 4, MOE_SCORE_SOFTMAX, B, p, NULL, p, NULL),
          MOE_ERR_INVALID_ARG);
+  EXPECT(moe_batched_gateup_swiglu_select(p, p, p, 8, 64, 64, 4, 6, MOE_SCORE_SOFTMAX, B, p, p, p, NULL),
+         MOE_ERR_INVALID_ARG);
+  EXPECT(moe_batched_gateup_swiglu_mxfp4_select(p, p, p, p, 8, 64, 64, 4, 6, MOE_SCORE_SOFTMAX, p, p, p, NULL),
+         MOE_ERR_INVALID_ARG);
   EXPECT(moe_batched_gateup_swiglu_mxfp4_select(p, p, p, p, 257, 64, 64, 8, 4, MOE_SCORE_SIGMOID, p, p, p, NULL),
          MOE_ERR_UNSUPPORTED);
   EXPECT(moe_batched_gateup_swiglu_mxfp4_select(p, NULL, p, p, 8, 64, 64, 8, 4, MOE_SCORE_SIGMOID, p, p, p, NULL),
