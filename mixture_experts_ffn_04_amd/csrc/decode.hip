@@ -128,13 +128,21 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
   for (int m0 = lo; m0 < hi; m0 += 16 * kMC) {
     const int mcn = min(kMC, (hi - m0 + 15) / 16);
     const uint16_t* xr[kMC];
+    int src[kMC];
 #pragma unroll
     for (int mc = 0; mc < kMC; ++mc) {
       const int row = m0 + mc * 16 + i16;        // rows past the group read a valid row; never stored
-      int src = row < hi ? row : lo;
-      if (rowmap) src = clamp_off(rowmap[src], rows - 1) / kdiv;
-      xr[mc] = A + static_cast<int64_t>(src) * K + kq * 16;
+      src[mc] = row < hi ? row : lo;
     }
+    if (rowmap) {                                // every map entry requested before any is used
+      int rm[kMC];
+#pragma unroll
+      for (int mc = 0; mc < kMC; ++mc) rm[mc] = rowmap[src[mc]];
+#pragma unroll
+      for (int mc = 0; mc < kMC; ++mc) src[mc] = clamp_off(rm[mc], rows - 1) / kdiv;
+    }
+#pragma unroll
+    for (int mc = 0; mc < kMC; ++mc) xr[mc] = A + static_cast<int64_t>(src[mc]) * K + kq * 16;
     f32x4 ag[kMC], au[kMC];
     if (mcn == 1) {
       decode_partial<SWIGLU, 1, 8>(wg, wu, xr, s0, s1, ag, au);
@@ -251,6 +259,13 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint16_t* __rest
   const gu4* w0p = Bg + static_cast<int64_t>(n0) * KC;
   const gu4* w1p = Bg + static_cast<int64_t>(r1) * KC;
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto token_row = [&](int m) {
+    const int src = rowmap ? clamp_off(rowmap[m], rows - 1) / kdiv : m;
+    return (const gu4*)A + static_cast<int64_t>(src) * KC;
+  };
+  // the first row's map entry is read before the weights, so its token
+  // loads need not wait behind the weight loads (loads return in order)
+  const gu4* xr_lo = token_row(lo);
   u32x4 w0[CI], w1[CI];
 #pragma unroll
   for (int i = 0; i < CI; ++i) {
@@ -258,12 +273,8 @@ __global__ __launch_bounds__(256) void decode_rows_kernel(const uint16_t* __rest
     w0[i] = c < KC ? w0p[c] : zero;
     w1[i] = c < KC ? w1p[c] : zero;
   }
-  auto token_row = [&](int m) {
-    const int src = rowmap ? clamp_off(rowmap[m], rows - 1) / kdiv : m;
-    return (const gu4*)A + static_cast<int64_t>(src) * KC;
-  };
   for (int m = lo; m < hi; ++m) {
-    const gu4* xr = token_row(m);
+    const gu4* xr = m == lo ? xr_lo : token_row(m);
     u32x4 x[CI];
 #pragma unroll
     for (int i = 0; i < CI; ++i) x[i] = (lane + 64 * i < KC) ? xr[lane + 64 * i] : zero;

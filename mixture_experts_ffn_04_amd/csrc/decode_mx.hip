@@ -57,12 +57,14 @@ __device__ __forceinline__ float block_dot(const u32x4& q, const u32x4 (&x)[4]) 
   return s;
 }
 
-// The codes and scales of the kMxRows weight rows wr[] of one expert (Bqg,
-// Bsg: its codes [rows][K/2] and scales [rows][K/32]): lane l holds blocks
-// l, l + 64, ... (CI of them).
+// The codes and scale codes of the kMxRows weight rows wr[] of one expert
+// (Bqg, Bsg: its codes [rows][K/2] and scales [rows][K/32]): lane l holds
+// blocks l, l + 64, ... (CI of them).  The scale codes stay raw bytes here
+// and are decoded where they are used, so no load waits for an earlier
+// one's data before it is issued.
 template <int CI>
 __device__ __forceinline__ void mx_load_rows(const uint8_t* Bqg, const uint8_t* Bsg, const int (&wr)[kMxRows], int K,
-                                             int KB, int lane, u32x4 (&wq)[kMxRows][CI], float (&ws)[kMxRows][CI]) {
+                                             int KB, int lane, u32x4 (&wq)[kMxRows][CI], uint32_t (&ws)[kMxRows][CI]) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int r = 0; r < kMxRows; ++r) {
@@ -71,29 +73,38 @@ __device__ __forceinline__ void mx_load_rows(const uint8_t* Bqg, const uint8_t* 
       const int b = lane + 64 * i;
       const bool ok = b < KB;
       wq[r][i] = ok ? *(const gu4*)(Bqg + static_cast<int64_t>(wr[r]) * (K / 2) + b * 16) : zero;
-      ws[r][i] = ok ? e8m0_to_f32(Bsg[static_cast<int64_t>(wr[r]) * KB + b]) : 0.0f;
+      ws[r][i] = ok ? Bsg[static_cast<int64_t>(wr[r]) * KB + b] : 0u;
     }
   }
 }
 
-// The wave's dot products of one activation row xr (bf16, K long) with its
-// kMxRows weight rows, in every lane: per lane, each block's sum times the
-// block's scale, accumulated over the lane's blocks in order, then summed
-// across the wave.
+// The 64 bytes of activation row xr (bf16, K long) under each of the
+// lane's blocks.
 template <int CI>
-__device__ __forceinline__ void mx_dot_rows(const u32x4 (&wq)[kMxRows][CI], const float (&ws)[kMxRows][CI],
-                                            const uint16_t* xr, int KB, int lane, float (&acc)[kMxRows]) {
+__device__ __forceinline__ void mx_load_x(const uint16_t* xr, int KB, int lane, u32x4 (&xv)[CI][4]) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < CI; ++i) {
+    const int b = lane + 64 * i;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xv[i][c] = b < KB ? *(const gu4*)(xr + b * 32 + c * 8) : zero;
+  }
+}
+
+// The wave's dot products of one activation row (xv, from mx_load_x) with
+// its kMxRows weight rows, in every lane: per lane, each block's sum times
+// the block's scale, accumulated over the lane's blocks in order, then
+// summed across the wave.
+template <int CI>
+__device__ __forceinline__ void mx_dot_rows(const u32x4 (&wq)[kMxRows][CI], const uint32_t (&ws)[kMxRows][CI],
+                                            const u32x4 (&xv)[CI][4], int KB, int lane, float (&acc)[kMxRows]) {
 #pragma unroll
   for (int r = 0; r < kMxRows; ++r) acc[r] = 0.0f;
 #pragma unroll
   for (int i = 0; i < CI; ++i) {
-    const int b = lane + 64 * i;
-    if (b < KB) {
-      u32x4 xv[4];
+    if (lane + 64 * i < KB) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) xv[c] = *(const gu4*)(xr + b * 32 + c * 8);
-#pragma unroll
-      for (int r = 0; r < kMxRows; ++r) acc[r] = fmaf(block_dot(wq[r][i], xv), ws[r][i], acc[r]);
+      for (int r = 0; r < kMxRows; ++r) acc[r] = fmaf(block_dot(wq[r][i], xv[i]), e8m0_to_f32(ws[r][i]), acc[r]);
     }
   }
 #pragma unroll
@@ -151,14 +162,24 @@ __global__ __launch_bounds__(256) void decode_mx_kernel(const uint16_t* __restri
   const int64_t brows = SWIGLU ? 2 * static_cast<int64_t>(N) : N;
   int wr[kMxRows];
   mx_wave_rows<SWIGLU>(n0, N, wr);
+  // the first row's map entry is read before the weights, so its
+  // activation loads need not wait behind the code loads (loads return in
+  // order)
+  const int src_lo = rowmap ? clamp_off(rowmap[lo], rows - 1) / kdiv : lo;
   u32x4 wq[kMxRows][CI];
-  float ws[kMxRows][CI];
+  uint32_t ws[kMxRows][CI];
   mx_load_rows<CI>(Bq + static_cast<int64_t>(g) * brows * (K / 2), Bs + static_cast<int64_t>(g) * brows * KB, wr, K,
                    KB, lane, wq, ws);
+  // the first row's activations are requested right behind the codes
+  u32x4 xv[CI][4];
+  mx_load_x<CI>(A + static_cast<int64_t>(src_lo) * K, KB, lane, xv);
   for (int m = lo; m < hi; ++m) {
-    const int src = rowmap ? clamp_off(rowmap[m], rows - 1) / kdiv : m;
+    if (m > lo) {
+      const int src = rowmap ? clamp_off(rowmap[m], rows - 1) / kdiv : m;
+      mx_load_x<CI>(A + static_cast<int64_t>(src) * K, KB, lane, xv);
+    }
     float acc[kMxRows];
-    mx_dot_rows<CI>(wq, ws, A + static_cast<int64_t>(src) * K, KB, lane, acc);
+    mx_dot_rows<CI>(wq, ws, xv, KB, lane, acc);
     mx_store<SWIGLU>(acc, lane, C + static_cast<int64_t>(m) * N + n0);
   }
 }
@@ -207,11 +228,13 @@ __global__ __launch_bounds__(256) void batched_mx_gateup_kernel(const uint16_t* 
   int wr[kMxRows];
   mx_wave_rows<true>(n0, N, wr);
   u32x4 wq[kMxRows][CI];
-  float ws[kMxRows][CI];
+  uint32_t ws[kMxRows][CI];
   mx_load_rows<CI>(Bq + static_cast<int64_t>(e) * 2 * N * (K / 2), Bs + static_cast<int64_t>(e) * 2 * N * KB, wr, K,
                    KB, lane, wq, ws);
+  u32x4 xv[CI][4];
+  mx_load_x<CI>(x + static_cast<int64_t>(p / k) * K, KB, lane, xv);
   float acc[kMxRows];
-  mx_dot_rows<CI>(wq, ws, x + static_cast<int64_t>(p / k) * K, KB, lane, acc);
+  mx_dot_rows<CI>(wq, ws, xv, KB, lane, acc);
   mx_store<true>(acc, lane, h + static_cast<int64_t>(p) * N + n0);
 }
 
@@ -240,10 +263,12 @@ __global__ __launch_bounds__(256) void batched_mx_down_combine_kernel(
       int wr[kMxRows];
       mx_wave_rows<false>(c0, N, wr);
       u32x4 wq[kMxRows][CI];
-      float ws[kMxRows][CI];
+      uint32_t ws[kMxRows][CI];
       mx_load_rows<CI>(Bq + static_cast<int64_t>(e) * N * (K / 2), Bs + static_cast<int64_t>(e) * N * KB, wr, K, KB,
                        lane, wq, ws);
-      mx_dot_rows<CI>(wq, ws, h + p * K, KB, lane, acc);
+      u32x4 xv[CI][4];
+      mx_load_x<CI>(h + p * K, KB, lane, xv);
+      mx_dot_rows<CI>(wq, ws, xv, KB, lane, acc);
     }
     if (lane == 0) {
 #pragma unroll
@@ -379,13 +404,21 @@ __global__ __launch_bounds__(256) void decode_mx_mfma_kernel(const uint16_t* __r
   for (int m0 = lo; m0 < hi; m0 += 16 * MCX) {
     const int mcn = min(MCX, (hi - m0 + 15) / 16);
     const uint16_t* xr[MCX];
+    int src[MCX];
 #pragma unroll
     for (int mc = 0; mc < MCX; ++mc) {
       const int row = m0 + mc * 16 + i16;             // rows past the group read a valid row; never stored
-      int src = row < hi ? row : lo;
-      if (rowmap) src = clamp_off(rowmap[src], rows - 1) / kdiv;
-      xr[mc] = A + static_cast<int64_t>(src) * K;
+      src[mc] = row < hi ? row : lo;
     }
+    if (rowmap) {                                     // every map entry requested before any is used
+      int rm[MCX];
+#pragma unroll
+      for (int mc = 0; mc < MCX; ++mc) rm[mc] = rowmap[src[mc]];
+#pragma unroll
+      for (int mc = 0; mc < MCX; ++mc) src[mc] = clamp_off(rm[mc], rows - 1) / kdiv;
+    }
+#pragma unroll
+    for (int mc = 0; mc < MCX; ++mc) xr[mc] = A + static_cast<int64_t>(src[mc]) * K;
     f32x4 ag[MCX], au[MCX];
     if (mcn == 1) {
       mx_partial<SWIGLU, 1, 4>(wq_g, ws_g, wq_u, ws_u, xr, q0, q1, part, KB, ag, au);
