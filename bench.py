@@ -45,12 +45,12 @@ KERNEL_SOURCES = {
     "down": ["gemm_bf16.hip", "grouped_gemm.h", "common.h"],
     "decode_gateup": ["decode.hip", "common.h"],
     "decode_down": ["decode.hip", "common.h"],
-    "decode_mx_gateup": ["decode_mx.hip", "common.h"],
-    "decode_mx_down": ["decode_mx.hip", "common.h"],
-    "batched_gateup": ["batched.hip", "common.h"],
-    "batched_down": ["batched.hip", "common.h"],
-    "batched_mx_gateup": ["decode_mx.hip", "common.h"],
-    "batched_mx_down": ["decode_mx.hip", "common.h"],
+    "decode_mx_gateup": ["decode_mx.hip", "common.h", "select.h"],
+    "decode_mx_down": ["decode_mx.hip", "common.h", "select.h"],
+    "batched_gateup": ["batched.hip", "common.h", "select.h"],
+    "batched_down": ["batched.hip", "common.h", "select.h"],
+    "batched_mx_gateup": ["decode_mx.hip", "common.h", "select.h"],
+    "batched_mx_down": ["decode_mx.hip", "common.h", "select.h"],
 }
 
 

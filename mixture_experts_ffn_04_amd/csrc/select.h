@@ -52,12 +52,15 @@ template <int S>
 __device__ __forceinline__ void topk_select(const float* row, int E, int k, float (&sel_v)[kMaxK],
                                             int (&sel_i)[kMaxK]) {
   const int lane = threadIdx.x & 63;
+  float v[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {                 // every logit requested before any is used
+    const int e = lane + 64 * i;
+    v[i] = row[e < E ? e : 0];
+  }
   unsigned key[S];
 #pragma unroll
-  for (int i = 0; i < S; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? logit_key(row[e]) : 0u;
-  }
+  for (int i = 0; i < S; ++i) key[i] = lane + 64 * i < E ? logit_key(v[i]) : 0u;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j >= k) break;
