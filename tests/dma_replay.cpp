@@ -221,6 +221,9 @@ int main() {
   replay<64, 128, 2, 4, EPI_STORE>("down 64x128 K2880 N2880", zipf_counts(32, 256, 0.5, 3), 2880, 2880, 0, {64});
   // router logits on flat tiles (one group of T rows, N = experts)
   replay<64, 128, 2, 4, EPI_F32B>("logits 64x128 K7168 N256", {16384}, 7168, 256, 0, {64});
+  replay<32, 128, 1, 4, EPI_STORE>("down 32x128 K2880 N2880", {8, 9, 7, 12, 0, 8, 31, 1}, 2880, 2880, 0, {32});
+  replay<64, 128, 1, 4, EPI_STORE>("down 64x128w4 K2880 N2880", {8, 9, 7, 12, 0, 8, 31, 1}, 2880, 2880, 0, {64});
+  replay<64, 256, 1, 4, EPI_STORE>("down 64x256 K2880 N2880", {8, 9, 7, 12, 0, 8, 31, 1}, 2880, 2880, 0, {64});
   replay<128, 128, 2, 4, EPI_F32B>("logits 128x128 K7168 N256", {16384}, 7168, 256, 0, {128});
   replay<128, 128, 2, 4, EPI_F32B>("logits 128x128 K64 N200 (ragged)", {300}, 64, 200, 0, {128});
   replay<64, 256, 2, 4, EPI_F32B>("logits 64x256 K7168 N256", {16384}, 7168, 256, 0, {64});
