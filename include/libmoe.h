@@ -330,9 +330,10 @@ MOE_API moe_status moe_decode_gateup_swiglu_gather(const void* x, const int32_t*
  *     ws_down [E][d][f/32]; h [rows][f], y_perm [rows][d] bf16.
  * Activations are bf16; products accumulate in fp32 (each block's sum is
  * scaled by its power of two, exact for scale codes 1..254 unless the
- * result overflows).  rows <= 1024, K (d for gate/up, f for down) <= 8192,
- * else MOE_ERR_UNSUPPORTED; codes, activations and outputs 16-byte
- * aligned.  Experts with no rows are never read.
+ * result overflows).  rows <= 1024, K (d for gate/up, f for down) <= 8192
+ * and d * f <= 2^30, else MOE_ERR_UNSUPPORTED; codes, scales, activations
+ * and outputs 16-byte aligned, else MOE_ERR_ALIGNMENT.  Experts with no
+ * rows are never read.
  */
 MOE_API moe_status moe_decode_gateup_swiglu_mxfp4(const void* x, const int32_t* perm, int32_t k,
                                                   const void* wq_gate_up, const void* ws_gate_up,

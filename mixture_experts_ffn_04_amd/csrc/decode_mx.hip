@@ -9,11 +9,13 @@
 // elements (two per byte, element 2i in the low nibble) sharing one E8M0
 // scale X = 2^(s - 127); an element's value is X times its E2M1 value.
 //
-// Workgroup = (expert g with rows, CPB output columns), 4 waves; each wave
-// owns R = 4 weight rows (gate/up: the gate and up rows of 2 columns; down:
-// 4 columns).  Lane l keeps blocks l, l + 64, ... of its 4 rows in
-// registers (16 code bytes and one scale per block), loaded once: the
-// expert's weights are read from HBM once.  Then for every token row of the
+// Two forms, by rows per expert.  From one row per expert on average, the
+// LDS-staged MFMA form (decode_mx_lds_kernel, below).  With fewer rows, the
+// vector form: workgroup = (expert g with rows, CPB output columns), 4
+// waves; each wave owns R = 4 weight rows (gate/up: the gate and up rows of
+// 2 columns; down: 4 columns).  Lane l keeps blocks l, l + 64, ... of its
+// 4 rows in registers (16 code bytes and one scale per block), loaded once:
+// the expert's weights are read from HBM once.  Then for every token row of the
 // expert, the lane loads the 64 bytes of activations under each of its
 // blocks, turns each code byte into two bf16 values
 // (v_cvt_scalef32_pk_bf16_fp4 with scale 1: E2M1 values are exact in
@@ -32,9 +34,10 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 constexpr int kMxRows = 4;            // weight rows per wave
 constexpr int64_t kMxMaxRows = 1024;  // routed rows per call (decode sizes)
-// Above this many rows per expert on average the split-K MFMA form runs:
-// the vector form re-reads each activation row for every 4 weight rows.
-constexpr int64_t kMxVectorRowsPerExpert = 1;
+// From this many rows per expert on average the LDS-staged MFMA form runs
+// (measured faster from one row per expert of the 32-expert workload); the
+// vector form re-reads each activation row for every 4 weight rows.
+constexpr int64_t kMxStagedRowsPerExpert = 1;
 
 // Elements 2B and 2B + 1 of a code dword (byte B) as bf16, times x's pair.
 template <int B>
@@ -291,189 +294,280 @@ __global__ __launch_bounds__(256) void batched_mx_down_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Several rows per expert: the split-K MFMA form (v_mfma_f32_16x16x32_bf16,
-// weight rows as the 16-row operand, tokens as the 16-column one).
-//
-// K is walked in quads of 128 elements.  In quad j, lane (row i = lane % 16,
-// part q = lane / 16) holds elements 128j + 32q + [0, 32) of its row: one
-// whole MX block, so a single 16-byte load brings its codes and one byte its
-// scale.  MFMA m (0..3) of the quad takes elements 128j + 32q + 8m + [0, 8)
-// from every lane, of the weights and of the tokens alike, which only
-// permutes the order of the reduction over K.  The gfx950 FP4 conversion
-// applies the block's power of two while decoding, so the bf16 operand is
-// the weight's value.  A last half quad (K % 128 == 64) leaves parts 2 and 3
-// without elements: their weights and tokens load as zeros.
-//
-// Workgroup = (expert g, 16 output columns), 4 waves splitting the quads;
-// each wave issues all loads of a batch of U quads before its MFMAs; the
-// four partial sums meet in LDS.
-template <bool SWIGLU, int MC, int U>
-__device__ __forceinline__ void mx_partial(const uint8_t* wq_g, const uint8_t* ws_g, const uint8_t* wq_u,
-                                           const uint8_t* ws_u, const uint16_t* const* xr, int q0, int q1, int part,
-                                           int KB, f32x4* ag, f32x4* au) {
+// Several rows per expert: one MX quad (4 blocks, 128 elements of K) of a
+// 16-row weight tile against 16 token rows on v_mfma_f32_16x16x32_bf16,
+// weight rows as the 16-row operand and tokens as the 16-column one.  Lane
+// (i = lane % 16, q = lane / 16) holds block q of weight row i (16 code
+// bytes and one scale code) and the 32 elements of token i under it; MFMA m
+// takes elements 8m .. 8m + 7 of every lane's block, of the weights and the
+// tokens alike, which only permutes the order of the reduction over K.  The
+// gfx950 FP4 conversion applies the block's power of two while decoding, so
+// the bf16 operand is the weight's value.
+struct MxQuad {
+  u32x4 c;       // codes of block q of weight row i
+  uint32_t s;    // its scale code (raw)
+  u32x4 t[4];    // t[m]: elements 8m .. 8m + 7 of the block, of token i
+};
+
+// E8M0 scale code -> the bits of 2^(code - 127) as fp32 without branches
+// (code 0 is the denormal 2^-127, code 255 NaN), as e8m0_to_f32.
+__device__ __forceinline__ uint32_t mx_scale_bits(uint32_t code) {
+  uint32_t b = code << 23;
+  b = code == 0u ? 0x00400000u : b;
+  b = code == 255u ? 0x7fc00000u : b;
+  return b;
+}
+
+// The quad's 4 MFMAs into acc.
+__device__ __forceinline__ void mx_quad_mma(const MxQuad& s, f32x4& acc) {
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const float f = __uint_as_float(mx_scale_bits(s.s));
 #pragma unroll
-  for (int mc = 0; mc < MC; ++mc) {
-    ag[mc] = f32x4{};
-    au[mc] = f32x4{};
-  }
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int qb = q0; qb < q1; qb += U) {
-    u32x4 cg[U], cu[U], tk[U][MC][4];
-    uint32_t sg[U], su[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = (qb + u) * 4 + part;             // this lane's block
-      const bool ok = qb + u < q1 && b < KB;
-      cg[u] = ok ? *(const gu4*)(wq_g + b * 16) : zero;
-      sg[u] = ok ? ws_g[b] : 127u;
-      if (SWIGLU) {
-        cu[u] = ok ? *(const gu4*)(wq_u + b * 16) : zero;
-        su[u] = ok ? ws_u[b] : 127u;
-      }
-#pragma unroll
-      for (int mc = 0; mc < MC; ++mc)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) tk[u][mc][c] = ok ? *(const gu4*)(xr[mc] + b * 32 + c * 8) : zero;
-    }
-    __builtin_amdgcn_sched_barrier(0);   // the whole batch of loads is issued before any MFMA waits
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float xg = e8m0_to_f32(sg[u]);
-      const float xu = SWIGLU ? e8m0_to_f32(su[u]) : 0.0f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        u32x4 wg, wu;
-        wg[0] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cg[u][m], xg, 0));
-        wg[1] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cg[u][m], xg, 1));
-        wg[2] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cg[u][m], xg, 2));
-        wg[3] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cg[u][m], xg, 3));
-        if (SWIGLU) {
-          wu[0] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cu[u][m], xu, 0));
-          wu[1] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cu[u][m], xu, 1));
-          wu[2] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cu[u][m], xu, 2));
-          wu[3] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cu[u][m], xu, 3));
-        }
-#pragma unroll
-        for (int mc = 0; mc < MC; ++mc) {
-          const bf16x8 t = __builtin_bit_cast(bf16x8, tk[u][mc][m]);
-          ag[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wg), t, ag[mc], 0, 0, 0);
-          if (SWIGLU)
-            au[mc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wu), t, au[mc], 0, 0, 0);
-        }
-      }
-    }
+  for (int m = 0; m < 4; ++m) {
+    u32x4 w;
+    w[0] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(s.c[m], f, 0));
+    w[1] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(s.c[m], f, 1));
+    w[2] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(s.c[m], f, 2));
+    w[3] = __builtin_bit_cast(uint32_t, (b2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(s.c[m], f, 3));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), __builtin_bit_cast(bf16x8, s.t[m]),
+                                                  acc, 0, 0, 0);
   }
 }
 
+// ---------------------------------------------------------------------------
+// Several rows per expert, LDS-staged form.  Workgroup = (expert g, 64
+// weight rows): gate/up the gate and up rows of 32 output columns, down 64
+// output columns.  Wave w owns one 16-row tile of them and one chunk of up
+// to 16 of the expert's token rows: gate/up rows 0-7 of the tile are the
+// gate rows and rows 8-15 the up rows of columns 8w .. 8w + 7, down the
+// rows of columns 16w .. 16w + 15.  Every operand reaches LDS by
+// direct-to-LDS loads of 1 KB contiguous in LDS: first the scales of the
+// 64 rows for the whole of K (contiguous pieces of the scale tensor), then
+// stages of two quads (256 elements of K): 128 bytes of codes of each weight
+// row (8 rows per load) and 512 bytes of each token row (2 rows per load,
+// gathered through the row map), in a ring of 4 stage buffers, so three
+// stages are in flight while one is used.  Whole 128-byte row pieces per
+// load measured faster than 64-byte ones (c3mx T=64 gate/up 66.7 vs 62.7
+// us); 80 KB of LDS lets two workgroups share a CU, so one's first loads
+// and last stores hide under the other's stream.  Chunk c of a 128-byte
+// code row r sits at c ^ ((r / 2) % 8) and chunk c of a 512-byte token row
+// r at c ^ (r % 16), so the 16 rows a wave reads at one chunk hit distinct
+// banks.  The MFMAs take the layout of MxQuad.  Loads past a buffer's end
+// read zeros (buffer range check); the elements of a last stage past K are
+// read but never used (loading only the pieces inside K measured 1-2%
+// slower).
+typedef __attribute__((address_space(3))) void mxl_lds_void;
+
+constexpr int kMxlStages = 4;
+constexpr int kMxlRows = 64;                                   // weight rows per workgroup
+constexpr int kMxlCodeBytes = kMxlRows * 128;                  // per stage: 128 bytes of each row
+constexpr int kMxlTokBytes = 16 * 512;                         // per stage: 512 bytes of 16 token rows
+constexpr int kMxlStageBytes = kMxlCodeBytes + kMxlTokBytes;
+constexpr int kMxlScaleBytes = kMxlRows * 256;                 // 64 rows x K / 32, K <= 8192
+constexpr int kMxlLdsBytes = kMxlScaleBytes + kMxlStages * kMxlStageBytes;   // 80 KB
+constexpr int kMxlOob = 0x7fff0000;                            // a lane offset past every buffer
+constexpr int kMxlBufFlags = 0x00020000;                       // raw untyped 32-bit accesses (gfx9)
+
+// One LDS DMA: 64 lanes x 16 bytes from buffer rs at lane offset voff into
+// LDS [lds_addr, lds_addr + 1024).  Asm, so the compiler adds no wait of its
+// own for it; the kernel waits with vmcnt before the barrier that publishes
+// a stage.  No register outputs; nothing else here uses m0.
+__device__ __forceinline__ void mxl_dma16(__amdgpu_buffer_rsrc_t rs, int voff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rs), "s"(lds_addr) : "memory", "m0");
+}
+
+// This wave's loads but the VM youngest have landed and its LDS reads are
+// done, then the barrier: every wave's loads of the stage are visible and
+// the buffer read before is free.
+template <int VM>
+__device__ __forceinline__ void mxl_wait_barrier() {
+  static_assert(VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Expert row of local weight row r (0 .. 63) of the block at output column
+// n0: gate/up tile t = r / 16 holds gate rows n0 + 8t .. and up rows
+// N + n0 + 8t ..; down rows are n0 + r.
 template <bool SWIGLU>
-__global__ __launch_bounds__(256) void decode_mx_mfma_kernel(const uint16_t* __restrict__ A,
-                                                             const uint8_t* __restrict__ Bq,
-                                                             const uint8_t* __restrict__ Bs,
-                                                             const int32_t* __restrict__ off,
-                                                             const int32_t* __restrict__ rowmap, int kdiv, int rows,
-                                                             int K, int N, int G, uint16_t* __restrict__ C) {
-  constexpr int MCX = 4;                              // 16-token chunks per pass (64 tokens)
-  constexpr int NH = SWIGLU ? 2 : 1;
-  __shared__ float red[4][MCX][NH][4][64];
-  const int ntiles = N / 16;
-  const int j = blockIdx.x / ntiles;
-  const int n0 = (blockIdx.x - j * ntiles) * 16;
-  const int g = (rows < G) ? nth_active_group(off, G, rows, j) : j;
-  if (g < 0 || g >= G) return;
+__device__ __forceinline__ int mxl_expert_row(int r, int n0, int N) {
+  if (!SWIGLU) return n0 + r;
+  const int t = r >> 4, h = r & 15;
+  return h < 8 ? n0 + 8 * t + h : N + n0 + 8 * t + h - 8;
+}
+
+// LDS scale row of local weight row r: gate/up [gate rows n0 .. n0 + 31][up
+// rows N + n0 .. N + n0 + 31], down rows n0 .. n0 + 63.
+template <bool SWIGLU>
+__device__ __forceinline__ int mxl_scale_row(int r) {
+  if (!SWIGLU) return r;
+  const int t = r >> 4, h = r & 15;
+  return h < 8 ? 8 * t + h : 32 + 8 * t + h - 8;
+}
+
+// rows >= G: every group has workgroups (those of groups without rows exit).
+template <bool SWIGLU>
+__global__ __launch_bounds__(256, 2) void decode_mx_lds_kernel(const uint16_t* __restrict__ A,
+                                                               const uint8_t* __restrict__ Bq,
+                                                               const uint8_t* __restrict__ Bs,
+                                                               const int32_t* __restrict__ off,
+                                                               const int32_t* __restrict__ rowmap, int kdiv,
+                                                               int rows, int K, int N, uint16_t* __restrict__ C) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kMxlLdsBytes];
+  constexpr int CPB = SWIGLU ? 32 : 64;                 // output columns per workgroup
+  const int ncb = (N + CPB - 1) / CPB;
+  const int g = blockIdx.x / ncb;
+  const int cb = blockIdx.x - g * ncb;
   const int lo = clamp_off(off[g], rows);
   const int hi = clamp_off(off[g + 1], rows);
-  if (hi <= lo) return;                               // expert without rows: its weights are never read
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (hi <= lo) return;                                 // expert without rows: its weights are never read
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int i16 = lane & 15, part = lane >> 4;
-  const int KB = K / 32;
-  const int64_t brows = SWIGLU ? 2 * static_cast<int64_t>(N) : N;
-  const int64_t wrow = n0 + i16;                      // N is a multiple of 16: always a valid row
-  const int64_t urow = SWIGLU ? N + wrow : wrow;
-  const uint8_t* Bqg = Bq + static_cast<int64_t>(g) * brows * (K / 2);
-  const uint8_t* Bsg = Bs + static_cast<int64_t>(g) * brows * KB;
-  const uint8_t* wq_g = Bqg + wrow * (K / 2);
-  const uint8_t* wq_u = Bqg + urow * (K / 2);
-  const uint8_t* ws_g = Bsg + wrow * KB;
-  const uint8_t* ws_u = Bsg + urow * KB;
-  // contiguous quads per wave
-  const int quads = (KB + 3) / 4;
-  const int per = (quads + 3) / 4;
-  const int q0 = min(quads, wave * per);
-  const int q1 = min(quads, q0 + per);
-  for (int m0 = lo; m0 < hi; m0 += 16 * MCX) {
-    const int mcn = min(MCX, (hi - m0 + 15) / 16);
-    const uint16_t* xr[MCX];
-    int src[MCX];
+  const int n0 = cb * CPB;
+  const int KB = K / 32, KH = K / 2;
+  const int nq = KB / 4;                                // whole quads; K % 128 == 64 adds a half quad
+  const int nst = (K + 255) / 256;
+  const int brows = SWIGLU ? 2 * N : N;
+  const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>((const mxl_lds_void*)lds));
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Bq) + static_cast<int64_t>(g) * brows * KH, 0, brows * KH, kMxlBufFlags);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(Bs) + static_cast<int64_t>(g) * brows * KB, 0, brows * KB, kMxlBufFlags);
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A), 0, (rows / kdiv) * K * 2, kMxlBufFlags);
+
+  // Scales as [64][KB] bytes: 16-byte chunk c comes from gate rows n0 ..
+  // (c < 2 KB) or up rows N + n0 .. (after), down rows n0 .. (rows past N
+  // lie past the buffer: zeros).
+  const int nsc = 4 * KB;                               // chunks (64 KB bytes)
+  for (int k = wave; k * 64 < nsc; k += 4) {
+    const int c = k * 64 + lane;
+    const int b = 16 * c;
+    const int gb = (SWIGLU && b >= 32 * KB) ? (N + n0) * KB + b - 32 * KB : n0 * KB + b;
+    mxl_dma16(srs, c < nsc ? gb : kMxlOob, __builtin_amdgcn_readfirstlane(lds0 + k * 1024));
+  }
+
+  // Code loads: wave w fills local rows 16 w .. 16 w + 15, 8 per load.
+  int cvo[2];
 #pragma unroll
-    for (int mc = 0; mc < MCX; ++mc) {
-      const int row = m0 + mc * 16 + i16;             // rows past the group read a valid row; never stored
-      src[mc] = row < hi ? row : lo;
+  for (int kk = 0; kk < 2; ++kk) {
+    const int r = 16 * wave + 8 * kk + (lane >> 3);
+    const int grow = mxl_expert_row<SWIGLU>(r, n0, N);
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    cvo[kk] = grow < brows ? grow * KH + chunk * 16 : kMxlOob;
+  }
+  // The lane's weight row (row i16 of the wave's tile).
+  const int rl = 16 * wave + i16;
+  const int sl = mxl_scale_row<SWIGLU>(rl) * KB;
+  const int swr = (rl >> 1) & 7;
+
+  for (int m0 = lo; m0 < hi; m0 += 16) {
+    // Token loads: wave w fills token rows 4 w .. 4 w + 3, 2 per load; the
+    // rows' sources are wave-uniform (scalar loads).
+    int tvo[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      int src[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = m0 + 4 * wave + 2 * kk + h;
+        int sr = -1;
+        if (m < hi) sr = rowmap ? clamp_off(rowmap[m], rows - 1) / kdiv : m;
+        src[h] = __builtin_amdgcn_readfirstlane(sr);
+      }
+      const int tr = 4 * wave + 2 * kk + (lane >> 5);
+      const int sr = (lane >> 5) ? src[1] : src[0];
+      tvo[kk] = sr >= 0 ? sr * (K * 2) + (((lane & 31) ^ (tr & 15)) * 16) : kMxlOob;
     }
-    if (rowmap) {                                     // every map entry requested before any is used
-      int rm[MCX];
+    // A token load whose two rows both lie past the expert's rows is not
+    // issued: the wave issues 2 + ntl loads per stage.  Those rows' LDS
+    // keeps older data, which only reaches the MFMA columns of token rows
+    // that are never stored.
+    const int ntl = min(2, max(0, (hi - m0 - 4 * wave + 1) / 2));
+    auto dma_stage = [&](int st, int buf) {
+      const unsigned sb = lds0 + kMxlScaleBytes + buf * kMxlStageBytes;
 #pragma unroll
-      for (int mc = 0; mc < MCX; ++mc) rm[mc] = rowmap[src[mc]];
+      for (int kk = 0; kk < 2; ++kk)
+        mxl_dma16(crs, cvo[kk] + st * 128, __builtin_amdgcn_readfirstlane(sb + (2 * wave + kk) * 1024));
 #pragma unroll
-      for (int mc = 0; mc < MCX; ++mc) src[mc] = clamp_off(rm[mc], rows - 1) / kdiv;
-    }
+      for (int kk = 0; kk < 2; ++kk)
+        if (kk < ntl)
+          mxl_dma16(trs, tvo[kk] + st * 512,
+                    __builtin_amdgcn_readfirstlane(sb + kMxlCodeBytes + (2 * wave + kk) * 1024));
+    };
+    for (int st = 0; st < kMxlStages - 1 && st < nst; ++st) dma_stage(st, st);
+    f32x4 acc = {};
+    for (int st = 0; st < nst; ++st) {
+      // this wave's later stages in flight: (ahead) x (2 + ntl) loads
+      switch (min(nst - 1 - st, kMxlStages - 2) * (2 + ntl)) {
+        case 8: mxl_wait_barrier<8>(); break;
+        case 6: mxl_wait_barrier<6>(); break;
+        case 4: mxl_wait_barrier<4>(); break;
+        case 3: mxl_wait_barrier<3>(); break;
+        case 2: mxl_wait_barrier<2>(); break;
+        default: mxl_wait_barrier<0>(); break;
+      }
+      if (st + kMxlStages - 1 < nst) dma_stage(st + kMxlStages - 1, (st + kMxlStages - 1) % kMxlStages);
+      const uint8_t* cbuf = lds + kMxlScaleBytes + (st % kMxlStages) * kMxlStageBytes;
+      const uint8_t* tbuf = cbuf + kMxlCodeBytes;
 #pragma unroll
-    for (int mc = 0; mc < MCX; ++mc) xr[mc] = A + static_cast<int64_t>(src[mc]) * K;
-    f32x4 ag[MCX], au[MCX];
-    if (mcn == 1) {
-      mx_partial<SWIGLU, 1, 4>(wq_g, ws_g, wq_u, ws_u, xr, q0, q1, part, KB, ag, au);
-    } else if (mcn == 2) {
-      mx_partial<SWIGLU, 2, 2>(wq_g, ws_g, wq_u, ws_u, xr, q0, q1, part, KB, ag, au);
-    } else {
-      mx_partial<SWIGLU, 4, 1>(wq_g, ws_g, wq_u, ws_u, xr, q0, q1, part, KB, ag, au);
-    }
+      for (int u = 0; u < 2; ++u) {
+        const int jq = 2 * st + u;                      // the quad
+        if (jq > nq || (jq == nq && !(KB & 3))) break;  // past K
+        MxQuad t;
+        t.c = *reinterpret_cast<const u32x4*>(cbuf + rl * 128 + (((4 * u + part) ^ swr) * 16));
+        t.s = lds[sl + 4 * jq + part];
 #pragma unroll
-    for (int mc = 0; mc < MCX; ++mc) {
-      if (mc < mcn) {
+        for (int m = 0; m < 4; ++m)
+          t.t[m] = *reinterpret_cast<const u32x4*>(tbuf + i16 * 512 + (((16 * u + 4 * part + m) ^ i16) * 16));
+        if (jq == nq && part >= 2) {                    // K % 128 == 64: blocks 2 and 3 of the last quad are past K
+          const u32x4 zero = {0u, 0u, 0u, 0u};
+          t.c = zero;
+          t.s = 127u;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          red[wave][mc][0][r][lane] = ag[mc][r];
-          if (SWIGLU) red[wave][mc][NH - 1][r][lane] = au[mc][r];
+          for (int m = 0; m < 4; ++m) t.t[m] = zero;
         }
+        mx_quad_mma(t, acc);
       }
     }
-    __syncthreads();
-    if (wave < mcn) {
-      const int mc = wave;
-      const int row = m0 + mc * 16 + i16;
-      if (row < hi) {
-        float o[4];
+    // lane (token i16, part) holds tile rows 4 part .. 4 part + 3
+    const int row = m0 + i16;
+    uint2 v;
+    if (SWIGLU) {
+      // gate rows (parts 0, 1) meet their up rows (parts 2, 3) 32 lanes up
+      float up[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float gs = red[0][mc][0][r][lane] + red[1][mc][0][r][lane] + red[2][mc][0][r][lane] +
-                     red[3][mc][0][r][lane];
-          if (SWIGLU) {
-            const float us = red[0][mc][NH - 1][r][lane] + red[1][mc][NH - 1][r][lane] +
-                             red[2][mc][NH - 1][r][lane] + red[3][mc][NH - 1][r][lane];
-            gs = silu(gs) * us;
-          }
-          o[r] = gs;
-        }
-        uint2 v;
-        v.x = pack_bf16x2(o[0], o[1]);
-        v.y = pack_bf16x2(o[2], o[3]);
-        *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * N + n0 + 4 * part) = v;
+      for (int r = 0; r < 4; ++r) {
+        const unsigned gb = __float_as_uint(acc[r]);
+        up[r] = __uint_as_float(__builtin_amdgcn_permlane32_swap(gb, gb, false, false)[1]);
       }
+      if (part < 2 && row < hi && n0 + 8 * wave < N) {
+        v.x = pack_bf16x2(silu(acc[0]) * up[0], silu(acc[1]) * up[1]);
+        v.y = pack_bf16x2(silu(acc[2]) * up[2], silu(acc[3]) * up[3]);
+        *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * N + n0 + 8 * wave + 4 * part) = v;
+      }
+    } else if (row < hi && n0 + 16 * wave < N) {
+      v.x = pack_bf16x2(acc[0], acc[1]);
+      v.y = pack_bf16x2(acc[2], acc[3]);
+      *reinterpret_cast<uint2*>(C + static_cast<int64_t>(row) * N + n0 + 16 * wave + 4 * part) = v;
     }
-    __syncthreads();
+    __syncthreads();                                    // every wave is done with the buffers the next chunk loads
   }
 }
 
 template <bool SWIGLU>
-moe_status launch_mx_mfma(const void* A, const void* Bq, const void* Bs, const int32_t* off, const int32_t* rowmap,
-                          int kdiv, int64_t rows, int64_t K, int64_t N, int G, void* C, hipStream_t st) {
-  const int64_t groups = G < rows ? G : rows;
-  const int64_t grid = groups * (N / 16);
-  if (grid == 0) return MOE_OK;
+moe_status launch_mx_lds(const void* A, const void* Bq, const void* Bs, const int32_t* off, const int32_t* rowmap,
+                         int kdiv, int64_t rows, int64_t K, int64_t N, int G, void* C, hipStream_t st) {
+  constexpr int CPB = SWIGLU ? 32 : 64;
+  if (rows < G) return MOE_ERR_UNSUPPORTED;               // the callers take the vector form then
+  const int64_t grid = static_cast<int64_t>(G) * ((N + CPB - 1) / CPB);
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((decode_mx_mfma_kernel<SWIGLU>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
+  hipLaunchKernelGGL((decode_mx_lds_kernel<SWIGLU>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
                      static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Bq), static_cast<const uint8_t*>(Bs),
-                     off, rowmap, kdiv, static_cast<int>(rows), static_cast<int>(K), static_cast<int>(N), G,
+                     off, rowmap, kdiv, static_cast<int>(rows), static_cast<int>(K), static_cast<int>(N),
                      static_cast<uint16_t*>(C));
   return launch_status();
 }
@@ -502,11 +596,13 @@ moe_status launch_mx(const void* A, const void* Bq, const void* Bs, const int32_
 moe_status check_mx(const void* in, const void* wq, const void* ws, const int32_t* offsets, int64_t rows, int64_t d,
                     int64_t f, int32_t E, const void* out, int64_t K) {
   if (rows < 0 || d <= 0 || f <= 0 || E < 1) return MOE_ERR_INVALID_ARG;
-  if (E > kMaxE || rows > kMxMaxRows || K > 8192) return MOE_ERR_UNSUPPORTED;
+  // K bounds the scale rows the LDS-staged form keeps; d * f bounds one
+  // expert's codes (d f bytes for gate/up) so 32-bit buffer offsets reach them
+  if (E > kMaxE || rows > kMxMaxRows || K > 8192 || d * f > (int64_t(1) << 30)) return MOE_ERR_UNSUPPORTED;
   if (d % 64 != 0 || f % 64 != 0) return MOE_ERR_ALIGNMENT;
   if (rows == 0) return MOE_OK;
   if (!in || !wq || !ws || !offsets || !out) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(in) || !aligned16(wq) || !aligned16(out)) return MOE_ERR_ALIGNMENT;
+  if (!aligned16(in) || !aligned16(wq) || !aligned16(ws) || !aligned16(out)) return MOE_ERR_ALIGNMENT;
   return MOE_OK;
 }
 
@@ -608,8 +704,8 @@ extern "C" moe_status moe_decode_gateup_swiglu_mxfp4(const void* x, const int32_
   moe_status s = check_mx(x, wq_gate_up, ws_gate_up, offsets, rows, d, f, E, h, d);
   if (s != MOE_OK || rows == 0) return s;
   if (perm && (k < 1 || k > kMaxK || rows % k != 0)) return MOE_ERR_INVALID_ARG;
-  if (rows > kMxVectorRowsPerExpert * E)
-    return launch_mx_mfma<true>(x, wq_gate_up, ws_gate_up, offsets, perm, perm ? k : 1, rows, d, f, E, h,
+  if (rows >= kMxStagedRowsPerExpert * E)
+    return launch_mx_lds<true>(x, wq_gate_up, ws_gate_up, offsets, perm, perm ? k : 1, rows, d, f, E, h,
                                 as_stream(stream));
   return launch_mx<true>(x, wq_gate_up, ws_gate_up, offsets, perm, perm ? k : 1, rows, d, f, E, h, as_stream(stream));
 }
@@ -619,7 +715,7 @@ extern "C" moe_status moe_decode_down_mxfp4(const void* h, const void* wq_down, 
                                             void* y_perm, void* stream) {
   moe_status s = check_mx(h, wq_down, ws_down, offsets, rows, d, f, E, y_perm, f);
   if (s != MOE_OK || rows == 0) return s;
-  if (rows > kMxVectorRowsPerExpert * E)
-    return launch_mx_mfma<false>(h, wq_down, ws_down, offsets, nullptr, 1, rows, f, d, E, y_perm, as_stream(stream));
+  if (rows >= kMxStagedRowsPerExpert * E)
+    return launch_mx_lds<false>(h, wq_down, ws_down, offsets, nullptr, 1, rows, f, d, E, y_perm, as_stream(stream));
   return launch_mx<false>(h, wq_down, ws_down, offsets, nullptr, 1, rows, f, d, E, y_perm, as_stream(stream));
 }

@@ -108,6 +108,8 @@ int main(void) {
   EXPECT(moe_decode_gateup_swiglu_mxfp4(NULL, NULL, 1, NULL, NULL, NULL, 0, 128, 128, 8, NULL, NULL), MOE_OK);
   EXPECT(moe_decode_down_mxfp4(p, p, p, p, 10, 128, 16384, 8, p, NULL), MOE_ERR_UNSUPPORTED);
   EXPECT(moe_decode_down_mxfp4(q, p, p, p, 10, 128, 128, 8, p, NULL), MOE_ERR_ALIGNMENT);
+  EXPECT(moe_decode_down_mxfp4(p, p, q, p, 10, 128, 128, 8, p, NULL), MOE_ERR_ALIGNMENT);
+  EXPECT(moe_decode_gateup_swiglu_mxfp4(p, NULL, 1, p, p, p, 10, 8192, 262144, 8, p, NULL), MOE_ERR_UNSUPPORTED);
   EXPECT(moe_batched_gateup_swiglu_mxfp4(p, p, p, p, 257, 64, 64, 8, 4, p, NULL), MOE_ERR_UNSUPPORTED);
   EXPECT(moe_batched_gateup_swiglu_mxfp4(p, p, p, p, 8, 96, 64, 8, 4, p, NULL), MOE_ERR_ALIGNMENT);
   EXPECT(moe_batched_gateup_swiglu_mxfp4(p, p, p, NULL, 8, 64, 64, 8, 4, p, NULL), MOE_ERR_INVALID_ARG);

@@ -871,7 +871,7 @@ def test_batched_mxfp4_calls(gpu, T, E, k, d, f):
     dn64 = {e: O.mxfp4_dequantize(dq[e], ds[e]) for e in used}
     h_ref = np.stack([O.gate_up_swiglu(x64[p // k][None], gu64[flat[p]])[0] for p in range(P)])
     U.assert_close(U.host_values(h), h_ref, "bf16", f"mxfp4 batched H T={T} E={E} k={k}")
-    if P <= E:      # the decode call's vector form (at most one row per expert on average): same arithmetic
+    if P < E:       # the decode call's vector form (fewer rows than experts): same arithmetic
         assert (U.host_bits(h) == U.host_bits(hd)[inv]).all(), "batched and decode gate/up rows differ"
     else:
         U.assert_close(U.host_values(h), U.host_values(hd)[inv], "bf16", "mxfp4 batched vs decode H")
