@@ -388,11 +388,14 @@ __device__ __forceinline__ void mxl_wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The form's address arithmetic, shared by the kernel and by the host
+// replay that checks it (tests/mx_lds_replay.cpp), so __host__ __device__.
+//
 // Expert row of local weight row r (0 .. 63) of the block at output column
 // n0: gate/up tile t = r / 16 holds gate rows n0 + 8t .. and up rows
 // N + n0 + 8t ..; down rows are n0 + r.
 template <bool SWIGLU>
-__device__ __forceinline__ int mxl_expert_row(int r, int n0, int N) {
+__host__ __device__ __forceinline__ int mxl_expert_row(int r, int n0, int N) {
   if (!SWIGLU) return n0 + r;
   const int t = r >> 4, h = r & 15;
   return h < 8 ? n0 + 8 * t + h : N + n0 + 8 * t + h - 8;
@@ -401,10 +404,66 @@ __device__ __forceinline__ int mxl_expert_row(int r, int n0, int N) {
 // LDS scale row of local weight row r: gate/up [gate rows n0 .. n0 + 31][up
 // rows N + n0 .. N + n0 + 31], down rows n0 .. n0 + 63.
 template <bool SWIGLU>
-__device__ __forceinline__ int mxl_scale_row(int r) {
+__host__ __device__ __forceinline__ int mxl_scale_row(int r) {
   if (!SWIGLU) return r;
   const int t = r >> 4, h = r & 15;
   return h < 8 ? 8 * t + h : 32 + 8 * t + h - 8;
+}
+
+// Scales as [64][KB] bytes in LDS: byte offset in the expert's scales of
+// 16-byte chunk c (gate rows n0 .. for c < 2 KB, up rows N + n0 .. after;
+// down rows n0 ..), or kMxlOob past the 64 rows.
+template <bool SWIGLU>
+__host__ __device__ __forceinline__ int mxl_scale_off(int c, int n0, int N, int KB) {
+  if (c >= 4 * KB) return kMxlOob;
+  const int b = 16 * c;
+  return (SWIGLU && b >= 32 * KB) ? (N + n0) * KB + b - 32 * KB : n0 * KB + b;
+}
+
+// Code load kk (0, 1) of wave w fills local rows 8 (2w + kk) .. + 7, 128
+// bytes each: the lane's local row, and its byte offset in the expert's
+// codes at stage 0 (stage st adds 128 st).  Chunk c of row r goes to slot
+// c ^ ((r / 2) % 8) of the row in LDS.
+__host__ __device__ __forceinline__ int mxl_code_row(int wave, int kk, int lane) {
+  return 16 * wave + 8 * kk + (lane >> 3);
+}
+
+template <bool SWIGLU>
+__host__ __device__ __forceinline__ int mxl_code_off(int wave, int kk, int lane, int n0, int N, int KH) {
+  const int r = mxl_code_row(wave, kk, lane);
+  const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+  return mxl_expert_row<SWIGLU>(r, n0, N) * KH + chunk * 16;
+}
+
+// Token load kk of wave w fills token rows 4w + 2kk and 4w + 2kk + 1 of the
+// chunk, 512 bytes each: the lane's row, and its byte offset in A at stage
+// 0 for source row src (stage st adds 512 st), or kMxlOob without one.
+// Chunk c of row r goes to slot c ^ (r % 16).
+__host__ __device__ __forceinline__ int mxl_tok_row(int wave, int kk, int lane) {
+  return 4 * wave + 2 * kk + (lane >> 5);
+}
+
+__host__ __device__ __forceinline__ int mxl_tok_off(int src, int K, int wave, int kk, int lane) {
+  const int tr = mxl_tok_row(wave, kk, lane);
+  return src >= 0 ? src * (K * 2) + (((lane & 31) ^ (tr & 15)) * 16) : kMxlOob;
+}
+
+// Token loads a wave issues per stage for a chunk of `left` rows (those
+// whose two rows both lie past the chunk are skipped).
+__host__ __device__ __forceinline__ int mxl_tok_loads(int left, int wave) {
+  const int n = (left - 4 * wave + 1) / 2;
+  return n < 0 ? 0 : (n > 2 ? 2 : n);
+}
+
+// LDS offsets a lane reads in quad u of a stage buffer: the codes of block
+// 4u + q of local row rl, and elements 8m .. 8m + 7 of that block of token
+// row i (from the buffer's code and token parts).
+__host__ __device__ __forceinline__ int mxl_code_read(int rl, int u, int q) {
+  return rl * 128 + (((4 * u + q) ^ ((rl >> 1) & 7)) * 16);
+}
+
+__host__ __device__ __forceinline__ int mxl_tok_read(int i, int u, int q, int m) {
+  return i * 512 + (((16 * u + 4 * q + m) ^ i) * 16);
 }
 
 // rows >= G: every group has workgroups (those of groups without rows exit).
@@ -439,30 +498,17 @@ __global__ __launch_bounds__(256, 2) void decode_mx_lds_kernel(const uint16_t* _
   const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(A), 0, (rows / kdiv) * K * 2, kMxlBufFlags);
 
-  // Scales as [64][KB] bytes: 16-byte chunk c comes from gate rows n0 ..
-  // (c < 2 KB) or up rows N + n0 .. (after), down rows n0 .. (rows past N
-  // lie past the buffer: zeros).
-  const int nsc = 4 * KB;                               // chunks (64 KB bytes)
-  for (int k = wave; k * 64 < nsc; k += 4) {
-    const int c = k * 64 + lane;
-    const int b = 16 * c;
-    const int gb = (SWIGLU && b >= 32 * KB) ? (N + n0) * KB + b - 32 * KB : n0 * KB + b;
-    mxl_dma16(srs, c < nsc ? gb : kMxlOob, __builtin_amdgcn_readfirstlane(lds0 + k * 1024));
-  }
+  // The 64 rows' scales for the whole of K, [64][KB] bytes.
+  for (int k = wave; k * 64 < 4 * KB; k += 4)
+    mxl_dma16(srs, mxl_scale_off<SWIGLU>(k * 64 + lane, n0, N, KB), __builtin_amdgcn_readfirstlane(lds0 + k * 1024));
 
   // Code loads: wave w fills local rows 16 w .. 16 w + 15, 8 per load.
   int cvo[2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int r = 16 * wave + 8 * kk + (lane >> 3);
-    const int grow = mxl_expert_row<SWIGLU>(r, n0, N);
-    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
-    cvo[kk] = grow < brows ? grow * KH + chunk * 16 : kMxlOob;
-  }
+  for (int kk = 0; kk < 2; ++kk) cvo[kk] = mxl_code_off<SWIGLU>(wave, kk, lane, n0, N, KH);
   // The lane's weight row (row i16 of the wave's tile).
   const int rl = 16 * wave + i16;
   const int sl = mxl_scale_row<SWIGLU>(rl) * KB;
-  const int swr = (rl >> 1) & 7;
 
   for (int m0 = lo; m0 < hi; m0 += 16) {
     // Token loads: wave w fills token rows 4 w .. 4 w + 3, 2 per load; the
@@ -478,15 +524,13 @@ __global__ __launch_bounds__(256, 2) void decode_mx_lds_kernel(const uint16_t* _
         if (m < hi) sr = rowmap ? clamp_off(rowmap[m], rows - 1) / kdiv : m;
         src[h] = __builtin_amdgcn_readfirstlane(sr);
       }
-      const int tr = 4 * wave + 2 * kk + (lane >> 5);
-      const int sr = (lane >> 5) ? src[1] : src[0];
-      tvo[kk] = sr >= 0 ? sr * (K * 2) + (((lane & 31) ^ (tr & 15)) * 16) : kMxlOob;
+      tvo[kk] = mxl_tok_off((lane >> 5) ? src[1] : src[0], K, wave, kk, lane);
     }
     // A token load whose two rows both lie past the expert's rows is not
     // issued: the wave issues 2 + ntl loads per stage.  Those rows' LDS
     // keeps older data, which only reaches the MFMA columns of token rows
     // that are never stored.
-    const int ntl = min(2, max(0, (hi - m0 - 4 * wave + 1) / 2));
+    const int ntl = mxl_tok_loads(hi - m0, wave);
     auto dma_stage = [&](int st, int buf) {
       const unsigned sb = lds0 + kMxlScaleBytes + buf * kMxlStageBytes;
 #pragma unroll
@@ -518,11 +562,10 @@ __global__ __launch_bounds__(256, 2) void decode_mx_lds_kernel(const uint16_t* _
         const int jq = 2 * st + u;                      // the quad
         if (jq > nq || (jq == nq && !(KB & 3))) break;  // past K
         MxQuad t;
-        t.c = *reinterpret_cast<const u32x4*>(cbuf + rl * 128 + (((4 * u + part) ^ swr) * 16));
+        t.c = *reinterpret_cast<const u32x4*>(cbuf + mxl_code_read(rl, u, part));
         t.s = lds[sl + 4 * jq + part];
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          t.t[m] = *reinterpret_cast<const u32x4*>(tbuf + i16 * 512 + (((16 * u + 4 * part + m) ^ i16) * 16));
+        for (int m = 0; m < 4; ++m) t.t[m] = *reinterpret_cast<const u32x4*>(tbuf + mxl_tok_read(i16, u, part, m));
         if (jq == nq && part >= 2) {                    // K % 128 == 64: blocks 2 and 3 of the last quad are past K
           const u32x4 zero = {0u, 0u, 0u, 0u};
           t.c = zero;
