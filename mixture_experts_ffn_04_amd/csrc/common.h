@@ -84,11 +84,13 @@ __device__ __forceinline__ int nth_active_group(const int32_t* __restrict__ off,
 }
 
 // MXFP4 (OCP Microscaling): E8M0 scale code -> 2^(code - 127) as fp32
-// (code 0: 2^-127, a denormal; code 255: NaN).
+// (code 0: 2^-127, a denormal; code 255: NaN), with selects rather than
+// branches, so no load waits on the decode of an earlier one.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
-  if (code == 0) return __uint_as_float(0x00400000u);
-  if (code == 255) return __uint_as_float(0x7fc00000u);
-  return __uint_as_float(code << 23);
+  uint32_t b = code << 23;
+  b = code == 0u ? 0x00400000u : b;
+  b = code == 255u ? 0x7fc00000u : b;
+  return __uint_as_float(b);
 }
 
 // ---------------------------------------------------------------- host

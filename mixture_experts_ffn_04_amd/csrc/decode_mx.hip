@@ -309,19 +309,10 @@ struct MxQuad {
   u32x4 t[4];    // t[m]: elements 8m .. 8m + 7 of the block, of token i
 };
 
-// E8M0 scale code -> the bits of 2^(code - 127) as fp32 without branches
-// (code 0 is the denormal 2^-127, code 255 NaN), as e8m0_to_f32.
-__device__ __forceinline__ uint32_t mx_scale_bits(uint32_t code) {
-  uint32_t b = code << 23;
-  b = code == 0u ? 0x00400000u : b;
-  b = code == 255u ? 0x7fc00000u : b;
-  return b;
-}
-
 // The quad's 4 MFMAs into acc.
 __device__ __forceinline__ void mx_quad_mma(const MxQuad& s, f32x4& acc) {
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-  const float f = __uint_as_float(mx_scale_bits(s.s));
+  const float f = e8m0_to_f32(s.s);
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     u32x4 w;
