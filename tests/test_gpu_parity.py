@@ -766,10 +766,12 @@ def test_mxfp4_projections(gpu, name):
     U.assert_close(U.host_values(y), O.grouped_down(W.values(hs, "bf16"), dn64, offsets), "bf16", f"{name} mxfp4 Y")
 
 
-# K of one, two and four 64-block columns per lane (2048, 4096, 8192), rows
-# from 1 to 64 per expert with empty experts in between
+# Both forms: from one row per expert on average the LDS-staged MFMA form
+# (K 2048, 4096, 8192; rows from 1 to 64 per expert with empty experts in
+# between, more than 16 for some), with fewer rows the vector form with one,
+# two and four 64-block columns per lane (K 1024, 4096, 8192)
 @pytest.mark.parametrize("E,rows,K,N", [(16, 40, 2048, 192), (64, 300, 4096, 128), (8, 200, 8192, 64),
-                                         (256, 24, 1024, 320)])
+                                         (256, 24, 1024, 320), (64, 40, 4096, 128), (32, 20, 8192, 64)])
 def test_mxfp4_shapes(gpu, E, rows, K, N):
     offsets = _skewed_offsets(E, rows, seed=K + N)
     xs = W.gen_matrix((rows, K), seed=K + 51)
@@ -1035,6 +1037,32 @@ def test_graph_replay_matches_eager(gpu, name):
         torch.cuda.synchronize()
         assert (U.host_bits(y) == ref).all(), f"replay {rep} differs from the eager layer"
         assert 0.0 < g.stage_ms()["gateup"] < 1e3
+        eager.forward(x2 if rep % 2 == 0 else x1)
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37"])
+def test_graph_replay_matches_eager_mxfp4(gpu, name):
+    """As above with MXFP4 experts: the batched calls for one token, the
+    LDS-staged decode kernels for more."""
+    wl, inp = U.small_inputs(name)
+    gq, gs, dq, ds = W.gen_all_experts_mxfp4(wl)
+    dev = U.device_weights(wl, inp)
+    weights = B().MoeWeights(dev.w_router, dev.bias, _mx_dev(gq, gpu), _mx_dev(dq, gpu),
+                             w_gate_up_scales=_mx_dev(gs, gpu), w_down_scales=_mx_dev(ds, gpu))
+    eager = B().MoeLayer(weights, wl.k, wl.score)
+    x1 = U.dev_tensor(inp["x"], "bf16")
+    pi = torch.from_numpy(np.random.default_rng(6).permutation(wl.T)).to(gpu)
+    x2 = (x1[pi] * 0.5).contiguous()
+    y1 = U.host_bits(eager.forward(x1).clone())
+    y2 = U.host_bits(eager.forward(x2).clone())
+    g = B().MoeLayerGraph(weights, wl.k, wl.score, wl.T, timed=("gateup",))
+    for rep in range(4):
+        src, ref = (x1, y1) if rep % 2 == 0 else (x2, y2)
+        g.x.copy_(src)
+        y = g.replay()
+        torch.cuda.synchronize()
+        assert (U.host_bits(y) == ref).all(), f"replay {rep} differs from the eager layer"
         eager.forward(x2 if rep % 2 == 0 else x1)
         torch.cuda.synchronize()
 
