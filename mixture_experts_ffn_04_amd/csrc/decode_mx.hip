@@ -311,7 +311,7 @@ struct MxQuad {
 
 // The quad's 4 MFMAs into acc.
 __device__ __forceinline__ void mx_quad_mma(const MxQuad& s, f32x4& acc) {
-  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  typedef bf16x2v b2;
   const float f = e8m0_to_f32(s.s);
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -338,9 +338,9 @@ __device__ __forceinline__ void mx_quad_mma(const MxQuad& s, f32x4& acc) {
 // row (8 rows per load) and 512 bytes of each token row (2 rows per load,
 // gathered through the row map), in a ring of 4 stage buffers, so three
 // stages are in flight while one is used.  Whole 128-byte row pieces per
-// load measured faster than 64-byte ones (c3mx T=64 gate/up 66.7 vs 62.7
-// us); 80 KB of LDS lets two workgroups share a CU, so one's first loads
-// and last stores hide under the other's stream.  Chunk c of a 128-byte
+// load measured faster than 64-byte ones (c3mx T=64 gate/up 62.7 against
+// 66.7 us); 80 KB of LDS lets two workgroups share a CU, so one's first
+// loads and last stores hide under the other's stream.  Chunk c of a 128-byte
 // code row r sits at c ^ ((r / 2) % 8) and chunk c of a 512-byte token row
 // r at c ^ (r % 16), so the 16 rows a wave reads at one chunk hit distinct
 // banks.  The MFMAs take the layout of MxQuad.  Loads past a buffer's end
