@@ -767,11 +767,13 @@ def test_mxfp4_projections(gpu, name):
 
 
 # Both forms: from one row per expert on average the LDS-staged MFMA form
-# (K 2048, 4096, 8192; rows from 1 to 64 per expert with empty experts in
-# between, more than 16 for some), with fewer rows the vector form with one,
-# two and four 64-block columns per lane (K 1024, 4096, 8192)
+# (K 2048, 2880 with its half quad at the end, 4096, 8192; rows from 1 to 64
+# per expert with empty experts in between, more than 16 -- several token
+# chunks -- for some), with fewer rows the vector form with one, two and four
+# 64-block columns per lane (K 1024, 4096, 8192)
 @pytest.mark.parametrize("E,rows,K,N", [(16, 40, 2048, 192), (64, 300, 4096, 128), (8, 200, 8192, 64),
-                                         (256, 24, 1024, 320), (64, 40, 4096, 128), (32, 20, 8192, 64)])
+                                         (4, 100, 2880, 192), (256, 24, 1024, 320), (64, 40, 4096, 128),
+                                         (32, 20, 8192, 64)])
 def test_mxfp4_shapes(gpu, E, rows, K, N):
     offsets = _skewed_offsets(E, rows, seed=K + N)
     xs = W.gen_matrix((rows, K), seed=K + 51)
