@@ -120,6 +120,10 @@ SMALL_WORKLOADS = {
                          router_std=0.02 * (2880 / 576) ** 0.5, experts="mxfp4"),
     "c3mxs_t37": Workload("c3mxs_t37", 37, 576, 640, 32, 4, "softmax", "bf16", seed=147,
                           router_std=0.02 * (2880 / 576) ** 0.5, experts="mxfp4"),
+    # the same layer at d = 1536, f = 1344 (a K that ends in half a
+    # 128-element MXFP4 quad, and 21 column blocks of 64), 37 tokens
+    "c3mxm_t37": Workload("c3mxm_t37", 37, 1536, 1344, 32, 4, "softmax", "bf16", seed=157,
+                          router_std=0.02 * (2880 / 1536) ** 0.5, experts="mxfp4"),
     "c4s": Workload("c4s", 517, 256, 192, 128, 8, "softmax", "bf16", zipf_s=1.1, seed=104,
                     router_std=0.02 * (2048 / 256) ** 0.5),
     "c5s": Workload("c5s", 301, 448, 128, 256, 8, "sigmoid", "bf16", zipf_s=1.0,

@@ -737,7 +737,7 @@ def _mx_dev(a, gpu):
     return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(gpu)
 
 
-@pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37"])
+@pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37", "c3mxm_t37"])
 def test_mxfp4_projections(gpu, name):
     """MXFP4 decode calls against the oracle's projections with the
     dequantised weights, every element: gate/up reading the rows through
@@ -767,13 +767,15 @@ def test_mxfp4_projections(gpu, name):
 
 
 # Both forms: from one row per expert on average the LDS-staged MFMA form
-# (K 2048, 2880 with its half quad at the end, 4096, 8192; rows from 1 to 64
-# per expert with empty experts in between, more than 16 -- several token
-# chunks -- for some), with fewer rows the vector form with one, two and four
-# 64-block columns per lane (K 1024, 4096, 8192)
+# (K 1024, 1088, 1536 with 256 experts, 2048, 2880 and 1344 with a half
+# quad at the end, 4096, 8192; rows from 1 to 64 per expert with empty
+# experts in between, more than 16 -- several token chunks -- for some),
+# with fewer rows the vector form with one, two and four 64-block columns
+# per lane (K 1024, 4096, 8192)
 @pytest.mark.parametrize("E,rows,K,N", [(16, 40, 2048, 192), (64, 300, 4096, 128), (8, 200, 8192, 64),
-                                         (4, 100, 2880, 192), (256, 24, 1024, 320), (64, 40, 4096, 128),
-                                         (32, 20, 8192, 64)])
+                                         (4, 100, 2880, 192), (8, 90, 1344, 128), (256, 600, 1536, 64),
+                                         (12, 70, 1088, 320), (8, 90, 1024, 128), (256, 24, 1024, 320),
+                                         (64, 40, 4096, 128), (32, 20, 8192, 64)])
 def test_mxfp4_shapes(gpu, E, rows, K, N):
     offsets = _skewed_offsets(E, rows, seed=K + N)
     xs = W.gen_matrix((rows, K), seed=K + 51)
@@ -797,7 +799,7 @@ def test_mxfp4_shapes(gpu, E, rows, K, N):
 
 
 @pytest.mark.parametrize("mode", ["auto", "decode"])
-@pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37"])
+@pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37", "c3mxm_t37"])
 def test_layer_mxfp4(gpu, name, mode):
     """The whole layer with MXFP4 experts against the oracle's eager loop
     over the dequantised experts, every token (auto: the batched calls for
@@ -1043,10 +1045,11 @@ def test_graph_replay_matches_eager(gpu, name):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37"])
+@pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37", "c3mxm_t37"])
 def test_graph_replay_matches_eager_mxfp4(gpu, name):
     """As above with MXFP4 experts: the batched calls for one token, the
-    LDS-staged decode kernels for more."""
+    LDS-staged decode kernels for more (d = 576, f = 640 and d = 1536,
+    f = 1344)."""
     wl, inp = U.small_inputs(name)
     gq, gs, dq, ds = W.gen_all_experts_mxfp4(wl)
     dev = U.device_weights(wl, inp)
