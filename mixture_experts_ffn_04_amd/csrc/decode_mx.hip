@@ -349,13 +349,28 @@ __device__ __forceinline__ void mx_quad_mma(const MxQuad& s, f32x4& acc) {
 // slower).
 typedef __attribute__((address_space(3))) void mxl_lds_void;
 
-constexpr int kMxlStages = 4;
 constexpr int kMxlRows = 64;                                   // weight rows per workgroup
 constexpr int kMxlCodeBytes = kMxlRows * 128;                  // per stage: 128 bytes of each row
 constexpr int kMxlTokBytes = 16 * 512;                         // per stage: 512 bytes of 16 token rows
 constexpr int kMxlStageBytes = kMxlCodeBytes + kMxlTokBytes;
-constexpr int kMxlScaleBytes = kMxlRows * 256;                 // 64 rows x K / 32, K <= 8192
-constexpr int kMxlLdsBytes = kMxlScaleBytes + kMxlStages * kMxlStageBytes;   // 80 KB
+// Two LDS shapes: NS stage buffers and a scale area of SCB bytes (the 64
+// rows' K / 32 scale bytes each, so K <= SCB / 2).  The wide one (4 stages,
+// K <= 8192, 80 KB: two workgroups per CU) for every projection; the
+// narrow one (2 stages, K <= 4096, 40 KB: four per CU) for gate/up.  With
+// the narrow shape a workgroup has one stage in flight instead of three, but
+// the CU holds twice the workgroups, whose phases drift apart: c3mx gate/up
+// 65 -> 61 us at T=32 and 68 -> 66 at T=64.  The down projection's 1,440
+// workgroups of 64 columns at d = 2880 make 1.4 rounds of four per CU there
+// and it measured slower (37 -> 40 us at T=64), so it keeps the wide shape.
+template <int NS, int SCB>
+struct MxlShape {
+  static constexpr int kStages = NS;
+  static constexpr int kScaleBytes = SCB;
+  static constexpr int kLdsBytes = SCB + NS * kMxlStageBytes;
+  static constexpr int kPerCu = (160 * 1024) / kLdsBytes;
+};
+typedef MxlShape<4, kMxlRows * 256> MxlWide;
+typedef MxlShape<2, kMxlRows * 128> MxlNarrow;
 constexpr int kMxlOob = 0x7fff0000;                            // a lane offset past every buffer
 constexpr int kMxlBufFlags = 0x00020000;                       // raw untyped 32-bit accesses (gfx9)
 
@@ -458,14 +473,16 @@ __host__ __device__ __forceinline__ int mxl_tok_read(int i, int u, int q, int m)
 }
 
 // rows >= G: every group has workgroups (those of groups without rows exit).
-template <bool SWIGLU>
-__global__ __launch_bounds__(256, 2) void decode_mx_lds_kernel(const uint16_t* __restrict__ A,
+// SH: the LDS shape (MxlWide or MxlNarrow).
+template <bool SWIGLU, typename SH>
+__global__ __launch_bounds__(256, SH::kPerCu) void decode_mx_lds_kernel(const uint16_t* __restrict__ A,
                                                                const uint8_t* __restrict__ Bq,
                                                                const uint8_t* __restrict__ Bs,
                                                                const int32_t* __restrict__ off,
                                                                const int32_t* __restrict__ rowmap, int kdiv,
                                                                int rows, int K, int N, uint16_t* __restrict__ C) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kMxlLdsBytes];
+  constexpr int NS = SH::kStages, SCB = SH::kScaleBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[SH::kLdsBytes];
   constexpr int CPB = SWIGLU ? 32 : 64;                 // output columns per workgroup
   const int ncb = (N + CPB - 1) / CPB;
   const int g = blockIdx.x / ncb;
@@ -523,7 +540,7 @@ __global__ __launch_bounds__(256, 2) void decode_mx_lds_kernel(const uint16_t* _
     // that are never stored.
     const int ntl = mxl_tok_loads(hi - m0, wave);
     auto dma_stage = [&](int st, int buf) {
-      const unsigned sb = lds0 + kMxlScaleBytes + buf * kMxlStageBytes;
+      const unsigned sb = lds0 + SCB + buf * kMxlStageBytes;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
         mxl_dma16(crs, cvo[kk] + st * 128, __builtin_amdgcn_readfirstlane(sb + (2 * wave + kk) * 1024));
@@ -533,11 +550,11 @@ __global__ __launch_bounds__(256, 2) void decode_mx_lds_kernel(const uint16_t* _
           mxl_dma16(trs, tvo[kk] + st * 512,
                     __builtin_amdgcn_readfirstlane(sb + kMxlCodeBytes + (2 * wave + kk) * 1024));
     };
-    for (int st = 0; st < kMxlStages - 1 && st < nst; ++st) dma_stage(st, st);
+    for (int st = 0; st < NS - 1 && st < nst; ++st) dma_stage(st, st);
     f32x4 acc = {};
     for (int st = 0; st < nst; ++st) {
       // this wave's later stages in flight: (ahead) x (2 + ntl) loads
-      switch (min(nst - 1 - st, kMxlStages - 2) * (2 + ntl)) {
+      switch (min(nst - 1 - st, NS - 2) * (2 + ntl)) {
         case 8: mxl_wait_barrier<8>(); break;
         case 6: mxl_wait_barrier<6>(); break;
         case 4: mxl_wait_barrier<4>(); break;
@@ -545,8 +562,8 @@ __global__ __launch_bounds__(256, 2) void decode_mx_lds_kernel(const uint16_t* _
         case 2: mxl_wait_barrier<2>(); break;
         default: mxl_wait_barrier<0>(); break;
       }
-      if (st + kMxlStages - 1 < nst) dma_stage(st + kMxlStages - 1, (st + kMxlStages - 1) % kMxlStages);
-      const uint8_t* cbuf = lds + kMxlScaleBytes + (st % kMxlStages) * kMxlStageBytes;
+      if (st + NS - 1 < nst) dma_stage(st + NS - 1, (st + NS - 1) % NS);
+      const uint8_t* cbuf = lds + SCB + (st % NS) * kMxlStageBytes;
       const uint8_t* tbuf = cbuf + kMxlCodeBytes;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -599,10 +616,18 @@ moe_status launch_mx_lds(const void* A, const void* Bq, const void* Bs, const in
   if (rows < G) return MOE_ERR_UNSUPPORTED;               // the callers take the vector form then
   const int64_t grid = static_cast<int64_t>(G) * ((N + CPB - 1) / CPB);
   if (grid > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((decode_mx_lds_kernel<SWIGLU>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Bq), static_cast<const uint8_t*>(Bs),
-                     off, rowmap, kdiv, static_cast<int>(rows), static_cast<int>(K), static_cast<int>(N),
-                     static_cast<uint16_t*>(C));
+#define MOE_MXL_LAUNCH(SH_)                                                                                   \
+  hipLaunchKernelGGL((decode_mx_lds_kernel<SWIGLU, SH_>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st,    \
+                     static_cast<const uint16_t*>(A), static_cast<const uint8_t*>(Bq),                         \
+                     static_cast<const uint8_t*>(Bs), off, rowmap, kdiv, static_cast<int>(rows),               \
+                     static_cast<int>(K), static_cast<int>(N), static_cast<uint16_t*>(C))
+  if constexpr (SWIGLU) {
+    if (K <= MxlNarrow::kScaleBytes / 2) MOE_MXL_LAUNCH(MxlNarrow);
+    else MOE_MXL_LAUNCH(MxlWide);
+  } else {
+    MOE_MXL_LAUNCH(MxlWide);
+  }
+#undef MOE_MXL_LAUNCH
   return launch_status();
 }
 
@@ -632,7 +657,8 @@ moe_status check_mx(const void* in, const void* wq, const void* ws, const int32_
   if (rows < 0 || d <= 0 || f <= 0 || E < 1) return MOE_ERR_INVALID_ARG;
   // K bounds the scale rows the LDS-staged form keeps; d * f bounds one
   // expert's codes (d f bytes for gate/up) so 32-bit buffer offsets reach them
-  if (E > kMaxE || rows > kMxMaxRows || K > 8192 || d * f > (int64_t(1) << 30)) return MOE_ERR_UNSUPPORTED;
+  if (E > kMaxE || rows > kMxMaxRows || K > MxlWide::kScaleBytes / 2 || d * f > (int64_t(1) << 30))
+    return MOE_ERR_UNSUPPORTED;
   if (d % 64 != 0 || f % 64 != 0) return MOE_ERR_ALIGNMENT;
   if (rows == 0) return MOE_OK;
   if (!in || !wq || !ws || !offsets || !out) return MOE_ERR_INVALID_ARG;

@@ -62,20 +62,22 @@ static void replay(const char* name, int N, int K, const std::vector<int>& count
   const int CPB = SWIGLU ? 32 : 64;
   const long checks0 = g_checks;
   const int fails0 = g_fails;
-  CHECK(kMxlScaleBytes + kMxlStages * kMxlStageBytes == kMxlLdsBytes && kMxlLdsBytes <= 80 * 1024, "lds %d",
-        kMxlLdsBytes);
-  CHECK(kMxlScaleBytes >= 64 * KB, "scale area for K %d", K);
+  // the LDS shape the launch picks for this projection and K
+  const int scb = (SWIGLU && K <= MxlNarrow::kScaleBytes / 2) ? MxlNarrow::kScaleBytes : MxlWide::kScaleBytes;
+  CHECK(MxlWide::kLdsBytes <= 80 * 1024 && MxlNarrow::kLdsBytes <= 40 * 1024, "lds %d %d", MxlWide::kLdsBytes,
+        MxlNarrow::kLdsBytes);
+  CHECK(scb >= 64 * KB, "scale area for K %d", K);
   for (int cb = 0; cb * CPB < N; ++cb) {
     const int n0 = cb * CPB;
     // scales
-    std::vector<long> simg(kMxlScaleBytes, -2);
+    std::vector<long> simg(scb, -2);
     for (int w = 0; w < 4; ++w)
       for (int k = w; k * 64 < 4 * KB; k += 4) {
-        CHECK((k + 1) * 1024 <= kMxlScaleBytes, "scale load %d", k);
+        CHECK((k + 1) * 1024 <= scb, "scale load %d", k);
         for (int lane = 0; lane < 64; ++lane) {
           const long o = mxl_scale_off<SWIGLU>(k * 64 + lane, n0, N, KB);
           CHECK(in_or_past(o, srec), "scale off %ld of %ld", o, srec);
-          for (int b = 0; b < 16 && k * 1024 + lane * 16 + b < kMxlScaleBytes; ++b)
+          for (int b = 0; b < 16 && k * 1024 + lane * 16 + b < scb; ++b)
             simg[k * 1024 + lane * 16 + b] = o < srec ? o + b : -1;
         }
       }
