@@ -63,13 +63,15 @@ def decode_tokens_per_s(bandwidth_bytes_per_s: float, active_params: float, byte
     return bandwidth_bytes_per_s / (active_params * bytes_per_param)
 
 
-def layer_flops(wl, P=None) -> float:
+def layer_flops(wl, P=None, Ts=None) -> float:
     """Algorithmic FLOPs of one layer call: router + 3 expert GEMMs per
     routed pair (+ the shared expert on every token).  P: the routed pairs
-    computed here (an expert-parallel share's), else all T*k."""
+    computed here (an expert-parallel share's), else all T*k; Ts: the
+    tokens the shared expert runs on here, else all T."""
     P = wl.P if P is None else P
+    Ts = wl.T if Ts is None else Ts
     return (2.0 * wl.T * wl.d * wl.E + 6.0 * P * wl.d * wl.f
-            + 6.0 * wl.T * wl.d * wl.f_shared)
+            + 6.0 * Ts * wl.d * wl.f_shared)
 
 
 def layer_bytes(wl, active: int) -> float:
@@ -119,7 +121,7 @@ def down_bytes(wl, active: int, P=None) -> float:
     return wl.expert_weight_bytes * wl.d * wl.f * active + b * (P * wl.f + P * wl.d)
 
 
-def kernel_rooflines(wl, active: int, kern_ms: dict, decode: bool, P=None) -> dict:
+def kernel_rooflines(wl, active: int, kern_ms: dict, decode: bool, P=None, Ts=None) -> dict:
     """Roofline position of each projection kernel from its mean duration
     (HIP events on the launch stream over the timed steps).  Grouped
     workloads: algorithmic FLOPs (gate/up 4 d f, down 2 d f per routed row;
@@ -134,8 +136,9 @@ def kernel_rooflines(wl, active: int, kern_ms: dict, decode: bool, P=None) -> di
     }
     if wl.f_shared:
         fs, b = wl.f_shared, wl.elem_bytes
-        work["shared_gateup"] = (4.0 * wl.T * wl.d * fs, b * (2.0 * fs * wl.d + wl.T * wl.d + wl.T * fs))
-        work["shared_down"] = (2.0 * wl.T * wl.d * fs, b * (fs * wl.d + wl.T * fs + wl.T * wl.d))
+        Ts = wl.T if Ts is None else Ts             # the shared expert's tokens here
+        work["shared_gateup"] = (4.0 * Ts * wl.d * fs, b * (2.0 * fs * wl.d + Ts * wl.d + Ts * fs))
+        work["shared_down"] = (2.0 * Ts * wl.d * fs, b * (fs * wl.d + Ts * fs + Ts * wl.d))
     for name, (flops, nbytes) in work.items():
         if name not in kern_ms:
             continue
@@ -176,12 +179,15 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared: bool = False, share: int = 1):
+def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared: bool = False, share: int = 1,
+          split_shared: bool = False):
     """Upload the workload's seeded inputs to the GPU and build the layer.
     With keep_host, the storage-format expert weights stay in host memory
     too (for the CPU oracle leg; the DeepSeek-shaped layer holds 22.5 GB).
     share > 1: one GPU's expert-parallel share of the layer -- experts
-    [0, E/share) and the shared expert -- with every token routed."""
+    [0, E/share) and the shared expert (with split_shared, the shared
+    expert on the share's 1/share of the tokens only) -- with every token
+    routed."""
     import torch
     from mixture_experts_ffn_04_amd import MoeLayer, MoeWeights
 
@@ -216,7 +222,8 @@ def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared
     weights = MoeWeights(dev(wr), None if bias is None else torch.from_numpy(bias).to(device), gu, dn,
                          None if sh is None else dev(sh[0]), None if sh is None else dev(sh[1]))
     layer = MoeLayer(weights, wl.k, wl.score, mode=mode, overlap_shared=overlap_shared,
-                     experts=None if share == 1 else (0, E_loc))
+                     experts=None if share == 1 else (0, E_loc),
+                     shared_part=(0, share) if split_shared and share > 1 else None)
     host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=sh)
     return layer, dev(x), host
 
@@ -600,6 +607,9 @@ def main(argv=None):
     ap.add_argument("--ep-share", type=int, default=1, metavar="N",
                     help="time one GPU's expert-parallel share of N (experts [0, E/N) and the shared expert, "
                          "every token routed, local pairs only); prefill workloads")
+    ap.add_argument("--split-shared", action="store_true",
+                    help="with --ep-share N: every share runs the shared expert on 1/N of the tokens (this one "
+                         "on tokens [0, T/N)) instead of share 0 on all of them")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernels", action="store_true", help="also print per-stage times to stderr")
@@ -654,8 +664,12 @@ def main(argv=None):
             return 2
         args.no_cpu = True          # the oracle leg needs every expert
 
+    if args.split_shared and share == 1:
+        print("--split-shared goes with --ep-share N (N > 1)", file=sys.stderr)
+        return 2
     layer, x, host = setup(wl, device, keep_host=not args.no_cpu, mode=args.mode,
-                           overlap_shared=args.overlap_shared, share=share)
+                           overlap_shared=args.overlap_shared, share=share, split_shared=args.split_shared)
+    Ts = wl.T // share if args.split_shared else None     # the shared expert's tokens here
     st = torch.cuda.current_stream()
     # the projection kernels are timed by events on the launch stream inside
     # the timed steps; an event pair costs a few microseconds, so the
@@ -725,7 +739,7 @@ def main(argv=None):
             kern_ms[name] = stage_ms[name]          # from the per-stage pass
     tokens_per_s = wl.T / (ms * 1e-3)
 
-    kernels = kernel_rooflines(wl, active, kern_ms, decode, P_here)
+    kernels = kernel_rooflines(wl, active, kern_ms, decode, P_here, Ts)
     if layer.use_batched(wl.T):
         kname = "batched_mx_gateup" if wl.experts == "mxfp4" else "batched_gateup"
     elif decode:
@@ -754,7 +768,8 @@ def main(argv=None):
                    "active_experts": active, "strategy": args.mode,
                    "parallelism": "single GPU" if share == 1 else
                    f"one GPU's expert-parallel share of {share}: experts 0..{wl.E // share - 1}"
-                   f"{' and the shared expert' if wl.f_shared else ''}, every token routed, {P_here} of {wl.P} "
+                   f"{'' if not wl.f_shared else ' and the shared expert on tokens 0..' + str(Ts - 1) if Ts else ' and the shared expert'}"
+                   f", every token routed, {P_here} of {wl.P} "
                    f"routed pairs here (the sum over shares is not run)",
                    "shared_expert": None if not wl.f_shared else
                    ("second stream beside the routed experts" if args.overlap_shared else "after the routed experts"),
@@ -762,8 +777,8 @@ def main(argv=None):
                              "kernel's events on every other step, the step time over the others" if decode
                    else "wall clock over the timed steps"},
         "roofline": roof,
-        "layer": {"tflops": layer_flops(wl, P_here) / (ms * 1e-3) / 1e12,
-                  "mfma_frac": layer_flops(wl, P_here) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "layer": {"tflops": layer_flops(wl, P_here, Ts) / (ms * 1e-3) / 1e12,
+                  "mfma_frac": layer_flops(wl, P_here, Ts) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                   "gbps": layer_bytes(wl, active) / (ms * 1e-3) / 1e9,
                   "hbm_frac": layer_bytes(wl, active) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                   "stage_ms": stage_ms, "wall_s": wall, "kernels": kernels,

@@ -319,12 +319,18 @@ class MoeLayer:
     forward returns the share's partial output (the pairs of other experts
     masked by moe_localize_ids); the partial outputs of all shares sum to
     the layer's output.
+
+    shared_part=(i, n) runs the shared expert (when the weights hold it)
+    on tokens [T i / n, T (i + 1) / n) only, so that n shares that each
+    hold it split its work: the partial output has the shared expert's
+    rows of that slice and zeros for it elsewhere.
     """
 
     DECODE_MAX_ROWS = 256
 
     def __init__(self, weights: MoeWeights, k: int, score: str, mode: str = "auto",
-                 experts: Optional[tuple] = None, overlap_shared: bool = False):
+                 experts: Optional[tuple] = None, overlap_shared: bool = False,
+                 shared_part: Optional[tuple] = None):
         load()
         self.w = weights
         # the shared expert does not depend on the routing: with
@@ -347,6 +353,11 @@ class MoeLayer:
             if e_count != self.E_loc or e_begin < 0 or e_begin + e_count > self.E:
                 raise ValueError("experts=(e_begin, e_count) does not match the expert weights")
             self.e_begin = int(e_begin)
+        if shared_part is not None:
+            i, n = shared_part
+            if n < 1 or not 0 <= i < n:
+                raise ValueError("shared_part=(i, n) needs 0 <= i < n")
+        self.shared_part = shared_part
         self.mx = weights.mxfp4
         self.f = weights.w_down.shape[2] * (2 if self.mx else 1)
         self.dev = weights.w_router.device
@@ -380,10 +391,19 @@ class MoeLayer:
         self.y = torch.empty(T, d, device=dev, dtype=dt)
         if self.w.shared_gate_up is not None:
             fs = self.w.shared_down.shape[2]
-            self.s_off = torch.tensor([0, T], device=dev, dtype=i32)
-            self.s_h = torch.empty(T, fs, device=dev, dtype=dt)
-            self.s_y = torch.empty(T, d, device=dev, dtype=dt)
+            t0, t1 = self.shared_rows(T)
+            self.s_off = torch.tensor([0, t1 - t0], device=dev, dtype=i32)
+            self.s_h = torch.empty(t1 - t0, fs, device=dev, dtype=dt)
+            # rows outside the slice are never written: zero once
+            self.s_y = (torch.zeros if (t0, t1) != (0, T) else torch.empty)(T, d, device=dev, dtype=dt)
         self._T = T
+
+    def shared_rows(self, T: int) -> tuple:
+        """The tokens [t0, t1) this layer runs the shared expert on."""
+        if self.shared_part is None:
+            return 0, T
+        i, n = self.shared_part
+        return T * i // n, T * (i + 1) // n
 
     def use_batched(self, T: int) -> bool:
         """The "batched_mm" strategy: when asked for, and in "auto" for a
@@ -436,14 +456,16 @@ class MoeLayer:
             ]
         ys = None
         if w.shared_gate_up is not None:
-            sdec = dec and T <= self.DECODE_MAX_ROWS
+            t0, t1 = self.shared_rows(T)
+            sdec = dec and t1 - t0 <= self.DECODE_MAX_ROWS
             ss = st
             if self.overlap_shared and not sdec:
                 if self._side is None:
                     self._side = torch.cuda.Stream(device=self.dev)     # default priority
                 ss = self._side
-            sh = [("shared_gateup", gateup_swiglu, (x, w.shared_gate_up, self.s_off, self.s_h, sdec, ss)),
-                  ("shared_down", down, (self.s_h, w.shared_down, self.s_off, self.s_y, sdec, ss))]
+            sh = [("shared_gateup", gateup_swiglu, (x[t0:t1], w.shared_gate_up, self.s_off, self.s_h, sdec, ss)),
+                  ("shared_down", down, (self.s_h, w.shared_down, self.s_off, self.s_y[t0:t1], sdec, ss))]
+            sh = sh if t1 > t0 else []
             ys = self.s_y
             out = sh + out if ss is not st else out + sh
         out.append(("combine", unpermute_combine, (self.y_perm, self.inv_perm, self.wts, ys, self.y, st)))
@@ -471,8 +493,11 @@ class MoeLayer:
             ids = self.lids
         ys = None
         if w.shared_gate_up is not None:
-            out.append(("shared_gateup", gateup_swiglu, (x, w.shared_gate_up, self.s_off, self.s_h, True, st)))
-            out.append(("shared_down", down, (self.s_h, w.shared_down, self.s_off, self.s_y, True, st)))
+            t0, t1 = self.shared_rows(T)
+            if t1 > t0:
+                out.append(("shared_gateup", gateup_swiglu,
+                            (x[t0:t1], w.shared_gate_up, self.s_off, self.s_h, True, st)))
+                out.append(("shared_down", down, (self.s_h, w.shared_down, self.s_off, self.s_y[t0:t1], True, st)))
             ys = self.s_y
         if self.mx:
             if select:

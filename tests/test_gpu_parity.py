@@ -948,26 +948,24 @@ def test_permute_masked_pairs(gpu, T, E, k, s):
     assert (inv.cpu().numpy() == ref_inv).all()
 
 
-@pytest.mark.parametrize("mode", ["grouped", "decode", "batched"])
-@pytest.mark.parametrize("name", ["c2s", "c3s_t37", "c4s", "c5s"])
-def test_expert_parallel_partition_sum(gpu, name, mode):
-    """Four expert-parallel shares (router over all experts, each share
-    holding a quarter of the expert weights, the shared expert on share 0):
-    their partial outputs sum to the oracle's layer output."""
-    wl, inp = U.small_inputs(name)
-    if mode in ("decode", "batched") and wl.P > 1024:
-        pytest.skip("decode and batched calls take at most 1024 rows")
+def _partition_sum(wl, inp, xs, mode, split_shared, n=4):
+    """n expert-parallel shares of the layer on tokens xs (router over all
+    experts, each share holding 1/n of the expert weights; the shared
+    expert on share 0, or on every share for 1/n of the tokens): their
+    partial outputs sum to the oracle's layer output."""
     full = U.device_weights(wl, inp)
-    x = U.dev_tensor(inp["x"], wl.dtype)
-    n = 4
+    x = U.dev_tensor(xs, wl.dtype)
+    T = xs.shape[0]
     ec = wl.E // n
-    total = np.zeros((wl.T, wl.d))
+    total = np.zeros((T, wl.d))
     first = None
     for g in range(n):
+        holds = split_shared or g == 0
         w = B().MoeWeights(full.w_router, full.bias, full.w_gate_up[g * ec:(g + 1) * ec],
                            full.w_down[g * ec:(g + 1) * ec],
-                           full.shared_gate_up if g == 0 else None, full.shared_down if g == 0 else None)
-        layer = B().MoeLayer(w, wl.k, wl.score, mode=mode, experts=(g * ec, ec))
+                           full.shared_gate_up if holds else None, full.shared_down if holds else None)
+        layer = B().MoeLayer(w, wl.k, wl.score, mode=mode, experts=(g * ec, ec),
+                             shared_part=(g, n) if split_shared else None)
         y = layer.forward(x)
         torch.cuda.synchronize()
         total += U.host_values(y)
@@ -975,7 +973,7 @@ def test_expert_parallel_partition_sum(gpu, name, mode):
             first = layer
     # every share routes all tokens identically: the oracle routes from share
     # 0's logits, and the summed partial outputs are compared on every token
-    x64 = W.values(inp["x"], wl.dtype)
+    x64 = W.values(xs, wl.dtype)
     wr = W.values(inp["wr"], wl.dtype)
     g_logits = first.logits.cpu().numpy().astype(np.float64)
     assert (np.abs(g_logits - O.router_logits(x64, wr, inp["bias"])) <= O.logit_error_bound(x64, wr, inp["bias"])).all()
@@ -985,7 +983,29 @@ def test_expert_parallel_partition_sum(gpu, name, mode):
     dn = W.values(inp["dn"], wl.dtype)
     sh = None if inp["shared"] is None else tuple(W.values(a, wl.dtype) for a in inp["shared"])
     ref = O.moe_layer_eager(x64, ids, w, lambda e: (gu[e], dn[e]), wl.E, sh)
-    U.assert_close(total, ref, wl.dtype, f"{name} sum of {n} expert-parallel shares")
+    U.assert_close(total, ref, wl.dtype, f"{wl.name} T={T} sum of {n} expert-parallel shares ({mode})")
+
+
+@pytest.mark.parametrize("mode", ["grouped", "decode", "batched"])
+@pytest.mark.parametrize("name", ["c2s", "c3s_t37", "c4s", "c5s"])
+def test_expert_parallel_partition_sum(gpu, name, mode):
+    """Four expert-parallel shares, the shared expert on share 0 (see
+    _partition_sum)."""
+    wl, inp = U.small_inputs(name)
+    if mode in ("decode", "batched") and wl.P > 1024:
+        pytest.skip("decode and batched calls take at most 1024 rows")
+    _partition_sum(wl, inp, np.asarray(inp["x"]), mode, split_shared=False)
+
+
+@pytest.mark.parametrize("T,mode", [(301, "grouped"), (40, "decode"), (3, "grouped"), (1, "batched"),
+                                    (1, "decode")])
+def test_expert_parallel_shared_expert_split(gpu, T, mode):
+    """The DeepSeek-shaped small layer as four expert-parallel shares that
+    each run the shared expert on a quarter of the tokens (with 3 and 1
+    tokens some shares get none of them): the partial outputs sum to the
+    oracle's layer output."""
+    wl, inp = U.small_inputs("c5s")
+    _partition_sum(wl, inp, np.asarray(inp["x"])[:T], mode, split_shared=True)
 
 
 @pytest.mark.parametrize("T", [301, 40])
