@@ -336,11 +336,12 @@ __device__ __forceinline__ void mx_quad_mma(const MxQuad& s, f32x4& acc) {
 // 64 rows for the whole of K (contiguous pieces of the scale tensor), then
 // stages of two quads (256 elements of K): 128 bytes of codes of each weight
 // row (8 rows per load) and 512 bytes of each token row (2 rows per load,
-// gathered through the row map), in a ring of 4 stage buffers, so three
-// stages are in flight while one is used.  Whole 128-byte row pieces per
-// load measured faster than 64-byte ones (c3mx T=64 gate/up 62.7 against
-// 66.7 us); 80 KB of LDS lets two workgroups share a CU, so one's first
-// loads and last stores hide under the other's stream.  Chunk c of a 128-byte
+// gathered through the row map), in a ring of stage buffers (4 in the wide
+// LDS shape, three stages in flight while one is used; 2 in the narrow one,
+// see MxlShape).  Whole 128-byte row pieces per load measured faster than
+// 64-byte ones (c3mx T=64 gate/up 62.7 against 66.7 us); 80 KB of LDS lets
+// two workgroups share a CU (40 KB: four), so one's first loads and last
+// stores hide under another's stream.  Chunk c of a 128-byte
 // code row r sits at c ^ ((r / 2) % 8) and chunk c of a 512-byte token row
 // r at c ^ (r % 16), so the 16 rows a wave reads at one chunk hit distinct
 // banks.  The MFMAs take the layout of MxQuad.  Loads past a buffer's end
