@@ -337,11 +337,11 @@ __device__ __forceinline__ void mx_quad_mma(const MxQuad& s, f32x4& acc) {
 // stages of two quads (256 elements of K): 128 bytes of codes of each weight
 // row (8 rows per load) and 512 bytes of each token row (2 rows per load,
 // gathered through the row map), in a ring of stage buffers (4 in the wide
-// LDS shape, three stages in flight while one is used; 2 in the narrow one,
-// see MxlShape).  Whole 128-byte row pieces per load measured faster than
+// LDS shape, three stages in flight while one is used; 2 in the others, see
+// MxlShape).  Whole 128-byte row pieces per load measured faster than
 // 64-byte ones (c3mx T=64 gate/up 62.7 against 66.7 us); 80 KB of LDS lets
-// two workgroups share a CU (40 KB: four), so one's first loads and last
-// stores hide under another's stream.  Chunk c of a 128-byte
+// two workgroups share a CU (48 KB: three, 40 KB: four), so one's first
+// loads and last stores hide under another's stream.  Chunk c of a 128-byte
 // code row r sits at c ^ ((r / 2) % 8) and chunk c of a 512-byte token row
 // r at c ^ (r % 16), so the 16 rows a wave reads at one chunk hit distinct
 // banks.  The MFMAs take the layout of MxQuad.  Loads past a buffer's end
@@ -354,15 +354,17 @@ constexpr int kMxlRows = 64;                                   // weight rows pe
 constexpr int kMxlCodeBytes = kMxlRows * 128;                  // per stage: 128 bytes of each row
 constexpr int kMxlTokBytes = 16 * 512;                         // per stage: 512 bytes of 16 token rows
 constexpr int kMxlStageBytes = kMxlCodeBytes + kMxlTokBytes;
-// Two LDS shapes: NS stage buffers and a scale area of SCB bytes (the 64
-// rows' K / 32 scale bytes each, so K <= SCB / 2).  The wide one (4 stages,
-// K <= 8192, 80 KB: two workgroups per CU) for every projection; the
-// narrow one (2 stages, K <= 4096, 40 KB: four per CU) for gate/up.  With
-// the narrow shape a workgroup has one stage in flight instead of three, but
-// the CU holds twice the workgroups, whose phases drift apart: c3mx gate/up
-// 65 -> 61 us at T=32 and 68 -> 66 at T=64.  The down projection's 1,440
-// workgroups of 64 columns at d = 2880 make 1.4 rounds of four per CU there
-// and it measured slower (37 -> 40 us at T=64), so it keeps the wide shape.
+// LDS shapes: NS stage buffers and a scale area of SCB bytes (the 64 rows'
+// K / 32 scale bytes each, so K <= SCB / 2).  Gate/up takes the narrow one
+// for K <= 4096 (2 stages, 40 KB: four workgroups per CU), the wide one
+// above (4 stages, K <= 8192, 80 KB: two per CU); down takes the middle one
+// (2 stages, K <= 8192, 48 KB: three per CU).  A shape with fewer stages
+// keeps fewer bytes in flight per workgroup, but the CU holds more
+// workgroups, whose phases drift apart, and the launch's rounds change.
+// Same-box A/B, c3mx at T=32 / T=64: gate/up narrow against wide 65 -> 61 /
+// 68 -> 66 us; down narrow against wide 37 -> 40 us at T=64 (1,440
+// workgroups of 64 columns at d = 2880 make 1.4 rounds of four per CU),
+// middle against wide 35.2 -> 33.4 / 36.9 -> 35.9 us (steps -2%).
 template <int NS, int SCB>
 struct MxlShape {
   static constexpr int kStages = NS;
@@ -372,6 +374,8 @@ struct MxlShape {
 };
 typedef MxlShape<4, kMxlRows * 256> MxlWide;
 typedef MxlShape<2, kMxlRows * 128> MxlNarrow;
+typedef MxlShape<2, kMxlRows * 256> MxlMid;
+static_assert(MxlWide::kPerCu == 2 && MxlMid::kPerCu == 3 && MxlNarrow::kPerCu == 4, "workgroups per CU");
 constexpr int kMxlOob = 0x7fff0000;                            // a lane offset past every buffer
 constexpr int kMxlBufFlags = 0x00020000;                       // raw untyped 32-bit accesses (gfx9)
 
@@ -626,7 +630,7 @@ moe_status launch_mx_lds(const void* A, const void* Bq, const void* Bs, const in
     if (K <= MxlNarrow::kScaleBytes / 2) MOE_MXL_LAUNCH(MxlNarrow);
     else MOE_MXL_LAUNCH(MxlWide);
   } else {
-    MOE_MXL_LAUNCH(MxlWide);
+    MOE_MXL_LAUNCH(MxlMid);
   }
 #undef MOE_MXL_LAUNCH
   return launch_status();

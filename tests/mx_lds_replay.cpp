@@ -62,10 +62,12 @@ static void replay(const char* name, int N, int K, const std::vector<int>& count
   const int CPB = SWIGLU ? 32 : 64;
   const long checks0 = g_checks;
   const int fails0 = g_fails;
-  // the LDS shape the launch picks for this projection and K
+  // the LDS shape the launch picks for this projection and K (the middle
+  // shape of the down projection has the wide one's scale area)
   const int scb = (SWIGLU && K <= MxlNarrow::kScaleBytes / 2) ? MxlNarrow::kScaleBytes : MxlWide::kScaleBytes;
-  CHECK(MxlWide::kLdsBytes <= 80 * 1024 && MxlNarrow::kLdsBytes <= 40 * 1024, "lds %d %d", MxlWide::kLdsBytes,
-        MxlNarrow::kLdsBytes);
+  CHECK(MxlMid::kScaleBytes == MxlWide::kScaleBytes, "middle scale area");
+  CHECK(MxlWide::kLdsBytes <= 80 * 1024 && MxlMid::kLdsBytes * 3 <= 160 * 1024 && MxlNarrow::kLdsBytes <= 40 * 1024,
+        "lds %d %d %d", MxlWide::kLdsBytes, MxlMid::kLdsBytes, MxlNarrow::kLdsBytes);
   CHECK(scb >= 64 * KB, "scale area for K %d", K);
   for (int cb = 0; cb * CPB < N; ++cb) {
     const int n0 = cb * CPB;
