@@ -16,13 +16,14 @@ namespace {
 
 constexpr int64_t kDecodeMaxRows = 1024;
 // Decode calls with several rows per expert on average run the grouped tile
-// kernel (in its 64-token shapes): with 3+ (gate/up) or 6+ (down) rows per
-// expert its loads of whole 128-byte row pieces into LDS stream the weights
-// faster than the split-K MFMA form (measured on 32 experts of 2880 x 2880:
-// gate/up at T=24, 3 rows per expert, 181 vs 194 us; down at T=48, 6 rows,
-// 104 vs 114 us, and level at 4 rows).
+// kernel (in its 64-token shapes): from 3 rows per expert its loads of whole
+// 128-byte row pieces into LDS stream the weights faster than the split-K
+// MFMA form (measured on 32 experts of 2880 x 2880: gate/up at T=24, 3 rows
+// per expert, 181 vs 194 us; down, in its two-stage tile of three
+// workgroups per CU, 93 us at 3, 4 and 5 rows per expert against 99, 104
+// and 109 us; at 2 rows the vector form's 87 us stays ahead).
 constexpr int64_t kDecodeTileGateUpRows = 3;   // per expert
-constexpr int64_t kDecodeTileDownRows = 6;
+constexpr int64_t kDecodeTileDownRows = 3;
 
 moe_status check_proj(const void* in, const void* w, const int32_t* offsets, int64_t rows, int64_t d, int64_t f,
                       int32_t E, moe_dtype dtype, const void* out) {

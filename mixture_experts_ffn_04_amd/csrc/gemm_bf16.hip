@@ -291,7 +291,7 @@ __host__ __device__ __forceinline__ void dma_offsets(const GemmArgs& a, const Ti
 
 // The tile kernel's shape constants: wave layout, fragments, load
 // instructions per wave and stage, and LDS stage sizes (16-byte units).
-template <int BM, int BN, int WM, int WN, int EPI, int BK>
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int WS = 3>
 struct DtlShape {
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
@@ -305,7 +305,7 @@ struct DtlShape {
   static constexpr int LX = BM / (RPI * NW);          // token load instructions
   static constexpr int LPS = LB + LX;
   static constexpr int WSTG = BN * CH, XSTG = BM * CH;   // units per weight / token stage
-  static constexpr int LDS_UNITS = 3 * WSTG + 2 * XSTG;
+  static constexpr int LDS_UNITS = WS * WSTG + 2 * XSTG;   // WS weight stages, 2 token stages
   // Fat tiles: an expert's last remainder of up to kFatExtraRows rows shared
   // out over its other row tiles, BMF = BM + kFatExtraRows rows at most,
   // with two stages of both operands (three weight stages no longer fit).
@@ -373,10 +373,16 @@ __host__ __device__ __forceinline__ TileBuffers tile_buffers(const GemmArgs& a, 
 // still be in flight) means stage k's tokens and weights have landed; the
 // s_barrier after it publishes them and also tells every wave that the
 // buffers of stage k-1, refilled during stage k, are no longer read.
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int SP, int LDS_EPI>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a) {
+// WS = 2 (two stages of both operands, a smaller LDS footprint so that
+// more workgroups share a CU): each stage's loads are issued right after
+// the barrier of the stage before, which waits for all of the wave's loads.
+// The waves-per-EU bound asks for three such workgroups per CU.
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int SP, int LDS_EPI, int WS>
+__global__ __launch_bounds__(64 * WM * WN, (WS == 2 ? 3 : 1) * WM * WN / 4) void gemm_bf16_dtl_kernel(GemmArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the body uses device-only types; the host pass needs only the stub
-  typedef DtlShape<BM, BN, WM, WN, EPI, BK> S;
+  static_assert(WS == 2 || WS == 3, "weight stages");
+  static_assert(WS == 3 || !(BM == 256 && WM == 2 && EPI != EPI_F32B), "fat tiles keep three weight stages");
+  typedef DtlShape<BM, BN, WM, WN, EPI, BK, WS> S;
   constexpr int NW = S::NW, NT = S::NT, TM = S::TM, TN = S::TN, FM = S::FM, FN = S::FN;
   static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "fragment shape");
   static_assert(EPI != EPI_SWIGLU || FN % 2 == 0, "SwiGLU pairs gate and up fragments");
@@ -502,8 +508,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   int voff[LPS];
   int dst[LPS];
   dma_offsets<EPI, BN, CH, RPI, NW, WN, LX, LPS>(a, tl, rowb, gather, wave, wm, wn, lane, TM, voff, dst);
-  const unsigned ldsw = lds_addr_of(lds);                          // weight stages 0..2
-  const unsigned ldsx = ldsw + 3u * WSTG * 16u;                    // token stages 0..1
+  const unsigned ldsw = lds_addr_of(lds);                          // weight stages 0 .. WS-1
+  const unsigned ldsx = ldsw + static_cast<unsigned>(WS) * WSTG * 16u;   // token stages 0..1
 
   // Load instruction i for weight stage kw_ into weight buffer wb_, or token
   // stage kx_ into token buffer xb_.
@@ -531,6 +537,40 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
 
   const int nk = static_cast<int>(K / BK);
   const int last = nk - 1;
+  if constexpr (WS == 2) {
+    // Stage kt in buffers kt & 1; token fragments at or past the row
+    // block's active ones are never read, so their loads are left out.
+    auto stage_dma = [&](int b, int k) {
+#pragma unroll
+      for (int i = 0; i < LPS; ++i)
+        if (i >= LX || i < nfm) MOE_DTL_DMA(i, b, k, b, k);
+    };
+    stage_dma(0, 0);
+#define MOE_TWO_LOOP(NF_)                                                               \
+    for (int kt = 0; kt < nk; ++kt) {                                                   \
+      wait_stage_barrier<0>();                                                          \
+      stage_dma((kt + 1) & 1, kt + 1 < last ? kt + 1 : last);                           \
+      const u32x4* sw_ = lds + (kt & 1) * WSTG;                                         \
+      const u32x4* sx_ = lds + 2 * WSTG + (kt & 1) * XSTG;                              \
+      _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                               \
+        bf16x8 wf_t[FN], tf_t[FM];                                                      \
+        MOE_DTL_FRAGS(wf_t, tf_t, sw_, sx_, ks, NF_);                                   \
+        MOE_MFMAS(wf_t, tf_t, NF_);                                                     \
+      }                                                                                 \
+    }
+    if (nfm == FM) {
+      MOE_TWO_LOOP(FM)
+    } else if (nfm == 0) {
+      MOE_TWO_LOOP(0)
+    } else if (nfm == 1) {
+      MOE_TWO_LOOP(1)
+    } else if (nfm == 2) {
+      MOE_TWO_LOOP(FM > 2 ? 2 : FM)
+    } else {
+      MOE_TWO_LOOP(FM > 3 ? 3 : FM)
+    }
+#undef MOE_TWO_LOOP
+  } else {
   // Prologue: tokens and weights of stage 0, then the weights of stage 1
   // (stages past the end are clamped: extra loads of valid memory, never
   // consumed).
@@ -598,6 +638,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
   } else {
     MOE_DTL_LOOP(FM > 3 ? 3 : FM)
   }
+  }
   drain_vm();
 #undef MOE_DTL_LOOP
 #undef MOE_DTL_COMPUTE
@@ -626,7 +667,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_dtl_kernel(GemmArgs a)
 // than the remainder tile it replaces.
 constexpr int64_t kFatMinK = 4096;
 
-template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int SP = 1, int LDS_EPI = 0>
+template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int SP = 1, int LDS_EPI = 0, int WS = 3>
 moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
   // A launch of fewer than kAdaptRounds rounds of full tiles may pick
@@ -646,7 +687,7 @@ moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   if (wbytes >= (int64_t(1) << 31) || static_cast<int64_t>(BM + kFatExtraRows) * a.K * 2 >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
   if (a.rowmap && (a.kdiv < 1 || a.a_rows * a.K * 2 >= (int64_t(1) << 31))) return MOE_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, SP, LDS_EPI>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((gemm_bf16_dtl_kernel<BM, BN, WM, WN, EPI, SN, BK, SP, LDS_EPI, WS>), dim3(static_cast<unsigned>(grid)),
                      dim3(64 * WM * WN), 0, st, b);
   return launch_status();
 }
@@ -672,15 +713,18 @@ moe_status gemm_bf16_down(const GemmArgs& a, hipStream_t st) {
 // Decode calls with several rows per expert (few tokens in all, weight
 // streaming bound): 64-token tiles.  Gate/up keeps 256 weight rows on 4
 // waves side by side; down takes 128 weight rows, so the experts' weights
-// spread over twice as many tiles (32 experts of 2880 x 2880: 736 tiles, 2.9
-// rounds on 256 CUs, instead of 384).  Measured at T = 32-64 against the
-// projections' 256 x 256 tile: gate/up 186 -> 180 us, down 110 -> 104 us.
+// spread over twice as many tiles (32 experts of 2880 x 2880: 736 tiles
+// instead of 384).  Measured at T = 32-64 against the projections' 256 x
+// 256 tile: gate/up 186 -> 180 us, down 110 -> 104 us.  Down then takes two
+// weight stages instead of three (48 KB of LDS, so three workgroups share a
+// CU and the 736 tiles make one round instead of 1.4 rounds of two): T=64
+// down 104 -> 93 us, outputs bit-identical (the K order is unchanged).
 moe_status gemm_bf16_gateup_swiglu_few(const GemmArgs& a, hipStream_t st) {
   return launch_dtl<64, 256, 1, 4, EPI_SWIGLU, 16, 64, 2, 0>(a, st);
 }
 
 moe_status gemm_bf16_down_few(const GemmArgs& a, hipStream_t st) {
-  return launch_dtl<64, 128, 2, 4, EPI_STORE, 16, 64, 3, 1>(a, st);
+  return launch_dtl<64, 128, 2, 4, EPI_STORE, 16, 64, 3, 1, 2>(a, st);
 }
 
 // Router logits (many experts and tokens): the same tile kernel with an

@@ -41,12 +41,14 @@ static int g_fails = 0;
     }                                         \
   } while (0)
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, int WS = 3>
 void replay(const char* name, const std::vector<int>& in_counts, int64_t K, int64_t N, int kdiv,
             const std::vector<int>& row_choices) {
-  typedef DtlShape<BM, BN, WM, WN, EPI, 64> S;
+  typedef DtlShape<BM, BN, WM, WN, EPI, 64, WS> S;
   constexpr int CH = S::CH, RPI = S::RPI, NW = S::NW;
   static_assert(S::LDS_UNITS * 16 <= 160 * 1024, "LDS");
+  // two weight stages: three workgroups share a CU
+  static_assert(WS == 3 || 3 * S::LDS_UNITS * 16 <= 160 * 1024, "LDS of three workgroups");
   static_assert(!S::FAT_OK || 2 * S::WSTG + 2 * S::XSTGF <= S::LDS_UNITS, "fat stages");
   const bool gather = kdiv > 0;
   std::vector<int> counts_v(in_counts);
@@ -219,6 +221,9 @@ int main() {
                                     {64});
   replay<64, 256, 1, 4, EPI_SWIGLU>("gate/up 64x256 gather k4", zipf_counts(32, 256, 0.5, 2), 2880, 2880, 4, {64});
   replay<64, 128, 2, 4, EPI_STORE>("down 64x128 K2880 N2880", zipf_counts(32, 256, 0.5, 3), 2880, 2880, 0, {64});
+  replay<64, 128, 2, 4, EPI_STORE, 2>("down 64x128 two stages K2880 N2880", zipf_counts(32, 256, 0.5, 3), 2880, 2880,
+                                      0, {64});
+  replay<64, 128, 2, 4, EPI_STORE, 2>("down 64x128 two stages K64 (one stage)", {8, 9, 0, 12}, 64, 320, 0, {64});
   // router logits on flat tiles (one group of T rows, N = experts)
   replay<64, 128, 2, 4, EPI_F32B>("logits 64x128 K7168 N256", {16384}, 7168, 256, 0, {64});
   replay<32, 128, 1, 4, EPI_STORE>("down 32x128 K2880 N2880", {8, 9, 7, 12, 0, 8, 31, 1}, 2880, 2880, 0, {32});

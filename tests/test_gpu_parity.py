@@ -405,11 +405,11 @@ def test_decode_few_rows_per_expert(gpu, E, rows, K, N):
     U.assert_close(U.host_values(y), O.grouped_down(x64, W.values(dn, "bf16"), offsets), "bf16", "Y_perm")
 
 
-@pytest.mark.parametrize("rows", [24, 40, 64, 112])
+@pytest.mark.parametrize("rows", [24, 40, 48, 64, 112])
 def test_decode_forms_by_rows_per_expert(gpu, rows):
     """The decode calls pick their kernel by rows per expert (16 experts): the
-    vector-ALU form (24 rows), the split-K MFMA form (40), the tile kernel
-    for gate/up only (64) and for both projections (112)."""
+    vector-ALU form (24 rows), the split-K MFMA form (40), the tile kernels
+    from 3 rows per expert (48, 64, 112; down in its two-stage tile)."""
     E, K, N = 16, 1024, 192
     offsets = _skewed_offsets(E, rows, seed=rows)
     xs = W.gen_matrix((rows, K), seed=rows + 31)
