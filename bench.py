@@ -649,9 +649,6 @@ def main(argv=None):
               "multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
-    import torch
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    device = torch.device("cuda:0")
     wl = W.get(args.workload)
     decode = args.workload.startswith("c3")   # weight streaming: timed per step after a cache flush
     if wl.experts == "mxfp4" and args.mode not in ("auto", "decode", "batched"):
@@ -667,6 +664,10 @@ def main(argv=None):
     if args.split_shared and share == 1:
         print("--split-shared goes with --ep-share N (N > 1)", file=sys.stderr)
         return 2
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    device = torch.device("cuda:0")
     layer, x, host = setup(wl, device, keep_host=not args.no_cpu, mode=args.mode,
                            overlap_shared=args.overlap_shared, share=share, split_shared=args.split_shared)
     Ts = wl.T // share if args.split_shared else None     # the shared expert's tokens here

@@ -40,6 +40,25 @@ def test_multi_gpu_request_refused(capsys):
     assert "one GPU" in capsys.readouterr().err
 
 
+def test_share_options_refused_before_any_gpu_work(capsys):
+    """Option combinations the share measurement does not take are refused
+    from the arguments alone."""
+    assert bench.main(["--split-shared"]) == 2
+    assert "--ep-share" in capsys.readouterr().err
+    assert bench.main(["--ep-share", "8", "--workload", "c3_t8"]) == 2
+    assert bench.main(["--ep-share", "3", "--workload", "c5"]) == 2        # 256 experts do not split in 3
+    assert bench.main(["--workload", "c3mx_t8", "--mode", "grouped"]) == 2
+
+
+def test_layer_flops_shared_slice():
+    """A share that runs the shared expert on T/N tokens counts its FLOPs
+    for those tokens only."""
+    wl = W.get("c5")
+    full = bench.layer_flops(wl)
+    part = bench.layer_flops(wl, Ts=wl.T // 8)
+    assert full - part == 6.0 * (wl.T - wl.T // 8) * wl.d * wl.f_shared
+
+
 def test_tile_work():
     wl = W.get("c2")
     # 1000 rows -> 1024 at 32-row fragments and at 256-row tiles; 40 -> 64 and 256; 0 rows: no tiles
