@@ -180,14 +180,14 @@ def load_traffic(kernel: str, workload: str):
 
 
 def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared: bool = False, share: int = 1,
-          split_shared: bool = False):
+          split_shared: bool = False, share_index: int = 0):
     """Upload the workload's seeded inputs to the GPU and build the layer.
     With keep_host, the storage-format expert weights stay in host memory
     too (for the CPU oracle leg; the DeepSeek-shaped layer holds 22.5 GB).
-    share > 1: one GPU's expert-parallel share of the layer -- experts
-    [0, E/share) and the shared expert (with split_shared, the shared
-    expert on the share's 1/share of the tokens only) -- with every token
-    routed."""
+    share > 1: one GPU's expert-parallel share of the layer, share_index
+    I of them -- experts [I E/share, (I + 1) E/share) and the shared expert
+    on share 0 (with split_shared, on every share for its 1/share of the
+    tokens) -- with every token routed."""
     import torch
     from mixture_experts_ffn_04_amd import MoeLayer, MoeWeights
 
@@ -210,20 +210,23 @@ def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared
         host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=None)
         return MoeLayer(weights, wl.k, wl.score, mode=mode), dev(x), host
     E_loc = wl.E // share
+    e0 = share_index * E_loc
     gu = torch.empty(E_loc, 2 * wl.f, wl.d, dtype=tdt, device=device)
     dn = torch.empty(E_loc, wl.d, wl.f, dtype=tdt, device=device)
     host_experts = {}
-    for e, g, w in W.iter_experts(wl, range(E_loc)):
-        gu[e].copy_(dev(g))
-        dn[e].copy_(dev(w))
+    for e, g, w in W.iter_experts(wl, range(e0, e0 + E_loc)):
+        gu[e - e0].copy_(dev(g))
+        dn[e - e0].copy_(dev(w))
         if keep_host:
             host_experts[e] = (g, w)
     sh = W.gen_shared(wl)
+    if share > 1 and share_index > 0 and not split_shared:
+        sh = None                                   # the shared expert lives on share 0
     weights = MoeWeights(dev(wr), None if bias is None else torch.from_numpy(bias).to(device), gu, dn,
                          None if sh is None else dev(sh[0]), None if sh is None else dev(sh[1]))
     layer = MoeLayer(weights, wl.k, wl.score, mode=mode, overlap_shared=overlap_shared,
-                     experts=None if share == 1 else (0, E_loc),
-                     shared_part=(0, share) if split_shared and share > 1 else None)
+                     experts=None if share == 1 else (e0, E_loc),
+                     shared_part=(share_index, share) if split_shared and share > 1 else None)
     host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=sh)
     return layer, dev(x), host
 
@@ -607,9 +610,11 @@ def main(argv=None):
     ap.add_argument("--ep-share", type=int, default=1, metavar="N",
                     help="time one GPU's expert-parallel share of N (experts [0, E/N) and the shared expert, "
                          "every token routed, local pairs only); prefill workloads")
+    ap.add_argument("--ep-index", type=int, default=0, metavar="I",
+                    help="with --ep-share N: time share I (experts [I E/N, (I + 1) E/N)) instead of share 0")
     ap.add_argument("--split-shared", action="store_true",
-                    help="with --ep-share N: every share runs the shared expert on 1/N of the tokens (this one "
-                         "on tokens [0, T/N)) instead of share 0 on all of them")
+                    help="with --ep-share N: every share runs the shared expert on 1/N of the tokens (share I on "
+                         "tokens [T I/N, T (I + 1)/N)) instead of share 0 on all of them")
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens for the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernels", action="store_true", help="also print per-stage times to stderr")
@@ -661,16 +666,22 @@ def main(argv=None):
             return 2
         args.no_cpu = True          # the oracle leg needs every expert
 
-    if args.split_shared and share == 1:
-        print("--split-shared goes with --ep-share N (N > 1)", file=sys.stderr)
+    if (args.split_shared or args.ep_index) and share == 1:
+        print("--split-shared and --ep-index go with --ep-share N (N > 1)", file=sys.stderr)
+        return 2
+    if not 0 <= args.ep_index < share:
+        print("--ep-index I needs 0 <= I < N", file=sys.stderr)
         return 2
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     device = torch.device("cuda:0")
     layer, x, host = setup(wl, device, keep_host=not args.no_cpu, mode=args.mode,
-                           overlap_shared=args.overlap_shared, share=share, split_shared=args.split_shared)
-    Ts = wl.T // share if args.split_shared else None     # the shared expert's tokens here
+                           overlap_shared=args.overlap_shared, share=share, split_shared=args.split_shared,
+                           share_index=args.ep_index)
+    # the shared expert's tokens here
+    ts0, ts1 = wl.T * args.ep_index // share, wl.T * (args.ep_index + 1) // share
+    Ts = ts1 - ts0 if args.split_shared else (0 if args.ep_index else None)
     st = torch.cuda.current_stream()
     # the projection kernels are timed by events on the launch stream inside
     # the timed steps; an event pair costs a few microseconds, so the
@@ -751,6 +762,12 @@ def main(argv=None):
     roof["kernel"] = kname
     roof["traffic"] = load_traffic(kname, wl.name) if share == 1 else None   # taken on the whole layer
 
+    if not wl.f_shared or Ts == 0:
+        shared_desc = ""
+    elif args.split_shared:
+        shared_desc = f" and the shared expert on tokens {ts0}..{ts1 - 1}"
+    else:
+        shared_desc = " and the shared expert"
     out = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -768,9 +785,9 @@ def main(argv=None):
                    "top_k": wl.k, "score": wl.score, "zipf_s": wl.zipf_s, "shared_d_ff": wl.f_shared,
                    "active_experts": active, "strategy": args.mode,
                    "parallelism": "single GPU" if share == 1 else
-                   f"one GPU's expert-parallel share of {share}: experts 0..{wl.E // share - 1}"
-                   f"{'' if not wl.f_shared else ' and the shared expert on tokens 0..' + str(Ts - 1) if Ts else ' and the shared expert'}"
-                   f", every token routed, {P_here} of {wl.P} "
+                   f"one GPU's expert-parallel share ({args.ep_index} of {share}): experts "
+                   f"{args.ep_index * (wl.E // share)}..{(args.ep_index + 1) * (wl.E // share) - 1}"
+                   f"{shared_desc}, every token routed, {P_here} of {wl.P} "
                    f"routed pairs here (the sum over shares is not run)",
                    "shared_expert": None if not wl.f_shared else
                    ("second stream beside the routed experts" if args.overlap_shared else "after the routed experts"),
