@@ -180,13 +180,14 @@ def load_traffic(kernel: str, workload: str):
 
 
 def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared: bool = False, share: int = 1,
-          split_shared: bool = False, share_index: int = 0):
+          split_shared: bool = False, share_index: int = 0, interleave: bool = False):
     """Upload the workload's seeded inputs to the GPU and build the layer.
     With keep_host, the storage-format expert weights stay in host memory
     too (for the CPU oracle leg; the DeepSeek-shaped layer holds 22.5 GB).
     share > 1: one GPU's expert-parallel share of the layer, share_index
-    I of them -- experts [I E/share, (I + 1) E/share) and the shared expert
-    on share 0 (with split_shared, on every share for its 1/share of the
+    I of them -- experts [I E/share, (I + 1) E/share), or with interleave
+    the experts I, I + share, I + 2 share, ..., and the shared expert on
+    share 0 (with split_shared, on every share for its 1/share of the
     tokens) -- with every token routed."""
     import torch
     from mixture_experts_ffn_04_amd import MoeLayer, MoeWeights
@@ -210,13 +211,15 @@ def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared
         host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=None)
         return MoeLayer(weights, wl.k, wl.score, mode=mode), dev(x), host
     E_loc = wl.E // share
-    e0 = share_index * E_loc
+    e0 = share_index if interleave else share_index * E_loc
+    stride = share if interleave else 1
+    held = [e0 + j * stride for j in range(E_loc)]          # global ids in local order
     gu = torch.empty(E_loc, 2 * wl.f, wl.d, dtype=tdt, device=device)
     dn = torch.empty(E_loc, wl.d, wl.f, dtype=tdt, device=device)
     host_experts = {}
-    for e, g, w in W.iter_experts(wl, range(e0, e0 + E_loc)):
-        gu[e - e0].copy_(dev(g))
-        dn[e - e0].copy_(dev(w))
+    for e, g, w in W.iter_experts(wl, held):
+        gu[(e - e0) // stride].copy_(dev(g))
+        dn[(e - e0) // stride].copy_(dev(w))
         if keep_host:
             host_experts[e] = (g, w)
     sh = W.gen_shared(wl)
@@ -225,7 +228,7 @@ def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared
     weights = MoeWeights(dev(wr), None if bias is None else torch.from_numpy(bias).to(device), gu, dn,
                          None if sh is None else dev(sh[0]), None if sh is None else dev(sh[1]))
     layer = MoeLayer(weights, wl.k, wl.score, mode=mode, overlap_shared=overlap_shared,
-                     experts=None if share == 1 else (e0, E_loc),
+                     experts=None if share == 1 else (e0, E_loc, stride),
                      shared_part=(share_index, share) if split_shared and share > 1 else None)
     host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=sh)
     return layer, dev(x), host
@@ -612,6 +615,8 @@ def main(argv=None):
                          "every token routed, local pairs only); prefill workloads")
     ap.add_argument("--ep-index", type=int, default=0, metavar="I",
                     help="with --ep-share N: time share I (experts [I E/N, (I + 1) E/N)) instead of share 0")
+    ap.add_argument("--ep-interleave", action="store_true",
+                    help="with --ep-share N: share I holds the experts I, I + N, I + 2N, ... instead of a block")
     ap.add_argument("--split-shared", action="store_true",
                     help="with --ep-share N: every share runs the shared expert on 1/N of the tokens (share I on "
                          "tokens [T I/N, T (I + 1)/N)) instead of share 0 on all of them")
@@ -666,8 +671,8 @@ def main(argv=None):
             return 2
         args.no_cpu = True          # the oracle leg needs every expert
 
-    if (args.split_shared or args.ep_index) and share == 1:
-        print("--split-shared and --ep-index go with --ep-share N (N > 1)", file=sys.stderr)
+    if (args.split_shared or args.ep_index or args.ep_interleave) and share == 1:
+        print("--split-shared, --ep-index and --ep-interleave go with --ep-share N (N > 1)", file=sys.stderr)
         return 2
     if not 0 <= args.ep_index < share:
         print("--ep-index I needs 0 <= I < N", file=sys.stderr)
@@ -678,7 +683,7 @@ def main(argv=None):
     device = torch.device("cuda:0")
     layer, x, host = setup(wl, device, keep_host=not args.no_cpu, mode=args.mode,
                            overlap_shared=args.overlap_shared, share=share, split_shared=args.split_shared,
-                           share_index=args.ep_index)
+                           share_index=args.ep_index, interleave=args.ep_interleave)
     # the shared expert's tokens here
     ts0, ts1 = wl.T * args.ep_index // share, wl.T * (args.ep_index + 1) // share
     Ts = ts1 - ts0 if args.split_shared else (0 if args.ep_index else None)
@@ -762,6 +767,10 @@ def main(argv=None):
     roof["kernel"] = kname
     roof["traffic"] = load_traffic(kname, wl.name) if share == 1 else None   # taken on the whole layer
 
+    if args.ep_interleave:
+        experts_desc = f"{args.ep_index}, {args.ep_index + share}, ... (every {share}th)"
+    else:
+        experts_desc = f"{args.ep_index * (wl.E // share)}..{(args.ep_index + 1) * (wl.E // share) - 1}"
     if not wl.f_shared or Ts == 0:
         shared_desc = ""
     elif args.split_shared:
@@ -785,8 +794,7 @@ def main(argv=None):
                    "top_k": wl.k, "score": wl.score, "zipf_s": wl.zipf_s, "shared_d_ff": wl.f_shared,
                    "active_experts": active, "strategy": args.mode,
                    "parallelism": "single GPU" if share == 1 else
-                   f"one GPU's expert-parallel share ({args.ep_index} of {share}): experts "
-                   f"{args.ep_index * (wl.E // share)}..{(args.ep_index + 1) * (wl.E // share) - 1}"
+                   f"one GPU's expert-parallel share ({args.ep_index} of {share}): experts {experts_desc}"
                    f"{shared_desc}, every token routed, {P_here} of {wl.P} "
                    f"routed pairs here (the sum over shares is not run)",
                    "shared_expert": None if not wl.f_shared else

@@ -25,7 +25,7 @@
  *   moe_grouped_gemm_down            per-expert down projection
  *   moe_unpermute_combine            weighted combine back to token order
  *   moe_localize_ids                 expert-parallel share: global ids to
- *                                    local ones, other experts masked
+ *   moe_localize_ids_strided         local ones, other experts masked
  *   moe_decode_gateup_swiglu         small-batch variants that stream only
  *   moe_decode_gateup_swiglu_gather  the active experts' weights (the
  *   moe_decode_down                  _gather form reads the rows through
@@ -259,6 +259,24 @@ MOE_API moe_status moe_unpermute_combine(const void* y_perm, const int32_t* inv_
  */
 MOE_API moe_status moe_localize_ids(const int32_t* topk_ids, int64_t n, int32_t e_begin,
                                     int32_t e_count, int32_t* local_ids, void* stream);
+
+/*
+ * moe_localize_ids for a share that holds every e_stride-th expert:
+ * e_begin, e_begin + e_stride, ..., e_begin + (e_count - 1) * e_stride (an
+ * interleaved assignment, share i of N taking e_begin = i, e_stride = N,
+ * spreads popular experts over the shares; the article's section "Expert
+ * Parallelism" gives each device E/N experts without fixing which):
+ *   local_ids[i] = (topk_ids[i] - e_begin) / e_stride
+ *                    if topk_ids[i] is one of those experts
+ *                = -1 otherwise
+ * The share's packed expert weights hold its experts in that order.
+ * e_stride = 1 is moe_localize_ids.  topk_ids, local_ids [n] int32
+ * (device); 0 <= e_begin, 1 <= e_stride, 1 <= e_count <= 256, else
+ * MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED.
+ */
+MOE_API moe_status moe_localize_ids_strided(const int32_t* topk_ids, int64_t n, int32_t e_begin,
+                                            int32_t e_stride, int32_t e_count, int32_t* local_ids,
+                                            void* stream);
 
 /*
  * moe_grouped_gemm_gateup_swiglu with the row gather of moe_permute folded

@@ -26,7 +26,8 @@ EXPORTS = (
     "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_gateup_swiglu",
     "moe_grouped_gemm_down", "moe_unpermute_combine", "moe_decode_gateup_swiglu",
     "moe_decode_down", "moe_decode_gateup_swiglu_gather", "moe_grouped_gemm_gateup_swiglu_gather",
-    "moe_localize_ids", "moe_permute_noalloc", "moe_batched_gateup_swiglu", "moe_batched_down_combine",
+    "moe_localize_ids", "moe_localize_ids_strided", "moe_permute_noalloc", "moe_batched_gateup_swiglu",
+    "moe_batched_down_combine",
     "moe_decode_gateup_swiglu_mxfp4", "moe_decode_down_mxfp4", "moe_batched_gateup_swiglu_mxfp4",
     "moe_batched_down_combine_mxfp4", "moe_batched_gateup_swiglu_select", "moe_batched_gateup_swiglu_mxfp4_select",
 )
@@ -51,6 +52,7 @@ _SIGS = {
     "moe_grouped_gemm_gateup_swiglu_gather": ([P, P, I32, P, P, I64, I64, I64, I32, ctypes.c_int, P, P],
                                               ctypes.c_int),
     "moe_localize_ids": ([P, I64, I32, I32, P, P], ctypes.c_int),
+    "moe_localize_ids_strided": ([P, I64, I32, I32, I32, P, P], ctypes.c_int),
     "moe_permute_noalloc": ([P, P, I64, I64, I32, I32, ctypes.c_int, P, P, P, P, P, P], ctypes.c_int),
     "moe_batched_gateup_swiglu": ([P, P, P, I64, I64, I64, I32, I32, ctypes.c_int, P, P], ctypes.c_int),
     "moe_batched_down_combine": ([P, P, P, P, P, I64, I64, I64, I32, I32, ctypes.c_int, P, P], ctypes.c_int),
@@ -137,10 +139,15 @@ def topk(logits, k: int, score: str, topk_ids, topk_w, stream=None):
                                        _ptr(topk_w), _stream(stream)))
 
 
-def localize_ids(topk_ids, e_begin: int, e_count: int, local_ids, stream=None):
-    """Expert-parallel share: global ids -> ids local to [e_begin, e_begin+e_count), -1 elsewhere."""
-    _check("moe_localize_ids", load().moe_localize_ids(_ptr(topk_ids), topk_ids.numel(), e_begin, e_count,
-                                                       _ptr(local_ids), _stream(stream)))
+def localize_ids(topk_ids, e_begin: int, e_count: int, local_ids, e_stride: int = 1, stream=None):
+    """Expert-parallel share: global ids -> ids local to the experts e_begin,
+    e_begin + e_stride, ... (e_count of them), -1 elsewhere."""
+    if e_stride == 1:
+        _check("moe_localize_ids", load().moe_localize_ids(_ptr(topk_ids), topk_ids.numel(), e_begin, e_count,
+                                                           _ptr(local_ids), _stream(stream)))
+    else:
+        _check("moe_localize_ids_strided", load().moe_localize_ids_strided(
+            _ptr(topk_ids), topk_ids.numel(), e_begin, e_stride, e_count, _ptr(local_ids), _stream(stream)))
 
 
 def permute_workspace_size(T: int, k: int, E: int) -> int:
@@ -315,7 +322,9 @@ class MoeLayer:
 
     experts=(e_begin, e_count) makes it one expert-parallel share: the
     router (weights.w_router) covers all experts, weights.w_gate_up and
-    weights.w_down hold only experts [e_begin, e_begin + e_count), and
+    weights.w_down hold only experts [e_begin, e_begin + e_count) (with
+    experts=(e_begin, e_count, e_stride) the experts e_begin, e_begin +
+    e_stride, ..., in that order: an interleaved assignment), and
     forward returns the share's partial output (the pairs of other experts
     masked by moe_localize_ids); the partial outputs of all shares sum to
     the layer's output.
@@ -349,10 +358,13 @@ class MoeLayer:
                 raise ValueError("expert weights cover a share of the experts: pass experts=(e_begin, e_count)")
             self.e_begin = None
         else:
-            e_begin, e_count = experts
-            if e_count != self.E_loc or e_begin < 0 or e_begin + e_count > self.E:
-                raise ValueError("experts=(e_begin, e_count) does not match the expert weights")
+            e_begin, e_count = experts[:2]
+            e_stride = experts[2] if len(experts) > 2 else 1
+            if (e_count != self.E_loc or e_begin < 0 or e_stride < 1
+                    or e_begin + (e_count - 1) * e_stride >= self.E):
+                raise ValueError("experts=(e_begin, e_count[, e_stride]) does not match the expert weights")
             self.e_begin = int(e_begin)
+            self.e_stride = int(e_stride)
         if shared_part is not None:
             i, n = shared_part
             if n < 1 or not 0 <= i < n:
@@ -438,7 +450,7 @@ class MoeLayer:
         out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st))]
         ids = self.ids
         if self.e_begin is not None:
-            out.append(("localize", localize_ids, (self.ids, self.e_begin, self.E_loc, self.lids, st)))
+            out.append(("localize", localize_ids, (self.ids, self.e_begin, self.E_loc, self.lids, self.e_stride, st)))
             ids = self.lids
         out += [
             ("permute", permute, (ids, x, self.E_loc, self.counts, self.offsets, self.perm, self.inv_perm,
@@ -489,7 +501,7 @@ class MoeLayer:
             out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, None, None, st))]
         else:
             out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st)),
-                   ("localize", localize_ids, (self.ids, self.e_begin, self.E_loc, self.lids, st))]
+                   ("localize", localize_ids, (self.ids, self.e_begin, self.E_loc, self.lids, self.e_stride, st))]
             ids = self.lids
         ys = None
         if w.shared_gate_up is not None:

@@ -400,30 +400,43 @@ extern "C" moe_status moe_permute_noalloc(const int32_t* topk_ids, const void* x
 
 // ---------------------------------------------------------------------------
 // Expert-parallel share (article "Mixture of Experts (MoEs) in Transformers",
-// section "Expert Parallelism"): a device holds the experts
-// [e_begin, e_begin + e_count); the router's global ids become local ids,
-// and pairs whose expert lives elsewhere are masked (-1), so moe_permute
-// gives them no row and moe_unpermute_combine adds nothing for them.
+// section "Expert Parallelism"): a device holds the experts e_begin,
+// e_begin + e_stride, ..., e_begin + (e_count - 1) e_stride (a contiguous
+// block with stride 1); the router's global ids become local ids, and pairs
+// whose expert lives elsewhere are masked (-1), so moe_permute gives them no
+// row and moe_unpermute_combine adds nothing for them.
 namespace moe {
 namespace {
 __global__ __launch_bounds__(256) void localize_kernel(const int32_t* __restrict__ ids, int64_t n, int e_begin,
-                                                       int e_count, int32_t* __restrict__ out) {
+                                                       int e_stride, int e_count, int32_t* __restrict__ out) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n) return;
   const int e = ids[i] - e_begin;
-  out[i] = (e >= 0 && e < e_count) ? e : -1;
+  const int j = e >= 0 ? e / e_stride : -1;
+  out[i] = (e >= 0 && j * e_stride == e && j < e_count) ? j : -1;
+}
+
+moe_status localize(const int32_t* topk_ids, int64_t n, int32_t e_begin, int32_t e_stride, int32_t e_count,
+                    int32_t* local_ids, void* stream) {
+  if (n < 0 || e_begin < 0 || e_stride < 1 || e_count < 1) return MOE_ERR_INVALID_ARG;
+  if (e_count > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (n >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (n == 0) return MOE_OK;
+  if (!topk_ids || !local_ids) return MOE_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(localize_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0, as_stream(stream),
+                     topk_ids, n, e_begin, e_stride, e_count, local_ids);
+  return launch_status();
 }
 }  // namespace
 }  // namespace moe
 
 extern "C" moe_status moe_localize_ids(const int32_t* topk_ids, int64_t n, int32_t e_begin, int32_t e_count,
                                        int32_t* local_ids, void* stream) {
-  if (n < 0 || e_begin < 0 || e_count < 1) return MOE_ERR_INVALID_ARG;
-  if (e_count > moe::kMaxE) return MOE_ERR_UNSUPPORTED;
-  if (n >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
-  if (n == 0) return MOE_OK;
-  if (!topk_ids || !local_ids) return MOE_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(moe::localize_kernel, dim3(static_cast<unsigned>(moe::ceil_div(n, 256))), dim3(256), 0,
-                     moe::as_stream(stream), topk_ids, n, e_begin, e_count, local_ids);
-  return moe::launch_status();
+  return moe::localize(topk_ids, n, e_begin, 1, e_count, local_ids, stream);
+}
+
+extern "C" moe_status moe_localize_ids_strided(const int32_t* topk_ids, int64_t n, int32_t e_begin,
+                                               int32_t e_stride, int32_t e_count, int32_t* local_ids,
+                                               void* stream) {
+  return moe::localize(topk_ids, n, e_begin, e_stride, e_count, local_ids, stream);
 }

@@ -922,6 +922,19 @@ def test_localize_ids(gpu):
     assert (out.cpu().numpy() == ref).all()
 
 
+def test_localize_ids_strided(gpu):
+    """A share holding every 8th expert from expert 3 (3, 11, ..., 59), and
+    masked input pairs (-1) staying masked."""
+    rng = np.random.default_rng(12)
+    ids = rng.integers(-1, 64, size=(257, 8)).astype(np.int32)
+    out = torch.empty(ids.shape, dtype=torch.int32, device=gpu)
+    B().localize_ids(_i32(ids), 3, 7, out, e_stride=8)        # 3 .. 51: expert 59 is not held
+    torch.cuda.synchronize()
+    held = (ids >= 3) & ((ids - 3) % 8 == 0) & ((ids - 3) // 8 < 7)
+    ref = np.where(held, (ids - 3) // 8, -1)
+    assert (out.cpu().numpy() == ref).all()
+
+
 @pytest.mark.parametrize("T,E,k,s", [(300, 8, 4, 1), (2000, 16, 8, 2), (5, 4, 6, 3)])
 def test_permute_masked_pairs(gpu, T, E, k, s):
     """Pairs with ids outside [0, E) get no row and inv_perm -1; the held
@@ -948,11 +961,12 @@ def test_permute_masked_pairs(gpu, T, E, k, s):
     assert (inv.cpu().numpy() == ref_inv).all()
 
 
-def _partition_sum(wl, inp, xs, mode, split_shared, n=4):
+def _partition_sum(wl, inp, xs, mode, split_shared, n=4, interleave=False):
     """n expert-parallel shares of the layer on tokens xs (router over all
-    experts, each share holding 1/n of the expert weights; the shared
-    expert on share 0, or on every share for 1/n of the tokens): their
-    partial outputs sum to the oracle's layer output."""
+    experts, each share holding 1/n of the expert weights -- a contiguous
+    block, or with interleave every n-th expert; the shared expert on share
+    0, or on every share for 1/n of the tokens): their partial outputs sum
+    to the oracle's layer output."""
     full = U.device_weights(wl, inp)
     x = U.dev_tensor(xs, wl.dtype)
     T = xs.shape[0]
@@ -961,10 +975,11 @@ def _partition_sum(wl, inp, xs, mode, split_shared, n=4):
     first = None
     for g in range(n):
         holds = split_shared or g == 0
-        w = B().MoeWeights(full.w_router, full.bias, full.w_gate_up[g * ec:(g + 1) * ec],
-                           full.w_down[g * ec:(g + 1) * ec],
+        sel = slice(g, None, n) if interleave else slice(g * ec, (g + 1) * ec)
+        w = B().MoeWeights(full.w_router, full.bias, full.w_gate_up[sel].contiguous(),
+                           full.w_down[sel].contiguous(),
                            full.shared_gate_up if holds else None, full.shared_down if holds else None)
-        layer = B().MoeLayer(w, wl.k, wl.score, mode=mode, experts=(g * ec, ec),
+        layer = B().MoeLayer(w, wl.k, wl.score, mode=mode, experts=(g, ec, n) if interleave else (g * ec, ec),
                              shared_part=(g, n) if split_shared else None)
         y = layer.forward(x)
         torch.cuda.synchronize()
@@ -995,6 +1010,18 @@ def test_expert_parallel_partition_sum(gpu, name, mode):
     if mode in ("decode", "batched") and wl.P > 1024:
         pytest.skip("decode and batched calls take at most 1024 rows")
     _partition_sum(wl, inp, np.asarray(inp["x"]), mode, split_shared=False)
+
+
+@pytest.mark.parametrize("name,mode", [("c5s", "grouped"), ("c4s", "grouped"), ("c3s_t37", "decode"),
+                                       ("c3s_t37", "batched"), ("c2s", "grouped")])
+def test_expert_parallel_interleaved(gpu, name, mode):
+    """Four expert-parallel shares that each hold every fourth expert
+    (moe_localize_ids_strided), the shared expert split over the shares'
+    token slices where there is one."""
+    wl, inp = U.small_inputs(name)
+    if mode in ("decode", "batched") and wl.P > 1024:
+        pytest.skip("decode and batched calls take at most 1024 rows")
+    _partition_sum(wl, inp, np.asarray(inp["x"]), mode, split_shared=inp["shared"] is not None, interleave=True)
 
 
 @pytest.mark.parametrize("T,mode", [(301, "grouped"), (40, "decode"), (3, "grouped"), (1, "batched"),
