@@ -798,6 +798,108 @@ def test_mxfp4_shapes(gpu, E, rows, K, N):
                    f"mxfp4 Y E={E} K={K}")
 
 
+def _mx_special_scales(rng, E, R, K):
+    """Scale codes 118-122 with a few blocks at the ends of the E8M0 range:
+    255 (NaN) in one block of row 3 of expert 1 and of row 9 of expert 4,
+    0 (2^-127) and 1 (2^-126) in single blocks of other rows."""
+    s = rng.integers(118, 123, size=(E, R, K // 32)).astype(np.uint8)
+    s[1, 3, 0] = 255
+    s[4, 9, K // 32 - 1] = 255
+    s[2, 10, 5] = 0
+    s[3, 20, 2] = 1
+    s[1, 30, 7] = 0
+    return s
+
+
+def _assert_close_by_column(got, ref, what):
+    """NaN exactly where the oracle has NaN; every other output column within
+    the bf16 tolerance of its own oracle column."""
+    got = np.asarray(got, np.float64)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all(), f"{what}: NaN pattern differs"
+    for c in range(ref.shape[1]):
+        ok = ~nan[:, c]
+        if ok.any():
+            U.assert_close(got[ok, c], ref[ok, c], "bf16", f"{what} column {c}")
+
+
+@pytest.mark.parametrize("rows", [6, 64], ids=["vector", "staged"])
+def test_mxfp4_special_scale_codes(gpu, rows):
+    """E8M0 scale codes at the ends of the range through the MXFP4 decode
+    calls (vector form with fewer rows than experts, LDS-staged form with
+    more): a NaN scale makes its weight row NaN and so its output column of
+    every row of that expert; 2^-127 and 2^-126 scales give near-zero
+    blocks; a 2^73 scale (down only, whose output is linear) gives one huge
+    block.  Against the oracle's dequantised weights (OCP MX v1.0 E8M0)."""
+    E, K, N = 8, 1024, 192
+    rng = np.random.default_rng(77)
+    counts = np.zeros(E, np.int64)
+    if rows < E:
+        counts[1:1 + rows] = 1
+    else:
+        counts[:] = rows // E
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    xs = W.gen_matrix((rows, K), seed=78)
+    gq = rng.integers(0, 256, size=(E, 2 * N, K // 2), dtype=np.uint8)
+    gs = _mx_special_scales(rng, E, 2 * N, K)
+    dq = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    ds = _mx_special_scales(rng, E, N, K)
+    ds[5, 40, 3] = 200
+    h = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    y = torch.empty(rows, N, dtype=torch.bfloat16, device=gpu)
+    xd = U.dev_tensor(xs, "bf16")
+    B().gateup_swiglu_mxfp4(xd, None, 1, _mx_dev(gq, gpu), _mx_dev(gs, gpu), _i32(offsets), h)
+    B().down_mxfp4(xd, _mx_dev(dq, gpu), _mx_dev(ds, gpu), _i32(offsets), y)
+    torch.cuda.synchronize()
+    x64 = W.values(xs, "bf16")
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref_h = O.grouped_gate_up_swiglu(x64, O.mxfp4_dequantize(gq, gs), offsets)
+        ref_y = O.grouped_down(x64, O.mxfp4_dequantize(dq, ds), offsets)
+    assert np.isnan(ref_h).any() and np.isnan(ref_y).any()
+    _assert_close_by_column(U.host_values(h), ref_h, "H")
+    _assert_close_by_column(U.host_values(y), ref_y, "Y")
+
+
+def test_mxfp4_special_scale_codes_batched(gpu):
+    """The same scale codes through the batched_mm calls: a pair whose expert
+    has a NaN weight row gets NaN in that column of its gate/up row, and the
+    down call's weighted sum carries a NaN down-projection column into every
+    token that chose that expert."""
+    T, E, k, K, N = 6, 8, 2, 1024, 192
+    rng = np.random.default_rng(79)
+    ids = np.array([[1, 2], [4, 0], [3, 5], [5, 1], [6, 7], [2, 4]], np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(1, keepdims=True)
+    xs = W.gen_matrix((T, K), seed=80)
+    gq = rng.integers(0, 256, size=(E, 2 * N, K // 2), dtype=np.uint8)
+    gs = _mx_special_scales(rng, E, 2 * N, K)
+    dq = rng.integers(0, 256, size=(E, K, N // 2), dtype=np.uint8)
+    ds = rng.integers(118, 123, size=(E, K, N // 32)).astype(np.uint8)
+    ds[4, 9, 0] = 255
+    ds[5, 40, 3] = 200
+    ds[2, 10, 5] = 0
+    h = torch.empty(T * k, N, dtype=torch.bfloat16, device=gpu)
+    xd = U.dev_tensor(xs, "bf16")
+    B().batched_gateup_swiglu_mxfp4(xd, _i32(ids), _mx_dev(gq, gpu), _mx_dev(gs, gpu), h)
+    hs = W.gen_matrix((T * k, N), seed=81, std=0.5)
+    y = torch.empty(T, K, dtype=torch.bfloat16, device=gpu)
+    B().batched_down_combine_mxfp4(U.dev_tensor(hs, "bf16"), _i32(ids), _f32(w), _mx_dev(dq, gpu), _mx_dev(ds, gpu),
+                                   None, y)
+    torch.cuda.synchronize()
+    x64 = W.values(xs, "bf16")
+    flat = ids.reshape(-1)
+    with np.errstate(invalid="ignore", over="ignore"):
+        gu64 = O.mxfp4_dequantize(gq, gs)
+        dn64 = O.mxfp4_dequantize(dq, ds)
+        ref_h = np.stack([O.gate_up_swiglu(x64[p // k][None], gu64[flat[p]])[0] for p in range(T * k)])
+        h64 = W.values(hs, "bf16")
+        yk = np.stack([O.down(h64[p][None], dn64[flat[p]])[0] for p in range(T * k)])
+        ref_y = O.unpermute_combine(yk, np.arange(T * k), w, None)
+    assert np.isnan(ref_h).any() and np.isnan(ref_y).any()
+    _assert_close_by_column(U.host_values(h), ref_h, "batched H")
+    _assert_close_by_column(U.host_values(y), ref_y, "batched Y")
+
+
 @pytest.mark.parametrize("mode", ["auto", "decode"])
 @pytest.mark.parametrize("name", ["c3mxs_t1", "c3mxs_t37", "c3mxm_t37"])
 def test_layer_mxfp4(gpu, name, mode):
