@@ -180,13 +180,15 @@ def load_traffic(kernel: str, workload: str):
 
 
 def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared: bool = False, share: int = 1,
-          split_shared: bool = False, share_index: int = 0, interleave: bool = False):
+          split_shared: bool = False, share_index: int = 0, interleave: bool = False, balanced: bool = False):
     """Upload the workload's seeded inputs to the GPU and build the layer.
     With keep_host, the storage-format expert weights stay in host memory
     too (for the CPU oracle leg; the DeepSeek-shaped layer holds 22.5 GB).
     share > 1: one GPU's expert-parallel share of the layer, share_index
     I of them -- experts [I E/share, (I + 1) E/share), or with interleave
-    the experts I, I + share, I + 2 share, ..., and the shared expert on
+    the experts I, I + share, I + 2 share, ..., or with balanced the
+    experts placement.balanced_shares gives share I from the routed load of
+    a calibration batch (calibration_loads), and the shared expert on
     share 0 (with split_shared, on every share for its 1/share of the
     tokens) -- with every token routed."""
     import torch
@@ -214,12 +216,16 @@ def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared
     e0 = share_index if interleave else share_index * E_loc
     stride = share if interleave else 1
     held = [e0 + j * stride for j in range(E_loc)]          # global ids in local order
+    if balanced:
+        from mixture_experts_ffn_04_amd.placement import balanced_shares
+        held = balanced_shares(calibration_loads(wl, device, wr, bias, dev), share)[share_index]
+    local = {e: j for j, e in enumerate(held)}
     gu = torch.empty(E_loc, 2 * wl.f, wl.d, dtype=tdt, device=device)
     dn = torch.empty(E_loc, wl.d, wl.f, dtype=tdt, device=device)
     host_experts = {}
     for e, g, w in W.iter_experts(wl, held):
-        gu[(e - e0) // stride].copy_(dev(g))
-        dn[(e - e0) // stride].copy_(dev(w))
+        gu[local[e]].copy_(dev(g))
+        dn[local[e]].copy_(dev(w))
         if keep_host:
             host_experts[e] = (g, w)
     sh = W.gen_shared(wl)
@@ -227,11 +233,27 @@ def setup(wl, device, keep_host: bool = True, mode: str = "auto", overlap_shared
         sh = None                                   # the shared expert lives on share 0
     weights = MoeWeights(dev(wr), None if bias is None else torch.from_numpy(bias).to(device), gu, dn,
                          None if sh is None else dev(sh[0]), None if sh is None else dev(sh[1]))
+    where = {} if share == 1 else dict(expert_ids=held) if balanced else dict(experts=(e0, E_loc, stride))
     layer = MoeLayer(weights, wl.k, wl.score, mode=mode, overlap_shared=overlap_shared,
-                     experts=None if share == 1 else (e0, E_loc, stride),
-                     shared_part=(share_index, share) if split_shared and share > 1 else None)
+                     shared_part=(share_index, share) if split_shared and share > 1 else None, **where)
     host = dict(x=x, wr=wr, bias=bias, experts=host_experts, shared=sh)
     return layer, dev(x), host
+
+
+def calibration_loads(wl, device, wr, bias, dev):
+    """Routed rows per expert for a calibration batch: T tokens drawn like
+    the workload's own but from another seed, routed by the library on the
+    GPU (the load statistics an expert placement is made from; the timed
+    batch is not used)."""
+    import torch
+    from mixture_experts_ffn_04_amd import binding
+    xc = dev(W.gen_x(wl.replace(seed=wl.seed + 7919)))
+    logits = torch.empty(wl.T, wl.E, device=device, dtype=torch.float32)
+    ids = torch.empty(wl.T, wl.k, device=device, dtype=torch.int32)
+    wts = torch.empty(wl.T, wl.k, device=device, dtype=torch.float32)
+    binding.route(xc, dev(wr), None if bias is None else torch.from_numpy(bias).to(device), wl.k, wl.score,
+                  logits, ids, wts)
+    return torch.bincount(ids.view(-1).long(), minlength=wl.E).cpu().numpy()
 
 
 # ------------------------------------------------------------ CPU oracle
@@ -617,6 +639,9 @@ def main(argv=None):
                     help="with --ep-share N: time share I (experts [I E/N, (I + 1) E/N)) instead of share 0")
     ap.add_argument("--ep-interleave", action="store_true",
                     help="with --ep-share N: share I holds the experts I, I + N, I + 2N, ... instead of a block")
+    ap.add_argument("--ep-balanced", action="store_true",
+                    help="with --ep-share N: share I holds the experts that a load-balanced placement gives it "
+                         "from the routed load of a calibration batch (T tokens of another seed)")
     ap.add_argument("--split-shared", action="store_true",
                     help="with --ep-share N: every share runs the shared expert on 1/N of the tokens (share I on "
                          "tokens [T I/N, T (I + 1)/N)) instead of share 0 on all of them")
@@ -671,8 +696,12 @@ def main(argv=None):
             return 2
         args.no_cpu = True          # the oracle leg needs every expert
 
-    if (args.split_shared or args.ep_index or args.ep_interleave) and share == 1:
-        print("--split-shared, --ep-index and --ep-interleave go with --ep-share N (N > 1)", file=sys.stderr)
+    if (args.split_shared or args.ep_index or args.ep_interleave or args.ep_balanced) and share == 1:
+        print("--split-shared, --ep-index, --ep-interleave and --ep-balanced go with --ep-share N (N > 1)",
+              file=sys.stderr)
+        return 2
+    if args.ep_interleave and args.ep_balanced:
+        print("--ep-interleave and --ep-balanced are two different placements: pass one", file=sys.stderr)
         return 2
     if not 0 <= args.ep_index < share:
         print("--ep-index I needs 0 <= I < N", file=sys.stderr)
@@ -683,7 +712,7 @@ def main(argv=None):
     device = torch.device("cuda:0")
     layer, x, host = setup(wl, device, keep_host=not args.no_cpu, mode=args.mode,
                            overlap_shared=args.overlap_shared, share=share, split_shared=args.split_shared,
-                           share_index=args.ep_index, interleave=args.ep_interleave)
+                           share_index=args.ep_index, interleave=args.ep_interleave, balanced=args.ep_balanced)
     # the shared expert's tokens here
     ts0, ts1 = wl.T * args.ep_index // share, wl.T * (args.ep_index + 1) // share
     Ts = ts1 - ts0 if args.split_shared else (0 if args.ep_index else None)
@@ -767,7 +796,10 @@ def main(argv=None):
     roof["kernel"] = kname
     roof["traffic"] = load_traffic(kname, wl.name) if share == 1 else None   # taken on the whole layer
 
-    if args.ep_interleave:
+    if args.ep_balanced:
+        experts_desc = (f"{(layer.emap >= 0).nonzero().view(-1).tolist()} (placed by the "
+                        f"routed load of a calibration batch)")
+    elif args.ep_interleave:
         experts_desc = f"{args.ep_index}, {args.ep_index + share}, ... (every {share}th)"
     else:
         experts_desc = f"{args.ep_index * (wl.E // share)}..{(args.ep_index + 1) * (wl.E // share) - 1}"

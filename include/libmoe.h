@@ -26,6 +26,7 @@
  *   moe_unpermute_combine            weighted combine back to token order
  *   moe_localize_ids                 expert-parallel share: global ids to
  *   moe_localize_ids_strided         local ones, other experts masked
+ *   moe_localize_ids_mapped          (a block, every N-th expert, or any set)
  *   moe_decode_gateup_swiglu         small-batch variants that stream only
  *   moe_decode_gateup_swiglu_gather  the active experts' weights (the
  *   moe_decode_down                  _gather form reads the rows through
@@ -277,6 +278,26 @@ MOE_API moe_status moe_localize_ids(const int32_t* topk_ids, int64_t n, int32_t 
 MOE_API moe_status moe_localize_ids_strided(const int32_t* topk_ids, int64_t n, int32_t e_begin,
                                             int32_t e_stride, int32_t e_count, int32_t* local_ids,
                                             void* stream);
+
+/*
+ * moe_localize_ids for a share that holds any set of e_count experts, in
+ * an order of the caller's choice (for instance an assignment that spreads
+ * the most loaded experts over the shares first; the article's section
+ * "Expert Parallelism" gives each device E/N experts without fixing which):
+ *   local_ids[i] = expert_map[topk_ids[i]]   if 0 <= topk_ids[i] < num_experts
+ *                                            and 0 <= that entry < e_count
+ *                = -1                        otherwise
+ * expert_map [num_experts] int32 (device, read only) gives each global
+ * expert's local id, or -1 for an expert held elsewhere; the share's packed
+ * expert weights hold its experts in local-id order, and no two experts
+ * should share a local id (the pairs of both would run on one expert's
+ * weights).  topk_ids, local_ids [n] int32 (device).  1 <= num_experts <=
+ * 256 and 1 <= e_count <= 256, else MOE_ERR_INVALID_ARG /
+ * MOE_ERR_UNSUPPORTED; n = 0 launches nothing.
+ */
+MOE_API moe_status moe_localize_ids_mapped(const int32_t* topk_ids, int64_t n, const int32_t* expert_map,
+                                           int32_t num_experts, int32_t e_count, int32_t* local_ids,
+                                           void* stream);
 
 /*
  * moe_grouped_gemm_gateup_swiglu with the row gather of moe_permute folded

@@ -5,3 +5,4 @@ include/libmoe.h (built into libmoe.so); `binding` is the Python binding.
 """
 from . import binding  # noqa: F401
 from .binding import MoeLayer, MoeLayerGraph, MoeWeights  # noqa: F401
+from .placement import balanced_shares, expert_map  # noqa: F401

@@ -14,6 +14,8 @@ from typing import Optional
 
 import torch
 
+from .placement import expert_map
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
@@ -26,7 +28,7 @@ EXPORTS = (
     "moe_permute_workspace_size", "moe_permute", "moe_grouped_gemm_gateup_swiglu",
     "moe_grouped_gemm_down", "moe_unpermute_combine", "moe_decode_gateup_swiglu",
     "moe_decode_down", "moe_decode_gateup_swiglu_gather", "moe_grouped_gemm_gateup_swiglu_gather",
-    "moe_localize_ids", "moe_localize_ids_strided", "moe_permute_noalloc", "moe_batched_gateup_swiglu",
+    "moe_localize_ids", "moe_localize_ids_strided", "moe_localize_ids_mapped", "moe_permute_noalloc", "moe_batched_gateup_swiglu",
     "moe_batched_down_combine",
     "moe_decode_gateup_swiglu_mxfp4", "moe_decode_down_mxfp4", "moe_batched_gateup_swiglu_mxfp4",
     "moe_batched_down_combine_mxfp4", "moe_batched_gateup_swiglu_select", "moe_batched_gateup_swiglu_mxfp4_select",
@@ -53,6 +55,7 @@ _SIGS = {
                                               ctypes.c_int),
     "moe_localize_ids": ([P, I64, I32, I32, P, P], ctypes.c_int),
     "moe_localize_ids_strided": ([P, I64, I32, I32, I32, P, P], ctypes.c_int),
+    "moe_localize_ids_mapped": ([P, I64, P, I32, I32, P, P], ctypes.c_int),
     "moe_permute_noalloc": ([P, P, I64, I64, I32, I32, ctypes.c_int, P, P, P, P, P, P], ctypes.c_int),
     "moe_batched_gateup_swiglu": ([P, P, P, I64, I64, I64, I32, I32, ctypes.c_int, P, P], ctypes.c_int),
     "moe_batched_down_combine": ([P, P, P, P, P, I64, I64, I64, I32, I32, ctypes.c_int, P, P], ctypes.c_int),
@@ -148,6 +151,14 @@ def localize_ids(topk_ids, e_begin: int, e_count: int, local_ids, e_stride: int 
     else:
         _check("moe_localize_ids_strided", load().moe_localize_ids_strided(
             _ptr(topk_ids), topk_ids.numel(), e_begin, e_stride, e_count, _ptr(local_ids), _stream(stream)))
+
+
+def localize_ids_mapped(topk_ids, expert_map, e_count: int, local_ids, stream=None):
+    """Expert-parallel share holding any set of experts: global id e ->
+    expert_map[e] (int32 [E] on the device, -1 for experts held elsewhere)."""
+    _check("moe_localize_ids_mapped", load().moe_localize_ids_mapped(
+        _ptr(topk_ids), topk_ids.numel(), _ptr(expert_map), expert_map.numel(), e_count, _ptr(local_ids),
+        _stream(stream)))
 
 
 def permute_workspace_size(T: int, k: int, E: int) -> int:
@@ -327,7 +338,9 @@ class MoeLayer:
     e_stride, ..., in that order: an interleaved assignment), and
     forward returns the share's partial output (the pairs of other experts
     masked by moe_localize_ids); the partial outputs of all shares sum to
-    the layer's output.
+    the layer's output.  expert_ids=[e0, e1, ...] instead names any set of
+    global experts that the weights hold, in that order (moe_localize_ids_mapped;
+    see placement.balanced_shares).
 
     shared_part=(i, n) runs the shared expert (when the weights hold it)
     on tokens [T i / n, T (i + 1) / n) only, so that n shares that each
@@ -339,7 +352,7 @@ class MoeLayer:
 
     def __init__(self, weights: MoeWeights, k: int, score: str, mode: str = "auto",
                  experts: Optional[tuple] = None, overlap_shared: bool = False,
-                 shared_part: Optional[tuple] = None):
+                 shared_part: Optional[tuple] = None, expert_ids=None):
         load()
         self.w = weights
         # the shared expert does not depend on the routing: with
@@ -353,7 +366,17 @@ class MoeLayer:
         self.mode = mode
         self.E, self.d = weights.w_router.shape          # experts seen by the router
         self.E_loc = weights.w_gate_up.shape[0]          # experts held here
-        if experts is None:
+        self.emap = None
+        if experts is not None and expert_ids is not None:
+            raise ValueError("pass experts=(e_begin, e_count[, e_stride]) or expert_ids, not both")
+        if expert_ids is not None:
+            held = [int(e) for e in expert_ids]
+            if len(held) != self.E_loc:
+                raise ValueError("expert_ids must name as many experts as the weights hold")
+            self.emap = torch.tensor(expert_map(held, self.E), dtype=torch.int32, device=weights.w_router.device)
+            self.e_begin = 0                             # a share: ids are localised
+            self.e_stride = 1
+        elif experts is None:
             if self.E_loc != self.E:
                 raise ValueError("expert weights cover a share of the experts: pass experts=(e_begin, e_count)")
             self.e_begin = None
@@ -410,6 +433,11 @@ class MoeLayer:
             self.s_y = (torch.zeros if (t0, t1) != (0, T) else torch.empty)(T, d, device=dev, dtype=dt)
         self._T = T
 
+    def _localize_stage(self, st) -> tuple:
+        if self.emap is not None:
+            return ("localize", localize_ids_mapped, (self.ids, self.emap, self.E_loc, self.lids, st))
+        return ("localize", localize_ids, (self.ids, self.e_begin, self.E_loc, self.lids, self.e_stride, st))
+
     def shared_rows(self, T: int) -> tuple:
         """The tokens [t0, t1) this layer runs the shared expert on."""
         if self.shared_part is None:
@@ -450,7 +478,7 @@ class MoeLayer:
         out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st))]
         ids = self.ids
         if self.e_begin is not None:
-            out.append(("localize", localize_ids, (self.ids, self.e_begin, self.E_loc, self.lids, self.e_stride, st)))
+            out.append(self._localize_stage(st))
             ids = self.lids
         out += [
             ("permute", permute, (ids, x, self.E_loc, self.counts, self.offsets, self.perm, self.inv_perm,
@@ -501,7 +529,7 @@ class MoeLayer:
             out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, None, None, st))]
         else:
             out = [("route", route, (x, w.w_router, w.bias, self.k, self.score, self.logits, self.ids, self.wts, st)),
-                   ("localize", localize_ids, (self.ids, self.e_begin, self.E_loc, self.lids, self.e_stride, st))]
+                   self._localize_stage(st)]
             ids = self.lids
         ys = None
         if w.shared_gate_up is not None:

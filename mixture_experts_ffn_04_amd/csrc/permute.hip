@@ -427,6 +427,30 @@ moe_status localize(const int32_t* topk_ids, int64_t n, int32_t e_begin, int32_t
                      topk_ids, n, e_begin, e_stride, e_count, local_ids);
   return launch_status();
 }
+// Any assignment of experts to the share: emap[e] is global expert e's
+// local id, negative where another share holds it.  Router ids outside
+// [0, E) and map entries outside [0, e_count) give -1 as well.
+__global__ __launch_bounds__(256) void localize_map_kernel(const int32_t* __restrict__ ids, int64_t n,
+                                                           const int32_t* __restrict__ emap, int E, int e_count,
+                                                           int32_t* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int e = ids[i];
+  const int j = (e >= 0 && e < E) ? emap[e] : -1;
+  out[i] = (j >= 0 && j < e_count) ? j : -1;
+}
+
+moe_status localize_map(const int32_t* topk_ids, int64_t n, const int32_t* expert_map, int32_t E,
+                        int32_t e_count, int32_t* local_ids, void* stream) {
+  if (n < 0 || E < 1 || e_count < 1) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE || e_count > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (n >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (n == 0) return MOE_OK;
+  if (!topk_ids || !expert_map || !local_ids) return MOE_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(localize_map_kernel, dim3(static_cast<unsigned>(ceil_div(n, 256))), dim3(256), 0,
+                     as_stream(stream), topk_ids, n, expert_map, E, e_count, local_ids);
+  return launch_status();
+}
 }  // namespace
 }  // namespace moe
 
@@ -439,4 +463,10 @@ extern "C" moe_status moe_localize_ids_strided(const int32_t* topk_ids, int64_t 
                                                int32_t e_stride, int32_t e_count, int32_t* local_ids,
                                                void* stream) {
   return moe::localize(topk_ids, n, e_begin, e_stride, e_count, local_ids, stream);
+}
+
+extern "C" moe_status moe_localize_ids_mapped(const int32_t* topk_ids, int64_t n, const int32_t* expert_map,
+                                              int32_t num_experts, int32_t e_count, int32_t* local_ids,
+                                              void* stream) {
+  return moe::localize_map(topk_ids, n, expert_map, num_experts, e_count, local_ids, stream);
 }

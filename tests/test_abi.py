@@ -94,6 +94,13 @@ def test_validation_without_gpu(lib):
     assert lib.moe_localize_ids_strided(P, 10, 1, 8, 0, P, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_localize_ids_strided(P, 10, 0, 2, 257, P, None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_localize_ids_strided(None, 0, 3, 8, 32, None, None) == B.MOE_OK
+    assert lib.moe_localize_ids_mapped(P, 10, P, 0, 4, P, None) == B.MOE_ERR_INVALID_ARG      # no experts
+    assert lib.moe_localize_ids_mapped(P, 10, P, 64, 0, P, None) == B.MOE_ERR_INVALID_ARG     # none held
+    assert lib.moe_localize_ids_mapped(P, -1, P, 64, 8, P, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_localize_ids_mapped(P, 10, P, 257, 8, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_localize_ids_mapped(P, 10, P, 64, 257, P, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_localize_ids_mapped(P, 10, None, 64, 8, P, None) == B.MOE_ERR_INVALID_ARG  # no map
+    assert lib.moe_localize_ids_mapped(None, 0, None, 64, 8, None, None) == B.MOE_OK
     g = lib.moe_decode_gateup_swiglu_gather
     assert g(P, P, 3, P, P, 100, 128, 128, 8, 1, P, None) == B.MOE_ERR_INVALID_ARG     # rows % k != 0
     assert g(P, P, 0, P, P, 100, 128, 128, 8, 1, P, None) == B.MOE_ERR_INVALID_ARG     # k < 1

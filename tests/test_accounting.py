@@ -50,6 +50,8 @@ def test_share_options_refused_before_any_gpu_work(capsys):
     assert bench.main(["--workload", "c3mx_t8", "--mode", "grouped"]) == 2
     assert bench.main(["--ep-index", "1"]) == 2
     assert bench.main(["--ep-share", "4", "--ep-index", "4", "--workload", "c5"]) == 2
+    assert bench.main(["--ep-balanced"]) == 2
+    assert bench.main(["--ep-share", "8", "--ep-balanced", "--ep-interleave"]) == 2
 
 
 def test_layer_flops_shared_slice():

@@ -54,6 +54,9 @@ int main(void) {
   EXPECT(moe_localize_ids(NULL, 0, 0, 4, NULL, NULL), MOE_OK);
   EXPECT(moe_localize_ids_strided(p, 10, 0, 0, 4, p, NULL), MOE_ERR_INVALID_ARG);
   EXPECT(moe_localize_ids_strided(p, 10, 0, 2, 257, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_localize_ids_mapped(p, 10, NULL, 64, 8, p, NULL), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_localize_ids_mapped(p, 10, p, 257, 8, p, NULL), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_localize_ids_mapped(NULL, 0, NULL, 64, 8, NULL, NULL), MOE_OK);
   /* projections */
   moe_status (*proj[4])(const void*, const void*, const int32_t*, int64_t, int64_t, int64_t, int32_t, moe_dtype,
                         void*, void*) = {moe_grouped_gemm_gateup_swiglu, moe_grouped_gemm_down,

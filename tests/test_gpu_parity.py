@@ -1063,12 +1063,13 @@ def test_permute_masked_pairs(gpu, T, E, k, s):
     assert (inv.cpu().numpy() == ref_inv).all()
 
 
-def _partition_sum(wl, inp, xs, mode, split_shared, n=4, interleave=False):
+def _partition_sum(wl, inp, xs, mode, split_shared, n=4, interleave=False, placement=None):
     """n expert-parallel shares of the layer on tokens xs (router over all
     experts, each share holding 1/n of the expert weights -- a contiguous
-    block, or with interleave every n-th expert; the shared expert on share
-    0, or on every share for 1/n of the tokens): their partial outputs sum
-    to the oracle's layer output."""
+    block, with interleave every n-th expert, or with placement the listed
+    global experts in the listed order; the shared expert on share 0, or on
+    every share for 1/n of the tokens): their partial outputs sum to the
+    oracle's layer output."""
     full = U.device_weights(wl, inp)
     x = U.dev_tensor(xs, wl.dtype)
     T = xs.shape[0]
@@ -1077,12 +1078,17 @@ def _partition_sum(wl, inp, xs, mode, split_shared, n=4, interleave=False):
     first = None
     for g in range(n):
         holds = split_shared or g == 0
-        sel = slice(g, None, n) if interleave else slice(g * ec, (g + 1) * ec)
+        if placement is not None:
+            sel = torch.tensor(placement[g], dtype=torch.int64, device=full.w_gate_up.device)
+            share = dict(expert_ids=placement[g])
+        elif interleave:
+            sel, share = slice(g, None, n), dict(experts=(g, ec, n))
+        else:
+            sel, share = slice(g * ec, (g + 1) * ec), dict(experts=(g * ec, ec))
         w = B().MoeWeights(full.w_router, full.bias, full.w_gate_up[sel].contiguous(),
                            full.w_down[sel].contiguous(),
                            full.shared_gate_up if holds else None, full.shared_down if holds else None)
-        layer = B().MoeLayer(w, wl.k, wl.score, mode=mode, experts=(g, ec, n) if interleave else (g * ec, ec),
-                             shared_part=(g, n) if split_shared else None)
+        layer = B().MoeLayer(w, wl.k, wl.score, mode=mode, shared_part=(g, n) if split_shared else None, **share)
         y = layer.forward(x)
         torch.cuda.synchronize()
         total += U.host_values(y)
@@ -1124,6 +1130,48 @@ def test_expert_parallel_interleaved(gpu, name, mode):
     if mode in ("decode", "batched") and wl.P > 1024:
         pytest.skip("decode and batched calls take at most 1024 rows")
     _partition_sum(wl, inp, np.asarray(inp["x"]), mode, split_shared=inp["shared"] is not None, interleave=True)
+
+
+@pytest.mark.parametrize("name,mode,order", [("c5s", "grouped", "id"), ("c4s", "grouped", "reversed"),
+                                             ("c3s_t37", "decode", "reversed"), ("c3s_t37", "batched", "id"),
+                                             ("c2s", "grouped", "reversed")])
+def test_expert_parallel_balanced(gpu, name, mode, order):
+    """Four expert-parallel shares placed by routed load
+    (placement.balanced_shares over the oracle's routing of these tokens),
+    each holding its experts in increasing or decreasing global id
+    (moe_localize_ids_mapped), the shared expert split over the shares'
+    token slices where there is one."""
+    wl, inp = U.small_inputs(name)
+    if mode in ("decode", "batched") and wl.P > 1024:
+        pytest.skip("decode and batched calls take at most 1024 rows")
+    xs = np.asarray(inp["x"])
+    x64, wr = W.values(xs, wl.dtype), W.values(inp["wr"], wl.dtype)
+    ids, _ = O.route(O.router_logits(x64, wr, inp["bias"]), wl.k, wl.score)
+    from mixture_experts_ffn_04_amd.placement import balanced_shares
+    shares = balanced_shares(np.bincount(ids.ravel(), minlength=wl.E), 4)
+    if order == "reversed":
+        shares = [h[::-1] for h in shares]
+    _partition_sum(wl, inp, xs, mode, split_shared=inp["shared"] is not None, placement=shares)
+
+
+def test_localize_ids_mapped(gpu):
+    """Any expert set: a seeded choice of 24 of 64 experts in a seeded
+    order; masked (-1) and out-of-range router ids and map entries at or
+    past e_count give -1."""
+    rng = np.random.default_rng(13)
+    E = 64
+    held = rng.permutation(E)[:24]
+    emap = np.full(E, -1, np.int32)
+    emap[held] = np.arange(24, dtype=np.int32)
+    emap[held[5]] = 30                                   # past e_count = 24: masked
+    ids = rng.integers(-2, E + 3, size=(333, 8)).astype(np.int32)
+    out = torch.empty(ids.shape, dtype=torch.int32, device=gpu)
+    B().localize_ids_mapped(_i32(ids), _i32(emap), 24, out)
+    torch.cuda.synchronize()
+    inside = (ids >= 0) & (ids < E)
+    ref = np.where(inside, emap[np.clip(ids, 0, E - 1)], -1)
+    ref = np.where((ref >= 0) & (ref < 24), ref, -1)
+    assert (out.cpu().numpy() == ref).all()
 
 
 @pytest.mark.parametrize("T,mode", [(301, "grouped"), (40, "decode"), (3, "grouped"), (1, "batched"),
