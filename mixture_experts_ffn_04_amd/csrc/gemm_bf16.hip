@@ -667,6 +667,9 @@ __global__ __launch_bounds__(64 * WM * WN, (WS == 2 ? 3 : 1) * WM * WN / 4) void
 // than the remainder tile it replaces.
 constexpr int64_t kFatMinK = 4096;
 
+// Short K loops walk the tile order in four interleaved quarters.
+constexpr int64_t kQuarterMaxK = 1024;
+
 template <int BM, int BN, int WM, int WN, int EPI, int SN, int BK, int SP = 1, int LDS_EPI = 0, int WS = 3>
 moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   constexpr int BNO = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
@@ -675,6 +678,7 @@ moe_status launch_dtl(const GemmArgs& a, hipStream_t st) {
   GemmArgs b = a;
   b.adapt_rows = 0;
   b.fat_rows = (BM == 256 && WM == 2 && EPI != EPI_F32B && a.K >= kFatMinK) ? 1 : 0;   // fat tiles: fewer tiles
+  b.quarters = (EPI != EPI_F32B && a.K < kQuarterMaxK) ? 1 : 0;
   int64_t grid = grouped_tile_bound(a.rows, a.G, BM, a.N, BNO);
   if (EPI != EPI_F32B && BM >= 32 * kRowChoices && grid < int64_t(kAdaptRounds) * kComputeUnits) {
     b.adapt_rows = 1;

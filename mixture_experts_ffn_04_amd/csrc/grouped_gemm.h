@@ -67,6 +67,9 @@ struct GemmArgs {
   // group's last remainder of at most kFatExtraRows rows is shared out over
   // its other row tiles, which then hold up to BM + kFatExtraRows rows.
   int fat_rows;
+  // Set by the launcher, not by callers: slots walk the tile order in 4
+  // interleaved quarters instead of 2 halves (tile_order).
+  int quarters;
 };
 
 constexpr int kComputeUnits = 256;   // MI355X: compute units, one tile workgroup each
@@ -207,7 +210,12 @@ __device__ __forceinline__ int scan_tiles(const GemmArgs& a, int& lo, int& hi, i
 // (slots are dealt to the 8 XCDs round-robin) come from a stretch of the
 // order shared with three other XCDs: fewer experts' weights are in flight
 // at once than with one contiguous stretch per XCD.
-__device__ __forceinline__ int tile_order(int bid, int total) {
+// With quarters, slot s walks quarter s mod 4 instead (short K loops).
+__device__ __forceinline__ int tile_order(int bid, int total, bool quarters) {
+  if (quarters) {
+    const int q = total >> 2;
+    return (bid < (q << 2)) ? ((bid & 3) * q + (bid >> 2)) : bid;
+  }
   const int q = total >> 1;
   return (bid < (q << 1)) ? ((bid & 1) * q + (bid >> 1)) : bid;
 }
@@ -273,7 +281,7 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& a, TileLoc& tl, int*
   const int total = scan_tiles<NT, BM, BNO>(a, lo, hi, cnt, excl, tr, scratch, s_red);
   const int bid = static_cast<int>(blockIdx.x);
   if (bid >= total) return false;     // uniform: total is the same in every thread
-  const int L = tile_order(bid, total);
+  const int L = tile_order(bid, total, a.quarters != 0);
   if (static_cast<int>(threadIdx.x) < a.G && cnt > 0 && L >= excl && L < excl + cnt) {
     s_hit[0] = threadIdx.x;
     s_hit[1] = lo;
