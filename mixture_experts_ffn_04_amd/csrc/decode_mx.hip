@@ -198,7 +198,37 @@ __global__ __launch_bounds__(256) void decode_mx_kernel(const uint16_t* __restri
 // h[p][n] for p < P: workgroup = (pair p, 8 output columns), two per wave.
 // S > 0: the experts are selected here from the router logits [T][E] (every
 // wave runs its token's selection), and the first workgroup of each token
-// writes the token's ids and weights.
+// writes the token's ids and weights.  The token's activation row is read
+// once per workgroup into LDS (its loads issued first, written to LDS after
+// the weight loads are issued), so a lane holds only its weight blocks while
+// their loads are in flight: the 5760 waves of one token with four experts
+// of the gpt-oss shape then make one round instead of 1.1 at the five waves
+// per SIMD that register-held activations allowed.  A row of K <= 2048 CI
+// elements is 256 CI chunks of 16 bytes: CI per thread.
+
+template <int CI>
+__device__ __forceinline__ void mx_dot_rows_lds(const u32x4 (&wq)[kMxRows][CI], const uint32_t (&ws)[kMxRows][CI],
+                                                const u32x4* xs, int KB, int lane, float (&acc)[kMxRows]) {
+#pragma unroll
+  for (int r = 0; r < kMxRows; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CI; ++i) {
+    const int b = lane + 64 * i;
+    if (b < KB) {
+      u32x4 xv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xv[c] = xs[b * 4 + c];
+#pragma unroll
+      for (int r = 0; r < kMxRows; ++r) acc[r] = fmaf(block_dot(wq[r][i], xv), e8m0_to_f32(ws[r][i]), acc[r]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+    for (int r = 0; r < kMxRows; ++r) acc[r] += __shfl_xor(acc[r], o, 64);
+  }
+}
+
 template <int CI, int S>
 __global__ __launch_bounds__(256) void batched_mx_gateup_kernel(const uint16_t* __restrict__ x,
                                                                 int32_t* __restrict__ ids,
@@ -211,7 +241,16 @@ __global__ __launch_bounds__(256) void batched_mx_gateup_kernel(const uint16_t* 
   const int ncb = N / CPB;
   const int p = blockIdx.x / ncb;
   const int cb = blockIdx.x - p * ncb;
-  if (p >= P) return;
+  if (p >= P) return;                                    // uniform over the workgroup
+  // the token's row: K / 8 chunks of 16 bytes, at most CI per thread
+  const uint16_t* xr = x + static_cast<int64_t>(p / k) * K;
+  const int nx = K / 8;
+  u32x4 xc[CI];
+#pragma unroll
+  for (int i = 0; i < CI; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nx) xc[i] = *(const gu4*)(xr + c * 8);
+  }
   int e;
   if constexpr (S > 0) {
     const int t = p / k, j = p - t * k;
@@ -224,7 +263,7 @@ __global__ __launch_bounds__(256) void batched_mx_gateup_kernel(const uint16_t* 
   } else {
     e = ids[p];
   }
-  if (e < 0 || e >= E) return;                           // a pair of an expert held elsewhere
+  if (e < 0 || e >= E) return;                           // a pair of an expert held elsewhere (uniform)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = cb * CPB + wave * CPW;
   const int KB = K / 32;
@@ -234,10 +273,15 @@ __global__ __launch_bounds__(256) void batched_mx_gateup_kernel(const uint16_t* 
   uint32_t ws[kMxRows][CI];
   mx_load_rows<CI>(Bq + static_cast<int64_t>(e) * 2 * N * (K / 2), Bs + static_cast<int64_t>(e) * 2 * N * KB, wr, K,
                    KB, lane, wq, ws);
-  u32x4 xv[CI][4];
-  mx_load_x<CI>(x + static_cast<int64_t>(p / k) * K, KB, lane, xv);
+  __shared__ u32x4 xs[256 * CI];
+#pragma unroll
+  for (int i = 0; i < CI; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nx) xs[c] = xc[i];
+  }
+  __syncthreads();
   float acc[kMxRows];
-  mx_dot_rows<CI>(wq, ws, xv, KB, lane, acc);
+  mx_dot_rows_lds<CI>(wq, ws, xs, KB, lane, acc);
   mx_store<true>(acc, lane, h + static_cast<int64_t>(p) * N + n0);
 }
 
